@@ -1,1 +1,7 @@
-"""Chunked gated delta-rule forward (KDA / Gated DeltaNet) for MI355X."""
+"""Chunked gated delta-rule forward (KDA / Gated DeltaNet) for MI355X (gfx950).
+
+The forward runs in hand-written HIP kernels behind the C interface of
+include/chunk_dr.h (libchunkdr.so); this package is its thin Python binding.
+"""
+from .ops import (chunk_dr_fwd, load_library, workspace_bytes, make_problem, check,  # noqa: F401
+                  STAGE_INTRA, STAGE_CHAIN, STAGE_OUTPUT, STAGE_ALL)

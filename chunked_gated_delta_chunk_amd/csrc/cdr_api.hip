@@ -1,0 +1,169 @@
+// C interface: validation, workspace layout and kernel launches (declared in chunk_dr.h).
+#include "chunk_dr.h"
+#include "cdr_common.h"
+
+namespace cdr {
+hipError_t launch_intra(int C, bool per_dim, const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                        const float* g, const float* beta, const ChunkMap& map, int nslots, int H,
+                        float scale, const Work& ws, hipStream_t stream);
+hipError_t launch_chain(int C, int BV, const ChunkMap& map, int N, int H, const float* s0, float* s_out,
+                        const Work& ws, hipStream_t stream);
+hipError_t launch_output(int C, const ChunkMap& map, int nslots, int H, uint16_t* o, const Work& ws,
+                         hipStream_t stream);
+}  // namespace cdr
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// chunk slots: fixed length B * ceil(T / C); varlen floor(T / C) + N (see ChunkMap)
+int64_t num_slots(const cdr_problem* p) {
+    if (p->varlen) return (int64_t)p->T / p->chunk_size + p->N;
+    return (int64_t)p->B * ((p->T + p->chunk_size - 1) / p->chunk_size);
+}
+
+struct Layout {
+    size_t off[12];
+    size_t total;
+};
+
+Layout layout(const cdr_problem* p) {
+    const size_t nch = (size_t)num_slots(p) * (size_t)p->H;
+    const size_t C = (size_t)p->chunk_size, K = (size_t)p->K, V = (size_t)p->V;
+    const size_t bytes[12] = {
+        nch * C * K * 2,  // w
+        nch * C * V * 4,  // u
+        nch * K * C * 2,  // kgT_hi
+        nch * K * C * 2,  // kgT_lo
+        nch * C * K * 2,  // qg
+        nch * C * C * 2,  // A2
+        nch * K * 4,      // gC
+        nch * V * K * 2,  // Sc
+        nch * V * C * 2,  // vnT
+        nch * K * C * 2,  // bwT_hi
+        nch * K * C * 2,  // bwT_lo
+        nch * V * C * 2,  // vT
+    };
+    Layout L;
+    size_t at = 0;
+    for (int i = 0; i < 12; ++i) {
+        L.off[i] = at;
+        at += align_up(bytes[i]);
+    }
+    L.total = at;
+    return L;
+}
+
+}  // namespace
+
+extern "C" {
+
+cdr_status cdr_check(const cdr_problem* p) {
+    if (p == nullptr) return CDR_ERR_NULL_ARG;
+    if (p->B <= 0 || p->T < 0 || p->H <= 0 || p->N <= 0 || p->K <= 0 || p->V <= 0) return CDR_ERR_BAD_SHAPE;
+    if (p->K != 128 || p->V != 128) return CDR_ERR_UNSUPPORTED;
+    if (p->chunk_size != 64 && p->chunk_size != 128) return CDR_ERR_UNSUPPORTED;
+    if (p->gate != CDR_GATE_PER_DIM && p->gate != CDR_GATE_PER_HEAD) return CDR_ERR_UNSUPPORTED;
+    if (p->varlen) {
+        if (p->B != 1) return CDR_ERR_VARLEN_BATCH;
+    } else if (p->N != p->B) {
+        return CDR_ERR_BAD_SHAPE;
+    }
+    // packed token offsets are int32 on the device side of the interface
+    if ((int64_t)p->B * p->T > INT32_MAX) return CDR_ERR_BAD_SHAPE;
+    if (num_slots(p) * (int64_t)p->H > (int64_t)INT32_MAX) return CDR_ERR_BAD_SHAPE;
+    return CDR_OK;
+}
+
+size_t cdr_workspace_bytes(const cdr_problem* p) {
+    if (cdr_check(p) != CDR_OK) return 0;
+    return layout(p).total;
+}
+
+cdr_status chunk_dr_fwd_stages(const cdr_problem* p, const void* q, const void* k, const void* v,
+                               const float* g, const float* beta, const float* initial_state,
+                               const int32_t* cu_seqlens, void* o, float* final_state, void* workspace,
+                               size_t workspace_bytes, int32_t stages, void* stream) {
+    const cdr_status st = cdr_check(p);
+    if (stages < 1 || stages > CDR_STAGE_ALL) return CDR_ERR_UNSUPPORTED;
+    if (st != CDR_OK) return st;
+    const int64_t tokens = (int64_t)p->B * p->T;
+    if (tokens > 0 && (!q || !k || !v || !g || !beta || !o)) return CDR_ERR_NULL_ARG;
+    if (p->has_initial_state && !initial_state) return CDR_ERR_NULL_ARG;
+    if (p->output_final_state && !final_state) return CDR_ERR_NULL_ARG;
+    if (p->varlen && !cu_seqlens) return CDR_ERR_NULL_ARG;
+    const Layout L = layout(p);
+    if (workspace == nullptr || workspace_bytes < L.total) return CDR_ERR_WORKSPACE;
+    if (reinterpret_cast<uintptr_t>(workspace) % kAlign != 0) return CDR_ERR_WORKSPACE;
+
+    char* wb = static_cast<char*>(workspace);
+    cdr::Work ws;
+    ws.w = reinterpret_cast<uint16_t*>(wb + L.off[0]);
+    ws.u = reinterpret_cast<float*>(wb + L.off[1]);
+    ws.kgT_hi = reinterpret_cast<uint16_t*>(wb + L.off[2]);
+    ws.kgT_lo = reinterpret_cast<uint16_t*>(wb + L.off[3]);
+    ws.qg = reinterpret_cast<uint16_t*>(wb + L.off[4]);
+    ws.A2 = reinterpret_cast<uint16_t*>(wb + L.off[5]);
+    ws.gC = reinterpret_cast<float*>(wb + L.off[6]);
+    ws.Sc = reinterpret_cast<uint16_t*>(wb + L.off[7]);
+    ws.vnT = reinterpret_cast<uint16_t*>(wb + L.off[8]);
+    ws.bwT_hi = reinterpret_cast<uint16_t*>(wb + L.off[9]);
+    ws.bwT_lo = reinterpret_cast<uint16_t*>(wb + L.off[10]);
+    ws.vT = reinterpret_cast<uint16_t*>(wb + L.off[11]);
+
+    cdr::ChunkMap map;
+    map.cu = p->varlen ? cu_seqlens : nullptr;
+    map.T = p->T;
+    map.N = p->N;
+    map.C = p->chunk_size;
+    map.nchunk = (p->T + p->chunk_size - 1) / p->chunk_size;
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int nslots = (int)num_slots(p);
+    const float* s0 = p->has_initial_state ? initial_state : nullptr;
+    float* s_out = p->output_final_state ? final_state : nullptr;
+    const int C = p->chunk_size;
+    // value-column blocks per chain: 16 columns unless there are enough chains to fill the chip
+    const int BV = ((int64_t)p->N * p->H * 4 >= 512) ? 32 : 16;
+
+    if ((stages & CDR_STAGE_INTRA) && nslots > 0) {
+        if (cdr::launch_intra(C, p->gate == CDR_GATE_PER_DIM, static_cast<const uint16_t*>(q),
+                              static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), g, beta, map,
+                              nslots, p->H, p->scale, ws, s) != hipSuccess)
+            return CDR_ERR_HIP;
+    }
+    if (stages & CDR_STAGE_CHAIN) {
+        if (cdr::launch_chain(C, BV, map, p->N, p->H, s0, s_out, ws, s) != hipSuccess) return CDR_ERR_HIP;
+    }
+    if ((stages & CDR_STAGE_OUTPUT) && nslots > 0) {
+        if (cdr::launch_output(C, map, nslots, p->H, static_cast<uint16_t*>(o), ws, s) != hipSuccess)
+            return CDR_ERR_HIP;
+    }
+    return CDR_OK;
+}
+
+cdr_status chunk_dr_fwd(const cdr_problem* p, const void* q, const void* k, const void* v, const float* g,
+                        const float* beta, const float* initial_state, const int32_t* cu_seqlens, void* o,
+                        float* final_state, void* workspace, size_t workspace_bytes, void* stream) {
+    return chunk_dr_fwd_stages(p, q, k, v, g, beta, initial_state, cu_seqlens, o, final_state, workspace,
+                               workspace_bytes, CDR_STAGE_ALL, stream);
+}
+
+const char* cdr_status_str(cdr_status s) {
+    switch (s) {
+        case CDR_OK: return "ok";
+        case CDR_ERR_NULL_ARG: return "a required pointer is NULL";
+        case CDR_ERR_BAD_SHAPE: return "non-positive or inconsistent sizes";
+        case CDR_ERR_UNSUPPORTED: return "unsupported configuration (K and V must be 128, chunk_size 64 or 128)";
+        case CDR_ERR_VARLEN_BATCH: return "cu_seqlens requires B == 1";
+        case CDR_ERR_WORKSPACE: return "workspace missing, too small or not 256-byte aligned";
+        case CDR_ERR_HIP: return "HIP kernel launch failed";
+    }
+    return "unknown status";
+}
+
+int32_t cdr_version(void) { return CDR_VERSION; }
+
+}  // extern "C"

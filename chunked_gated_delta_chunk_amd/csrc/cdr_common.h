@@ -1,0 +1,154 @@
+// Shared device helpers for the chunked gated delta-rule kernels (gfx950).
+//
+// MFMA operand layouts used throughout (wave64, lane l, r = l & 15, q = l >> 4):
+//   v_mfma_f32_16x16x32_bf16: A[m = r][k = 8q + i], B[k = 8q + i][n = r] (i = 0..7),
+//                             D[m = 4q + i][n = r] (i = 0..3)
+//   v_mfma_f32_16x16x16_bf16: A[m = r][k = 4q + i], B[k = 4q + i][n = r] (i = 0..3),
+//                             D as above, so a D tile is directly a K=16 B operand.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace cdr {
+
+typedef __attribute__((__vector_size__(8 * sizeof(short)))) short bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(short)))) short bf16x4;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+
+constexpr int KD = 128;  // key dimension
+constexpr int VD = 128;  // value dimension
+constexpr int NTHREADS = 256;
+
+__device__ __forceinline__ f32x4 mfma32(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma16(const bf16x4& a, const bf16x4& b, const f32x4& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+
+// fp32 -> bf16, round to nearest even (inputs are finite)
+__device__ __forceinline__ uint16_t f2bf(float f) {
+    uint32_t u = __float_as_uint(f);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+__device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
+
+// x = hi + lo with hi = bf16(x) and lo = bf16(x - hi): a 16-bit-mantissa pair.
+__device__ __forceinline__ void split_bf(float x, short& hi, short& lo) {
+    uint16_t h = f2bf(x);
+    hi = (short)h;
+    lo = (short)f2bf(x - bf2f(h));
+}
+
+// natural exponential through the hardware base-2 exponential
+__device__ __forceinline__ float ex(float x) { return __builtin_amdgcn_exp2f(x * 1.44269504088896341f); }
+
+__device__ __forceinline__ void unpack8(const uint4& p, float* f) {
+    const uint32_t w[4] = {p.x, p.y, p.z, p.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        f[2 * i] = __uint_as_float(w[i] << 16);
+        f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+}
+__device__ __forceinline__ bf16x8 as_bf16x8(const uint4& p) {
+    bf16x8 r;
+    const uint32_t w[4] = {p.x, p.y, p.z, p.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        r[2 * i] = (short)(w[i] & 0xffffu);
+        r[2 * i + 1] = (short)(w[i] >> 16);
+    }
+    return r;
+}
+__device__ __forceinline__ uint4 pack8(const short* s) {
+    uint4 p;
+    p.x = (uint32_t)(uint16_t)s[0] | ((uint32_t)(uint16_t)s[1] << 16);
+    p.y = (uint32_t)(uint16_t)s[2] | ((uint32_t)(uint16_t)s[3] << 16);
+    p.z = (uint32_t)(uint16_t)s[4] | ((uint32_t)(uint16_t)s[5] << 16);
+    p.w = (uint32_t)(uint16_t)s[6] | ((uint32_t)(uint16_t)s[7] << 16);
+    return p;
+}
+__device__ __forceinline__ uint2 pack4(const short* s) {
+    uint2 p;
+    p.x = (uint32_t)(uint16_t)s[0] | ((uint32_t)(uint16_t)s[1] << 16);
+    p.y = (uint32_t)(uint16_t)s[2] | ((uint32_t)(uint16_t)s[3] << 16);
+    return p;
+}
+
+// wait for this wave's own LDS traffic; keeps the compiler from reordering across it
+__device__ __forceinline__ void wave_lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+// ---------------------------------------------------------------------------------------
+// Chunk map. Tokens are packed along one axis; sequence n owns tokens [bos, bos + len).
+// Fixed length: bos = n*T, len = T, and sequence n owns chunk slots
+// [n*ceil(T/C), (n+1)*ceil(T/C)).  Varlen: sequence n owns the slots starting at
+// floor(cu[n]/C) + n, which never overlap and stay below floor(T/C) + N.
+// ---------------------------------------------------------------------------------------
+struct ChunkMap {
+    const int32_t* cu;  // NULL for fixed length
+    int32_t T;          // tokens per sequence (fixed) or total packed tokens (varlen)
+    int32_t N;          // sequences
+    int32_t C;          // chunk size
+    int32_t nchunk;     // ceil(T / C), fixed length only
+};
+
+__device__ __forceinline__ void seq_info(const ChunkMap& m, int n, int64_t& bos, int& len, int& slot0) {
+    if (m.cu == nullptr) {
+        bos = (int64_t)n * m.T;
+        len = m.T;
+        slot0 = n * m.nchunk;
+    } else {
+        const int a = m.cu[n], b = m.cu[n + 1];
+        bos = a;
+        len = b - a;
+        slot0 = a / m.C + n;
+    }
+}
+
+// Maps a chunk slot to (first token, valid rows). rows == 0 marks an unused slot.
+__device__ __forceinline__ void slot_chunk(const ChunkMap& m, int slot, int64_t& tok0, int& rows) {
+    int n, c;
+    if (m.cu == nullptr) {
+        n = slot / m.nchunk;
+        c = slot - n * m.nchunk;
+    } else {
+        int lo = 0, hi = m.N - 1;  // largest n with cu[n]/C + n <= slot
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (m.cu[mid] / m.C + mid <= slot) lo = mid; else hi = mid - 1;
+        }
+        n = lo;
+        c = slot - (m.cu[n] / m.C + n);
+    }
+    int64_t bos;
+    int len, slot0;
+    seq_info(m, n, bos, len, slot0);
+    const int start = c * m.C;
+    if (c < 0 || start >= len) {
+        tok0 = 0;
+        rows = 0;
+        return;
+    }
+    tok0 = bos + start;
+    rows = min(m.C, len - start);
+}
+
+// Per-chunk intermediates in the workspace; index ch = slot * H + h.
+struct Work {
+    uint16_t* w;       // [ch][C][K]  bf16   w = (I+A)^-1 diag(beta) (exp(gamma) * k)
+    float* u;          // [ch][C][V]  fp32   u = (I+A)^-1 diag(beta) v
+    uint16_t* kgT_hi;  // [ch][K][C]  bf16   (exp(gamma_C - gamma) * k)^T, high part
+    uint16_t* kgT_lo;  // [ch][K][C]  bf16   low part
+    uint16_t* qg;      // [ch][C][K]  bf16   scale * q * exp(gamma)
+    uint16_t* A2;      // [ch][C][C]  bf16   in-chunk output block (lower triangle incl. diagonal)
+    float* gC;         // [ch][K]     fp32   exp(gamma_C)
+    uint16_t* Sc;      // [ch][V][K]  bf16   state entering the chunk (transposed)
+    uint16_t* vnT;     // [ch][V][C]  bf16   corrected values v_new (transposed)
+    uint16_t* bwT_hi;  // [ch][K][C]  bf16   (exp(gamma) * k)^T, high part (intra scratch)
+    uint16_t* bwT_lo;  // [ch][K][C]  bf16   low part
+    uint16_t* vT;      // [ch][V][C]  bf16   v^T (intra scratch)
+};
+
+}  // namespace cdr

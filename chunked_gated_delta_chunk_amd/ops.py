@@ -1,0 +1,198 @@
+"""Python binding of the C interface declared in include/chunk_dr.h.
+
+Argument marshalling only: dtype and shape checks, allocation of the outputs and the
+workspace with torch, and one call into libchunkdr.so on the current stream.  Every
+step of the forward runs in the HIP kernels; there is no fallback of any kind, and
+calling without the built library raises.
+"""
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libchunkdr.so")
+
+CDR_OK = 0
+_STATUS_EXC = {1: ValueError, 2: ValueError, 3: ValueError, 4: ValueError, 5: RuntimeError,
+               6: RuntimeError}
+GATE_PER_DIM = 0
+GATE_PER_HEAD = 1
+
+EXPORTED = ("cdr_check", "cdr_workspace_bytes", "chunk_dr_fwd", "chunk_dr_fwd_stages",
+            "cdr_status_str", "cdr_version")
+STAGE_INTRA, STAGE_CHAIN, STAGE_OUTPUT, STAGE_ALL = 1, 2, 4, 7
+
+
+class cdr_problem(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("T", ctypes.c_int32), ("H", ctypes.c_int32),
+                ("K", ctypes.c_int32), ("V", ctypes.c_int32), ("N", ctypes.c_int32),
+                ("gate", ctypes.c_int32), ("chunk_size", ctypes.c_int32),
+                ("scale", ctypes.c_float), ("has_initial_state", ctypes.c_int32),
+                ("output_final_state", ctypes.c_int32), ("varlen", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH):
+    """Load libchunkdr.so (built by chunked_gated_delta_chunk_amd.build); raise if missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with "
+                           "`python -m chunked_gated_delta_chunk_amd.build` (no fallback exists)")
+    lib = ctypes.CDLL(path)
+    P = ctypes.POINTER(cdr_problem)
+    vp = ctypes.c_void_p
+    lib.cdr_check.argtypes = [P]
+    lib.cdr_check.restype = ctypes.c_int
+    lib.cdr_workspace_bytes.argtypes = [P]
+    lib.cdr_workspace_bytes.restype = ctypes.c_size_t
+    lib.chunk_dr_fwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    lib.chunk_dr_fwd.restype = ctypes.c_int
+    lib.chunk_dr_fwd_stages.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t,
+                                        ctypes.c_int32, vp]
+    lib.chunk_dr_fwd_stages.restype = ctypes.c_int
+    lib.cdr_status_str.argtypes = [ctypes.c_int]
+    lib.cdr_status_str.restype = ctypes.c_char_p
+    lib.cdr_version.argtypes = []
+    lib.cdr_version.restype = ctypes.c_int32
+    _lib = lib
+    return lib
+
+
+def _raise(status: int, what: str):
+    lib = load_library()
+    msg = lib.cdr_status_str(status).decode()
+    raise _STATUS_EXC.get(status, RuntimeError)(f"{what}: {msg} (status {status})")
+
+
+def make_problem(B, T, H, K, V, N, per_dim_gate, chunk_size, scale, has_initial_state,
+                 output_final_state, varlen) -> cdr_problem:
+    return cdr_problem(int(B), int(T), int(H), int(K), int(V), int(N),
+                       GATE_PER_DIM if per_dim_gate else GATE_PER_HEAD, int(chunk_size),
+                       float(scale), int(bool(has_initial_state)), int(bool(output_final_state)),
+                       int(bool(varlen)))
+
+
+def check(p: cdr_problem) -> int:
+    """cdr_check: host-only validation status."""
+    return load_library().cdr_check(ctypes.byref(p))
+
+
+def workspace_bytes(p: cdr_problem) -> int:
+    return load_library().cdr_workspace_bytes(ctypes.byref(p))
+
+
+def _need(t, name, dtype, shape=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _dev_ptr(t: torch.Tensor, device) -> int:
+    if t.device != device:
+        raise ValueError(f"tensor on {t.device}, expected {device}")
+    if t.data_ptr() % 16:
+        raise ValueError("tensor data must be 16-byte aligned")
+    return t.data_ptr()
+
+
+def chunk_dr_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
+                 beta: torch.Tensor, scale: Optional[float] = None,
+                 initial_state: Optional[torch.Tensor] = None,
+                 cu_seqlens: Optional[torch.Tensor] = None, chunk_size: int = 64,
+                 output_final_state: bool = False,
+                 workspace: Optional[torch.Tensor] = None,
+                 out: Optional[torch.Tensor] = None,
+                 final_state_out: Optional[torch.Tensor] = None,
+                 stages: int = STAGE_ALL,
+                 ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Chunked gated delta-rule forward on the GPU.
+
+    q, k ``[B,T,H,K]`` bf16; v ``[B,T,H,V]`` bf16; g ``[B,T,H,K]`` (per-dimension gate)
+    or ``[B,T,H]`` (per-head gate) fp32; beta ``[B,T,H]`` fp32; initial_state
+    ``[N,H,V,K]`` fp32 or None (zeros); cu_seqlens ``[N+1]`` int32 on the device, or
+    None (then N = B). ``scale=None`` means ``K ** -0.5``.  Returns ``(o, S)`` with o
+    ``[B,T,H,V]`` bf16 and S ``[N,H,V,K]`` fp32 (None unless output_final_state).
+    ``workspace`` optionally supplies the device scratch buffer (uint8, at least
+    :func:`workspace_bytes` bytes); otherwise one is allocated.  ``out`` and
+    ``final_state_out`` optionally supply the output buffers.  ``stages`` selects kernel
+    stages as chunk_dr_fwd_stages does (default: all).
+    """
+    lib = load_library()
+    _need(q, "q", torch.bfloat16)
+    if q.dim() != 4:
+        raise ValueError("q must be [B, T, H, K]")
+    B, T, H, K = q.shape
+    _need(k, "k", torch.bfloat16, (B, T, H, K))
+    if v.dim() != 4 or tuple(v.shape[:3]) != (B, T, H):
+        raise ValueError("v must be [B, T, H, V]")
+    _need(v, "v", torch.bfloat16)
+    V = v.shape[3]
+    _need(g, "g", torch.float32)
+    if tuple(g.shape) == (B, T, H, K):
+        per_dim = True
+    elif tuple(g.shape) == (B, T, H):
+        per_dim = False
+    else:
+        raise ValueError(f"g must be [B,T,H,K] or [B,T,H], got {tuple(g.shape)}")
+    _need(beta, "beta", torch.float32, (B, T, H))
+    if cu_seqlens is not None:
+        _need(cu_seqlens, "cu_seqlens", torch.int32)
+        if cu_seqlens.dim() != 1 or cu_seqlens.numel() < 2:
+            raise ValueError("cu_seqlens must be a 1-D tensor of N + 1 offsets")
+        N = cu_seqlens.numel() - 1
+    else:
+        N = B
+    if initial_state is not None:
+        _need(initial_state, "initial_state", torch.float32, (N, H, V, K))
+    if scale is None:
+        scale = K ** -0.5
+    p = make_problem(B, T, H, K, V, N, per_dim, chunk_size, scale, initial_state is not None,
+                     output_final_state, cu_seqlens is not None)
+    st = lib.cdr_check(ctypes.byref(p))
+    if st != CDR_OK:
+        _raise(st, "chunk_dr_fwd")
+    device = q.device
+    if device.type != "cuda":
+        raise ValueError("inputs must be on a GPU device")
+    q, k, v, g, beta = (t.contiguous() for t in (q, k, v, g, beta))
+    s0 = initial_state.contiguous() if initial_state is not None else None
+    cu = cu_seqlens.contiguous() if cu_seqlens is not None else None
+    if out is None:
+        o = torch.empty((B, T, H, V), dtype=torch.bfloat16, device=device)
+    else:
+        _need(out, "out", torch.bfloat16, (B, T, H, V))
+        o = out
+    S = None
+    if output_final_state:
+        if final_state_out is None:
+            S = torch.empty((N, H, V, K), dtype=torch.float32, device=device)
+        else:
+            _need(final_state_out, "final_state_out", torch.float32, (N, H, V, K))
+            S = final_state_out
+    nbytes = lib.cdr_workspace_bytes(ctypes.byref(p))
+    if workspace is None:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    elif workspace.numel() * workspace.element_size() < nbytes:
+        raise ValueError("workspace too small")
+    ptr = lambda t: None if t is None else _dev_ptr(t, device)  # noqa: E731
+    stream = torch.cuda.current_stream(device).cuda_stream
+    nb = workspace.numel() * workspace.element_size()
+    if stages == STAGE_ALL:
+        st = lib.chunk_dr_fwd(ctypes.byref(p), ptr(q), ptr(k), ptr(v), ptr(g), ptr(beta), ptr(s0),
+                              ptr(cu), ptr(o), ptr(S), ptr(workspace), nb, stream)
+    else:
+        st = lib.chunk_dr_fwd_stages(ctypes.byref(p), ptr(q), ptr(k), ptr(v), ptr(g), ptr(beta),
+                                     ptr(s0), ptr(cu), ptr(o), ptr(S), ptr(workspace), nb,
+                                     int(stages), stream)
+    if st != CDR_OK:
+        _raise(st, "chunk_dr_fwd")
+    return o, S

@@ -1,0 +1,158 @@
+/*
+ * chunk_dr.h -- C interface of the chunked gated delta-rule forward for MI355X (gfx950).
+ *
+ * The operation (page "PyPTO-Gym 的 chunk_kda 算子实战", sections 算子定位与算法背景
+ * and M1-M4): for every sequence n and head h, starting from a K x V state S
+ * (the transpose of initial_state[n, h], or zero), and for every token t in order,
+ *
+ *     S   <- diag(exp(g_t)) S                  per-dimension gate (g_t in R^K), or the
+ *                                              scalar per-head gate g_t times the identity
+ *     S   <- S + beta_t k_t (v_t - S^T k_t)^T
+ *     o_t <- scale * S^T q_t
+ *
+ * evaluated chunk by chunk (chunk_size tokens; chunks restart at every sequence
+ * start): an in-chunk prefix sum of g, the decayed strictly lower-triangular
+ * A = beta k k^T, the inverse of (I + A), the w/u projections, and an fp32 state
+ * carried from one chunk to the next.  The final state is returned as
+ * [N, H, V, K], the transpose of the internal K x V matrix, as on that page
+ * (section 算子签名与 I/O 规格).
+ *
+ * Conventions shared by every entry point:
+ *  - Tensor pointers are DEVICE pointers to contiguous row-major buffers.
+ *  - Tokens are packed: fixed-length batches are addressed as B*T consecutive tokens
+ *    (sequence b owns tokens [b*T, (b+1)*T)); a varlen batch has B == 1 and its
+ *    sequences are given by cu_seqlens.
+ *  - The caller owns every buffer.  The library never allocates, frees, copies
+ *    to the host or synchronises; kernels are queued on the given stream and the
+ *    call returns immediately.
+ *  - Errors are returned as cdr_status values; nothing is printed or thrown.
+ */
+#ifndef CHUNK_DR_H
+#define CHUNK_DR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define CDR_VERSION 1
+
+typedef enum {
+    CDR_OK = 0,
+    CDR_ERR_NULL_ARG = 1,      /* a required pointer is NULL */
+    CDR_ERR_BAD_SHAPE = 2,     /* non-positive or inconsistent sizes */
+    CDR_ERR_UNSUPPORTED = 3,   /* K or V != 128, chunk_size not 64 or 128, unknown gate */
+    CDR_ERR_VARLEN_BATCH = 4,  /* cu_seqlens given with B != 1 */
+    CDR_ERR_WORKSPACE = 5,     /* workspace NULL or smaller than cdr_workspace_bytes() */
+    CDR_ERR_HIP = 6            /* a kernel launch failed (hipGetLastError) */
+} cdr_status;
+
+typedef enum {
+    CDR_GATE_PER_DIM = 0,      /* g [B*T, H, K] fp32: per-key-dimension log gate (KDA) */
+    CDR_GATE_PER_HEAD = 1      /* g [B*T, H] fp32: one log gate per token and head (Gated DeltaNet) */
+} cdr_gate;
+
+/* Problem description.  All fields are plain host values. */
+typedef struct {
+    int32_t B;                  /* batch rows; must be 1 when varlen != 0 */
+    int32_t T;                  /* tokens per batch row (total packed tokens when varlen) */
+    int32_t H;                  /* heads */
+    int32_t K;                  /* key dimension; must be 128 */
+    int32_t V;                  /* value dimension; must be 128 */
+    int32_t N;                  /* sequences: B when varlen == 0, else len(cu_seqlens) - 1 */
+    int32_t gate;               /* cdr_gate */
+    int32_t chunk_size;         /* 64 or 128 */
+    float scale;                /* multiplies q; the usual choice is K^-0.5 */
+    int32_t has_initial_state;  /* initial_state is read when non-zero, else S starts at 0 */
+    int32_t output_final_state; /* final_state is written when non-zero */
+    int32_t varlen;             /* cu_seqlens is read when non-zero */
+} cdr_problem;
+
+/*
+ * Host-only validation of a problem description; never touches the device.
+ * Returns CDR_OK or the first violated rule (see cdr_status).
+ */
+cdr_status cdr_check(const cdr_problem* p);
+
+/*
+ * Bytes of device workspace chunk_dr_fwd needs for problem p (0 if p is invalid).
+ * The size depends only on the shape fields (B, T, H, K, V, N, chunk_size): it
+ * holds the per-chunk intermediates (w, u, decayed keys and queries, the in-chunk
+ * attention block, the chunk-entry states and the corrected values), about
+ * 290 KiB per chunk and head at chunk_size 128.
+ */
+size_t cdr_workspace_bytes(const cdr_problem* p);
+
+/*
+ * Chunked gated delta-rule forward.
+ *
+ *   q, k          bf16 [B*T, H, K]   queries and keys
+ *   v             bf16 [B*T, H, V]   values
+ *   g             fp32 [B*T, H, K] (CDR_GATE_PER_DIM) or [B*T, H] (CDR_GATE_PER_HEAD);
+ *                 log-domain forget gate, expected <= 0
+ *   beta          fp32 [B*T, H]      delta-rule step size
+ *   initial_state fp32 [N, H, V, K]  read when p->has_initial_state, else may be NULL
+ *   cu_seqlens    int32 [N + 1]      device array of sequence offsets into the packed token
+ *                                    axis (0 = cu[0] <= cu[1] <= ... <= cu[N] = T); read when
+ *                                    p->varlen, else may be NULL.  Its contents are not
+ *                                    validated; offsets outside [0, T] are undefined behaviour.
+ *   o             bf16 [B*T, H, V]   output, written for every token of every sequence
+ *   final_state   fp32 [N, H, V, K]  written when p->output_final_state, else may be NULL.
+ *                                    An empty sequence returns its initial state (or zeros).
+ *   workspace     device buffer of at least cdr_workspace_bytes(p) bytes, 256-byte aligned;
+ *                 its contents on entry do not matter.  It must not be used by another call
+ *                 until the kernels of this call have finished on `stream`.
+ *   stream        hipStream_t to launch on (NULL = the default stream)
+ *
+ * The result does not depend on the contents of the workspace or on previous calls:
+ * repeated calls on the same inputs give bit-identical o and final_state.
+ * Returns CDR_OK after queueing the kernels, or an error status without launching
+ * anything (CDR_ERR_HIP if a launch failed).
+ */
+cdr_status chunk_dr_fwd(const cdr_problem* p,
+                        const void* q, const void* k, const void* v,
+                        const float* g, const float* beta,
+                        const float* initial_state, const int32_t* cu_seqlens,
+                        void* o, float* final_state,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * The same forward, split into its three kernel stages so that each can be timed or
+ * profiled on its own.  `stages` is a bit mask of
+ *   CDR_STAGE_INTRA  (1)  per-chunk work independent of the carried state: gate prefix sum,
+ *                         decayed A and its inverse, w, u, decayed q and k, the in-chunk
+ *                         output block (page sections M1-M3)
+ *   CDR_STAGE_CHAIN  (2)  the sequential chunk-to-chunk state recurrence, v_new and the
+ *                         final state (section M4)
+ *   CDR_STAGE_OUTPUT (4)  o = qg S + A2 v_new for every chunk (section M4)
+ * Stages run in this order.  A stage reads what earlier stages left in the workspace, so a
+ * call with a stage whose predecessors are not in `stages` is only meaningful after a call
+ * with the same problem, inputs and workspace that ran them.  chunk_dr_fwd(...) is
+ * chunk_dr_fwd_stages(..., CDR_STAGE_ALL, stream).  Arguments and errors as chunk_dr_fwd;
+ * a mask outside 1..7 returns CDR_ERR_UNSUPPORTED.
+ */
+#define CDR_STAGE_INTRA 1
+#define CDR_STAGE_CHAIN 2
+#define CDR_STAGE_OUTPUT 4
+#define CDR_STAGE_ALL 7
+cdr_status chunk_dr_fwd_stages(const cdr_problem* p,
+                               const void* q, const void* k, const void* v,
+                               const float* g, const float* beta,
+                               const float* initial_state, const int32_t* cu_seqlens,
+                               void* o, float* final_state,
+                               void* workspace, size_t workspace_bytes,
+                               int32_t stages, void* stream);
+
+/* Human-readable name of a status code (static storage). */
+const char* cdr_status_str(cdr_status s);
+
+/* CDR_VERSION of the built library. */
+int32_t cdr_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CHUNK_DR_H */

@@ -1,0 +1,106 @@
+"""The C interface on the CPU: the library loads, exports what include/chunk_dr.h
+declares, and validates problems on the host without touching a device."""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import chunked_gated_delta_chunk_amd as cdr
+from chunked_gated_delta_chunk_amd import ops
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    text = open(os.path.join(ROOT, "include", "chunk_dr.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return set(re.findall(r"^[A-Za-z_][\w \*]*?\b(\w+)\s*\(", text, flags=re.M)) - {"if"}
+
+
+def test_library_exports_every_declared_function():
+    lib = cdr.load_library()
+    declared = _declared_functions()
+    assert {"chunk_dr_fwd", "cdr_check", "cdr_workspace_bytes", "cdr_status_str",
+            "cdr_version"} <= declared
+    for name in declared:
+        assert hasattr(lib, name), f"{name} declared in chunk_dr.h but not exported"
+    assert lib.cdr_version() == 1
+
+
+def _p(**kw):
+    base = dict(B=1, T=256, H=2, K=128, V=128, N=1, per_dim_gate=True, chunk_size=64,
+                scale=128 ** -0.5, has_initial_state=False, output_final_state=True, varlen=False)
+    base.update(kw)
+    return cdr.make_problem(**base)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(), 0),
+    (dict(K=64), 3), (dict(V=256), 3), (dict(chunk_size=32), 3), (dict(chunk_size=256), 3),
+    (dict(B=0), 2), (dict(H=0), 2), (dict(T=-1), 2), (dict(N=2), 2),
+    (dict(B=2, N=3, varlen=True), 4),
+    (dict(B=1, N=5, T=100, varlen=True), 0),
+    (dict(T=0), 0),
+])
+def test_check_status(kw, status):
+    assert cdr.check(_p(**kw)) == status
+
+
+def test_check_rejects_unknown_gate():
+    p = _p()
+    p.gate = 7
+    assert cdr.check(p) == 3
+
+
+def test_workspace_size_scales_with_chunks():
+    a = cdr.workspace_bytes(_p(T=256, chunk_size=64))
+    b = cdr.workspace_bytes(_p(T=512, chunk_size=64))
+    assert a > 0 and b > a
+    assert cdr.workspace_bytes(_p(K=64)) == 0
+    # varlen sizes for floor(T/C) + N chunk slots
+    v = cdr.workspace_bytes(_p(T=256, N=3, varlen=True))
+    assert v > a
+
+
+def test_fwd_rejects_bad_problem_without_touching_device():
+    lib = cdr.load_library()
+    p = _p(K=64)
+    st = lib.chunk_dr_fwd(ctypes.byref(p), *([None] * 10), 0, None)
+    assert st == 3
+    p = _p()
+    st = lib.chunk_dr_fwd(ctypes.byref(p), *([None] * 10), 0, None)
+    assert st == 1  # null tensor pointers
+    st = lib.chunk_dr_fwd(ctypes.byref(p), *([1 << 20] * 9), None, 0, None)
+    assert st == 5  # no workspace
+    assert lib.cdr_status_str(5).decode().startswith("workspace")
+
+
+def test_binding_type_and_shape_errors():
+    B, T, H, K = 1, 8, 2, 128
+    q = torch.zeros(B, T, H, K, dtype=torch.bfloat16)
+    g = torch.zeros(B, T, H, K)
+    beta = torch.zeros(B, T, H)
+    with pytest.raises(TypeError):
+        cdr.chunk_dr_fwd(q.float(), q, q, g, beta)
+    with pytest.raises(TypeError):
+        cdr.chunk_dr_fwd(q, q, q, g.double(), beta)
+    with pytest.raises(ValueError):
+        cdr.chunk_dr_fwd(q, q, q, g[..., :3], beta)
+    with pytest.raises(ValueError):
+        cdr.chunk_dr_fwd(q, q, q, g, beta, chunk_size=32)
+    with pytest.raises(ValueError):  # K != 128
+        cdr.chunk_dr_fwd(q[..., :64].contiguous(), q[..., :64].contiguous(), q, g[..., :64], beta)
+    with pytest.raises(ValueError):  # varlen needs B == 1
+        q2 = torch.zeros(2, T, H, K, dtype=torch.bfloat16)
+        cdr.chunk_dr_fwd(q2, q2, q2, torch.zeros(2, T, H, K), torch.zeros(2, T, H),
+                         cu_seqlens=torch.tensor([0, 8], dtype=torch.int32))
+    with pytest.raises(ValueError):  # host tensors are not accepted: no CPU path exists
+        cdr.chunk_dr_fwd(q, q, q, g, beta)
+
+
+def test_no_cpu_fallback_when_library_missing(monkeypatch, tmp_path):
+    monkeypatch.setattr(ops, "_lib", None)
+    with pytest.raises(RuntimeError, match="missing"):
+        ops.load_library(str(tmp_path / "absent.so"))
