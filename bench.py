@@ -1,0 +1,234 @@
+#!/usr/bin/env python3
+"""Throughput of the chunked gated delta-rule forward on one MI355X.
+
+A step is one full forward (intra-chunk kernel, chunk-to-chunk chain, output kernel) over
+one batch of seeded synthetic inputs of the KDA workload B=1, T=8192, H=16, K=V=128,
+chunk 128, with a std-0.1 initial state and the final state returned.  Inputs are
+resident in HBM before timing starts; three input sets are rotated so that a step does
+not find its inputs in the 256 MB memory-attached cache from the previous step.
+
+Prints one JSON line: tokens/s for the whole job, ms per step, per-kernel durations from
+HIP events on the launch stream, the roofline of the dominant kernel, and the fp64
+oracle timed on the host cores as a CPU baseline.
+
+    python bench.py [--steps K] [--warmup W] [--workload kda_t8192] [--no-cpu-baseline]
+"""
+import argparse
+import glob
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "forward tokens/s + % bf16 MFMA peak, KDA T=8192 H=16 K=V=128"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+SEED_BASE = 1003            # workload seeds: 1000 + position of the workload in the list
+
+
+def algorithmic(w, lengths):
+    """Algorithmic flops and bytes per kernel for a batch of sequences of the given lengths.
+
+    Per chunk of n tokens and head (K = V = 128): the intra kernel owns A, A2, w (n^2 K
+    each), u (n^2 V) and the inverse (n^3 / 3); the chain owns w S and kg^T v_new
+    (n K V each); the output kernel owns qg S (n K V) and A2 v_new (n^2 V); two flops per
+    multiply-add.  Bytes are the compulsory ones: q, k, v, o in bf16, g and beta in fp32,
+    the initial and final state in fp32; intermediates are not counted."""
+    K, V, C, H = w.K, w.V, w.chunk_size, w.H
+    f = {"intra": 0.0, "chain": 0.0, "output": 0.0}
+    for L in lengths:
+        for c0 in range(0, L, C):
+            n = min(C, L - c0)
+            f["intra"] += H * (2.0 * (3 * n * n * K + n * n * V) + n ** 3 / 3.0)
+            f["chain"] += H * (2.0 * 2 * n * K * V)
+            f["output"] += H * (2.0 * (n * K * V + n * n * V))
+    tokens = sum(lengths)
+    gate_bytes = 4 * K if w.per_dim_gate else 4
+    b = {"intra": tokens * H * (2 * 2 * K + 2 * V + gate_bytes + 4),
+         "chain": len(lengths) * H * K * V * 4 * (2 if w.initial_state else 1),
+         "output": tokens * H * 2 * V}
+    return f, b
+
+
+def source_hash():
+    h = hashlib.sha256()
+    for p in sorted(glob.glob(os.path.join(ROOT, "chunked_gated_delta_chunk_amd", "csrc", "*"))):
+        with open(p, "rb") as fh:
+            h.update(os.path.basename(p).encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel, workload):
+    """HBM bytes per launch from the committed counter summary, if it matches the sources."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as fh:
+            data = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    rec = data.get(workload, {}).get(kernel)
+    if not rec or rec.get("source_sha") != source_hash():
+        return None
+    return rec.get("hbm_bytes")
+
+
+def cpu_baseline(inp, w, budget_s):
+    """Time the fp64 oracle on the host: all heads, a prefix of the tokens sized to the
+    time budget (all tokens when it fits)."""
+    import numpy as np  # noqa: F401
+    import oracle
+    threads = oracle.num_threads()
+    chains = w.N * w.H
+    T = w.tokens
+
+    def run(tsub):
+        sl = lambda t: None if t is None else t[:, :tsub].contiguous()  # noqa: E731
+        t0 = time.perf_counter()
+        oracle.recurrent_fwd(sl(inp.q), sl(inp.k), sl(inp.v), sl(inp.g), sl(inp.beta),
+                             initial_state=inp.initial_state)
+        return time.perf_counter() - t0
+
+    probe = min(T, 512)
+    dt = run(probe)
+    tsub = T if dt * T / probe <= budget_s else max(probe, int(budget_s / dt * probe) // 64 * 64)
+    if tsub != probe:
+        dt = run(tsub)
+    return {"value": tsub * w.B / dt if w.lengths is None else tsub / dt, "unit": "tokens/s",
+            "cores": min(threads, chains), "kind": "oracle",
+            "sample": (f"fp64 per-token recurrence (C, OpenMP over {chains} (sequence, head) chains) "
+                       f"on the first {tsub} of {T} tokens of every head, {dt:.2f} s wall")}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="kda_t8192")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=8.0, help="seconds of oracle wall time")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: there is no multi-GPU path; the forward "
+              "would shard over heads and sequences with no exchange between them",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import chunked_gated_delta_chunk_amd as cdr
+    from chunked_gated_delta_chunk_amd.synth import WORKLOADS, workload_inputs
+
+    w = WORKLOADS[args.workload]
+    seed = 1000 + list(WORKLOADS).index(args.workload) + 1
+    dev = torch.device("cuda:0")
+    per_set = w.tokens * w.H * (3 * 2 * w.K + (4 * w.K if w.per_dim_gate else 4) + 4)
+    nsets = 3 if per_set * 3 <= 8 * 2 ** 30 else 1
+    host_sets = [workload_inputs(w, seed=seed + 1000 * i) for i in range(nsets)]
+    calls = []
+    shared_ws = None
+    for hs in host_sets:
+        d = hs.to(dev)
+        call = cdr.PreparedForward(d.q, d.k, d.v, d.g, d.beta, initial_state=d.initial_state,
+                                   cu_seqlens=d.cu_seqlens, chunk_size=w.chunk_size,
+                                   output_final_state=True, workspace=shared_ws)
+        shared_ws = call.workspace
+        calls.append(call)
+    torch.cuda.synchronize()
+
+    stages = (cdr.STAGE_INTRA, cdr.STAGE_CHAIN, cdr.STAGE_OUTPUT)
+    names = ("intra", "chain", "output")
+    for i in range(args.warmup):
+        for s in stages:
+            calls[i % nsets](s)
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        c = calls[i % nsets]
+        ev[i][0].record()
+        for j, s in enumerate(stages):
+            c(s)
+            ev[i][j + 1].record()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / K
+    kern_ms = {n: sum(ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(K)) / K
+               for j, n in enumerate(names)}
+    gpu_ms = sum(kern_ms.values())
+
+    lengths = list(w.lengths) if w.lengths is not None else [w.T] * w.B
+    flops, bytes_ = algorithmic(w, lengths)
+    f_nom = sum(flops.values())
+    tokens = w.tokens
+    value = tokens / (ms_step * 1e-3)
+    step_tflops = f_nom / (ms_step * 1e-3) / 1e12
+
+    per_kernel = {}
+    for n in names:
+        sec = kern_ms[n] * 1e-3
+        tf = flops[n] / sec / 1e12
+        gbs = bytes_[n] / sec / 1e9
+        per_kernel[n] = {"us": round(kern_ms[n] * 1e3, 2), "tflops": round(tf, 2),
+                         "mfma_frac": round(tf / PEAK_BF16_TFLOPS, 4),
+                         "hbm_gbs": round(gbs, 1), "hbm_frac": round(gbs / PEAK_HBM_GBS, 4)}
+    dom = max(names, key=lambda n: kern_ms[n])
+    pk = per_kernel[dom]
+    if pk["mfma_frac"] >= pk["hbm_frac"]:
+        roof = {"bound": "mfma", "achieved": pk["tflops"], "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s"}
+    else:
+        roof = {"bound": "hbm", "achieved": pk["hbm_gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s"}
+    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
+    roof["traffic"] = load_traffic(dom, args.workload)
+    roof["kernel"] = dom
+    roof["duration_us"] = pk["us"]
+
+    # parity spot check of the timed buffers against the oracle on one head, so the
+    # reported number is for a forward that is correct
+    spot = None
+    if not args.no_cpu_baseline:
+        import numpy as np
+        import oracle
+        hs = host_sets[(K - 1) % nsets]
+        one = lambda t: None if t is None else t[:, :, :1].contiguous()  # noqa: E731
+        s0 = None if hs.initial_state is None else hs.initial_state[:, :1].contiguous()
+        o_ref, S_ref = oracle.recurrent_fwd(one(hs.q), one(hs.k), one(hs.v), one(hs.g), one(hs.beta),
+                                            initial_state=s0, cu_seqlens=hs.cu_seqlens)
+        o_gpu = calls[(K - 1) % nsets].o[:, :, :1].float().cpu().numpy()
+        S_gpu = calls[(K - 1) % nsets].S[:, :1].cpu().numpy()
+        spot = {"o_err_over_tol": float(np.max(np.abs(o_gpu - o_ref) / (1e-2 + 1e-2 * np.abs(o_ref)))),
+                "S_err_over_tol": float(np.max(np.abs(S_gpu - S_ref) / (1e-3 + 1e-3 * np.abs(S_ref)))),
+                "heads_checked": 1}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(host_sets[0], w, args.cpu_budget)
+
+    line = {
+        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": K, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "B": w.B, "T": w.T, "H": w.H, "K": w.K, "V": w.V,
+                   "chunk_size": w.chunk_size, "gate": "per_dim" if w.per_dim_gate else "per_head",
+                   "initial_state": w.initial_state, "output_final_state": True,
+                   "lengths": list(w.lengths) if w.lengths else None, "input_sets_rotated": nsets},
+        "tflops_nominal": round(step_tflops, 2),
+        "mfma_frac_bf16_peak": round(step_tflops / PEAK_BF16_TFLOPS, 4),
+        "gpu_ms_per_step_events": round(gpu_ms, 5),
+        "per_kernel": per_kernel,
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "parity_spot_check": spot,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -104,6 +104,97 @@ def _dev_ptr(t: torch.Tensor, device) -> int:
     return t.data_ptr()
 
 
+class PreparedForward:
+    """A validated call of the forward whose arguments are marshalled once.
+
+    Construction takes the same arguments as :func:`chunk_dr_fwd` and allocates the
+    outputs and the workspace unless they are given; each call then queues the kernels
+    (``stages`` as in chunk_dr_fwd_stages) on the current stream with a single ctypes
+    call, so repeated launches carry no per-call host work beyond it.
+    """
+
+    def __init__(self, q, k, v, g, beta, scale=None, initial_state=None, cu_seqlens=None,
+                 chunk_size=64, output_final_state=False, workspace=None, out=None,
+                 final_state_out=None):
+        lib = load_library()
+        _need(q, "q", torch.bfloat16)
+        if q.dim() != 4:
+            raise ValueError("q must be [B, T, H, K]")
+        B, T, H, K = q.shape
+        _need(k, "k", torch.bfloat16, (B, T, H, K))
+        if v.dim() != 4 or tuple(v.shape[:3]) != (B, T, H):
+            raise ValueError("v must be [B, T, H, V]")
+        _need(v, "v", torch.bfloat16)
+        V = v.shape[3]
+        _need(g, "g", torch.float32)
+        if tuple(g.shape) == (B, T, H, K):
+            per_dim = True
+        elif tuple(g.shape) == (B, T, H):
+            per_dim = False
+        else:
+            raise ValueError(f"g must be [B,T,H,K] or [B,T,H], got {tuple(g.shape)}")
+        _need(beta, "beta", torch.float32, (B, T, H))
+        if cu_seqlens is not None:
+            _need(cu_seqlens, "cu_seqlens", torch.int32)
+            if cu_seqlens.dim() != 1 or cu_seqlens.numel() < 2:
+                raise ValueError("cu_seqlens must be a 1-D tensor of N + 1 offsets")
+            N = cu_seqlens.numel() - 1
+        else:
+            N = B
+        if initial_state is not None:
+            _need(initial_state, "initial_state", torch.float32, (N, H, V, K))
+        if scale is None:
+            scale = K ** -0.5
+        self.problem = make_problem(B, T, H, K, V, N, per_dim, chunk_size, scale,
+                                    initial_state is not None, output_final_state,
+                                    cu_seqlens is not None)
+        st = lib.cdr_check(ctypes.byref(self.problem))
+        if st != CDR_OK:
+            _raise(st, "chunk_dr_fwd")
+        device = q.device
+        if device.type != "cuda":
+            raise ValueError("inputs must be on a GPU device")
+        self.device = device
+        # keep references: the library reads these buffers when the kernels run
+        self.inputs = tuple(t.contiguous() for t in (q, k, v, g, beta))
+        self.s0 = initial_state.contiguous() if initial_state is not None else None
+        self.cu = cu_seqlens.contiguous() if cu_seqlens is not None else None
+        if out is None:
+            out = torch.empty((B, T, H, V), dtype=torch.bfloat16, device=device)
+        else:
+            _need(out, "out", torch.bfloat16, (B, T, H, V))
+        self.o = out
+        self.S = None
+        if output_final_state:
+            if final_state_out is None:
+                final_state_out = torch.empty((N, H, V, K), dtype=torch.float32, device=device)
+            else:
+                _need(final_state_out, "final_state_out", torch.float32, (N, H, V, K))
+            self.S = final_state_out
+        nbytes = lib.cdr_workspace_bytes(ctypes.byref(self.problem))
+        if workspace is None:
+            workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+        elif workspace.numel() * workspace.element_size() < nbytes:
+            raise ValueError("workspace too small")
+        self.workspace = workspace
+        ptr = lambda t: None if t is None else _dev_ptr(t, device)  # noqa: E731
+        qq, kk, vv, gg, bb = self.inputs
+        self._args = (ctypes.byref(self.problem), ptr(qq), ptr(kk), ptr(vv), ptr(gg), ptr(bb),
+                      ptr(self.s0), ptr(self.cu), ptr(self.o), ptr(self.S), ptr(workspace),
+                      workspace.numel() * workspace.element_size())
+        self._lib = lib
+
+    def __call__(self, stages: int = STAGE_ALL):
+        stream = torch.cuda.current_stream(self.device).cuda_stream
+        if stages == STAGE_ALL:
+            st = self._lib.chunk_dr_fwd(*self._args, stream)
+        else:
+            st = self._lib.chunk_dr_fwd_stages(*self._args, int(stages), stream)
+        if st != CDR_OK:
+            _raise(st, "chunk_dr_fwd")
+        return self.o, self.S
+
+
 def chunk_dr_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
                  beta: torch.Tensor, scale: Optional[float] = None,
                  initial_state: Optional[torch.Tensor] = None,
@@ -126,73 +217,8 @@ def chunk_dr_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Ten
     ``final_state_out`` optionally supply the output buffers.  ``stages`` selects kernel
     stages as chunk_dr_fwd_stages does (default: all).
     """
-    lib = load_library()
-    _need(q, "q", torch.bfloat16)
-    if q.dim() != 4:
-        raise ValueError("q must be [B, T, H, K]")
-    B, T, H, K = q.shape
-    _need(k, "k", torch.bfloat16, (B, T, H, K))
-    if v.dim() != 4 or tuple(v.shape[:3]) != (B, T, H):
-        raise ValueError("v must be [B, T, H, V]")
-    _need(v, "v", torch.bfloat16)
-    V = v.shape[3]
-    _need(g, "g", torch.float32)
-    if tuple(g.shape) == (B, T, H, K):
-        per_dim = True
-    elif tuple(g.shape) == (B, T, H):
-        per_dim = False
-    else:
-        raise ValueError(f"g must be [B,T,H,K] or [B,T,H], got {tuple(g.shape)}")
-    _need(beta, "beta", torch.float32, (B, T, H))
-    if cu_seqlens is not None:
-        _need(cu_seqlens, "cu_seqlens", torch.int32)
-        if cu_seqlens.dim() != 1 or cu_seqlens.numel() < 2:
-            raise ValueError("cu_seqlens must be a 1-D tensor of N + 1 offsets")
-        N = cu_seqlens.numel() - 1
-    else:
-        N = B
-    if initial_state is not None:
-        _need(initial_state, "initial_state", torch.float32, (N, H, V, K))
-    if scale is None:
-        scale = K ** -0.5
-    p = make_problem(B, T, H, K, V, N, per_dim, chunk_size, scale, initial_state is not None,
-                     output_final_state, cu_seqlens is not None)
-    st = lib.cdr_check(ctypes.byref(p))
-    if st != CDR_OK:
-        _raise(st, "chunk_dr_fwd")
-    device = q.device
-    if device.type != "cuda":
-        raise ValueError("inputs must be on a GPU device")
-    q, k, v, g, beta = (t.contiguous() for t in (q, k, v, g, beta))
-    s0 = initial_state.contiguous() if initial_state is not None else None
-    cu = cu_seqlens.contiguous() if cu_seqlens is not None else None
-    if out is None:
-        o = torch.empty((B, T, H, V), dtype=torch.bfloat16, device=device)
-    else:
-        _need(out, "out", torch.bfloat16, (B, T, H, V))
-        o = out
-    S = None
-    if output_final_state:
-        if final_state_out is None:
-            S = torch.empty((N, H, V, K), dtype=torch.float32, device=device)
-        else:
-            _need(final_state_out, "final_state_out", torch.float32, (N, H, V, K))
-            S = final_state_out
-    nbytes = lib.cdr_workspace_bytes(ctypes.byref(p))
-    if workspace is None:
-        workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)
-    elif workspace.numel() * workspace.element_size() < nbytes:
-        raise ValueError("workspace too small")
-    ptr = lambda t: None if t is None else _dev_ptr(t, device)  # noqa: E731
-    stream = torch.cuda.current_stream(device).cuda_stream
-    nb = workspace.numel() * workspace.element_size()
-    if stages == STAGE_ALL:
-        st = lib.chunk_dr_fwd(ctypes.byref(p), ptr(q), ptr(k), ptr(v), ptr(g), ptr(beta), ptr(s0),
-                              ptr(cu), ptr(o), ptr(S), ptr(workspace), nb, stream)
-    else:
-        st = lib.chunk_dr_fwd_stages(ctypes.byref(p), ptr(q), ptr(k), ptr(v), ptr(g), ptr(beta),
-                                     ptr(s0), ptr(cu), ptr(o), ptr(S), ptr(workspace), nb,
-                                     int(stages), stream)
-    if st != CDR_OK:
-        _raise(st, "chunk_dr_fwd")
-    return o, S
+    call = PreparedForward(q, k, v, g, beta, scale=scale, initial_state=initial_state,
+                           cu_seqlens=cu_seqlens, chunk_size=chunk_size,
+                           output_final_state=output_final_state, workspace=workspace, out=out,
+                           final_state_out=final_state_out)
+    return call(stages)
