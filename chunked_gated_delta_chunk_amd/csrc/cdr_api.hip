@@ -34,7 +34,7 @@ Layout layout(const cdr_problem* p) {
     const size_t C = (size_t)p->chunk_size, K = (size_t)p->K, V = (size_t)p->V;
     const size_t bytes[12] = {
         nch * C * K * 2,  // w
-        nch * C * V * 4,  // u
+        nch * V * C * 4,  // uT
         nch * K * C * 2,  // kgT_hi
         nch * K * C * 2,  // kgT_lo
         nch * C * K * 2,  // qg
@@ -101,7 +101,7 @@ cdr_status chunk_dr_fwd_stages(const cdr_problem* p, const void* q, const void* 
     char* wb = static_cast<char*>(workspace);
     cdr::Work ws;
     ws.w = reinterpret_cast<uint16_t*>(wb + L.off[0]);
-    ws.u = reinterpret_cast<float*>(wb + L.off[1]);
+    ws.uT = reinterpret_cast<float*>(wb + L.off[1]);
     ws.kgT_hi = reinterpret_cast<uint16_t*>(wb + L.off[2]);
     ws.kgT_lo = reinterpret_cast<uint16_t*>(wb + L.off[3]);
     ws.qg = reinterpret_cast<uint16_t*>(wb + L.off[4]);

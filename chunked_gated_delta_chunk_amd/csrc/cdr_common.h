@@ -26,12 +26,15 @@ __device__ __forceinline__ f32x4 mfma16(const bf16x4& a, const bf16x4& b, const 
     return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
 }
 
-// fp32 -> bf16, round to nearest even (inputs are finite)
-__device__ __forceinline__ uint16_t f2bf(float f) {
-    uint32_t u = __float_as_uint(f);
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return (uint16_t)(u >> 16);
+// fp32 -> bf16 with the hardware round-to-nearest-even conversion (v_cvt_pk_bf16_f32)
+typedef __bf16 bf16v2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf2(float a, float b) {
+    bf16v2 r;
+    r.x = (__bf16)a;
+    r.y = (__bf16)b;
+    return __builtin_bit_cast(uint32_t, r);
 }
+__device__ __forceinline__ uint16_t f2bf(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
 __device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
 
 // x = hi + lo with hi = bf16(x) and lo = bf16(x - hi): a 16-bit-mantissa pair.
@@ -39,6 +42,11 @@ __device__ __forceinline__ void split_bf(float x, short& hi, short& lo) {
     uint16_t h = f2bf(x);
     hi = (short)h;
     lo = (short)f2bf(x - bf2f(h));
+}
+// the same for two values, packed two bf16 per register
+__device__ __forceinline__ void split_pk(float a, float b, uint32_t& hi, uint32_t& lo) {
+    hi = pack_bf2(a, b);
+    lo = pack_bf2(a - __uint_as_float(hi << 16), b - __uint_as_float(hi & 0xffff0000u));
 }
 
 // natural exponential through the hardware base-2 exponential
@@ -79,6 +87,15 @@ __device__ __forceinline__ uint2 pack4(const short* s) {
 
 // wait for this wave's own LDS traffic; keeps the compiler from reordering across it
 __device__ __forceinline__ void wave_lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+// Workgroup barrier that orders LDS only.  __syncthreads() also waits for every outstanding
+// global load and store of the wave, which would drain loads issued ahead of time; use this
+// one wherever the threads only exchange data through LDS.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
 
 // ---------------------------------------------------------------------------------------
 // Chunk map. Tokens are packed along one axis; sequence n owns tokens [bos, bos + len).
@@ -135,20 +152,37 @@ __device__ __forceinline__ void slot_chunk(const ChunkMap& m, int slot, int64_t&
     rows = min(m.C, len - start);
 }
 
-// Per-chunk intermediates in the workspace; index ch = slot * H + h.
+// ---------------------------------------------------------------------------------------
+// Fragment-major storage.  Every intermediate that one kernel writes and another reads as
+// an MFMA operand is stored in the order the 16x16x32 instruction consumes it: a fragment
+// covers 16 non-contracted x 32 contracted indices, lane l of a wave holds non-contracted
+// index l % 16 and contracted indices 8 (l / 16) .. + 7, and the 64 lane slots of 16 bytes
+// follow each other.  A wave-wide load of a fragment is then one contiguous 1 KiB read.
+// A matrix with the non-contracted index in 16-blocks a and the contracted index in
+// 32-blocks b (nb of them) keeps fragment (a, b) at element ((a * nb + b) * 512).
+// ---------------------------------------------------------------------------------------
+__device__ __forceinline__ size_t frag(int a, int b, int nb) { return ((size_t)a * nb + b) * 512; }
+// Element offset, inside a fragment, of the four values a D-layout tile lane (r, q) holds
+// when the tile is the transpose of the operand (tile rows = contracted index 16 t + 4 q + e
+// within the fragment's 32, tile column = non-contracted index r): four consecutive slots.
+__device__ __forceinline__ int fragT(int t, int r, int q) { return (r + 16 * (2 * t + (q >> 1))) * 8 + 4 * (q & 1); }
+
+// Per-chunk intermediates in the workspace; index ch = slot * H + h.  Shapes name
+// (non-contracted, contracted) for fragment-major arrays.
 struct Work {
-    uint16_t* w;       // [ch][C][K]  bf16   w = (I+A)^-1 diag(beta) (exp(gamma) * k)
-    float* u;          // [ch][C][V]  fp32   u = (I+A)^-1 diag(beta) v
-    uint16_t* kgT_hi;  // [ch][K][C]  bf16   (exp(gamma_C - gamma) * k)^T, high part
-    uint16_t* kgT_lo;  // [ch][K][C]  bf16   low part
-    uint16_t* qg;      // [ch][C][K]  bf16   scale * q * exp(gamma)
-    uint16_t* A2;      // [ch][C][C]  bf16   in-chunk output block (lower triangle incl. diagonal)
-    float* gC;         // [ch][K]     fp32   exp(gamma_C)
-    uint16_t* Sc;      // [ch][V][K]  bf16   state entering the chunk (transposed)
-    uint16_t* vnT;     // [ch][V][C]  bf16   corrected values v_new (transposed)
-    uint16_t* bwT_hi;  // [ch][K][C]  bf16   (exp(gamma) * k)^T, high part (intra scratch)
-    uint16_t* bwT_lo;  // [ch][K][C]  bf16   low part
-    uint16_t* vT;      // [ch][V][C]  bf16   v^T (intra scratch)
+    uint16_t* w;       // (C, K) frag  bf16   w = (I+A)^-1 diag(beta) (exp(gamma) * k); A of w S
+    float* uT;         // D tiles      fp32   u = (I+A)^-1 diag(beta) v, (C/16) x (V/16) tiles of
+                       //                     64 lanes x 4 rows, the layout of the w S accumulator
+    uint16_t* kgT_hi;  // (K, C) frag  bf16   exp(gamma_C - gamma) * k, high part; A of kg^T v_new
+    uint16_t* kgT_lo;  // (K, C) frag  bf16   low part
+    uint16_t* qg;      // (C, K) frag  bf16   scale * q * exp(gamma); A of qg S
+    uint16_t* A2;      // (C, C) frag  bf16   in-chunk output block (j <= i), lower fragments only
+    float* gC;         // [K]          fp32   exp(gamma_C)
+    uint16_t* Sc;      // (V, K) frag  bf16   state entering the chunk; B of qg S
+    uint16_t* vnT;     // (V, C) frag  bf16   corrected values v_new; B of A2 v_new
+    uint16_t* bwT_hi;  // (K, C) frag  bf16   exp(gamma) * k, high part (intra scratch)
+    uint16_t* bwT_lo;  // (K, C) frag  bf16   low part
+    uint16_t* vT;      // (V, C) frag  bf16   v (intra scratch)
 };
 
 }  // namespace cdr
