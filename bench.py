@@ -64,7 +64,7 @@ def source_hash():
 
 def load_traffic(kernel, workload):
     """HBM bytes per launch from the committed counter summary, if it matches the sources."""
-    path = os.path.join(ROOT, "profiles", "traffic.json")
+    path = os.path.join(ROOT, "profiles", f"{workload}_hbm_traffic.json")
     try:
         with open(path) as fh:
             data = json.load(fh)
@@ -111,7 +111,20 @@ def main():
     ap.add_argument("--workload", default="kda_t8192")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=8.0, help="seconds of oracle wall time")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of MIB MiB (reference for the "
+                         "HBM byte counters) and exit")
     args = ap.parse_args()
+    if args.calibrate_copy:
+        import torch
+        n = args.calibrate_copy * 2 ** 20
+        src = torch.ones(n // 4, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes_read": n, "calibrate_copy_bytes_written": n, "launches": 3}))
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: there is no multi-GPU path; the forward "
               "would shard over heads and sequences with no exchange between them",
