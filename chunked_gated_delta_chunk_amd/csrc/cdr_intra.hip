@@ -3,36 +3,42 @@
 // "PyPTO-Gym 的 chunk_kda 算子实战" (gate prefix sum, decayed A with its triangular
 // inverse, the w / u projections) plus the chunk-local factors that section M4 consumes.
 //
-// One workgroup (4 waves) per (chunk slot, head).  Phases:
-//   E    every thread owns a 16-row x 4-column block of the chunk (one 16-row tile) and
-//        issues all of its loads (g, k, q, v) at once.  gamma = prefix sum of g inside the
-//        tile, plus the totals of the tiles above (through LDS).  Per-element decay
-//        factors relative to the tile's middle row m, and the element-wise outputs: qg,
-//        kg^T (split), exp(gamma_C), (exp(gamma) k)^T (split, scratch) and v^T (scratch).
-//   AA2  16x16 tiles of A (strictly lower, times beta) and A2 (lower incl. diagonal,
-//        times scale) on bf16 MFMA.  Per-dimension gates enter the operands through
-//        the tile pivots: for rows i in tile R and columns j in tile J <= R,
+// One workgroup of 8 waves per (chunk slot, head); the LDS it needs leaves room for one
+// workgroup per CU, so the two waves per SIMD are what hides latency.  Phases:
+//   E    every thread owns a 16-row x 2-column block of the chunk (one 16-row tile) and
+//        issues all of its loads (g, k, v) at once.  gamma = prefix sum of g inside the tile
+//        plus the totals of the tiles above (through LDS).  Per-element decay factors
+//        relative to the tile's middle row m, and the element-wise outputs: kg (split),
+//        exp(gamma_C), exp(gamma) k (split, scratch) and v (scratch), fragment-major.
+//   AA2  16x16 tiles of A (strictly lower, times beta) and A2 (lower incl. diagonal, times
+//        scale) on bf16 MFMA.  Per-dimension gates enter the operands through the tile
+//        pivots: for rows i in tile R and columns j in tile J <= R,
 //          exp(g_i - g_j) = [exp(g_i - g_m(R)) exp(g_m(R) - g_m(J))] * exp(g_m(J) - g_j)
 //        so no factor exceeds exp(half a tile's gate span) and the product never
 //        overflows.  A uses hi/lo split operands (three MFMAs); A2 feeds only the output
-//        and uses single bf16 operands.  Per-head gates use raw q, k (exact bf16
-//        products) and apply the scalar decay afterwards.  Wave w owns tile rows w and
-//        NT-1-w, which balances the triangle.
+//        and uses single bf16 operands (stored transposed).  Per-head gates use raw q, k
+//        (exact bf16 products) and apply the scalar decay afterwards.  Tile rows w and
+//        NT-1-w form one list of NT+1 tiles shared by waves w and w+4.  qg is produced on
+//        the diagonal tiles.
 //   INV  T = (I + A)^-1 by block-triangular inversion: the 16x16 diagonal blocks by
 //        forward substitution in fp32, then blocks are merged 16->32->64->128 with
 //        T21 = -T22 (A21 T11), two tile-parallel steps per level on split-bf16 MFMAs.
-//   WU   w = T diag(beta) (exp(gamma) k) and u = T diag(beta) v on split-bf16 MFMAs; the
-//        right-hand-side fragments are fetched right after phase E.
+//   WU   w^T = (exp(gamma) k)^T T'^T and u = T' v with T' = T diag(beta), split-bf16 MFMAs;
+//        wave w produces 16 columns of each.
 #include "cdr_common.h"
 
 namespace cdr {
+
+constexpr int IWAVES = 8;
+constexpr int ITHREADS = 64 * IWAVES;
 
 template <int C>
 struct IntraShape {
     static constexpr int NT = C / 16;                  // 16-row tiles per chunk
     static constexpr int NPAIR = NT * (NT + 1) / 2;    // lower tiles incl. diagonal
     static constexpr int NOFF = NT * (NT - 1) / 2;     // strictly lower tiles
-    static constexpr int SMAX = NT + 1;                // tiles per wave in phase AA2
+    static constexpr int HF = (NT + 1) / 2;            // tiles of a row pair done by the first wave
+    static constexpr int SMAX = NT + 1 - HF;           // tiles per wave in phase AA2
     static constexpr int EP_LD = KD + 4;               // padded row stride (floats)
     static constexpr int COL_LD = KD + 8;              // padded row stride (bf16)
     static constexpr int TILE_LD = 20;                 // padded 16x16 tile row stride
@@ -55,19 +61,20 @@ __device__ __forceinline__ int tri(int R, int J) { return R * (R + 1) / 2 + J; }
 // 16x16x16 split-bf16 product accumulate: acc += A_tile(fp32, LDS, row-major) * B_tile(fp32, LDS)
 __device__ __forceinline__ void tile_mma(f32x4& acc, const float* At, const float* Bt, int r16, int q4, int ld) {
     const float4 av = *reinterpret_cast<const float4*>(At + r16 * ld + 4 * q4);
-    const float aa[4] = {av.x, av.y, av.z, av.w};
     const float bb[4] = {Bt[(4 * q4 + 0) * ld + r16], Bt[(4 * q4 + 1) * ld + r16], Bt[(4 * q4 + 2) * ld + r16],
                          Bt[(4 * q4 + 3) * ld + r16]};
-    bf16x4 ah, al, bh, bl;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        short x, y;
-        split_bf(aa[e], x, y); ah[e] = x; al[e] = y;
-        split_bf(bb[e], x, y); bh[e] = x; bl[e] = y;
-    }
-    acc = mfma16(ah, bh, acc);
-    acc = mfma16(al, bh, acc);
-    acc = mfma16(ah, bl, acc);
+    uint32_t ah[2], al[2], bh[2], bl[2];
+    split_pk(av.x, av.y, ah[0], al[0]);
+    split_pk(av.z, av.w, ah[1], al[1]);
+    split_pk(bb[0], bb[1], bh[0], bl[0]);
+    split_pk(bb[2], bb[3], bh[1], bl[1]);
+    const bf16x4 Ah = __builtin_bit_cast(bf16x4, make_uint2(ah[0], ah[1]));
+    const bf16x4 Al = __builtin_bit_cast(bf16x4, make_uint2(al[0], al[1]));
+    const bf16x4 Bh = __builtin_bit_cast(bf16x4, make_uint2(bh[0], bh[1]));
+    const bf16x4 Bl = __builtin_bit_cast(bf16x4, make_uint2(bl[0], bl[1]));
+    acc = mfma16(Ah, Bh, acc);
+    acc = mfma16(Al, Bh, acc);
+    acc = mfma16(Ah, Bl, acc);
 }
 
 __device__ __forceinline__ void tile_store(float* Tt, const f32x4& v, float sgn, int r16, int q4, int ld) {
@@ -76,7 +83,7 @@ __device__ __forceinline__ void tile_store(float* Tt, const f32x4& v, float sgn,
 }
 
 template <int C, bool PER_DIM>
-__global__ __launch_bounds__(NTHREADS) void intra_kernel(
+__global__ __launch_bounds__(ITHREADS) void intra_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const float* __restrict__ g, const float* __restrict__ beta, ChunkMap map, int H, float scale,
     Work ws) {
@@ -109,10 +116,10 @@ __global__ __launch_bounds__(NTHREADS) void intra_kernel(
 
     // ------------------------------------------------------------------ phase E
     {
-        const int R = tid >> 5, d0 = 4 * (tid & 31);  // tile row R, columns d0..d0+3
+        const int R = tid >> 6, d0 = 2 * (tid & 63);  // tile row R, columns d0, d0 + 1
         const bool act = R < NT;
-        float gm4[16][4];
-        uint2 kr[16], vr[16];
+        float gm2[16][2];
+        uint32_t kr[16], vr[16];
         if (tid < C) {
             const float bv = beta[(size_t)(tok0 + min(tid, rows - 1)) * H + h];
             bet[tid] = (tid < rows) ? bv : 0.f;
@@ -124,100 +131,99 @@ __global__ __launch_bounds__(NTHREADS) void intra_kernel(
                 // loads stay unconditional and can all be in flight together
                 const int i = 16 * R + ii, ic = min(i, rows - 1);
                 const bool ok = i < rows;
-                float4 gv;
+                float2 gv;
                 if constexpr (PER_DIM) {
-                    gv = *reinterpret_cast<const float4*>(g + base + (size_t)ic * rs + d0);
+                    gv = *reinterpret_cast<const float2*>(g + base + (size_t)ic * rs + d0);
                 } else {
                     const float s1 = g[(size_t)(tok0 + ic) * H + h];
-                    gv = make_float4(s1, s1, s1, s1);
+                    gv = make_float2(s1, s1);
                 }
-                const uint2 kx = *reinterpret_cast<const uint2*>(k + base + (size_t)ic * rs + d0);
-                const uint2 vx = *reinterpret_cast<const uint2*>(v + base + (size_t)ic * rs + d0);
-                kr[ii] = ok ? kx : make_uint2(0, 0);
-                vr[ii] = ok ? vx : make_uint2(0, 0);
-                gm4[ii][0] = ok ? gv.x : 0.f; gm4[ii][1] = ok ? gv.y : 0.f;
-                gm4[ii][2] = ok ? gv.z : 0.f; gm4[ii][3] = ok ? gv.w : 0.f;
+                const uint32_t kx = *reinterpret_cast<const uint32_t*>(k + base + (size_t)ic * rs + d0);
+                const uint32_t vx = *reinterpret_cast<const uint32_t*>(v + base + (size_t)ic * rs + d0);
+                kr[ii] = ok ? kx : 0u;
+                vr[ii] = ok ? vx : 0u;
+                gm2[ii][0] = ok ? gv.x : 0.f;
+                gm2[ii][1] = ok ? gv.y : 0.f;
             }
 #pragma unroll
-            for (int ii = 1; ii < 16; ++ii)
-#pragma unroll
-                for (int c = 0; c < 4; ++c) gm4[ii][c] += gm4[ii - 1][c];
-            *reinterpret_cast<float4*>(ttot + R * KD + d0) = make_float4(gm4[15][0], gm4[15][1], gm4[15][2], gm4[15][3]);
+            for (int ii = 1; ii < 16; ++ii) {
+                gm2[ii][0] += gm2[ii - 1][0];
+                gm2[ii][1] += gm2[ii - 1][1];
+            }
+            *reinterpret_cast<float2*>(ttot + R * KD + d0) = make_float2(gm2[15][0], gm2[15][1]);
         }
         lds_barrier();
         if (act) {
-            float off[4] = {0.f, 0.f, 0.f, 0.f}, gcl[4] = {0.f, 0.f, 0.f, 0.f};
+            float off[2] = {0.f, 0.f}, gcl[2] = {0.f, 0.f};
             for (int Rp = 0; Rp < NT; ++Rp) {
-                const float4 t = *reinterpret_cast<const float4*>(ttot + Rp * KD + d0);
-                const float tv[4] = {t.x, t.y, t.z, t.w};
-#pragma unroll
-                for (int c = 0; c < 4; ++c) {
-                    if (Rp < R) off[c] += tv[c];
-                    gcl[c] += tv[c];
+                const float2 t = *reinterpret_cast<const float2*>(ttot + Rp * KD + d0);
+                if (Rp < R) {
+                    off[0] += t.x;
+                    off[1] += t.y;
                 }
+                gcl[0] += t.x;
+                gcl[1] += t.y;
             }
 #pragma unroll
-            for (int ii = 0; ii < 16; ++ii)
+            for (int ii = 0; ii < 16; ++ii) {
+                gm2[ii][0] += off[0];
+                gm2[ii][1] += off[1];
+            }
+            float gmv[2], e_gm[2], e_cm[2];
 #pragma unroll
-                for (int c = 0; c < 4; ++c) gm4[ii][c] += off[c];
-            float gmv[4], e_gm[4], e_cm[4];
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                gmv[c] = gm4[8][c];
+            for (int c = 0; c < 2; ++c) {
+                gmv[c] = gm2[8][c];
                 e_gm[c] = ex(gmv[c]);            // exp(gamma_m)
                 e_cm[c] = ex(gcl[c] - gmv[c]);   // exp(gamma_C - gamma_m) <= 1
             }
-            *reinterpret_cast<float4*>(gmid + R * KD + d0) = make_float4(gmv[0], gmv[1], gmv[2], gmv[3]);
-            *reinterpret_cast<float4*>(egm + R * KD + d0) = make_float4(e_gm[0], e_gm[1], e_gm[2], e_gm[3]);
-            if (R == 0)
-                *reinterpret_cast<float4*>(ws.gC + ch * KD + d0) =
-                    make_float4(ex(gcl[0]), ex(gcl[1]), ex(gcl[2]), ex(gcl[3]));
+            *reinterpret_cast<float2*>(gmid + R * KD + d0) = make_float2(gmv[0], gmv[1]);
+            *reinterpret_cast<float2*>(egm + R * KD + d0) = make_float2(e_gm[0], e_gm[1]);
+            if (R == 0) *reinterpret_cast<float2*>(ws.gC + ch * KD + d0) = make_float2(ex(gcl[0]), ex(gcl[1]));
             if constexpr (!PER_DIM) {
-                if ((tid & 31) == 0) {
+                if ((tid & 63) == 0) {
 #pragma unroll
-                    for (int ii = 0; ii < 16; ++ii) grow[16 * R + ii] = gm4[ii][0];
+                    for (int ii = 0; ii < 16; ++ii) grow[16 * R + ii] = gm2[ii][0];
                 }
             }
 #pragma unroll
             for (int hh = 0; hh < 2; ++hh) {
-                // transposed outputs of rows 16R + 8hh .. +7, packed two bf16 per register
-                uint32_t bwh[4][4], bwl[4][4], kgh[4][4], kgl[4][4], vtp[4][4];
+                // column-major outputs of rows 16R + 8hh .. +7, two bf16 (consecutive rows) per register
+                uint32_t bwh[2][4], bwl[2][4], kgh[2][4], kgl[2][4], vtp[2][4];
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const int ii = 8 * hh + e, i = 16 * R + ii;
-                    float kf[4], ep[4];
-                    kf[0] = __uint_as_float(kr[ii].x << 16); kf[1] = __uint_as_float(kr[ii].x & 0xffff0000u);
-                    kf[2] = __uint_as_float(kr[ii].y << 16); kf[3] = __uint_as_float(kr[ii].y & 0xffff0000u);
-                    const uint32_t vh[4] = {vr[ii].x & 0xffffu, vr[ii].x >> 16, vr[ii].y & 0xffffu, vr[ii].y >> 16};
-                    short chs[4], cls[4];
+                for (int e2 = 0; e2 < 4; ++e2) {
+                    float kf[2][2], ep[2][2], em[2][2];   // [row of the pair][column]
 #pragma unroll
-                    for (int c = 0; c < 4; ++c) {
-                        const float x = gm4[ii][c] - gmv[c];
-                        ep[c] = ex(x);             // exp(gamma_i - gamma_m)
-                        const float em = ex(-x);   // exp(gamma_m - gamma_i)
-                        if constexpr (PER_DIM) split_bf(kf[c] * em, chs[c], cls[c]);
-                        const float egi = e_gm[c] * ep[c];               // exp(gamma_i)
-                        short bh, bl, gh, gl;
-                        split_bf(kf[c] * egi, bh, bl);                   // beta enters through T diag(beta)
-                        split_bf(kf[c] * (em * e_cm[c]), gh, gl);        // exp(gamma_C - gamma_i) k
-                        if ((e & 1) == 0) {
-                            bwh[c][e >> 1] = (uint16_t)bh; bwl[c][e >> 1] = (uint16_t)bl;
-                            kgh[c][e >> 1] = (uint16_t)gh; kgl[c][e >> 1] = (uint16_t)gl;
-                            vtp[c][e >> 1] = vh[c];
-                        } else {
-                            bwh[c][e >> 1] |= (uint32_t)(uint16_t)bh << 16; bwl[c][e >> 1] |= (uint32_t)(uint16_t)bl << 16;
-                            kgh[c][e >> 1] |= (uint32_t)(uint16_t)gh << 16; kgl[c][e >> 1] |= (uint32_t)(uint16_t)gl << 16;
-                            vtp[c][e >> 1] |= vh[c] << 16;
+                    for (int rr = 0; rr < 2; ++rr) {
+                        const int ii = 8 * hh + 2 * e2 + rr;
+                        kf[rr][0] = __uint_as_float(kr[ii] << 16);
+                        kf[rr][1] = __uint_as_float(kr[ii] & 0xffff0000u);
+#pragma unroll
+                        for (int c = 0; c < 2; ++c) {
+                            const float x = gm2[ii][c] - gmv[c];
+                            ep[rr][c] = ex(x);     // exp(gamma_i - gamma_m)
+                            em[rr][c] = ex(-x);    // exp(gamma_m - gamma_i)
+                        }
+                        if constexpr (PER_DIM) {
+                            const int i = 16 * R + ii;
+                            *reinterpret_cast<float2*>(Ep + i * S::EP_LD + d0) = make_float2(ep[rr][0], ep[rr][1]);
+                            uint32_t chv, clv;
+                            split_pk(kf[rr][0] * em[rr][0], kf[rr][1] * em[rr][1], chv, clv);
+                            *reinterpret_cast<uint32_t*>(colh + i * S::COL_LD + d0) = chv;
+                            *reinterpret_cast<uint32_t*>(coll + i * S::COL_LD + d0) = clv;
                         }
                     }
-                    if constexpr (PER_DIM) {
-                        *reinterpret_cast<float4*>(Ep + i * S::EP_LD + d0) = make_float4(ep[0], ep[1], ep[2], ep[3]);
-                        *reinterpret_cast<uint2*>(colh + i * S::COL_LD + d0) = pack4(chs);
-                        *reinterpret_cast<uint2*>(coll + i * S::COL_LD + d0) = pack4(cls);
+#pragma unroll
+                    for (int c = 0; c < 2; ++c) {
+                        // exp(gamma_i) k (beta enters through T diag(beta)) and exp(gamma_C - gamma_i) k
+                        split_pk(kf[0][c] * (e_gm[c] * ep[0][c]), kf[1][c] * (e_gm[c] * ep[1][c]), bwh[c][e2], bwl[c][e2]);
+                        split_pk(kf[0][c] * (em[0][c] * e_cm[c]), kf[1][c] * (em[1][c] * e_cm[c]), kgh[c][e2], kgl[c][e2]);
                     }
+                    const uint32_t v0 = vr[8 * hh + 2 * e2], v1 = vr[8 * hh + 2 * e2 + 1];
+                    vtp[0][e2] = (v0 & 0xffffu) | (v1 << 16);
+                    vtp[1][e2] = (v0 >> 16) | (v1 & 0xffff0000u);
                 }
 #pragma unroll
-                for (int c = 0; c < 4; ++c) {
+                for (int c = 0; c < 2; ++c) {
                     // (K, C) / (V, C) fragment (d / 16, R / 2): rows 16 R + 8 hh .. +7 of column d
                     // are exactly the 16-byte slot of lane (d % 16) + 16 (2 (R % 2) + hh)
                     const int d = d0 + c;
@@ -233,7 +239,7 @@ __global__ __launch_bounds__(NTHREADS) void intra_kernel(
         lds_barrier();
         if constexpr (PER_DIM) {
             // strictly lower pairs p = R(R-1)/2 + J: F = exp(gamma_m(R) - gamma_m(J)) <= 1
-            for (int e = 4 * tid; e < S::NOFF * KD; e += 4 * NTHREADS) {
+            for (int e = 4 * tid; e < S::NOFF * KD; e += 4 * ITHREADS) {
                 const int p = e / KD, d = e % KD;
                 const int R = (int)((1.f + __builtin_sqrtf(8.f * p + 1.f)) * 0.5f);  // R(R-1)/2 <= p < R(R+1)/2
                 const int J = p - R * (R - 1) / 2;
@@ -244,31 +250,32 @@ __global__ __launch_bounds__(NTHREADS) void intra_kernel(
         }
     }
     lds_barrier();
-    // row-operand fragments of phase AA2 (rows w and NT-1-w)
-    const bool aa_active = wave < NT / 2;
-    const int Rown[2] = {wave, NT - 1 - wave};
+
+    // ------------------------------------------------------------------ phase AA2
+    // waves w and w + 4 share tile rows cp = w % 4 and NT-1-cp: NT+1 tiles, HF for the first
+    const int cp = wave & 3, part = wave >> 2;
+    const bool aa_active = cp < NT / 2;
+    const int Rown[2] = {cp, NT - 1 - cp};
     uint4 kfr[2][KD / 32], qfr[2][KD / 32];
 #pragma unroll
     for (int o = 0; o < 2; ++o)
 #pragma unroll
         for (int ks = 0; ks < KD / 32; ++ks) {
-            const int i = 16 * Rown[o] + r16, ic = min(i, rows - 1);
+            const int i = 16 * Rown[o] + r16, ic = min(max(i, 0), rows - 1);
             const uint4 kx = *reinterpret_cast<const uint4*>(k + base + (size_t)ic * rs + 32 * ks + 8 * q4);
             const uint4 qx = *reinterpret_cast<const uint4*>(q + base + (size_t)ic * rs + 32 * ks + 8 * q4);
             kfr[o][ks] = (i < rows) ? kx : make_uint4(0, 0, 0, 0);
             qfr[o][ks] = (i < rows) ? qx : make_uint4(0, 0, 0, 0);
         }
-
-    // ------------------------------------------------------------------ phase AA2
     f32x4 accA[S::SMAX];
 #pragma unroll
     for (int s = 0; s < S::SMAX; ++s) {
         accA[s] = f32x4{0.f, 0.f, 0.f, 0.f};
-        if (!aa_active) continue;
-        const int o = (s <= wave) ? 0 : 1;          // which owned row
+        const int p = (part ? S::HF : 0) + s;  // position in the row pair's tile list
+        if (!aa_active || p >= NT + 1 || (part == 0 && s >= S::HF)) continue;
+        const int o = (p <= cp) ? 0 : 1;
         const int R = Rown[o];
-        const int J = (o == 0) ? s : s - wave - 1;
-        if (J > R) continue;
+        const int J = (o == 0) ? p : p - cp - 1;
         const int i = 16 * R + r16, j = 16 * J + r16;
         f32x4 acc = {0.f, 0.f, 0.f, 0.f}, acc2 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -289,8 +296,7 @@ __global__ __launch_bounds__(NTHREADS) void intra_kernel(
                     const float4 f0 = fp[0], f1 = fp[1];
                     ep[0] *= f0.x; ep[1] *= f0.y; ep[2] *= f0.z; ep[3] *= f0.w;
                     ep[4] *= f1.x; ep[5] *= f1.y; ep[6] *= f1.z; ep[7] *= f1.w;
-                }
-                if (J == R) {
+                } else {
                     // qg = scale q exp(gamma) = scale q Ep exp(gamma_m): (C, K) fragment (R, ks)
                     const float4* gp = reinterpret_cast<const float4*>(egm + R * KD + dd);
                     const float4 g0 = gp[0], g1 = gp[1];
@@ -302,21 +308,22 @@ __global__ __launch_bounds__(NTHREADS) void intra_kernel(
                     pq.w = pack_bf2(scale * qf[6] * ep[6] * eg[6], scale * qf[7] * ep[7] * eg[7]);
                     *reinterpret_cast<uint4*>(ws.qg + ch * C * KD + frag(R, ks, KD / 32) + lane * 8) = pq;
                 }
-                bf16x8 ahi, alo, aq;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    short hh, ll;
-                    split_bf(kf[e] * ep[e], hh, ll);
-                    ahi[e] = hh;
-                    alo[e] = ll;
-                    aq[e] = (short)f2bf(qf[e] * ep[e]);
-                }
+                uint4 ah, al, aq;
+                split_pk(kf[0] * ep[0], kf[1] * ep[1], ah.x, al.x);
+                split_pk(kf[2] * ep[2], kf[3] * ep[3], ah.y, al.y);
+                split_pk(kf[4] * ep[4], kf[5] * ep[5], ah.z, al.z);
+                split_pk(kf[6] * ep[6], kf[7] * ep[7], ah.w, al.w);
+                aq.x = pack_bf2(qf[0] * ep[0], qf[1] * ep[1]);
+                aq.y = pack_bf2(qf[2] * ep[2], qf[3] * ep[3]);
+                aq.z = pack_bf2(qf[4] * ep[4], qf[5] * ep[5]);
+                aq.w = pack_bf2(qf[6] * ep[6], qf[7] * ep[7]);
+                const bf16x8 ahi = as_bf16x8(ah), alo = as_bf16x8(al), aqv = as_bf16x8(aq);
                 const bf16x8 bhi = as_bf16x8(*reinterpret_cast<const uint4*>(colh + j * S::COL_LD + dd));
                 const bf16x8 blo = as_bf16x8(*reinterpret_cast<const uint4*>(coll + j * S::COL_LD + dd));
                 acc = mfma32(ahi, bhi, acc);
                 acc = mfma32(alo, bhi, acc);
                 acc = mfma32(ahi, blo, acc);
-                acc2 = mfma32(bhi, aq, acc2);   // A2^T tile: rows j, columns i
+                acc2 = mfma32(bhi, aqv, acc2);   // A2^T tile: rows j, columns i
             } else {
                 const uint4 kx = *reinterpret_cast<const uint4*>(k + base + (size_t)min(j, rows - 1) * rs + dd);
                 const bf16x8 b = as_bf16x8((j < rows) ? kx : make_uint4(0, 0, 0, 0));
@@ -358,17 +365,17 @@ __global__ __launch_bounds__(NTHREADS) void intra_kernel(
     // ------------------------------------------------------------------ phase INV
 #pragma unroll
     for (int s = 0; s < S::SMAX; ++s) {
-        if (!aa_active) continue;
-        const int o = (s <= wave) ? 0 : 1;
+        const int p = (part ? S::HF : 0) + s;
+        if (!aa_active || p >= NT + 1 || (part == 0 && s >= S::HF)) continue;
+        const int o = (p <= cp) ? 0 : 1;
         const int R = Rown[o];
-        const int J = (o == 0) ? s : s - wave - 1;
-        if (J > R) continue;
+        const int J = (o == 0) ? p : p - cp - 1;
         tile_store(Atile + tri(R, J) * S::TILE_SZ, accA[s], 1.f, r16, q4, S::TILE_LD);
     }
     lds_barrier();
-    {   // diagonal blocks: T_RR = (I + A_RR)^-1, lane r16 owns column r16
-        const int R = wave + 4 * q4;
-        if (q4 < 2 && R < NT) {
+    {   // diagonal blocks: T_RR = (I + A_RR)^-1, wave R, lane r16 owns column r16
+        const int R = wave;
+        if (q4 == 0 && R < NT) {
             const float* Ad = Atile + tri(R, R) * S::TILE_SZ;
             const int jc = r16;
             float t[16];
@@ -391,7 +398,7 @@ __global__ __launch_bounds__(NTHREADS) void intra_kernel(
         const int npair = NT / (2 * m);
         const int ntile = npair * m * m;      // output tiles per step
         // step 1: P[r][c] = sum_{x >= c} A21[r][x] T11[x][c]
-        for (int t = wave; t < ntile; t += 4) {
+        for (int t = wave; t < ntile; t += IWAVES) {
             const int p = t / (m * m), rc = t % (m * m);
             const int r = (rc / m + rc % m) % m, c = rc % m;   // spread the long sums over waves
             const int b1 = 2 * p * m, b2 = b1 + m;
@@ -403,7 +410,7 @@ __global__ __launch_bounds__(NTHREADS) void intra_kernel(
         }
         lds_barrier();
         // step 2: T21[r][c] = -sum_{x <= r} T22[r][x] P[x][c]
-        for (int t = wave; t < ntile; t += 4) {
+        for (int t = wave; t < ntile; t += IWAVES) {
             const int p = t / (m * m), rc = t % (m * m);
             const int r = rc / m, c = (rc / m + rc % m) % m;
             const int b1 = 2 * p * m, b2 = b1 + m;
@@ -419,21 +426,17 @@ __global__ __launch_bounds__(NTHREADS) void intra_kernel(
     // ------------------------------------------------------------------ phase WU
     // phase E's global stores (read back here) are visible to the whole workgroup
     __syncthreads();
-    // right-hand-side fragments of phase WU (written above by this workgroup)
-    uint4 bwh_f[NS][2], bwl_f[NS][2], vt_f[NS][2];
+    const int dt = wave;  // 16-block of K (for w) and of V (for u) this wave produces
+    uint4 bwh_f[NS], bwl_f[NS], vt_f[NS];
 #pragma unroll
-    for (int s = 0; s < NS; ++s)
-#pragma unroll
-        for (int ct = 0; ct < 2; ++ct) {
-            const size_t off = ch * KD * C + frag(2 * wave + ct, s, C / 32) + lane * 8;
-            bwh_f[s][ct] = *reinterpret_cast<const uint4*>(ws.bwT_hi + off);
-            bwl_f[s][ct] = *reinterpret_cast<const uint4*>(ws.bwT_lo + off);
-            vt_f[s][ct] = *reinterpret_cast<const uint4*>(ws.vT + off);
-        }
-
+    for (int s = 0; s < NS; ++s) {
+        const size_t off = ch * KD * C + frag(dt, s, C / 32) + lane * 8;
+        bwh_f[s] = *reinterpret_cast<const uint4*>(ws.bwT_hi + off);
+        bwl_f[s] = *reinterpret_cast<const uint4*>(ws.bwT_lo + off);
+        vt_f[s] = *reinterpret_cast<const uint4*>(ws.vT + off);
+    }
     for (int R = 0; R < NT; ++R) {
-        f32x4 accw[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-        f32x4 accu[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+        f32x4 accw = {0.f, 0.f, 0.f, 0.f}, accu = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
             if (2 * s > R) break;
@@ -450,34 +453,24 @@ __global__ __launch_bounds__(NTHREADS) void intra_kernel(
 #pragma unroll
                 for (int e = 0; e < 8; ++e) tv[e] = 0.f;
             }
-            bf16x8 thi, tlo;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                short x, y;
-                split_bf(tv[e] * bet[jb + e], x, y);
-                thi[e] = x;
-                tlo[e] = y;
-            }
-#pragma unroll
-            for (int ct = 0; ct < 2; ++ct) {
-                const bf16x8 bwh = as_bf16x8(bwh_f[s][ct]), bwl = as_bf16x8(bwl_f[s][ct]);
-                const bf16x8 vv = as_bf16x8(vt_f[s][ct]);
-                // w^T tile (rows d, columns i) = (exp(gamma) k)^T T'^T; u tile = T' v
-                accw[ct] = mfma32(bwh, thi, accw[ct]);
-                accw[ct] = mfma32(bwl, thi, accw[ct]);
-                accw[ct] = mfma32(bwh, tlo, accw[ct]);
-                accu[ct] = mfma32(thi, vv, accu[ct]);
-                accu[ct] = mfma32(tlo, vv, accu[ct]);
-            }
+            uint4 th, tl;
+            split_pk(tv[0] * bet[jb + 0], tv[1] * bet[jb + 1], th.x, tl.x);
+            split_pk(tv[2] * bet[jb + 2], tv[3] * bet[jb + 3], th.y, tl.y);
+            split_pk(tv[4] * bet[jb + 4], tv[5] * bet[jb + 5], th.z, tl.z);
+            split_pk(tv[6] * bet[jb + 6], tv[7] * bet[jb + 7], th.w, tl.w);
+            const bf16x8 thi = as_bf16x8(th), tlo = as_bf16x8(tl);
+            const bf16x8 bwh = as_bf16x8(bwh_f[s]), bwl = as_bf16x8(bwl_f[s]), vv = as_bf16x8(vt_f[s]);
+            // w^T tile (rows d, columns i) = (exp(gamma) k)^T T'^T; u tile = T' v
+            accw = mfma32(bwh, thi, accw);
+            accw = mfma32(bwl, thi, accw);
+            accw = mfma32(bwh, tlo, accw);
+            accu = mfma32(thi, vv, accu);
+            accu = mfma32(tlo, vv, accu);
         }
-#pragma unroll
-        for (int ct = 0; ct < 2; ++ct) {
-            const int dt = 2 * wave + ct;   // 16-block of K (for w) and of V (for u)
-            *reinterpret_cast<uint2*>(ws.w + ch * C * KD + frag(R, dt >> 1, KD / 32) + fragT(dt & 1, r16, q4)) =
-                make_uint2(pack_bf2(accw[ct][0], accw[ct][1]), pack_bf2(accw[ct][2], accw[ct][3]));
-            *reinterpret_cast<float4*>(ws.uT + ch * C * VD + ((size_t)(R * (VD / 16) + dt) * 64 + lane) * 4) =
-                make_float4(accu[ct][0], accu[ct][1], accu[ct][2], accu[ct][3]);
-        }
+        *reinterpret_cast<uint2*>(ws.w + ch * C * KD + frag(R, dt >> 1, KD / 32) + fragT(dt & 1, r16, q4)) =
+            make_uint2(pack_bf2(accw[0], accw[1]), pack_bf2(accw[2], accw[3]));
+        *reinterpret_cast<float4*>(ws.uT + ch * C * VD + ((size_t)(R * (VD / 16) + dt) * 64 + lane) * 4) =
+            make_float4(accu[0], accu[1], accu[2], accu[3]);
     }
 }
 
@@ -485,7 +478,7 @@ template <int C, bool PER_DIM>
 static hipError_t launch_intra_t(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float* g,
                                  const float* beta, const ChunkMap& map, int nslots, int H, float scale,
                                  const Work& ws, hipStream_t stream) {
-    hipLaunchKernelGGL((intra_kernel<C, PER_DIM>), dim3(nslots, H), dim3(NTHREADS), 0, stream, q, k, v, g,
+    hipLaunchKernelGGL((intra_kernel<C, PER_DIM>), dim3(nslots, H), dim3(ITHREADS), 0, stream, q, k, v, g,
                        beta, map, H, scale, ws);
     return hipGetLastError();
 }
