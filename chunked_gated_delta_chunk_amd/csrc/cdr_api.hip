@@ -5,9 +5,9 @@
 namespace cdr {
 hipError_t launch_intra(int C, bool per_dim, const uint16_t* q, const uint16_t* k, const uint16_t* v,
                         const float* g, const float* beta, const ChunkMap& map, int nslots, int H,
-                        float scale, const Work& ws, hipStream_t stream);
-hipError_t launch_chain(int C, int BV, const ChunkMap& map, int N, int H, const float* s0, float* s_out,
-                        const Work& ws, hipStream_t stream);
+                        float scale, const Work& ws, int nscratch, hipStream_t stream);
+hipError_t launch_chain(const ChunkMap& map, int N, int H, const float* s0, float* s_out, const Work& ws,
+                        hipStream_t stream);
 hipError_t launch_output(int C, const ChunkMap& map, int nslots, int H, uint16_t* o, const Work& ws,
                          hipStream_t stream);
 }  // namespace cdr
@@ -24,31 +24,41 @@ int64_t num_slots(const cdr_problem* p) {
     return (int64_t)p->B * ((p->T + p->chunk_size - 1) / p->chunk_size);
 }
 
+constexpr int kArrays = 14;
+constexpr int64_t kScratchSlots = 512; // at most this many intra workgroups run at once
+
+size_t scratch_slots(const cdr_problem* p) {
+    const int64_t nch = num_slots(p) * p->H;
+    return (size_t)(nch < kScratchSlots ? nch : kScratchSlots);
+}
+
 struct Layout {
-    size_t off[12];
+    size_t off[kArrays];
     size_t total;
 };
 
 Layout layout(const cdr_problem* p) {
-    const size_t nch = (size_t)num_slots(p) * (size_t)p->H;
+    const size_t nch = (size_t)num_slots(p) * (size_t)p->H, nsc = scratch_slots(p);
     const size_t C = (size_t)p->chunk_size, K = (size_t)p->K, V = (size_t)p->V;
-    const size_t bytes[12] = {
-        nch * C * K * 2,  // w
-        nch * V * C * 4,  // uT
-        nch * K * C * 2,  // kgT_hi
-        nch * K * C * 2,  // kgT_lo
-        nch * C * K * 2,  // qg
-        nch * C * C * 2,  // A2
+    const size_t bytes[kArrays] = {
+        nch * K * K * 2,  // Pn_hi
+        nch * K * K * 2,  // Pn_lo
+        nch * K * V * 4,  // Bm
+        nch * C * K * 2,  // Qp
+        nch * C * V * 2,  // Up
         nch * K * 4,      // gC
         nch * V * K * 2,  // Sc
-        nch * V * C * 2,  // vnT
-        nch * K * C * 2,  // bwT_hi
-        nch * K * C * 2,  // bwT_lo
-        nch * V * C * 2,  // vT
+        nsc * K * C * 2,  // bwT_hi
+        nsc * K * C * 2,  // bwT_lo
+        nsc * V * C * 2,  // vT
+        nsc * K * C * 2,  // kgT_hi
+        nsc * K * C * 2,  // kgT_lo
+        nsc * C * C * 2,  // A2s
+        nsc * C * K * 2,  // qgs
     };
     Layout L;
     size_t at = 0;
-    for (int i = 0; i < 12; ++i) {
+    for (int i = 0; i < kArrays; ++i) {
         L.off[i] = at;
         at += align_up(bytes[i]);
     }
@@ -100,18 +110,20 @@ cdr_status chunk_dr_fwd_stages(const cdr_problem* p, const void* q, const void* 
 
     char* wb = static_cast<char*>(workspace);
     cdr::Work ws;
-    ws.w = reinterpret_cast<uint16_t*>(wb + L.off[0]);
-    ws.uT = reinterpret_cast<float*>(wb + L.off[1]);
-    ws.kgT_hi = reinterpret_cast<uint16_t*>(wb + L.off[2]);
-    ws.kgT_lo = reinterpret_cast<uint16_t*>(wb + L.off[3]);
-    ws.qg = reinterpret_cast<uint16_t*>(wb + L.off[4]);
-    ws.A2 = reinterpret_cast<uint16_t*>(wb + L.off[5]);
-    ws.gC = reinterpret_cast<float*>(wb + L.off[6]);
-    ws.Sc = reinterpret_cast<uint16_t*>(wb + L.off[7]);
-    ws.vnT = reinterpret_cast<uint16_t*>(wb + L.off[8]);
-    ws.bwT_hi = reinterpret_cast<uint16_t*>(wb + L.off[9]);
-    ws.bwT_lo = reinterpret_cast<uint16_t*>(wb + L.off[10]);
-    ws.vT = reinterpret_cast<uint16_t*>(wb + L.off[11]);
+    ws.Pn_hi = reinterpret_cast<uint16_t*>(wb + L.off[0]);
+    ws.Pn_lo = reinterpret_cast<uint16_t*>(wb + L.off[1]);
+    ws.Bm = reinterpret_cast<float*>(wb + L.off[2]);
+    ws.Qp = reinterpret_cast<uint16_t*>(wb + L.off[3]);
+    ws.Up = reinterpret_cast<uint16_t*>(wb + L.off[4]);
+    ws.gC = reinterpret_cast<float*>(wb + L.off[5]);
+    ws.Sc = reinterpret_cast<uint16_t*>(wb + L.off[6]);
+    ws.bwT_hi = reinterpret_cast<uint16_t*>(wb + L.off[7]);
+    ws.bwT_lo = reinterpret_cast<uint16_t*>(wb + L.off[8]);
+    ws.vT = reinterpret_cast<uint16_t*>(wb + L.off[9]);
+    ws.kgT_hi = reinterpret_cast<uint16_t*>(wb + L.off[10]);
+    ws.kgT_lo = reinterpret_cast<uint16_t*>(wb + L.off[11]);
+    ws.A2s = reinterpret_cast<uint16_t*>(wb + L.off[12]);
+    ws.qgs = reinterpret_cast<uint16_t*>(wb + L.off[13]);
 
     cdr::ChunkMap map;
     map.cu = p->varlen ? cu_seqlens : nullptr;
@@ -125,17 +137,15 @@ cdr_status chunk_dr_fwd_stages(const cdr_problem* p, const void* q, const void* 
     const float* s0 = p->has_initial_state ? initial_state : nullptr;
     float* s_out = p->output_final_state ? final_state : nullptr;
     const int C = p->chunk_size;
-    // value-column blocks per chain: 16 columns unless there are enough chains to fill the chip
-    const int BV = ((int64_t)p->N * p->H * 4 >= 512) ? 32 : 16;
 
     if ((stages & CDR_STAGE_INTRA) && nslots > 0) {
         if (cdr::launch_intra(C, p->gate == CDR_GATE_PER_DIM, static_cast<const uint16_t*>(q),
                               static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), g, beta, map,
-                              nslots, p->H, p->scale, ws, s) != hipSuccess)
+                              nslots, p->H, p->scale, ws, (int)scratch_slots(p), s) != hipSuccess)
             return CDR_ERR_HIP;
     }
     if (stages & CDR_STAGE_CHAIN) {
-        if (cdr::launch_chain(C, BV, map, p->N, p->H, s0, s_out, ws, s) != hipSuccess) return CDR_ERR_HIP;
+        if (cdr::launch_chain(map, p->N, p->H, s0, s_out, ws, s) != hipSuccess) return CDR_ERR_HIP;
     }
     if ((stages & CDR_STAGE_OUTPUT) && nslots > 0) {
         if (cdr::launch_output(C, map, nslots, p->H, static_cast<uint16_t*>(o), ws, s) != hipSuccess)

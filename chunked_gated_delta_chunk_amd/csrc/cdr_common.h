@@ -97,6 +97,14 @@ __device__ __forceinline__ void lds_barrier() {
     asm volatile("" ::: "memory");
 }
 
+// 16-byte global-to-LDS copy of one 1 KiB fragment by one wave: lane l moves the 16 bytes
+// at gfrag + 8 l to lfrag + 8 l (elements).  lfrag must be the same for the whole wave.  The
+// copy is counted by vmcnt: wait for it with __syncthreads() (not lds_barrier()).
+__device__ __forceinline__ void frag_to_lds(const uint16_t* gfrag, uint16_t* lfrag, int lane) {
+    __builtin_amdgcn_global_load_lds(static_cast<const void*>(gfrag + lane * 8),
+                                     (__attribute__((address_space(3))) void*)(lfrag), 16, 0, 0);
+}
+
 // ---------------------------------------------------------------------------------------
 // Chunk map. Tokens are packed along one axis; sequence n owns tokens [bos, bos + len).
 // Fixed length: bos = n*T, len = T, and sequence n owns chunk slots
@@ -167,22 +175,38 @@ __device__ __forceinline__ size_t frag(int a, int b, int nb) { return ((size_t)a
 // within the fragment's 32, tile column = non-contracted index r): four consecutive slots.
 __device__ __forceinline__ int fragT(int t, int r, int q) { return (r + 16 * (2 * t + (q >> 1))) * 8 + 4 * (q & 1); }
 
+// Interleaved contraction order.  A 16x16 accumulator tile leaves lane (r, q) holding rows
+// 4 q .. 4 q + 3 of column r, which is the operand layout of the 16x16x16 instruction.  Two
+// such tiles (contracted rows 0-15 and 16-31) feed one 16x16x32 instruction directly from
+// registers when the other operand lists its 32 contracted indices in the same order:
+// lane slot i of lane group q holds contracted index 16 (i / 4) + 4 q + i % 4.  Arrays
+// stored in this order ("pi order") are fragment-major like the others; inside fragment
+// (a, b), tile t = 0, 1 of the pair puts the four values of lane (r, q) at
+__device__ __forceinline__ int fragP(int t, int r, int q) { return (r + 16 * q) * 8 + 4 * t; }
+
 // Per-chunk intermediates in the workspace; index ch = slot * H + h.  Shapes name
-// (non-contracted, contracted) for fragment-major arrays.
+// (non-contracted, contracted) for fragment-major arrays.  The state update of a chunk is
+// re-associated as  S' = exp(gamma_C) S - P S + B  with P = kg^T w and B = kg^T u, and its
+// output as  o = Q S + U  with Q = qg - A2 w and U = A2 u, so the sequential kernel only
+// needs P, B and exp(gamma_C).
 struct Work {
-    uint16_t* w;       // (C, K) frag  bf16   w = (I+A)^-1 diag(beta) (exp(gamma) * k); A of w S
-    float* uT;         // D tiles      fp32   u = (I+A)^-1 diag(beta) v, (C/16) x (V/16) tiles of
-                       //                     64 lanes x 4 rows, the layout of the w S accumulator
-    uint16_t* kgT_hi;  // (K, C) frag  bf16   exp(gamma_C - gamma) * k, high part; A of kg^T v_new
-    uint16_t* kgT_lo;  // (K, C) frag  bf16   low part
-    uint16_t* qg;      // (C, K) frag  bf16   scale * q * exp(gamma); A of qg S
-    uint16_t* A2;      // (C, C) frag  bf16   in-chunk output block (j <= i), lower fragments only
-    float* gC;         // [K]          fp32   exp(gamma_C)
-    uint16_t* Sc;      // (V, K) frag  bf16   state entering the chunk; B of qg S
-    uint16_t* vnT;     // (V, C) frag  bf16   corrected values v_new; B of A2 v_new
-    uint16_t* bwT_hi;  // (K, C) frag  bf16   exp(gamma) * k, high part (intra scratch)
-    uint16_t* bwT_lo;  // (K, C) frag  bf16   low part
-    uint16_t* vT;      // (V, C) frag  bf16   v (intra scratch)
+    uint16_t* Pn_hi;   // (K, K) frag pi bf16   -P, high part; A operand of -P S
+    uint16_t* Pn_lo;   // (K, K) frag pi bf16   low part
+    float* Bm;         // D tiles        fp32   B = kg^T u, (K/16) x (V/16) tiles of 64 lanes x 4
+                       //                       rows, the layout of the state accumulator
+    uint16_t* Qp;      // (C, K) frag pi bf16   Q = qg - A2 w; B operand of (Q S)^T
+    uint16_t* Up;      // D tiles        bf16   U^T = (A2 u)^T, (C/16) x (V/16) tiles, the layout
+                       //                       of the transposed output accumulator
+    float* gC;         // [K]            fp32   exp(gamma_C)
+    uint16_t* Sc;      // (V, K) frag pi bf16   state entering the chunk; A operand of (Q S)^T
+    // scratch of the intra kernel (written and read back by the same workgroup)
+    uint16_t* bwT_hi;  // (K, C) frag    bf16   exp(gamma) * k, high part
+    uint16_t* bwT_lo;  // (K, C) frag    bf16   low part
+    uint16_t* vT;      // (V, C) frag    bf16   v
+    uint16_t* kgT_hi;  // (K, C) frag pi bf16   exp(gamma_C - gamma) * k, high part
+    uint16_t* kgT_lo;  // (K, C) frag pi bf16   low part
+    uint16_t* A2s;     // (C, C) frag pi bf16   in-chunk output block (j <= i), lower fragments
+    uint16_t* qgs;     // D tiles        bf16   (scale * q * exp(gamma))^T, (C/16) x (K/16) tiles
 };
 
 }  // namespace cdr

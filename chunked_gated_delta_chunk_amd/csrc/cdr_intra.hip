@@ -8,24 +8,32 @@
 //   E    every thread owns a 16-row x 2-column block of the chunk (one 16-row tile) and
 //        issues all of its loads (g, k, v) at once.  gamma = prefix sum of g inside the tile
 //        plus the totals of the tiles above (through LDS).  Per-element decay factors
-//        relative to the tile's middle row m, and the element-wise outputs: kg (split),
-//        exp(gamma_C), exp(gamma) k (split, scratch) and v (scratch), fragment-major.
+//        relative to the tile's middle row m, and the element-wise outputs: exp(gamma_C),
+//        kg = exp(gamma_C - gamma) k (split), exp(gamma) k (split) and v, fragment-major
+//        (scratch read back by this workgroup).
 //   AA2  16x16 tiles of A (strictly lower, times beta) and A2 (lower incl. diagonal, times
 //        scale) on bf16 MFMA.  Per-dimension gates enter the operands through the tile
 //        pivots: for rows i in tile R and columns j in tile J <= R,
 //          exp(g_i - g_j) = [exp(g_i - g_m(R)) exp(g_m(R) - g_m(J))] * exp(g_m(J) - g_j)
 //        so no factor exceeds exp(half a tile's gate span) and the product never
 //        overflows.  A uses hi/lo split operands (three MFMAs); A2 feeds only the output
-//        and uses single bf16 operands (stored transposed).  Per-head gates use raw q, k
-//        (exact bf16 products) and apply the scalar decay afterwards.  Tile rows w and
-//        NT-1-w form one list of NT+1 tiles shared by waves w and w+4.  qg is produced on
-//        the diagonal tiles.
+//        and uses single bf16 operands (stored transposed, scratch).  Per-head gates use
+//        raw q, k (exact bf16 products) and apply the scalar decay afterwards.  Tile rows w
+//        and NT-1-w form one list of NT+1 tiles shared by waves w and w+4.  qg (scratch) is
+//        produced on the diagonal tiles.
 //   INV  T = (I + A)^-1 by block-triangular inversion: the 16x16 diagonal blocks by
 //        forward substitution in fp32, then blocks are merged 16->32->64->128 with
 //        T21 = -T22 (A21 T11), two tile-parallel steps per level on split-bf16 MFMAs.
-//   WU   w^T = (exp(gamma) k)^T T'^T and u = T' v with T' = T diag(beta), split-bf16 MFMAs;
-//        wave w produces 16 columns of each.
+//   WU   w = T' (exp(gamma) k) and u = T' v with T' = T diag(beta), split-bf16 MFMAs; wave
+//        w keeps 16 columns of each in registers, as accumulator tiles.
+//   PQ   the factors of the re-associated chunk step (section M4):
+//          P = kg^T w, B = kg^T u          (split-bf16, they carry the state)
+//          Q = qg - A2 w, U = A2 u         (single bf16, they only reach the output)
+//        The w and u tiles are used as MFMA operands straight from registers (pi order),
+//        kg^T and A2 are staged in LDS by direct global-to-LDS loads issued during WU.
 #include "cdr_common.h"
+
+#include <atomic>
 
 namespace cdr {
 
@@ -82,14 +90,33 @@ __device__ __forceinline__ void tile_store(float* Tt, const f32x4& v, float sgn,
     for (int rr = 0; rr < 4; ++rr) Tt[(4 * q4 + rr) * ld + r16] = sgn * v[rr];
 }
 
+// qg values of lane (r, q) of a diagonal tile R, columns 32 ks + 8 q .. + 7, into the
+// accumulator layout of (qg)^T tiles (rows d, columns i): tile (R, d / 16), lane
+// (i % 16) + 16 ((d % 16) / 4), element d % 4
+__device__ __forceinline__ void store_qg(uint16_t* base, int R, int ks, int r, int q, const uint4& pq) {
+    uint16_t* t = base + (size_t)(R * (KD / 16) + 2 * ks + (q >> 1)) * 256;
+    *reinterpret_cast<uint2*>(t + (r + 16 * (2 * (q & 1))) * 4) = make_uint2(pq.x, pq.y);
+    *reinterpret_cast<uint2*>(t + (r + 16 * (2 * (q & 1) + 1)) * 4) = make_uint2(pq.z, pq.w);
+}
+
+// Position of A2 fragment (I, s), s <= I / 2, in the list of lower fragments
+__device__ __forceinline__ int a2_slot(int I, int s) {
+    const int h = I >> 1;
+    return I + ((I & 1) ? h * h : h * (h - 1)) + s;
+}
+
+__device__ __forceinline__ uint4 neg_bf16x8(const uint4& a) {
+    return make_uint4(a.x ^ 0x80008000u, a.y ^ 0x80008000u, a.z ^ 0x80008000u, a.w ^ 0x80008000u);
+}
+
+// One (chunk slot, head) item.  sc is the workgroup's scratch slot.
 template <int C, bool PER_DIM>
-__global__ __launch_bounds__(ITHREADS) void intra_kernel(
+__device__ __forceinline__ void intra_item(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    const float* __restrict__ g, const float* __restrict__ beta, ChunkMap map, int H, float scale,
-    Work ws) {
+    const float* __restrict__ g, const float* __restrict__ beta, const ChunkMap& map, int H, float scale,
+    const Work& ws, unsigned char* smem, int slot, int h, size_t sc) {
     using S = IntraShape<C>;
     constexpr int NT = S::NT, NS = S::NS;
-    __shared__ __attribute__((aligned(16))) unsigned char smem[S::BYTES];
     float* Ep = reinterpret_cast<float*>(smem);                                   // [C][EP_LD]
     uint16_t* colh = reinterpret_cast<uint16_t*>(smem + S::R1);                   // [C][COL_LD]
     uint16_t* coll = colh + C * S::COL_LD;
@@ -103,13 +130,16 @@ __global__ __launch_bounds__(ITHREADS) void intra_kernel(
     float* Pscr = Atile + S::NPAIR * S::TILE_SZ;                                  // merge scratch
     float* Ttile = reinterpret_cast<float*>(smem + S::R1);
 
-    const int slot = blockIdx.x, h = blockIdx.y;
     int64_t tok0;
     int rows;
     slot_chunk(map, slot, tok0, rows);
     if (rows == 0) return;
     const size_t ch = (size_t)slot * H + h;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    // laundered so that the per-thread offsets derived from it are recomputed for every item
+    // instead of being hoisted out of the item loop and held in registers across it
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    const int lane = tid & 63, wave = tid >> 6;
     const int r16 = lane & 15, q4 = lane >> 4;
     const size_t rs = (size_t)H * KD;  // token stride of q, k, v, per-dim g (elements)
     const size_t base = (size_t)tok0 * rs + (size_t)h * KD;
@@ -227,11 +257,15 @@ __global__ __launch_bounds__(ITHREADS) void intra_kernel(
                     // (K, C) / (V, C) fragment (d / 16, R / 2): rows 16 R + 8 hh .. +7 of column d
                     // are exactly the 16-byte slot of lane (d % 16) + 16 (2 (R % 2) + hh)
                     const int d = d0 + c;
-                    const size_t tcol = ch * KD * C + frag(d >> 4, R >> 1, C / 32) + ((d & 15) + 16 * (2 * (R & 1) + hh)) * 8;
+                    const size_t tcol = sc * KD * C + frag(d >> 4, R >> 1, C / 32) + ((d & 15) + 16 * (2 * (R & 1) + hh)) * 8;
                     *reinterpret_cast<uint4*>(ws.bwT_hi + tcol) = make_uint4(bwh[c][0], bwh[c][1], bwh[c][2], bwh[c][3]);
                     *reinterpret_cast<uint4*>(ws.bwT_lo + tcol) = make_uint4(bwl[c][0], bwl[c][1], bwl[c][2], bwl[c][3]);
-                    *reinterpret_cast<uint4*>(ws.kgT_hi + tcol) = make_uint4(kgh[c][0], kgh[c][1], kgh[c][2], kgh[c][3]);
-                    *reinterpret_cast<uint4*>(ws.kgT_lo + tcol) = make_uint4(kgl[c][0], kgl[c][1], kgl[c][2], kgl[c][3]);
+                    // kg^T in pi order: rows 16 R + 4 q .. + 3 go to lane (d % 16) + 16 q, half R % 2
+                    const size_t pcol = sc * KD * C + frag(d >> 4, R >> 1, C / 32);
+                    *reinterpret_cast<uint2*>(ws.kgT_hi + pcol + fragP(R & 1, d & 15, 2 * hh)) = make_uint2(kgh[c][0], kgh[c][1]);
+                    *reinterpret_cast<uint2*>(ws.kgT_hi + pcol + fragP(R & 1, d & 15, 2 * hh + 1)) = make_uint2(kgh[c][2], kgh[c][3]);
+                    *reinterpret_cast<uint2*>(ws.kgT_lo + pcol + fragP(R & 1, d & 15, 2 * hh)) = make_uint2(kgl[c][0], kgl[c][1]);
+                    *reinterpret_cast<uint2*>(ws.kgT_lo + pcol + fragP(R & 1, d & 15, 2 * hh + 1)) = make_uint2(kgl[c][2], kgl[c][3]);
                     *reinterpret_cast<uint4*>(ws.vT + tcol) = make_uint4(vtp[c][0], vtp[c][1], vtp[c][2], vtp[c][3]);
                 }
             }
@@ -306,7 +340,7 @@ __global__ __launch_bounds__(ITHREADS) void intra_kernel(
                     pq.y = pack_bf2(scale * qf[2] * ep[2] * eg[2], scale * qf[3] * ep[3] * eg[3]);
                     pq.z = pack_bf2(scale * qf[4] * ep[4] * eg[4], scale * qf[5] * ep[5] * eg[5]);
                     pq.w = pack_bf2(scale * qf[6] * ep[6] * eg[6], scale * qf[7] * ep[7] * eg[7]);
-                    *reinterpret_cast<uint4*>(ws.qg + ch * C * KD + frag(R, ks, KD / 32) + lane * 8) = pq;
+                    store_qg(ws.qgs + sc * C * KD, R, ks, r16, q4, pq);
                 }
                 uint4 ah, al, aq;
                 split_pk(kf[0] * ep[0], kf[1] * ep[1], ah.x, al.x);
@@ -336,7 +370,7 @@ __global__ __launch_bounds__(ITHREADS) void intra_kernel(
                     pq.y = pack_bf2(f * qf[2], f * qf[3]);
                     pq.z = pack_bf2(f * qf[4], f * qf[5]);
                     pq.w = pack_bf2(f * qf[6], f * qf[7]);
-                    *reinterpret_cast<uint4*>(ws.qg + ch * C * KD + frag(R, ks, KD / 32) + lane * 8) = pq;
+                    store_qg(ws.qgs + sc * C * KD, R, ks, r16, q4, pq);
                 }
                 acc = mfma32(as_bf16x8(krv), b, acc);
                 acc2 = mfma32(b, as_bf16x8(qrv), acc2);   // A2^T tile: rows j, columns i
@@ -357,8 +391,10 @@ __global__ __launch_bounds__(ITHREADS) void intra_kernel(
             accA[s][rr] = (jj < ii) ? a * bet[ii] : 0.f;
             a2v[rr] = (j2 <= i2) ? a2 * scale : 0.f;
         }
-        *reinterpret_cast<uint2*>(ws.A2 + ch * C * C + frag(R, J >> 1, C / 32) + fragT(J & 1, r16, q4)) =
-            make_uint2(pack_bf2(a2v[0], a2v[1]), pack_bf2(a2v[2], a2v[3]));
+        uint16_t* a2f = ws.A2s + sc * C * C + frag(R, J >> 1, C / 32);
+        *reinterpret_cast<uint2*>(a2f + fragP(J & 1, r16, q4)) = make_uint2(pack_bf2(a2v[0], a2v[1]), pack_bf2(a2v[2], a2v[3]));
+        // tile (R, R + 1) shares the fragment of an even diagonal tile and is zero
+        if (J == R && (R & 1) == 0) *reinterpret_cast<uint2*>(a2f + fragP(1, r16, q4)) = make_uint2(0u, 0u);
     }
     lds_barrier();
 
@@ -426,17 +462,39 @@ __global__ __launch_bounds__(ITHREADS) void intra_kernel(
     // ------------------------------------------------------------------ phase WU
     // phase E's global stores (read back here) are visible to the whole workgroup
     __syncthreads();
+    constexpr int NKG = 2 * (KD / 16) * NS;       // kg^T fragments (high, then low)
+    constexpr int NA2 = NT + (NT / 2) * (NT / 2 - 1);  // lower A2 fragments
+    uint16_t* kgL = reinterpret_cast<uint16_t*>(smem);                              // R1: dead after INV
+    uint16_t* a2L = reinterpret_cast<uint16_t*>(smem + S::R1 + S::NPAIR * S::TILE_SZ * 4);  // R2 after the T tiles
+    static_assert(NKG * 1024 <= S::R1, "kg^T staging");
+    static_assert(S::NPAIR * S::TILE_SZ * 4 + NA2 * 1024 <= S::R2, "A2 staging");
+    for (int f = wave; f < NKG + NA2; f += IWAVES) {
+        if (f < NKG) {
+            const int hl = f / (NKG / 2), x = (f % (NKG / 2)) / NS, s = f % NS;
+            const uint16_t* src = (hl ? ws.kgT_lo : ws.kgT_hi) + sc * KD * C + frag(x, s, C / 32);
+            frag_to_lds(src, kgL + f * 512, lane);
+        } else {
+            int I = 0;
+            while (I + 1 < NT && a2_slot(I + 1, 0) <= f - NKG) ++I;
+            const int s = f - NKG - a2_slot(I, 0);
+            frag_to_lds(ws.A2s + sc * C * C + frag(I, s, C / 32), a2L + (f - NKG) * 512, lane);
+        }
+    }
     const int dt = wave;  // 16-block of K (for w) and of V (for u) this wave produces
     uint4 bwh_f[NS], bwl_f[NS], vt_f[NS];
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
-        const size_t off = ch * KD * C + frag(dt, s, C / 32) + lane * 8;
+        const size_t off = sc * KD * C + frag(dt, s, C / 32) + lane * 8;
         bwh_f[s] = *reinterpret_cast<const uint4*>(ws.bwT_hi + off);
         bwl_f[s] = *reinterpret_cast<const uint4*>(ws.bwT_lo + off);
         vt_f[s] = *reinterpret_cast<const uint4*>(ws.vT + off);
     }
+    // accw[R]: w tile (rows 16 R + 4 q4 + e, column 16 dt + r16); accu[R] the same for u
+    f32x4 accw[NT], accu[NT];
+#pragma unroll
     for (int R = 0; R < NT; ++R) {
-        f32x4 accw = {0.f, 0.f, 0.f, 0.f}, accu = {0.f, 0.f, 0.f, 0.f};
+        accw[R] = f32x4{0.f, 0.f, 0.f, 0.f};
+        accu[R] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
             if (2 * s > R) break;
@@ -460,37 +518,129 @@ __global__ __launch_bounds__(ITHREADS) void intra_kernel(
             split_pk(tv[6] * bet[jb + 6], tv[7] * bet[jb + 7], th.w, tl.w);
             const bf16x8 thi = as_bf16x8(th), tlo = as_bf16x8(tl);
             const bf16x8 bwh = as_bf16x8(bwh_f[s]), bwl = as_bf16x8(bwl_f[s]), vv = as_bf16x8(vt_f[s]);
-            // w^T tile (rows d, columns i) = (exp(gamma) k)^T T'^T; u tile = T' v
-            accw = mfma32(bwh, thi, accw);
-            accw = mfma32(bwl, thi, accw);
-            accw = mfma32(bwh, tlo, accw);
-            accu = mfma32(thi, vv, accu);
-            accu = mfma32(tlo, vv, accu);
+            accw[R] = mfma32(thi, bwh, accw[R]);
+            accw[R] = mfma32(tlo, bwh, accw[R]);
+            accw[R] = mfma32(thi, bwl, accw[R]);
+            accu[R] = mfma32(thi, vv, accu[R]);
+            accu[R] = mfma32(tlo, vv, accu[R]);
         }
-        *reinterpret_cast<uint2*>(ws.w + ch * C * KD + frag(R, dt >> 1, KD / 32) + fragT(dt & 1, r16, q4)) =
-            make_uint2(pack_bf2(accw[0], accw[1]), pack_bf2(accw[2], accw[3]));
-        *reinterpret_cast<float4*>(ws.uT + ch * C * VD + ((size_t)(R * (VD / 16) + dt) * 64 + lane) * 4) =
-            make_float4(accu[0], accu[1], accu[2], accu[3]);
     }
+
+    // ------------------------------------------------------------------ phase PQ
+    // w and u as pi-order operands: tiles 2s and 2s+1 give the 32 contracted rows of step s
+    uint4 wh[NS], wl[NS], uh[NS], ul[NS];
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+        split_pk(accw[2 * s][0], accw[2 * s][1], wh[s].x, wl[s].x);
+        split_pk(accw[2 * s][2], accw[2 * s][3], wh[s].y, wl[s].y);
+        split_pk(accw[2 * s + 1][0], accw[2 * s + 1][1], wh[s].z, wl[s].z);
+        split_pk(accw[2 * s + 1][2], accw[2 * s + 1][3], wh[s].w, wl[s].w);
+        split_pk(accu[2 * s][0], accu[2 * s][1], uh[s].x, ul[s].x);
+        split_pk(accu[2 * s][2], accu[2 * s][3], uh[s].y, ul[s].y);
+        split_pk(accu[2 * s + 1][0], accu[2 * s + 1][1], uh[s].z, ul[s].z);
+        split_pk(accu[2 * s + 1][2], accu[2 * s + 1][3], uh[s].w, ul[s].w);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // direct-to-LDS copies of this wave
+    __syncthreads();  // staged kg^T and A2 have landed in LDS
+    // P^T tile (rows d in block dt, columns k in block x) = w^T kg; B tile (rows k in x,
+    // columns v in dt) = kg^T u.  -P goes out in pi order as the A operand of -P S.
+#pragma unroll 2
+    for (int x = 0; x < KD / 16; ++x) {
+        f32x4 pt = {0.f, 0.f, 0.f, 0.f}, bt = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+            const bf16x8 kh = as_bf16x8(*reinterpret_cast<const uint4*>(kgL + (x * NS + s) * 512 + lane * 8));
+            const bf16x8 kl = as_bf16x8(*reinterpret_cast<const uint4*>(kgL + (NKG / 2 + x * NS + s) * 512 + lane * 8));
+            pt = mfma32(as_bf16x8(wh[s]), kh, pt);
+            pt = mfma32(as_bf16x8(wl[s]), kh, pt);
+            pt = mfma32(as_bf16x8(wh[s]), kl, pt);
+            bt = mfma32(kh, as_bf16x8(uh[s]), bt);
+            bt = mfma32(kl, as_bf16x8(uh[s]), bt);
+            bt = mfma32(kh, as_bf16x8(ul[s]), bt);
+        }
+        uint2 ph, pl;
+        split_pk(-pt[0], -pt[1], ph.x, pl.x);
+        split_pk(-pt[2], -pt[3], ph.y, pl.y);
+        const size_t po = ch * KD * KD + frag(x, dt >> 1, KD / 32) + fragP(dt & 1, r16, q4);
+        *reinterpret_cast<uint2*>(ws.Pn_hi + po) = ph;
+        *reinterpret_cast<uint2*>(ws.Pn_lo + po) = pl;
+        *reinterpret_cast<float4*>(ws.Bm + ch * KD * VD + ((size_t)(x * (VD / 16) + dt) * 64 + lane) * 4) =
+            make_float4(bt[0], bt[1], bt[2], bt[3]);
+    }
+    // Q^T tile (rows d in dt, columns i in I) = (qg)^T - w^T A2^T; U^T tile (rows v in dt,
+    // columns i in I) = u^T A2^T.  A2 fragment (I, s) is the B operand of both.
+#pragma unroll
+    for (int I = 0; I < NT; ++I) {
+        const uint2 qv = *reinterpret_cast<const uint2*>(ws.qgs + sc * C * KD + ((size_t)(I * (KD / 16) + dt) * 64 + lane) * 4);
+        f32x4 qt = {__uint_as_float(qv.x << 16), __uint_as_float(qv.x & 0xffff0000u), __uint_as_float(qv.y << 16),
+                    __uint_as_float(qv.y & 0xffff0000u)};
+        f32x4 ut = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+            if (2 * s > I) break;
+            const bf16x8 a2 = as_bf16x8(*reinterpret_cast<const uint4*>(a2L + a2_slot(I, s) * 512 + lane * 8));
+            qt = mfma32(as_bf16x8(neg_bf16x8(wh[s])), a2, qt);
+            ut = mfma32(as_bf16x8(uh[s]), a2, ut);
+        }
+        *reinterpret_cast<uint2*>(ws.Qp + ch * C * KD + frag(I, dt >> 1, KD / 32) + fragP(dt & 1, r16, q4)) =
+            make_uint2(pack_bf2(qt[0], qt[1]), pack_bf2(qt[2], qt[3]));
+        *reinterpret_cast<uint2*>(ws.Up + ch * C * VD + ((size_t)(I * (VD / 16) + dt) * 64 + lane) * 4) =
+            make_uint2(pack_bf2(ut[0], ut[1]), pack_bf2(ut[2], ut[3]));
+    }
+}
+
+// Persistent: workgroup b takes items b, b + gridDim.x, ... (item = slot * H + head) and
+// keeps its scratch in slot b, so the scratch of all workgroups stays cache-resident.
+template <int C, bool PER_DIM>
+__global__ __launch_bounds__(ITHREADS) void intra_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const float* __restrict__ g, const float* __restrict__ beta, ChunkMap map, int H, float scale,
+    Work ws, int nitems) {
+    __shared__ __attribute__((aligned(16))) unsigned char smem[IntraShape<C>::BYTES];
+    for (int item = blockIdx.x; item < nitems; item += gridDim.x) {
+        __syncthreads();  // the previous item is done with LDS
+        intra_item<C, PER_DIM>(q, k, v, g, beta, map, H, scale, ws, smem, item / H, item % H, blockIdx.x);
+    }
+}
+
+// Workgroups of this kernel that the current device holds at once (cached per device).
+template <int C, bool PER_DIM>
+static int resident_groups() {
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 1;
+    if (dev >= 0 && dev < 64) {
+        const int c = cache[dev].load(std::memory_order_relaxed);
+        if (c > 0) return c;
+    }
+    int ncu = 0, per_cu = 0;
+    if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, intra_kernel<C, PER_DIM>, ITHREADS, 0) != hipSuccess)
+        return 1;
+    const int r = max(1, ncu * per_cu);
+    if (dev >= 0 && dev < 64) cache[dev].store(r, std::memory_order_relaxed);
+    return r;
 }
 
 template <int C, bool PER_DIM>
 static hipError_t launch_intra_t(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float* g,
                                  const float* beta, const ChunkMap& map, int nslots, int H, float scale,
-                                 const Work& ws, hipStream_t stream) {
-    hipLaunchKernelGGL((intra_kernel<C, PER_DIM>), dim3(nslots, H), dim3(ITHREADS), 0, stream, q, k, v, g,
-                       beta, map, H, scale, ws);
+                                 const Work& ws, int nscratch, hipStream_t stream) {
+    const int nitems = nslots * H;
+    const int grid = min(min(nitems, nscratch), resident_groups<C, PER_DIM>());
+    hipLaunchKernelGGL((intra_kernel<C, PER_DIM>), dim3(grid), dim3(ITHREADS), 0, stream, q, k, v, g, beta, map, H,
+                       scale, ws, nitems);
     return hipGetLastError();
 }
 
 hipError_t launch_intra(int C, bool per_dim, const uint16_t* q, const uint16_t* k, const uint16_t* v,
                         const float* g, const float* beta, const ChunkMap& map, int nslots, int H,
-                        float scale, const Work& ws, hipStream_t stream) {
+                        float scale, const Work& ws, int nscratch, hipStream_t stream) {
     if (C == 64)
-        return per_dim ? launch_intra_t<64, true>(q, k, v, g, beta, map, nslots, H, scale, ws, stream)
-                       : launch_intra_t<64, false>(q, k, v, g, beta, map, nslots, H, scale, ws, stream);
-    return per_dim ? launch_intra_t<128, true>(q, k, v, g, beta, map, nslots, H, scale, ws, stream)
-                   : launch_intra_t<128, false>(q, k, v, g, beta, map, nslots, H, scale, ws, stream);
+        return per_dim ? launch_intra_t<64, true>(q, k, v, g, beta, map, nslots, H, scale, ws, nscratch, stream)
+                       : launch_intra_t<64, false>(q, k, v, g, beta, map, nslots, H, scale, ws, nscratch, stream);
+    return per_dim ? launch_intra_t<128, true>(q, k, v, g, beta, map, nslots, H, scale, ws, nscratch, stream)
+                   : launch_intra_t<128, false>(q, k, v, g, beta, map, nslots, H, scale, ws, nscratch, stream);
 }
 
 }  // namespace cdr
