@@ -85,6 +85,31 @@ __device__ __forceinline__ uint2 pack4(const short* s) {
     return p;
 }
 
+// Streaming (non-temporal) global accesses for data touched once: inputs and per-chunk
+// results, so that they do not push reused data out of the caches.
+typedef unsigned int u32x2v __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint32_t ld_nt(const uint32_t* p) { return __builtin_nontemporal_load(p); }
+__device__ __forceinline__ float ld_nt(const float* p) { return __builtin_nontemporal_load(p); }
+__device__ __forceinline__ float2 ld_nt(const float2* p) {
+    const u32x2v v = __builtin_nontemporal_load(reinterpret_cast<const u32x2v*>(p));
+    return make_float2(__uint_as_float(v.x), __uint_as_float(v.y));
+}
+__device__ __forceinline__ uint4 ld_nt(const uint4* p) {
+    const u32x4v v = __builtin_nontemporal_load(reinterpret_cast<const u32x4v*>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void st_nt(uint2* p, const uint2& v) {
+    __builtin_nontemporal_store(u32x2v{v.x, v.y}, reinterpret_cast<u32x2v*>(p));
+}
+__device__ __forceinline__ void st_nt(float2* p, const float2& v) {
+    __builtin_nontemporal_store(u32x2v{__float_as_uint(v.x), __float_as_uint(v.y)}, reinterpret_cast<u32x2v*>(p));
+}
+__device__ __forceinline__ void st_nt(float4* p, const float4& v) {
+    __builtin_nontemporal_store(u32x4v{__float_as_uint(v.x), __float_as_uint(v.y), __float_as_uint(v.z), __float_as_uint(v.w)},
+                                reinterpret_cast<u32x4v*>(p));
+}
+
 // wait for this wave's own LDS traffic; keeps the compiler from reordering across it
 __device__ __forceinline__ void wave_lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 

@@ -109,12 +109,55 @@ __device__ __forceinline__ uint4 neg_bf16x8(const uint4& a) {
     return make_uint4(a.x ^ 0x80008000u, a.y ^ 0x80008000u, a.z ^ 0x80008000u, a.w ^ 0x80008000u);
 }
 
-// One (chunk slot, head) item.  sc is the workgroup's scratch slot.
+// Phase E inputs of one item, held in registers: thread (R = wave, d0 = 2 (lane)) owns rows
+// 16 R .. 16 R + 15 and columns d0, d0 + 1; loaded one item ahead.  Rows past the end of
+// the sequence read its last row (masked when used), so the loads stay unconditional.
+struct EIn {
+    float2 g[16];
+    uint32_t k[16], v[16];
+    float b;
+};
+
+template <int C, bool PER_DIM>
+__device__ __forceinline__ void e_load(EIn& in, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+                                       const float* __restrict__ g, const float* __restrict__ beta,
+                                       const ChunkMap& map, int H, int item, int tid) {
+    // Every register is written on every path (no item or an empty chunk slot load token 0,
+    // which exists whenever there are items), so the previous contents are dead once this
+    // is called and nothing has to be kept alive across the item.
+    item = max(item, 0);
+    const int slot = item / H, h = item % H;
+    int64_t tok0;
+    int rows;
+    slot_chunk(map, slot, tok0, rows);
+    const int last = max(rows - 1, 0);
+    const size_t rs = (size_t)H * KD;
+    const size_t base = (size_t)tok0 * rs + (size_t)h * KD;
+    const int R = min(tid >> 6, C / 16 - 1), d0 = 2 * (tid & 63);
+    in.b = beta[(size_t)(tok0 + min(tid, last)) * H + h];
+    {
+#pragma unroll
+        for (int ii = 0; ii < 16; ++ii) {
+            const int ic = min(16 * R + ii, last);
+            if constexpr (PER_DIM) {
+                in.g[ii] = *reinterpret_cast<const float2*>(g + base + (size_t)ic * rs + d0);
+            } else {
+                const float s1 = g[(size_t)(tok0 + ic) * H + h];
+                in.g[ii] = make_float2(s1, s1);
+            }
+            in.k[ii] = *reinterpret_cast<const uint32_t*>(k + base + (size_t)ic * rs + d0);
+            in.v[ii] = *reinterpret_cast<const uint32_t*>(v + base + (size_t)ic * rs + d0);
+        }
+    }
+}
+
+// One (chunk slot, head) item.  sc is the workgroup's scratch slot; ein holds the item's
+// phase E inputs on entry and those of next_item (-1: none) on exit.
 template <int C, bool PER_DIM>
 __device__ __forceinline__ void intra_item(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const float* __restrict__ g, const float* __restrict__ beta, const ChunkMap& map, int H, float scale,
-    const Work& ws, unsigned char* smem, int slot, int h, size_t sc) {
+    const Work& ws, unsigned char* smem, int slot, int h, size_t sc, EIn& ein, int next_item) {
     using S = IntraShape<C>;
     constexpr int NT = S::NT, NS = S::NS;
     float* Ep = reinterpret_cast<float*>(smem);                                   // [C][EP_LD]
@@ -130,50 +173,55 @@ __device__ __forceinline__ void intra_item(
     float* Pscr = Atile + S::NPAIR * S::TILE_SZ;                                  // merge scratch
     float* Ttile = reinterpret_cast<float*>(smem + S::R1);
 
-    int64_t tok0;
-    int rows;
-    slot_chunk(map, slot, tok0, rows);
-    if (rows == 0) return;
-    const size_t ch = (size_t)slot * H + h;
     // laundered so that the per-thread offsets derived from it are recomputed for every item
     // instead of being hoisted out of the item loop and held in registers across it
     int tid = threadIdx.x;
     asm volatile("" : "+v"(tid));
+    int64_t tok0;
+    int rows;
+    slot_chunk(map, slot, tok0, rows);
+    if (rows == 0) {
+        e_load<C, PER_DIM>(ein, k, v, g, beta, map, H, next_item, tid);
+        return;
+    }
+    const size_t ch = (size_t)slot * H + h;
     const int lane = tid & 63, wave = tid >> 6;
     const int r16 = lane & 15, q4 = lane >> 4;
     const size_t rs = (size_t)H * KD;  // token stride of q, k, v, per-dim g (elements)
     const size_t base = (size_t)tok0 * rs + (size_t)h * KD;
 
+    // Row operands of phase AA2 (raw k and q rows of the wave's two tile rows), loaded
+    // before phase E so that their latency is hidden behind it.
+    // waves w and w + 4 share tile rows cp = w % 4 and NT-1-cp: NT+1 tiles, HF for the first
+    const int cp = wave & 3, part = wave >> 2;
+    const bool aa_active = cp < NT / 2;
+    const int Rown[2] = {cp, NT - 1 - cp};
+    uint4 kfr[2][KD / 32], qfr[2][KD / 32];
+#pragma unroll
+    for (int o = 0; o < 2; ++o)
+#pragma unroll
+        for (int ks = 0; ks < KD / 32; ++ks) {
+            const int i = 16 * Rown[o] + r16, ic = min(max(i, 0), rows - 1);
+            const uint4 kx = *reinterpret_cast<const uint4*>(k + base + (size_t)ic * rs + 32 * ks + 8 * q4);
+            const uint4 qx = *reinterpret_cast<const uint4*>(q + base + (size_t)ic * rs + 32 * ks + 8 * q4);
+            kfr[o][ks] = (i < rows) ? kx : make_uint4(0, 0, 0, 0);
+            qfr[o][ks] = (i < rows) ? qx : make_uint4(0, 0, 0, 0);
+        }
     // ------------------------------------------------------------------ phase E
     {
         const int R = tid >> 6, d0 = 2 * (tid & 63);  // tile row R, columns d0, d0 + 1
         const bool act = R < NT;
         float gm2[16][2];
         uint32_t kr[16], vr[16];
-        if (tid < C) {
-            const float bv = beta[(size_t)(tok0 + min(tid, rows - 1)) * H + h];
-            bet[tid] = (tid < rows) ? bv : 0.f;
-        }
+        if (tid < C) bet[tid] = (tid < rows) ? ein.b : 0.f;
         if (act) {
 #pragma unroll
             for (int ii = 0; ii < 16; ++ii) {
-                // rows past the end of the sequence read its last row and are zeroed: the
-                // loads stay unconditional and can all be in flight together
-                const int i = 16 * R + ii, ic = min(i, rows - 1);
-                const bool ok = i < rows;
-                float2 gv;
-                if constexpr (PER_DIM) {
-                    gv = *reinterpret_cast<const float2*>(g + base + (size_t)ic * rs + d0);
-                } else {
-                    const float s1 = g[(size_t)(tok0 + ic) * H + h];
-                    gv = make_float2(s1, s1);
-                }
-                const uint32_t kx = *reinterpret_cast<const uint32_t*>(k + base + (size_t)ic * rs + d0);
-                const uint32_t vx = *reinterpret_cast<const uint32_t*>(v + base + (size_t)ic * rs + d0);
-                kr[ii] = ok ? kx : 0u;
-                vr[ii] = ok ? vx : 0u;
-                gm2[ii][0] = ok ? gv.x : 0.f;
-                gm2[ii][1] = ok ? gv.y : 0.f;
+                const bool ok = 16 * R + ii < rows;  // rows past the end are zero
+                kr[ii] = ok ? ein.k[ii] : 0u;
+                vr[ii] = ok ? ein.v[ii] : 0u;
+                gm2[ii][0] = ok ? ein.g[ii].x : 0.f;
+                gm2[ii][1] = ok ? ein.g[ii].y : 0.f;
             }
 #pragma unroll
             for (int ii = 1; ii < 16; ++ii) {
@@ -208,7 +256,7 @@ __device__ __forceinline__ void intra_item(
             }
             *reinterpret_cast<float2*>(gmid + R * KD + d0) = make_float2(gmv[0], gmv[1]);
             *reinterpret_cast<float2*>(egm + R * KD + d0) = make_float2(e_gm[0], e_gm[1]);
-            if (R == 0) *reinterpret_cast<float2*>(ws.gC + ch * KD + d0) = make_float2(ex(gcl[0]), ex(gcl[1]));
+            if (R == 0) st_nt(reinterpret_cast<float2*>(ws.gC + ch * KD + d0), make_float2(ex(gcl[0]), ex(gcl[1])));
             if constexpr (!PER_DIM) {
                 if ((tid & 63) == 0) {
 #pragma unroll
@@ -286,21 +334,6 @@ __device__ __forceinline__ void intra_item(
     lds_barrier();
 
     // ------------------------------------------------------------------ phase AA2
-    // waves w and w + 4 share tile rows cp = w % 4 and NT-1-cp: NT+1 tiles, HF for the first
-    const int cp = wave & 3, part = wave >> 2;
-    const bool aa_active = cp < NT / 2;
-    const int Rown[2] = {cp, NT - 1 - cp};
-    uint4 kfr[2][KD / 32], qfr[2][KD / 32];
-#pragma unroll
-    for (int o = 0; o < 2; ++o)
-#pragma unroll
-        for (int ks = 0; ks < KD / 32; ++ks) {
-            const int i = 16 * Rown[o] + r16, ic = min(max(i, 0), rows - 1);
-            const uint4 kx = *reinterpret_cast<const uint4*>(k + base + (size_t)ic * rs + 32 * ks + 8 * q4);
-            const uint4 qx = *reinterpret_cast<const uint4*>(q + base + (size_t)ic * rs + 32 * ks + 8 * q4);
-            kfr[o][ks] = (i < rows) ? kx : make_uint4(0, 0, 0, 0);
-            qfr[o][ks] = (i < rows) ? qx : make_uint4(0, 0, 0, 0);
-        }
     f32x4 accA[S::SMAX];
 #pragma unroll
     for (int s = 0; s < S::SMAX; ++s) {
@@ -396,9 +429,21 @@ __device__ __forceinline__ void intra_item(
         // tile (R, R + 1) shares the fragment of an even diagonal tile and is zero
         if (J == R && (R & 1) == 0) *reinterpret_cast<uint2*>(a2f + fragP(1, r16, q4)) = make_uint2(0u, 0u);
     }
+    // the global stores of phases E and AA2 complete before the barrier: from here on the
+    // whole workgroup reads them back
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     lds_barrier();
 
     // ------------------------------------------------------------------ phase INV
+    const int dt = wave;  // 16-block of K (for w) and of V (for u) this wave produces in WU
+    uint4 bwh_f[NS], bwl_f[NS], vt_f[NS];
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+        const size_t off = sc * KD * C + frag(dt, s, C / 32) + lane * 8;
+        bwh_f[s] = *reinterpret_cast<const uint4*>(ws.bwT_hi + off);
+        bwl_f[s] = *reinterpret_cast<const uint4*>(ws.bwT_lo + off);
+        vt_f[s] = *reinterpret_cast<const uint4*>(ws.vT + off);
+    }
 #pragma unroll
     for (int s = 0; s < S::SMAX; ++s) {
         const int p = (part ? S::HF : 0) + s;
@@ -460,8 +505,7 @@ __device__ __forceinline__ void intra_item(
     }
 
     // ------------------------------------------------------------------ phase WU
-    // phase E's global stores (read back here) are visible to the whole workgroup
-    __syncthreads();
+    // kg^T and A2 to LDS (R1 is free since the last merge barrier)
     constexpr int NKG = 2 * (KD / 16) * NS;       // kg^T fragments (high, then low)
     constexpr int NA2 = NT + (NT / 2) * (NT / 2 - 1);  // lower A2 fragments
     uint16_t* kgL = reinterpret_cast<uint16_t*>(smem);                              // R1: dead after INV
@@ -479,15 +523,6 @@ __device__ __forceinline__ void intra_item(
             const int s = f - NKG - a2_slot(I, 0);
             frag_to_lds(ws.A2s + sc * C * C + frag(I, s, C / 32), a2L + (f - NKG) * 512, lane);
         }
-    }
-    const int dt = wave;  // 16-block of K (for w) and of V (for u) this wave produces
-    uint4 bwh_f[NS], bwl_f[NS], vt_f[NS];
-#pragma unroll
-    for (int s = 0; s < NS; ++s) {
-        const size_t off = sc * KD * C + frag(dt, s, C / 32) + lane * 8;
-        bwh_f[s] = *reinterpret_cast<const uint4*>(ws.bwT_hi + off);
-        bwl_f[s] = *reinterpret_cast<const uint4*>(ws.bwT_lo + off);
-        vt_f[s] = *reinterpret_cast<const uint4*>(ws.vT + off);
     }
     // accw[R]: w tile (rows 16 R + 4 q4 + e, column 16 dt + r16); accu[R] the same for u
     f32x4 accw[NT], accu[NT];
@@ -527,6 +562,11 @@ __device__ __forceinline__ void intra_item(
     }
 
     // ------------------------------------------------------------------ phase PQ
+    uint2 qgv[NT];  // (qg)^T tiles (I, dt) used after the P, B loop
+#pragma unroll
+    for (int I = 0; I < NT; ++I)
+        qgv[I] = *reinterpret_cast<const uint2*>(ws.qgs + sc * C * KD + ((size_t)(I * (KD / 16) + dt) * 64 + lane) * 4);
+    e_load<C, PER_DIM>(ein, k, v, g, beta, map, H, next_item, tid);  // next item, in flight through PQ
     // w and u as pi-order operands: tiles 2s and 2s+1 give the 32 contracted rows of step s
     uint4 wh[NS], wl[NS], uh[NS], ul[NS];
 #pragma unroll
@@ -544,34 +584,41 @@ __device__ __forceinline__ void intra_item(
     __syncthreads();  // staged kg^T and A2 have landed in LDS
     // P^T tile (rows d in block dt, columns k in block x) = w^T kg; B tile (rows k in x,
     // columns v in dt) = kg^T u.  -P goes out in pi order as the A operand of -P S.
-#pragma unroll 2
+#pragma unroll 1
     for (int x = 0; x < KD / 16; ++x) {
-        f32x4 pt = {0.f, 0.f, 0.f, 0.f}, bt = {0.f, 0.f, 0.f, 0.f};
+        // four independent accumulation chains
+        f32x4 p0 = {0.f, 0.f, 0.f, 0.f}, p1 = p0, b0 = p0, b1 = p0;
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
             const bf16x8 kh = as_bf16x8(*reinterpret_cast<const uint4*>(kgL + (x * NS + s) * 512 + lane * 8));
             const bf16x8 kl = as_bf16x8(*reinterpret_cast<const uint4*>(kgL + (NKG / 2 + x * NS + s) * 512 + lane * 8));
-            pt = mfma32(as_bf16x8(wh[s]), kh, pt);
-            pt = mfma32(as_bf16x8(wl[s]), kh, pt);
-            pt = mfma32(as_bf16x8(wh[s]), kl, pt);
-            bt = mfma32(kh, as_bf16x8(uh[s]), bt);
-            bt = mfma32(kl, as_bf16x8(uh[s]), bt);
-            bt = mfma32(kh, as_bf16x8(ul[s]), bt);
+            p0 = mfma32(as_bf16x8(wh[s]), kh, p0);
+            b0 = mfma32(kh, as_bf16x8(uh[s]), b0);
+            p1 = mfma32(as_bf16x8(wl[s]), kh, p1);
+            b1 = mfma32(kl, as_bf16x8(uh[s]), b1);
+            p1 = mfma32(as_bf16x8(wh[s]), kl, p1);
+            b1 = mfma32(kh, as_bf16x8(ul[s]), b1);
+        }
+        f32x4 pt, bt;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            pt[e] = p0[e] + p1[e];
+            bt[e] = b0[e] + b1[e];
         }
         uint2 ph, pl;
         split_pk(-pt[0], -pt[1], ph.x, pl.x);
         split_pk(-pt[2], -pt[3], ph.y, pl.y);
         const size_t po = ch * KD * KD + frag(x, dt >> 1, KD / 32) + fragP(dt & 1, r16, q4);
-        *reinterpret_cast<uint2*>(ws.Pn_hi + po) = ph;
-        *reinterpret_cast<uint2*>(ws.Pn_lo + po) = pl;
-        *reinterpret_cast<float4*>(ws.Bm + ch * KD * VD + ((size_t)(x * (VD / 16) + dt) * 64 + lane) * 4) =
-            make_float4(bt[0], bt[1], bt[2], bt[3]);
+        st_nt(reinterpret_cast<uint2*>(ws.Pn_hi + po), ph);
+        st_nt(reinterpret_cast<uint2*>(ws.Pn_lo + po), pl);
+        st_nt(reinterpret_cast<float4*>(ws.Bm + ch * KD * VD + ((size_t)(x * (VD / 16) + dt) * 64 + lane) * 4),
+              make_float4(bt[0], bt[1], bt[2], bt[3]));
     }
     // Q^T tile (rows d in dt, columns i in I) = (qg)^T - w^T A2^T; U^T tile (rows v in dt,
     // columns i in I) = u^T A2^T.  A2 fragment (I, s) is the B operand of both.
 #pragma unroll
     for (int I = 0; I < NT; ++I) {
-        const uint2 qv = *reinterpret_cast<const uint2*>(ws.qgs + sc * C * KD + ((size_t)(I * (KD / 16) + dt) * 64 + lane) * 4);
+        const uint2 qv = qgv[I];
         f32x4 qt = {__uint_as_float(qv.x << 16), __uint_as_float(qv.x & 0xffff0000u), __uint_as_float(qv.y << 16),
                     __uint_as_float(qv.y & 0xffff0000u)};
         f32x4 ut = {0.f, 0.f, 0.f, 0.f};
@@ -582,10 +629,10 @@ __device__ __forceinline__ void intra_item(
             qt = mfma32(as_bf16x8(neg_bf16x8(wh[s])), a2, qt);
             ut = mfma32(as_bf16x8(uh[s]), a2, ut);
         }
-        *reinterpret_cast<uint2*>(ws.Qp + ch * C * KD + frag(I, dt >> 1, KD / 32) + fragP(dt & 1, r16, q4)) =
-            make_uint2(pack_bf2(qt[0], qt[1]), pack_bf2(qt[2], qt[3]));
-        *reinterpret_cast<uint2*>(ws.Up + ch * C * VD + ((size_t)(I * (VD / 16) + dt) * 64 + lane) * 4) =
-            make_uint2(pack_bf2(ut[0], ut[1]), pack_bf2(ut[2], ut[3]));
+        st_nt(reinterpret_cast<uint2*>(ws.Qp + ch * C * KD + frag(I, dt >> 1, KD / 32) + fragP(dt & 1, r16, q4)),
+              make_uint2(pack_bf2(qt[0], qt[1]), pack_bf2(qt[2], qt[3])));
+        st_nt(reinterpret_cast<uint2*>(ws.Up + ch * C * VD + ((size_t)(I * (VD / 16) + dt) * 64 + lane) * 4),
+              make_uint2(pack_bf2(ut[0], ut[1]), pack_bf2(ut[2], ut[3])));
     }
 }
 
@@ -597,9 +644,12 @@ __global__ __launch_bounds__(ITHREADS) void intra_kernel(
     const float* __restrict__ g, const float* __restrict__ beta, ChunkMap map, int H, float scale,
     Work ws, int nitems) {
     __shared__ __attribute__((aligned(16))) unsigned char smem[IntraShape<C>::BYTES];
+    EIn ein;
+    e_load<C, PER_DIM>(ein, k, v, g, beta, map, H, blockIdx.x < nitems ? (int)blockIdx.x : -1, threadIdx.x);
     for (int item = blockIdx.x; item < nitems; item += gridDim.x) {
         __syncthreads();  // the previous item is done with LDS
-        intra_item<C, PER_DIM>(q, k, v, g, beta, map, H, scale, ws, smem, item / H, item % H, blockIdx.x);
+        const int next = item + (int)gridDim.x < nitems ? item + (int)gridDim.x : -1;
+        intra_item<C, PER_DIM>(q, k, v, g, beta, map, H, scale, ws, smem, item / H, item % H, blockIdx.x, ein, next);
     }
 }
 
