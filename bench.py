@@ -30,22 +30,41 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 SEED_BASE = 1003            # workload seeds: 1000 + position of the workload in the list
 
 
-def algorithmic(w, lengths):
-    """Algorithmic flops and bytes per kernel for a batch of sequences of the given lengths.
+def nominal_flops(w, lengths):
+    """The headline work F_nom of the method as the page writes it, per chunk of n tokens and
+    head (K = V = 128): A, A2 and w as full n x n products (n^2 K each), u and A2 v_new
+    (n^2 V each), w S, qg S and kg^T v_new (n K V each), two flops per multiply-add, plus
+    n^3 / 3 for the inverse.  Tail chunks count with their real n."""
+    K, V, C, H = w.K, w.V, w.chunk_size, w.H
+    f = 0.0
+    for L in lengths:
+        for c0 in range(0, L, C):
+            n = min(C, L - c0)
+            f += H * (2.0 * (3 * n * n * K + 2 * n * n * V + 3 * n * K * V) + n ** 3 / 3.0)
+    return f
 
-    Per chunk of n tokens and head (K = V = 128): the intra kernel owns A, A2, w (n^2 K
-    each), u (n^2 V) and the inverse (n^3 / 3); the chain owns w S and kg^T v_new
-    (n K V each); the output kernel owns qg S (n K V) and A2 v_new (n^2 V); two flops per
-    multiply-add.  Bytes are the compulsory ones: q, k, v, o in bf16, g and beta in fp32,
-    the initial and final state in fp32; intermediates are not counted."""
+
+def kernel_work(w, lengths):
+    """Algorithmic flops and compulsory bytes per kernel of this implementation, in which the
+    chunk step is re-associated (S' = exp(gamma_C) S - P S + B, o = Q S + U).  Per chunk of n
+    tokens and head:
+      intra   A, A2 (full n x n products, 2 n^2 K each), the inverse (n^3 / 3), w (2 n^2 K),
+              u (2 n^2 V), P = kg^T w (2 n K^2), B = kg^T u (2 n K V), A2 w (2 n^2 K),
+              A2 u (2 n^2 V)
+      chain   P S (2 K^2 V, whatever n)
+      output  Q S (2 n K V)
+    Bytes are the compulsory ones each kernel owns: q, k, v, g, beta read by the intra
+    kernel, the initial and final state moved by the chain, o written by the output kernel;
+    intermediates are not counted."""
     K, V, C, H = w.K, w.V, w.chunk_size, w.H
     f = {"intra": 0.0, "chain": 0.0, "output": 0.0}
     for L in lengths:
         for c0 in range(0, L, C):
             n = min(C, L - c0)
-            f["intra"] += H * (2.0 * (3 * n * n * K + n * n * V) + n ** 3 / 3.0)
-            f["chain"] += H * (2.0 * 2 * n * K * V)
-            f["output"] += H * (2.0 * (n * K * V + n * n * V))
+            f["intra"] += H * (2.0 * (2 * n * n * K) + n ** 3 / 3.0 + 2.0 * (n * n * K + n * n * V)
+                               + 2.0 * (n * K * K + n * K * V) + 2.0 * (n * n * K + n * n * V))
+            f["chain"] += H * 2.0 * K * K * V
+            f["output"] += H * 2.0 * n * K * V
     tokens = sum(lengths)
     gate_bytes = 4 * K if w.per_dim_gate else 4
     b = {"intra": tokens * H * (2 * 2 * K + 2 * V + gate_bytes + 4),
@@ -160,7 +179,7 @@ def main():
     torch.cuda.synchronize()
 
     K = args.steps
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)] for _ in range(K)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(K):
@@ -177,8 +196,8 @@ def main():
     gpu_ms = sum(kern_ms.values())
 
     lengths = list(w.lengths) if w.lengths is not None else [w.T] * w.B
-    flops, bytes_ = algorithmic(w, lengths)
-    f_nom = sum(flops.values())
+    flops, bytes_ = kernel_work(w, lengths)
+    f_nom = nominal_flops(w, lengths)
     tokens = w.tokens
     value = tokens / (ms_step * 1e-3)
     step_tflops = f_nom / (ms_step * 1e-3) / 1e12

@@ -145,6 +145,29 @@ def test_chunk_sizes_agree():
     assert ratio(S1.cpu().numpy(), S2.double().cpu().numpy(), S_TOL) <= 1.0
 
 
+STAGED = [
+    ("kda_C128", dict(B=1, T=1000, H=3, chunk_size=128, initial_state=True, gate_mean=2.0)),
+    ("kda_C64_varlen", dict(B=1, T=700, H=2, chunk_size=64, initial_state=True, lengths=(100, 0, 333, 267))),
+    ("gdn_C64", dict(B=2, T=300, H=2, chunk_size=64, initial_state=True, per_dim_gate=False)),
+]
+
+
+@pytest.mark.parametrize("label,kw", STAGED, ids=[s[0] for s in STAGED])
+def test_staged_calls_equal_one_call(label, kw):
+    """The three kernels launched one stage per call give the bits of one full call."""
+    kw = dict(kw)
+    inp = make_inputs(kw.pop("B"), kw.pop("T"), kw.pop("H"), seed=14, **kw)
+    note(f"[staged==full] {label}")
+    o1, S1 = run_gpu(inp)
+    d = inp.to(DEV)
+    call = cdr.PreparedForward(d.q, d.k, d.v, d.g, d.beta, initial_state=d.initial_state,
+                               cu_seqlens=d.cu_seqlens, chunk_size=inp.chunk_size, output_final_state=True)
+    for st in (cdr.STAGE_INTRA, cdr.STAGE_CHAIN, cdr.STAGE_OUTPUT):
+        call(st)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, call.o) and torch.equal(S1, call.S)
+
+
 def test_no_final_state_requested():
     inp = make_inputs(1, 128, 2, seed=13, chunk_size=64)
     note("[no final state]")
