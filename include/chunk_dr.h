@@ -122,11 +122,13 @@ cdr_status chunk_dr_fwd(const cdr_problem* p,
  * The same forward, split into its three kernel stages so that each can be timed or
  * profiled on its own.  `stages` is a bit mask of
  *   CDR_STAGE_INTRA  (1)  per-chunk work independent of the carried state: gate prefix sum,
- *                         decayed A and its inverse, w, u, decayed q and k, the in-chunk
- *                         output block (page sections M1-M3)
- *   CDR_STAGE_CHAIN  (2)  the sequential chunk-to-chunk state recurrence, v_new and the
- *                         final state (section M4)
- *   CDR_STAGE_OUTPUT (4)  o = qg S + A2 v_new for every chunk (section M4)
+ *                         decayed A and its inverse, w, u (page sections M1-M3), and the
+ *                         factors of the chunk step of section M4 re-associated, P = kg^T w,
+ *                         B = kg^T u, Q = qg - A2 w, U = A2 u
+ *   CDR_STAGE_CHAIN  (2)  the sequential chunk-to-chunk state recurrence
+ *                         S <- exp(gamma_C) S - P S + B, the chunk-entry states and the final
+ *                         state (section M4; the same sums as u - w S carried through v_new)
+ *   CDR_STAGE_OUTPUT (4)  o = Q S_entry + U for every chunk (= qg S + A2 v_new, section M4)
  * Stages run in this order.  A stage reads what earlier stages left in the workspace, so a
  * call with a stage whose predecessors are not in `stages` is only meaningful after a call
  * with the same problem, inputs and workspace that ran them.  chunk_dr_fwd(...) is
