@@ -96,27 +96,31 @@ def make_inputs(B: int, T: int, H: int, K: int = 128, V: int = 128, *, seed: int
                 initial_state: bool = False, chunk_size: int = 64,
                 gate_mean: float = 0.0, gate: str = "logsigmoid",
                 beta_mode: str = "sigmoid", state_std: float = 0.1,
-                normalise: bool = True) -> Inputs:
+                normalise: bool = True, HV: Optional[int] = None) -> Inputs:
     """Draw one seeded batch.
 
     gate: "logsigmoid" -> g = logsigmoid(N(gate_mean, 1)); "zero" -> g = 0.
     beta_mode: "sigmoid" -> sigmoid(N(0, 1)); "zero" -> 0; "one" -> 1.
     With ``lengths`` the batch is packed (B must be 1, T = sum(lengths)) and
-    ``cu_seqlens`` is the int32 prefix sum of the lengths.
+    ``cu_seqlens`` is the int32 prefix sum of the lengths.  ``HV`` (a multiple of H)
+    gives v, g, beta and the initial state HV value heads while q and k keep H.
     """
     if lengths is not None:
         if B != 1 or T != sum(lengths):
             raise ValueError("packed batches need B == 1 and T == sum(lengths)")
     gen = torch.Generator("cpu").manual_seed(int(seed))
     randn = lambda *shape: torch.randn(*shape, generator=gen, dtype=torch.float32)  # noqa: E731
+    Hv = H if HV is None else int(HV)
+    if Hv % H:
+        raise ValueError("HV must be a multiple of H")
     q = randn(B, T, H, K)
     k = randn(B, T, H, K)
-    v = randn(B, T, H, V)
-    gshape = (B, T, H, K) if per_dim_gate else (B, T, H)
+    v = randn(B, T, Hv, V)
+    gshape = (B, T, Hv, K) if per_dim_gate else (B, T, Hv)
     g0 = randn(*gshape)
-    b0 = randn(B, T, H)
+    b0 = randn(B, T, Hv)
     N = len(lengths) if lengths is not None else B
-    s0 = randn(N, H, V, K) * state_std if initial_state else None
+    s0 = randn(N, Hv, V, K) * state_std if initial_state else None
     if normalise:
         q, k = l2_normalise(q), l2_normalise(k)
     if gate == "logsigmoid":
@@ -128,9 +132,9 @@ def make_inputs(B: int, T: int, H: int, K: int = 128, V: int = 128, *, seed: int
     if beta_mode == "sigmoid":
         beta = torch.sigmoid(b0)
     elif beta_mode == "zero":
-        beta = torch.zeros(B, T, H)
+        beta = torch.zeros(B, T, Hv)
     elif beta_mode == "one":
-        beta = torch.ones(B, T, H)
+        beta = torch.ones(B, T, Hv)
     else:
         raise ValueError(beta_mode)
     cu = None

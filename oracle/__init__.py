@@ -39,8 +39,8 @@ def _load():
         lib = ctypes.CDLL(path)
         lib.oracle_recurrent_fwd.restype = ctypes.c_int
         lib.oracle_recurrent_fwd.argtypes = [
-            ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
-            ctypes.c_int, ctypes.c_int,
+            ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+            ctypes.c_int, ctypes.c_int, ctypes.c_int,
             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
             ctypes.c_void_p, ctypes.c_double, ctypes.c_void_p, ctypes.c_void_p,
@@ -81,21 +81,23 @@ def _f64(x):
 
 
 def recurrent_fwd(q, k, v, g, beta, scale=None, initial_state=None, cu_seqlens=None,
-                  threads=0):
+                  threads=0, use_qk_l2norm=False):
     """fp64 per-token recurrence.
 
-    Shapes follow the page's I/O table: q, k ``[B,T,H,K]`` bf16; v ``[B,T,H,V]``
-    bf16; g ``[B,T,H,K]`` (per-dimension) or ``[B,T,H]`` (per-head) fp32; beta
-    ``[B,T,H]`` fp32; initial_state ``[N,H,V,K]`` (any float dtype, widened to
-    fp64) or None; cu_seqlens ``[N+1]`` int32 or None (then N = B).
+    Shapes follow the page's I/O table: q, k ``[B,T,Hk,K]`` bf16; v ``[B,T,H,V]``
+    bf16 with H a multiple of Hk (value head h reads key head ``h // (H // Hk)``); g
+    ``[B,T,H,K]`` (per-dimension) or ``[B,T,H]`` (per-head) fp32; beta ``[B,T,H]``
+    fp32; initial_state ``[N,H,V,K]`` (any float dtype, widened to fp64) or None;
+    cu_seqlens ``[N+1]`` int32 or None (then N = B).  With ``use_qk_l2norm`` q and k
+    are normalised per token, ``x / sqrt(|x|^2 + 1e-6)``.
 
     Returns ``(o, S)`` as fp64 numpy arrays: o ``[B,T,H,V]``, S ``[N,H,V,K]``.
     ``scale=None`` means ``K ** -0.5``.
     """
     qb, kb, vb = _bf16_bits(q), _bf16_bits(k), _bf16_bits(v)
-    B, T, H, K = qb.shape
-    V = vb.shape[-1]
-    if kb.shape != (B, T, H, K) or vb.shape != (B, T, H, V):
+    B, T, Hk, K = qb.shape
+    H, V = vb.shape[2], vb.shape[-1]
+    if kb.shape != (B, T, Hk, K) or vb.shape[:2] != (B, T) or H % Hk:
         raise ValueError("q/k/v shape mismatch")
     gf = _f32(g)
     if gf.shape == (B, T, H, K):
@@ -124,7 +126,8 @@ def recurrent_fwd(q, k, v, g, beta, scale=None, initial_state=None, cu_seqlens=N
     o = np.zeros((B, T, H, V), dtype=np.float64)
     s = np.zeros((N, H, V, K), dtype=np.float64)
     ptr = lambda a: None if a is None else a.ctypes.data  # noqa: E731
-    rc = _load().oracle_recurrent_fwd(B, T, H, K, V, N, per_dim, ptr(qb), ptr(kb), ptr(vb),
+    rc = _load().oracle_recurrent_fwd(B, T, Hk, H, K, V, N, per_dim, int(bool(use_qk_l2norm)),
+                                      ptr(qb), ptr(kb), ptr(vb),
                                       ptr(gf), ptr(bf), ptr(s0), ptr(cu), float(scale),
                                       ptr(o), ptr(s), int(threads))
     if rc != 0:

@@ -57,10 +57,16 @@ def _chunk(q, k, v, g, beta, S, scale):
 
 
 def chunked_fwd(q, k, v, g, beta, scale=None, initial_state=None, cu_seqlens=None,
-                chunk_size=64):
+                chunk_size=64, use_qk_l2norm=False):
     """fp64 chunked forward. Same argument conventions and return values as
     :func:`oracle.recurrent_fwd`: o ``[B,T,H,V]`` and S ``[N,H,V,K]`` (fp64)."""
     q, k, v, g, beta = (_as_f64(x) for x in (q, k, v, g, beta))
+    if use_qk_l2norm:   # per token over K, before anything else
+        q = q / np.sqrt(np.sum(q * q, axis=-1, keepdims=True) + 1e-6)
+        k = k / np.sqrt(np.sum(k * k, axis=-1, keepdims=True) + 1e-6)
+    if v.shape[2] != q.shape[2]:   # grouped value heads: key head h // group for value head h
+        grp = v.shape[2] // q.shape[2]
+        q, k = np.repeat(q, grp, axis=2), np.repeat(k, grp, axis=2)
     B, T, H, K = q.shape
     V = v.shape[-1]
     if g.ndim == 3:                                   # per-head gate, same for every d

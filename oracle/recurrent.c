@@ -10,13 +10,17 @@
  *     S <- S + beta_t * k_t (v_t - S^T k_t)^T     the read uses the decayed S
  *     o_t <- scale * S^T q_t                      read after the update
  *
- * The interface follows that page's I/O table (section 算子签名与 I/O 规格):
- *   q, k      [B*T, H, K]   bf16 (passed as raw uint16 bit patterns)
+ * The interface follows that page's I/O table (section 算子签名与 I/O 规格), with
+ * H value heads sharing Hk query/key heads (value head h reads key head h / (H / Hk);
+ * Hk == H is the plain case):
+ *   q, k      [B*T, Hk, K]  bf16 (passed as raw uint16 bit patterns)
  *   v         [B*T, H, V]   bf16
  *   g         [B*T, H, K] fp32 (per-dimension gate) or [B*T, H] fp32 (per-head gate)
  *   beta      [B*T, H]      fp32
  *   s0        [N, H, V, K]  fp64 or NULL (zeros); the page's state layout is the
  *             transpose of the internal K x V matrix
+ * With qk_l2norm (the page's use_qk_l2norm_in_kernel switch, section 测试与验证体系),
+ * q_t and k_t are first replaced by x / sqrt(sum_d x_d^2 + 1e-6).
  *   cu        [N+1]         int32 sequence offsets into the packed token axis, or
  *             NULL, in which case the N = B sequences have T tokens each
  *   o         [B*T, H, V]   fp64 output
@@ -41,12 +45,12 @@ static double bf16_to_f64(uint16_t b) {
     return (double)f;
 }
 
-int oracle_recurrent_fwd(int B, int T, int H, int K, int V, int N, int gate_per_dim,
-                         const uint16_t* q, const uint16_t* k, const uint16_t* v,
+int oracle_recurrent_fwd(int B, int T, int Hk, int H, int K, int V, int N, int gate_per_dim,
+                         int qk_l2norm, const uint16_t* q, const uint16_t* k, const uint16_t* v,
                          const float* g, const float* beta, const double* s0,
                          const int32_t* cu, double scale, double* o, double* s_out,
                          int nthreads) {
-    if (B <= 0 || T < 0 || H <= 0 || K <= 0 || V <= 0 || N <= 0) return -1;
+    if (B <= 0 || T < 0 || H <= 0 || Hk <= 0 || H % Hk != 0 || K <= 0 || V <= 0 || N <= 0) return -1;
     if (!q || !k || !v || !g || !beta || !o) return -2;
     if (cu == NULL && N != B) return -3;
     const long long total = (long long)B * T;
@@ -85,6 +89,7 @@ int oracle_recurrent_fwd(int B, int T, int H, int K, int V, int N, int gate_per_
                     s0 ? s0[(((size_t)n * H + h) * V + vv) * K + kk] : 0.0;
         for (long long t = bos; t < eos; ++t) {
             const size_t row = (size_t)t * H + h;
+            const size_t krow = (size_t)t * Hk + h / (H / Hk);
             /* 1. decay each row of S by exp(g) */
             for (int kk = 0; kk < K; ++kk) {
                 const double gv = gate_per_dim ? (double)g[row * K + kk] : (double)g[row];
@@ -93,8 +98,20 @@ int oracle_recurrent_fwd(int B, int T, int H, int K, int V, int N, int gate_per_
             }
             /* 2. delta correction: S += beta k (v - S^T k)^T */
             for (int kk = 0; kk < K; ++kk) {
-                kt[kk] = bf16_to_f64(k[row * K + kk]);
-                qt[kk] = bf16_to_f64(q[row * K + kk]);
+                kt[kk] = bf16_to_f64(k[krow * K + kk]);
+                qt[kk] = bf16_to_f64(q[krow * K + kk]);
+            }
+            if (qk_l2norm) {
+                double sk = 0.0, sq = 0.0;
+                for (int kk = 0; kk < K; ++kk) {
+                    sk += kt[kk] * kt[kk];
+                    sq += qt[kk] * qt[kk];
+                }
+                const double fk = 1.0 / sqrt(sk + 1e-6), fq = 1.0 / sqrt(sq + 1e-6);
+                for (int kk = 0; kk < K; ++kk) {
+                    kt[kk] *= fk;
+                    qt[kk] *= fq;
+                }
             }
             const double b = (double)beta[row];
             for (int vv = 0; vv < V; ++vv) {

@@ -261,3 +261,76 @@ def test_chunk_size_does_not_change_the_result():
     for o, S in outs[1:]:
         np.testing.assert_allclose(o, outs[0][0], rtol=1e-10, atol=1e-12)
         np.testing.assert_allclose(S, outs[0][1], rtol=1e-10, atol=1e-12)
+
+
+# ----------------------------------------------------------------------------------------
+# input variants: grouped value heads, in-kernel q/k normalisation
+# ----------------------------------------------------------------------------------------
+
+def test_grouped_value_heads_read_key_head_by_group():
+    """HV = 6 value heads on H = 2 key heads: value head hv equals a one-head run with key
+    head hv // 3 (consecutive value heads share a key head)."""
+    inp = make_inputs(1, 40, 2, 16, 12, seed=31, initial_state=True, HV=6)
+    o, S = oracle.recurrent_fwd(inp.q, inp.k, inp.v, inp.g, inp.beta, scale=0.5,
+                                initial_state=inp.initial_state)
+    for hv in range(6):
+        hk = hv // 3
+        one = lambda t, h: t[:, :, h:h + 1].contiguous()  # noqa: E731
+        o1, S1 = oracle.recurrent_fwd(one(inp.q, hk), one(inp.k, hk), one(inp.v, hv), one(inp.g, hv),
+                                      one(inp.beta, hv), scale=0.5,
+                                      initial_state=inp.initial_state[:, hv:hv + 1].contiguous())
+        np.testing.assert_array_equal(o[:, :, hv], o1[:, :, 0])
+        np.testing.assert_array_equal(S[:, hv], S1[:, 0])
+    # and the other grouping (hv % H) would not agree
+    o_alt, _ = oracle.recurrent_fwd(inp.q[:, :, 1:2].contiguous(), inp.k[:, :, 1:2].contiguous(),
+                                    inp.v[:, :, 1:2].contiguous(), inp.g[:, :, 1:2].contiguous(),
+                                    inp.beta[:, :, 1:2].contiguous(), scale=0.5,
+                                    initial_state=inp.initial_state[:, 1:2].contiguous())
+    assert np.max(np.abs(o_alt[:, :, 0] - o[:, :, 1])) > 1e-3
+
+
+def test_l2norm_is_per_token_and_scale_invariant():
+    """With in-kernel normalisation the result does not change when each token's q and
+    k are multiplied by its own power of two (exact in bf16), but does change when the
+    switch is off; any other normalisation axis would break the invariance."""
+    T, H = 33, 2
+    inp = make_inputs(1, T, H, 32, 16, seed=32, initial_state=True, normalise=False)
+    gen = torch.Generator("cpu").manual_seed(5)
+    f = 2.0 ** torch.randint(-2, 3, (1, T, H, 1), generator=gen).float()
+    q2 = (inp.q.float() * f).to(torch.bfloat16)
+    k2 = (inp.k.float() * torch.flip(f, dims=[1])).to(torch.bfloat16)
+    args = dict(scale=0.25, initial_state=inp.initial_state, use_qk_l2norm=True)
+    o1, S1 = oracle.recurrent_fwd(inp.q, inp.k, inp.v, inp.g, inp.beta, **args)
+    o2, S2 = oracle.recurrent_fwd(q2, k2, inp.v, inp.g, inp.beta, **args)
+    # the eps under the square root moves the scales by < 1e-6 relative
+    np.testing.assert_allclose(o2, o1, rtol=1e-6, atol=1e-7)
+    np.testing.assert_allclose(S2, S1, rtol=1e-6, atol=1e-7)
+    o3, _ = oracle.recurrent_fwd(inp.q, inp.k, inp.v, inp.g, inp.beta, scale=0.25,
+                                 initial_state=inp.initial_state)
+    assert np.max(np.abs(o3 - o1)) > 1e-4
+
+
+def test_l2norm_single_token_closed_form():
+    """One token from zero with normalisation: S = beta k^ v^T, o = scale beta (q^ . k^) v,
+    x^ = x / sqrt(|x|^2 + 1e-6)."""
+    K, V = 16, 12
+    inp = make_inputs(1, 1, 1, K, V, seed=33, normalise=False)
+    o, S = oracle.recurrent_fwd(inp.q, inp.k, inp.v, inp.g, inp.beta, scale=0.3, use_qk_l2norm=True)
+    q, k, v = (_widen(x).reshape(-1) for x in (inp.q, inp.k, inp.v))
+    qh, kh = q / np.sqrt(q @ q + 1e-6), k / np.sqrt(k @ k + 1e-6)
+    b = float(inp.beta)
+    np.testing.assert_allclose(S.reshape(V, K), b * np.outer(v, kh), rtol=1e-13, atol=0)
+    np.testing.assert_allclose(o.reshape(V), 0.3 * b * np.dot(qh, kh) * v, rtol=1e-12, atol=1e-15)
+
+
+@pytest.mark.parametrize("per_dim", [True, False])
+def test_chunked_matches_recurrent_grouped_and_normalised(per_dim):
+    """The two formulations agree with grouped value heads and in-kernel normalisation."""
+    inp = make_inputs(1, 150, 2, 32, 16, seed=34, initial_state=True, normalise=False, HV=4,
+                      per_dim_gate=per_dim, chunk_size=64, gate_mean=1.0)
+    a = oracle.recurrent_fwd(inp.q, inp.k, inp.v, inp.g, inp.beta, initial_state=inp.initial_state,
+                             use_qk_l2norm=True)
+    b = oracle.chunked_fwd(inp.q, inp.k, inp.v, inp.g, inp.beta, initial_state=inp.initial_state,
+                           chunk_size=64, use_qk_l2norm=True)
+    for x, y in zip(a, b):
+        np.testing.assert_allclose(x, y, rtol=1e-9, atol=1e-9)
