@@ -4,8 +4,8 @@
 
 namespace cdr {
 hipError_t launch_intra(int C, bool per_dim, const uint16_t* q, const uint16_t* k, const uint16_t* v,
-                        const float* g, const float* beta, const ChunkMap& map, int nslots, int H,
-                        float scale, const Work& ws, int nscratch, hipStream_t stream);
+                        const float* g, const float* beta, const ChunkMap& map, int nslots, int H, int Hk,
+                        int l2n, float scale, const Work& ws, int nscratch, hipStream_t stream);
 hipError_t launch_chain(const ChunkMap& map, int N, int H, const float* s0, float* s_out, const Work& ws,
                         hipStream_t stream);
 hipError_t launch_output(int C, const ChunkMap& map, int nslots, int H, uint16_t* o, const Work& ws,
@@ -15,6 +15,9 @@ hipError_t launch_output(int C, const ChunkMap& map, int nslots, int H, uint16_t
 namespace {
 
 constexpr size_t kAlign = 256;
+
+// value heads (the state, v, g, beta and o carry them); q and k have p->H
+int64_t value_heads(const cdr_problem* p) { return p->HV > 0 ? p->HV : p->H; }
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
@@ -28,7 +31,7 @@ constexpr int kArrays = 14;
 constexpr int64_t kScratchSlots = 512; // at most this many intra workgroups run at once
 
 size_t scratch_slots(const cdr_problem* p) {
-    const int64_t nch = num_slots(p) * p->H;
+    const int64_t nch = num_slots(p) * value_heads(p);
     return (size_t)(nch < kScratchSlots ? nch : kScratchSlots);
 }
 
@@ -38,7 +41,7 @@ struct Layout {
 };
 
 Layout layout(const cdr_problem* p) {
-    const size_t nch = (size_t)num_slots(p) * (size_t)p->H, nsc = scratch_slots(p);
+    const size_t nch = (size_t)num_slots(p) * (size_t)value_heads(p), nsc = scratch_slots(p);
     const size_t C = (size_t)p->chunk_size, K = (size_t)p->K, V = (size_t)p->V;
     const size_t bytes[kArrays] = {
         nch * K * K * 2,  // Pn_hi
@@ -72,7 +75,9 @@ extern "C" {
 
 cdr_status cdr_check(const cdr_problem* p) {
     if (p == nullptr) return CDR_ERR_NULL_ARG;
-    if (p->B <= 0 || p->T < 0 || p->H <= 0 || p->N <= 0 || p->K <= 0 || p->V <= 0) return CDR_ERR_BAD_SHAPE;
+    if (p->B <= 0 || p->T < 0 || p->H <= 0 || p->N <= 0 || p->K <= 0 || p->V <= 0 || p->HV < 0)
+        return CDR_ERR_BAD_SHAPE;
+    if (value_heads(p) % p->H != 0) return CDR_ERR_BAD_SHAPE;  // whole groups of value heads per key head
     if (p->K != 128 || p->V != 128) return CDR_ERR_UNSUPPORTED;
     if (p->chunk_size != 64 && p->chunk_size != 128) return CDR_ERR_UNSUPPORTED;
     if (p->gate != CDR_GATE_PER_DIM && p->gate != CDR_GATE_PER_HEAD) return CDR_ERR_UNSUPPORTED;
@@ -83,7 +88,7 @@ cdr_status cdr_check(const cdr_problem* p) {
     }
     // packed token offsets are int32 on the device side of the interface
     if ((int64_t)p->B * p->T > INT32_MAX) return CDR_ERR_BAD_SHAPE;
-    if (num_slots(p) * (int64_t)p->H > (int64_t)INT32_MAX) return CDR_ERR_BAD_SHAPE;
+    if (num_slots(p) * value_heads(p) > (int64_t)INT32_MAX) return CDR_ERR_BAD_SHAPE;
     return CDR_OK;
 }
 
@@ -141,14 +146,15 @@ cdr_status chunk_dr_fwd_stages(const cdr_problem* p, const void* q, const void* 
     if ((stages & CDR_STAGE_INTRA) && nslots > 0) {
         if (cdr::launch_intra(C, p->gate == CDR_GATE_PER_DIM, static_cast<const uint16_t*>(q),
                               static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), g, beta, map,
-                              nslots, p->H, p->scale, ws, (int)scratch_slots(p), s) != hipSuccess)
+                              nslots, (int)value_heads(p), p->H, p->qk_l2norm != 0, p->scale, ws,
+                              (int)scratch_slots(p), s) != hipSuccess)
             return CDR_ERR_HIP;
     }
     if (stages & CDR_STAGE_CHAIN) {
-        if (cdr::launch_chain(map, p->N, p->H, s0, s_out, ws, s) != hipSuccess) return CDR_ERR_HIP;
+        if (cdr::launch_chain(map, p->N, (int)value_heads(p), s0, s_out, ws, s) != hipSuccess) return CDR_ERR_HIP;
     }
     if ((stages & CDR_STAGE_OUTPUT) && nslots > 0) {
-        if (cdr::launch_output(C, map, nslots, p->H, static_cast<uint16_t*>(o), ws, s) != hipSuccess)
+        if (cdr::launch_output(C, map, nslots, (int)value_heads(p), static_cast<uint16_t*>(o), ws, s) != hipSuccess)
             return CDR_ERR_HIP;
     }
     return CDR_OK;

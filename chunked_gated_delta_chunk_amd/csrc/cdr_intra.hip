@@ -38,6 +38,7 @@
 namespace cdr {
 
 constexpr int IWAVES = 8;
+constexpr float L2N_EPS = 1e-6f;  // in-kernel q/k normalisation: x / sqrt(|x|^2 + eps)
 constexpr int ITHREADS = 64 * IWAVES;
 
 template <int C>
@@ -57,7 +58,7 @@ struct IntraShape {
     static constexpr int R2 = 2 * C * COL_LD * 2;      // column operands; later T tiles
     static constexpr int RF = (NOFF > NT ? NOFF : NT) * KD * 4;  // tile totals, later F
     static constexpr int RG = 2 * NT * KD * 4;         // gamma and exp(gamma) at tile middles
-    static constexpr int RMISC = 2 * C * 4;            // beta, per-head gamma
+    static constexpr int RMISC = 3 * C * 4;            // beta, per-head gamma, key row scales
     static constexpr int BYTES = R1 + R2 + RF + RG + RMISC;
     static_assert((NPAIR + (NT / 2) * (NT / 2)) * TILE_SZ * 4 <= R1, "A tiles + merge scratch");
     static_assert(NPAIR * TILE_SZ * 4 <= R2, "T tiles");
@@ -121,7 +122,7 @@ struct EIn {
 template <int C, bool PER_DIM>
 __device__ __forceinline__ void e_load(EIn& in, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
                                        const float* __restrict__ g, const float* __restrict__ beta,
-                                       const ChunkMap& map, int H, int item, int tid) {
+                                       const ChunkMap& map, int H, int Hk, int item, int tid) {
     // Every register is written on every path (no item or an empty chunk slot load token 0,
     // which exists whenever there are items), so the previous contents are dead once this
     // is called and nothing has to be kept alive across the item.
@@ -131,8 +132,10 @@ __device__ __forceinline__ void e_load(EIn& in, const uint16_t* __restrict__ k, 
     int rows;
     slot_chunk(map, slot, tok0, rows);
     const int last = max(rows - 1, 0);
-    const size_t rs = (size_t)H * KD;
+    // value head h reads key head h / (H / Hk); v and g have H heads
+    const size_t rs = (size_t)H * KD, rsk = (size_t)Hk * KD;
     const size_t base = (size_t)tok0 * rs + (size_t)h * KD;
+    const size_t basek = (size_t)tok0 * rsk + (size_t)(h / (H / Hk)) * KD;
     const int R = min(tid >> 6, C / 16 - 1), d0 = 2 * (tid & 63);
     in.b = beta[(size_t)(tok0 + min(tid, last)) * H + h];
     {
@@ -145,7 +148,7 @@ __device__ __forceinline__ void e_load(EIn& in, const uint16_t* __restrict__ k, 
                 const float s1 = g[(size_t)(tok0 + ic) * H + h];
                 in.g[ii] = make_float2(s1, s1);
             }
-            in.k[ii] = *reinterpret_cast<const uint32_t*>(k + base + (size_t)ic * rs + d0);
+            in.k[ii] = *reinterpret_cast<const uint32_t*>(k + basek + (size_t)ic * rsk + d0);
             in.v[ii] = *reinterpret_cast<const uint32_t*>(v + base + (size_t)ic * rs + d0);
         }
     }
@@ -156,8 +159,8 @@ __device__ __forceinline__ void e_load(EIn& in, const uint16_t* __restrict__ k, 
 template <int C, bool PER_DIM>
 __device__ __forceinline__ void intra_item(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    const float* __restrict__ g, const float* __restrict__ beta, const ChunkMap& map, int H, float scale,
-    const Work& ws, unsigned char* smem, int slot, int h, size_t sc, EIn& ein, int next_item) {
+    const float* __restrict__ g, const float* __restrict__ beta, const ChunkMap& map, int H, int Hk, bool l2n,
+    float scale, const Work& ws, unsigned char* smem, int slot, int h, size_t sc, EIn& ein, int next_item) {
     using S = IntraShape<C>;
     constexpr int NT = S::NT, NS = S::NS;
     float* Ep = reinterpret_cast<float*>(smem);                                   // [C][EP_LD]
@@ -169,6 +172,7 @@ __device__ __forceinline__ void intra_item(
     float* egm = gmid + NT * KD;                                                  // [NT][KD]
     float* bet = egm + NT * KD;                                                   // [C]
     float* grow = bet + C;                                                        // [C] per-head gamma
+    float* knr = grow + C;                                                        // [C] key row scales
     float* Atile = reinterpret_cast<float*>(smem);                                // after AA2
     float* Pscr = Atile + S::NPAIR * S::TILE_SZ;                                  // merge scratch
     float* Ttile = reinterpret_cast<float*>(smem + S::R1);
@@ -181,14 +185,15 @@ __device__ __forceinline__ void intra_item(
     int rows;
     slot_chunk(map, slot, tok0, rows);
     if (rows == 0) {
-        e_load<C, PER_DIM>(ein, k, v, g, beta, map, H, next_item, tid);
+        e_load<C, PER_DIM>(ein, k, v, g, beta, map, H, Hk, next_item, tid);
         return;
     }
     const size_t ch = (size_t)slot * H + h;
     const int lane = tid & 63, wave = tid >> 6;
     const int r16 = lane & 15, q4 = lane >> 4;
-    const size_t rs = (size_t)H * KD;  // token stride of q, k, v, per-dim g (elements)
-    const size_t base = (size_t)tok0 * rs + (size_t)h * KD;
+    // q and k: key head h / (H / Hk) of Hk
+    const size_t rsk = (size_t)Hk * KD;
+    const size_t basek = (size_t)tok0 * rsk + (size_t)(h / (H / Hk)) * KD;
 
     // Row operands of phase AA2 (raw k and q rows of the wave's two tile rows), loaded
     // before phase E so that their latency is hidden behind it.
@@ -202,8 +207,8 @@ __device__ __forceinline__ void intra_item(
 #pragma unroll
         for (int ks = 0; ks < KD / 32; ++ks) {
             const int i = 16 * Rown[o] + r16, ic = min(max(i, 0), rows - 1);
-            const uint4 kx = *reinterpret_cast<const uint4*>(k + base + (size_t)ic * rs + 32 * ks + 8 * q4);
-            const uint4 qx = *reinterpret_cast<const uint4*>(q + base + (size_t)ic * rs + 32 * ks + 8 * q4);
+            const uint4 kx = *reinterpret_cast<const uint4*>(k + basek + (size_t)ic * rsk + 32 * ks + 8 * q4);
+            const uint4 qx = *reinterpret_cast<const uint4*>(q + basek + (size_t)ic * rsk + 32 * ks + 8 * q4);
             kfr[o][ks] = (i < rows) ? kx : make_uint4(0, 0, 0, 0);
             qfr[o][ks] = (i < rows) ? qx : make_uint4(0, 0, 0, 0);
         }
@@ -229,6 +234,25 @@ __device__ __forceinline__ void intra_item(
                 gm2[ii][1] += gm2[ii - 1][1];
             }
             *reinterpret_cast<float2*>(ttot + R * KD + d0) = make_float2(gm2[15][0], gm2[15][1]);
+        }
+        // in-kernel L2 normalisation of keys: k / sqrt(|k|^2 + eps) per token, the row sum of
+        // squares reduced across the wave (the 64 lanes hold the row's 128 columns)
+        float rnk[16];
+#pragma unroll
+        for (int ii = 0; ii < 16; ++ii) rnk[ii] = 1.f;
+        if (l2n && act) {
+#pragma unroll
+            for (int ii = 0; ii < 16; ++ii) {
+                const float a = __uint_as_float(kr[ii] << 16), b = __uint_as_float(kr[ii] & 0xffff0000u);
+                float ssq = a * a + b * b;
+#pragma unroll
+                for (int m = 1; m < 64; m <<= 1) ssq += __shfl_xor(ssq, m, 64);
+                rnk[ii] = rsqrtf(ssq + L2N_EPS);
+            }
+            if ((tid & 63) == 0) {
+#pragma unroll
+                for (int ii = 0; ii < 16; ++ii) knr[16 * R + ii] = rnk[ii];
+            }
         }
         lds_barrier();
         if (act) {
@@ -273,8 +297,8 @@ __device__ __forceinline__ void intra_item(
 #pragma unroll
                     for (int rr = 0; rr < 2; ++rr) {
                         const int ii = 8 * hh + 2 * e2 + rr;
-                        kf[rr][0] = __uint_as_float(kr[ii] << 16);
-                        kf[rr][1] = __uint_as_float(kr[ii] & 0xffff0000u);
+                        kf[rr][0] = __uint_as_float(kr[ii] << 16) * rnk[ii];
+                        kf[rr][1] = __uint_as_float(kr[ii] & 0xffff0000u) * rnk[ii];
 #pragma unroll
                         for (int c = 0; c < 2; ++c) {
                             const float x = gm2[ii][c] - gmv[c];
@@ -334,6 +358,31 @@ __device__ __forceinline__ void intra_item(
     lds_barrier();
 
     // ------------------------------------------------------------------ phase AA2
+    // L2 scales of the wave's own q and k rows: lanes r16 + 16 q4 (q4 = 0..3) share a row
+    float rk2[2] = {1.f, 1.f}, rq2[2] = {1.f, 1.f};
+    if (l2n) {
+#pragma unroll
+        for (int o = 0; o < 2; ++o) {
+            float sk = 0.f, sq = 0.f;
+#pragma unroll
+            for (int ks = 0; ks < KD / 32; ++ks) {
+                float kf[8], qf[8];
+                unpack8(kfr[o][ks], kf);
+                unpack8(qfr[o][ks], qf);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    sk += kf[e] * kf[e];
+                    sq += qf[e] * qf[e];
+                }
+            }
+            sk += __shfl_xor(sk, 16, 64);
+            sk += __shfl_xor(sk, 32, 64);
+            sq += __shfl_xor(sq, 16, 64);
+            sq += __shfl_xor(sq, 32, 64);
+            rk2[o] = rsqrtf(sk + L2N_EPS);
+            rq2[o] = rsqrtf(sq + L2N_EPS);
+        }
+    }
     f32x4 accA[S::SMAX];
 #pragma unroll
     for (int s = 0; s < S::SMAX; ++s) {
@@ -344,6 +393,7 @@ __device__ __forceinline__ void intra_item(
         const int R = Rown[o];
         const int J = (o == 0) ? p : p - cp - 1;
         const int i = 16 * R + r16, j = 16 * J + r16;
+        const float rk = o ? rk2[1] : rk2[0], rq = o ? rq2[1] : rq2[0];
         f32x4 acc = {0.f, 0.f, 0.f, 0.f}, acc2 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < KD / 32; ++ks) {
@@ -354,6 +404,11 @@ __device__ __forceinline__ void intra_item(
                 float kf[8], qf[8], ep[8];
                 unpack8(krv, kf);
                 unpack8(qrv, qf);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    kf[e] *= rk;
+                    qf[e] *= rq;
+                }
                 const float4* epp = reinterpret_cast<const float4*>(Ep + i * S::EP_LD + dd);
                 const float4 e0 = epp[0], e1 = epp[1];
                 ep[0] = e0.x; ep[1] = e0.y; ep[2] = e0.z; ep[3] = e0.w;
@@ -392,12 +447,12 @@ __device__ __forceinline__ void intra_item(
                 acc = mfma32(ahi, blo, acc);
                 acc2 = mfma32(bhi, aqv, acc2);   // A2^T tile: rows j, columns i
             } else {
-                const uint4 kx = *reinterpret_cast<const uint4*>(k + base + (size_t)min(j, rows - 1) * rs + dd);
+                const uint4 kx = *reinterpret_cast<const uint4*>(k + basek + (size_t)min(j, rows - 1) * rsk + dd);
                 const bf16x8 b = as_bf16x8((j < rows) ? kx : make_uint4(0, 0, 0, 0));
                 if (J == R) {
                     float qf[8];
                     unpack8(qrv, qf);
-                    const float f = scale * ex(grow[i]);
+                    const float f = scale * ex(grow[i]) * rq;
                     uint4 pq;
                     pq.x = pack_bf2(f * qf[0], f * qf[1]);
                     pq.y = pack_bf2(f * qf[2], f * qf[3]);
@@ -420,6 +475,10 @@ __device__ __forceinline__ void intra_item(
             if constexpr (!PER_DIM) {
                 a *= (jj <= ii) ? ex(grow[ii] - grow[jj]) : 0.f;
                 a2 *= (j2 <= i2) ? ex(grow[i2] - grow[j2]) : 0.f;
+                if (l2n) {  // raw q, k products: apply the row scales afterwards
+                    a *= knr[ii] * knr[jj];
+                    a2 *= rq * knr[j2];
+                }
             }
             accA[s][rr] = (jj < ii) ? a * bet[ii] : 0.f;
             a2v[rr] = (j2 <= i2) ? a2 * scale : 0.f;
@@ -566,7 +625,7 @@ __device__ __forceinline__ void intra_item(
 #pragma unroll
     for (int I = 0; I < NT; ++I)
         qgv[I] = *reinterpret_cast<const uint2*>(ws.qgs + sc * C * KD + ((size_t)(I * (KD / 16) + dt) * 64 + lane) * 4);
-    e_load<C, PER_DIM>(ein, k, v, g, beta, map, H, next_item, tid);  // next item, in flight through PQ
+    e_load<C, PER_DIM>(ein, k, v, g, beta, map, H, Hk, next_item, tid);  // next item, in flight through PQ
     // w and u as pi-order operands: tiles 2s and 2s+1 give the 32 contracted rows of step s
     uint4 wh[NS], wl[NS], uh[NS], ul[NS];
 #pragma unroll
@@ -641,15 +700,16 @@ __device__ __forceinline__ void intra_item(
 template <int C, bool PER_DIM>
 __global__ __launch_bounds__(ITHREADS) void intra_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    const float* __restrict__ g, const float* __restrict__ beta, ChunkMap map, int H, float scale,
-    Work ws, int nitems) {
+    const float* __restrict__ g, const float* __restrict__ beta, ChunkMap map, int H, int Hk, int l2n,
+    float scale, Work ws, int nitems) {
     __shared__ __attribute__((aligned(16))) unsigned char smem[IntraShape<C>::BYTES];
     EIn ein;
-    e_load<C, PER_DIM>(ein, k, v, g, beta, map, H, blockIdx.x < nitems ? (int)blockIdx.x : -1, threadIdx.x);
+    e_load<C, PER_DIM>(ein, k, v, g, beta, map, H, Hk, blockIdx.x < nitems ? (int)blockIdx.x : -1, threadIdx.x);
     for (int item = blockIdx.x; item < nitems; item += gridDim.x) {
         __syncthreads();  // the previous item is done with LDS
         const int next = item + (int)gridDim.x < nitems ? item + (int)gridDim.x : -1;
-        intra_item<C, PER_DIM>(q, k, v, g, beta, map, H, scale, ws, smem, item / H, item % H, blockIdx.x, ein, next);
+        intra_item<C, PER_DIM>(q, k, v, g, beta, map, H, Hk, l2n != 0, scale, ws, smem, item / H, item % H,
+                               blockIdx.x, ein, next);
     }
 }
 
@@ -674,23 +734,23 @@ static int resident_groups() {
 
 template <int C, bool PER_DIM>
 static hipError_t launch_intra_t(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float* g,
-                                 const float* beta, const ChunkMap& map, int nslots, int H, float scale,
-                                 const Work& ws, int nscratch, hipStream_t stream) {
+                                 const float* beta, const ChunkMap& map, int nslots, int H, int Hk, int l2n,
+                                 float scale, const Work& ws, int nscratch, hipStream_t stream) {
     const int nitems = nslots * H;
     const int grid = min(min(nitems, nscratch), resident_groups<C, PER_DIM>());
     hipLaunchKernelGGL((intra_kernel<C, PER_DIM>), dim3(grid), dim3(ITHREADS), 0, stream, q, k, v, g, beta, map, H,
-                       scale, ws, nitems);
+                       Hk, l2n, scale, ws, nitems);
     return hipGetLastError();
 }
 
 hipError_t launch_intra(int C, bool per_dim, const uint16_t* q, const uint16_t* k, const uint16_t* v,
-                        const float* g, const float* beta, const ChunkMap& map, int nslots, int H,
-                        float scale, const Work& ws, int nscratch, hipStream_t stream) {
+                        const float* g, const float* beta, const ChunkMap& map, int nslots, int H, int Hk,
+                        int l2n, float scale, const Work& ws, int nscratch, hipStream_t stream) {
     if (C == 64)
-        return per_dim ? launch_intra_t<64, true>(q, k, v, g, beta, map, nslots, H, scale, ws, nscratch, stream)
-                       : launch_intra_t<64, false>(q, k, v, g, beta, map, nslots, H, scale, ws, nscratch, stream);
-    return per_dim ? launch_intra_t<128, true>(q, k, v, g, beta, map, nslots, H, scale, ws, nscratch, stream)
-                   : launch_intra_t<128, false>(q, k, v, g, beta, map, nslots, H, scale, ws, nscratch, stream);
+        return per_dim ? launch_intra_t<64, true>(q, k, v, g, beta, map, nslots, H, Hk, l2n, scale, ws, nscratch, stream)
+                       : launch_intra_t<64, false>(q, k, v, g, beta, map, nslots, H, Hk, l2n, scale, ws, nscratch, stream);
+    return per_dim ? launch_intra_t<128, true>(q, k, v, g, beta, map, nslots, H, Hk, l2n, scale, ws, nscratch, stream)
+                   : launch_intra_t<128, false>(q, k, v, g, beta, map, nslots, H, Hk, l2n, scale, ws, nscratch, stream);
 }
 
 }  // namespace cdr

@@ -30,7 +30,8 @@ class cdr_problem(ctypes.Structure):
                 ("K", ctypes.c_int32), ("V", ctypes.c_int32), ("N", ctypes.c_int32),
                 ("gate", ctypes.c_int32), ("chunk_size", ctypes.c_int32),
                 ("scale", ctypes.c_float), ("has_initial_state", ctypes.c_int32),
-                ("output_final_state", ctypes.c_int32), ("varlen", ctypes.c_int32)]
+                ("output_final_state", ctypes.c_int32), ("varlen", ctypes.c_int32),
+                ("HV", ctypes.c_int32), ("qk_l2norm", ctypes.c_int32)]
 
 
 _lib = None
@@ -71,11 +72,11 @@ def _raise(status: int, what: str):
 
 
 def make_problem(B, T, H, K, V, N, per_dim_gate, chunk_size, scale, has_initial_state,
-                 output_final_state, varlen) -> cdr_problem:
+                 output_final_state, varlen, HV=0, qk_l2norm=False) -> cdr_problem:
     return cdr_problem(int(B), int(T), int(H), int(K), int(V), int(N),
                        GATE_PER_DIM if per_dim_gate else GATE_PER_HEAD, int(chunk_size),
                        float(scale), int(bool(has_initial_state)), int(bool(output_final_state)),
-                       int(bool(varlen)))
+                       int(bool(varlen)), int(HV), int(bool(qk_l2norm)))
 
 
 def check(p: cdr_problem) -> int:
@@ -115,25 +116,25 @@ class PreparedForward:
 
     def __init__(self, q, k, v, g, beta, scale=None, initial_state=None, cu_seqlens=None,
                  chunk_size=64, output_final_state=False, workspace=None, out=None,
-                 final_state_out=None):
+                 final_state_out=None, use_qk_l2norm_in_kernel=False):
         lib = load_library()
         _need(q, "q", torch.bfloat16)
         if q.dim() != 4:
             raise ValueError("q must be [B, T, H, K]")
         B, T, H, K = q.shape
         _need(k, "k", torch.bfloat16, (B, T, H, K))
-        if v.dim() != 4 or tuple(v.shape[:3]) != (B, T, H):
-            raise ValueError("v must be [B, T, H, V]")
+        if v.dim() != 4 or tuple(v.shape[:2]) != (B, T) or v.shape[2] % H:
+            raise ValueError("v must be [B, T, HV, V] with HV a multiple of the q/k heads")
         _need(v, "v", torch.bfloat16)
-        V = v.shape[3]
+        HV, V = v.shape[2], v.shape[3]
         _need(g, "g", torch.float32)
-        if tuple(g.shape) == (B, T, H, K):
+        if tuple(g.shape) == (B, T, HV, K):
             per_dim = True
-        elif tuple(g.shape) == (B, T, H):
+        elif tuple(g.shape) == (B, T, HV):
             per_dim = False
         else:
-            raise ValueError(f"g must be [B,T,H,K] or [B,T,H], got {tuple(g.shape)}")
-        _need(beta, "beta", torch.float32, (B, T, H))
+            raise ValueError(f"g must be [B,T,HV,K] or [B,T,HV], got {tuple(g.shape)}")
+        _need(beta, "beta", torch.float32, (B, T, HV))
         if cu_seqlens is not None:
             _need(cu_seqlens, "cu_seqlens", torch.int32)
             if cu_seqlens.dim() != 1 or cu_seqlens.numel() < 2:
@@ -142,12 +143,12 @@ class PreparedForward:
         else:
             N = B
         if initial_state is not None:
-            _need(initial_state, "initial_state", torch.float32, (N, H, V, K))
+            _need(initial_state, "initial_state", torch.float32, (N, HV, V, K))
         if scale is None:
             scale = K ** -0.5
         self.problem = make_problem(B, T, H, K, V, N, per_dim, chunk_size, scale,
                                     initial_state is not None, output_final_state,
-                                    cu_seqlens is not None)
+                                    cu_seqlens is not None, HV, use_qk_l2norm_in_kernel)
         st = lib.cdr_check(ctypes.byref(self.problem))
         if st != CDR_OK:
             _raise(st, "chunk_dr_fwd")
@@ -160,16 +161,16 @@ class PreparedForward:
         self.s0 = initial_state.contiguous() if initial_state is not None else None
         self.cu = cu_seqlens.contiguous() if cu_seqlens is not None else None
         if out is None:
-            out = torch.empty((B, T, H, V), dtype=torch.bfloat16, device=device)
+            out = torch.empty((B, T, HV, V), dtype=torch.bfloat16, device=device)
         else:
-            _need(out, "out", torch.bfloat16, (B, T, H, V))
+            _need(out, "out", torch.bfloat16, (B, T, HV, V))
         self.o = out
         self.S = None
         if output_final_state:
             if final_state_out is None:
-                final_state_out = torch.empty((N, H, V, K), dtype=torch.float32, device=device)
+                final_state_out = torch.empty((N, HV, V, K), dtype=torch.float32, device=device)
             else:
-                _need(final_state_out, "final_state_out", torch.float32, (N, H, V, K))
+                _need(final_state_out, "final_state_out", torch.float32, (N, HV, V, K))
             self.S = final_state_out
         nbytes = lib.cdr_workspace_bytes(ctypes.byref(self.problem))
         if workspace is None:
@@ -204,14 +205,18 @@ def chunk_dr_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Ten
                  out: Optional[torch.Tensor] = None,
                  final_state_out: Optional[torch.Tensor] = None,
                  stages: int = STAGE_ALL,
+                 use_qk_l2norm_in_kernel: bool = False,
                  ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Chunked gated delta-rule forward on the GPU.
 
-    q, k ``[B,T,H,K]`` bf16; v ``[B,T,H,V]`` bf16; g ``[B,T,H,K]`` (per-dimension gate)
-    or ``[B,T,H]`` (per-head gate) fp32; beta ``[B,T,H]`` fp32; initial_state
-    ``[N,H,V,K]`` fp32 or None (zeros); cu_seqlens ``[N+1]`` int32 on the device, or
-    None (then N = B). ``scale=None`` means ``K ** -0.5``.  Returns ``(o, S)`` with o
-    ``[B,T,H,V]`` bf16 and S ``[N,H,V,K]`` fp32 (None unless output_final_state).
+    q, k ``[B,T,H,K]`` bf16; v ``[B,T,HV,V]`` bf16 with HV a multiple of H (value head hv
+    uses query/key head ``hv // (HV // H)``); g ``[B,T,HV,K]`` (per-dimension gate) or
+    ``[B,T,HV]`` (per-head gate) fp32; beta ``[B,T,HV]`` fp32; initial_state
+    ``[N,HV,V,K]`` fp32 or None (zeros); cu_seqlens ``[N+1]`` int32 on the device, or
+    None (then N = B). ``scale=None`` means ``K ** -0.5``.  With
+    ``use_qk_l2norm_in_kernel`` q and k are normalised over K per token inside the
+    kernels (``x / sqrt(|x|^2 + 1e-6)``).  Returns ``(o, S)`` with o ``[B,T,HV,V]`` bf16
+    and S ``[N,HV,V,K]`` fp32 (None unless output_final_state).
     ``workspace`` optionally supplies the device scratch buffer (uint8, at least
     :func:`workspace_bytes` bytes); otherwise one is allocated.  ``out`` and
     ``final_state_out`` optionally supply the output buffers.  ``stages`` selects kernel
@@ -220,5 +225,6 @@ def chunk_dr_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Ten
     call = PreparedForward(q, k, v, g, beta, scale=scale, initial_state=initial_state,
                            cu_seqlens=cu_seqlens, chunk_size=chunk_size,
                            output_final_state=output_final_state, workspace=workspace, out=out,
-                           final_state_out=final_state_out)
+                           final_state_out=final_state_out,
+                           use_qk_l2norm_in_kernel=use_qk_l2norm_in_kernel)
     return call(stages)

@@ -17,6 +17,13 @@
  * [N, H, V, K], the transpose of the internal K x V matrix, as on that page
  * (section 算子签名与 I/O 规格).
  *
+ * Two variants of the inputs are supported.  Grouped value heads: HV value heads (v, g,
+ * beta, o, state) share H query/key heads in groups of HV / H, value head hv reading key
+ * head hv / (HV / H), as in the workloads of the page "flash-linear-attention 中的
+ * G_T_CONTIG" (H = 4, HV = 8).  In-kernel normalisation (the wrapper switch
+ * use_qk_l2norm_in_kernel of the chunk_kda page, section 测试与验证体系): q_t and k_t are
+ * replaced by x / sqrt(|x|^2 + 1e-6) over K before anything else.
+ *
  * Conventions shared by every entry point:
  *  - Tensor pointers are DEVICE pointers to contiguous row-major buffers.
  *  - Tokens are packed: fixed-length batches are addressed as B*T consecutive tokens
@@ -37,7 +44,7 @@
 extern "C" {
 #endif
 
-#define CDR_VERSION 1
+#define CDR_VERSION 2
 
 typedef enum {
     CDR_OK = 0,
@@ -50,15 +57,15 @@ typedef enum {
 } cdr_status;
 
 typedef enum {
-    CDR_GATE_PER_DIM = 0,      /* g [B*T, H, K] fp32: per-key-dimension log gate (KDA) */
-    CDR_GATE_PER_HEAD = 1      /* g [B*T, H] fp32: one log gate per token and head (Gated DeltaNet) */
+    CDR_GATE_PER_DIM = 0,      /* g [B*T, HV, K] fp32: per-key-dimension log gate (KDA) */
+    CDR_GATE_PER_HEAD = 1      /* g [B*T, HV] fp32: one log gate per token and head (Gated DeltaNet) */
 } cdr_gate;
 
 /* Problem description.  All fields are plain host values. */
 typedef struct {
     int32_t B;                  /* batch rows; must be 1 when varlen != 0 */
     int32_t T;                  /* tokens per batch row (total packed tokens when varlen) */
-    int32_t H;                  /* heads */
+    int32_t H;                  /* query/key heads */
     int32_t K;                  /* key dimension; must be 128 */
     int32_t V;                  /* value dimension; must be 128 */
     int32_t N;                  /* sequences: B when varlen == 0, else len(cu_seqlens) - 1 */
@@ -68,6 +75,10 @@ typedef struct {
     int32_t has_initial_state;  /* initial_state is read when non-zero, else S starts at 0 */
     int32_t output_final_state; /* final_state is written when non-zero */
     int32_t varlen;             /* cu_seqlens is read when non-zero */
+    int32_t HV;                 /* value heads (v, g, beta, o and the state); 0 means H.  Must be a
+                                   multiple of H: value head hv uses query/key head hv / (HV / H) */
+    int32_t qk_l2norm;          /* when non-zero, q and k are L2-normalised over K per token inside
+                                   the kernels, x / sqrt(|x|^2 + 1e-6) */
 } cdr_problem;
 
 /*
@@ -78,7 +89,7 @@ cdr_status cdr_check(const cdr_problem* p);
 
 /*
  * Bytes of device workspace chunk_dr_fwd needs for problem p (0 if p is invalid).
- * The size depends only on the shape fields (B, T, H, K, V, N, chunk_size): it
+ * The size depends only on the shape fields (B, T, H, HV, K, V, N, chunk_size): it
  * holds the per-chunk intermediates (w, u, decayed keys and queries, the in-chunk
  * attention block, the chunk-entry states and the corrected values), about
  * 290 KiB per chunk and head at chunk_size 128.
@@ -89,17 +100,17 @@ size_t cdr_workspace_bytes(const cdr_problem* p);
  * Chunked gated delta-rule forward.
  *
  *   q, k          bf16 [B*T, H, K]   queries and keys
- *   v             bf16 [B*T, H, V]   values
- *   g             fp32 [B*T, H, K] (CDR_GATE_PER_DIM) or [B*T, H] (CDR_GATE_PER_HEAD);
+ *   v             bf16 [B*T, HV, V]  values (HV value heads, see cdr_problem)
+ *   g             fp32 [B*T, HV, K] (CDR_GATE_PER_DIM) or [B*T, HV] (CDR_GATE_PER_HEAD);
  *                 log-domain forget gate, expected <= 0
- *   beta          fp32 [B*T, H]      delta-rule step size
- *   initial_state fp32 [N, H, V, K]  read when p->has_initial_state, else may be NULL
+ *   beta          fp32 [B*T, HV]     delta-rule step size
+ *   initial_state fp32 [N, HV, V, K] read when p->has_initial_state, else may be NULL
  *   cu_seqlens    int32 [N + 1]      device array of sequence offsets into the packed token
  *                                    axis (0 = cu[0] <= cu[1] <= ... <= cu[N] = T); read when
  *                                    p->varlen, else may be NULL.  Its contents are not
  *                                    validated; offsets outside [0, T] are undefined behaviour.
- *   o             bf16 [B*T, H, V]   output, written for every token of every sequence
- *   final_state   fp32 [N, H, V, K]  written when p->output_final_state, else may be NULL.
+ *   o             bf16 [B*T, HV, V]  output, written for every token of every sequence
+ *   final_state   fp32 [N, HV, V, K] written when p->output_final_state, else may be NULL.
  *                                    An empty sequence returns its initial state (or zeros).
  *   workspace     device buffer of at least cdr_workspace_bytes(p) bytes, 256-byte aligned;
  *                 its contents on entry do not matter.  It must not be used by another call

@@ -26,7 +26,29 @@ def test_library_exports_every_declared_function():
             "cdr_version"} <= declared
     for name in declared:
         assert hasattr(lib, name), f"{name} declared in chunk_dr.h but not exported"
-    assert lib.cdr_version() == 1
+    header = open(os.path.join(ROOT, "include", "chunk_dr.h")).read()
+    assert lib.cdr_version() == int(re.search(r"#define CDR_VERSION (\d+)", header).group(1))
+
+
+def test_problem_struct_matches_header():
+    """The ctypes mirror lists the C struct's fields in order."""
+    text = open(os.path.join(ROOT, "include", "chunk_dr.h")).read()
+    body = re.search(r"typedef struct \{(.*?)\} cdr_problem;", text, flags=re.S).group(1)
+    body = re.sub(r"/\*.*?\*/", "", body, flags=re.S)
+    fields = re.findall(r"(?:int32_t|float)\s+(\w+);", body)
+    assert fields == [f[0] for f in ops.cdr_problem._fields_]
+
+
+def test_value_heads_validation_and_workspace():
+    lib = cdr.load_library()
+    assert cdr.check(_p(H=2, HV=4)) == 0
+    assert cdr.check(_p(H=2, HV=3)) == 2      # not whole groups
+    assert cdr.check(_p(H=2, HV=-1)) == 2
+    assert cdr.check(_p(H=2, HV=0)) == 0      # 0 means HV = H
+    a = cdr.workspace_bytes(_p(H=2, HV=2))
+    b = cdr.workspace_bytes(_p(H=2, HV=4))
+    assert cdr.workspace_bytes(_p(H=2, HV=0)) == a and b > a
+    del lib
 
 
 def _p(**kw):

@@ -26,11 +26,12 @@ def note(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def run_gpu(inp, output_final_state=True, workspace=None):
+def run_gpu(inp, output_final_state=True, workspace=None, l2n=False):
     d = inp.to(DEV)
     o, S = cdr.chunk_dr_fwd(d.q, d.k, d.v, d.g, d.beta, initial_state=d.initial_state,
                             cu_seqlens=d.cu_seqlens, chunk_size=inp.chunk_size,
-                            output_final_state=output_final_state, workspace=workspace)
+                            output_final_state=output_final_state, workspace=workspace,
+                            use_qk_l2norm_in_kernel=l2n)
     torch.cuda.synchronize()
     return o, S
 
@@ -40,16 +41,17 @@ def ratio(x, ref, tol):
     return float(np.max(np.abs(x - ref) / (tol + tol * np.abs(ref)))) if ref.size else 0.0
 
 
-def check(inp, heads=None, label=""):
+def check(inp, heads=None, label="", l2n=False):
     """GPU vs oracle; `heads` restricts the oracle (and the comparison) to a head subset."""
-    note(f"[parity] {label} q{tuple(inp.q.shape)} C={inp.chunk_size}")
-    o, S = run_gpu(inp)
+    note(f"[parity] {label} q{tuple(inp.q.shape)} v{tuple(inp.v.shape)} C={inp.chunk_size} l2n={l2n}")
+    o, S = run_gpu(inp, l2n=l2n)
     assert torch.isfinite(o.float()).all() and torch.isfinite(S).all()
     sel = slice(None) if heads is None else heads
     sub = lambda t: None if t is None else t[:, :, sel].contiguous()  # noqa: E731
     s0 = None if inp.initial_state is None else inp.initial_state[:, sel].contiguous()
     o_ref, S_ref = oracle.recurrent_fwd(sub(inp.q), sub(inp.k), sub(inp.v), sub(inp.g),
-                                        sub(inp.beta), initial_state=s0, cu_seqlens=inp.cu_seqlens)
+                                        sub(inp.beta), initial_state=s0, cu_seqlens=inp.cu_seqlens,
+                                        use_qk_l2norm=l2n)
     ro = ratio(o[:, :, sel].float().cpu().numpy(), o_ref, O_TOL)
     rs = ratio(S[:, sel].cpu().numpy(), S_ref, S_TOL)
     note(f"[parity] {label}: o err/tol {ro:.3f}  S err/tol {rs:.3f}")
@@ -166,6 +168,35 @@ def test_staged_calls_equal_one_call(label, kw):
         call(st)
     torch.cuda.synchronize()
     assert torch.equal(o1, call.o) and torch.equal(S1, call.S)
+
+
+# ---------------------------------------------------------------- input variants
+VARIANTS = [
+    # label, B, T, H, HV, C, per_dim, lengths, normalise on the host, in-kernel l2 norm
+    ("kda_gva_C128_tail", 1, 300, 2, 4, 128, True, None, True, False),
+    ("gdn_gva_C64_varlen", 1, 400, 1, 3, 64, False, (150, 0, 250), True, False),
+    ("kda_l2n_C64", 2, 200, 2, None, 64, True, None, False, True),
+    ("kda_l2n_gva_C128_varlen", 1, 500, 2, 4, 128, True, (129, 371), False, True),
+    ("gdn_l2n_gva_C128", 1, 260, 2, 4, 128, False, None, False, True),
+]
+
+
+@pytest.mark.parametrize("case", VARIANTS, ids=[c[0] for c in VARIANTS])
+def test_input_variants(case):
+    label, B, T, H, HV, C, per_dim, lengths, normalise, l2n = case
+    inp = make_inputs(B, T, H, seed=21, per_dim_gate=per_dim, lengths=lengths, initial_state=True,
+                      chunk_size=C, normalise=normalise, HV=HV, gate_mean=1.0)
+    check(inp, label=label, l2n=l2n)
+
+
+def test_l2norm_switch_changes_the_output():
+    """As the page's feature-switch test asks: the normalised run differs from the plain
+    one by more than 1e-4 on unnormalised inputs."""
+    inp = make_inputs(1, 128, 2, seed=22, chunk_size=64, normalise=False)
+    note("[l2n switch]")
+    o1, _ = run_gpu(inp, l2n=True)
+    o2, _ = run_gpu(inp, l2n=False)
+    assert (o1.float() - o2.float()).abs().max().item() > 1e-4
 
 
 def test_no_final_state_requested():
