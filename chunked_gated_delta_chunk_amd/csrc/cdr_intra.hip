@@ -156,10 +156,10 @@ __device__ __forceinline__ void e_load(EIn& in, const uint16_t* __restrict__ k, 
 
 // One (chunk slot, head) item.  sc is the workgroup's scratch slot; ein holds the item's
 // phase E inputs on entry and those of next_item (-1: none) on exit.
-template <int C, bool PER_DIM>
+template <int C, bool PER_DIM, bool L2N>
 __device__ __forceinline__ void intra_item(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    const float* __restrict__ g, const float* __restrict__ beta, const ChunkMap& map, int H, int Hk, bool l2n,
+    const float* __restrict__ g, const float* __restrict__ beta, const ChunkMap& map, int H, int Hk,
     float scale, const Work& ws, unsigned char* smem, int slot, int h, size_t sc, EIn& ein, int next_item) {
     using S = IntraShape<C>;
     constexpr int NT = S::NT, NS = S::NS;
@@ -240,7 +240,7 @@ __device__ __forceinline__ void intra_item(
         float rnk[16];
 #pragma unroll
         for (int ii = 0; ii < 16; ++ii) rnk[ii] = 1.f;
-        if (l2n && act) {
+        if (L2N && act) {
 #pragma unroll
             for (int ii = 0; ii < 16; ++ii) {
                 const float a = __uint_as_float(kr[ii] << 16), b = __uint_as_float(kr[ii] & 0xffff0000u);
@@ -360,7 +360,7 @@ __device__ __forceinline__ void intra_item(
     // ------------------------------------------------------------------ phase AA2
     // L2 scales of the wave's own q and k rows: lanes r16 + 16 q4 (q4 = 0..3) share a row
     float rk2[2] = {1.f, 1.f}, rq2[2] = {1.f, 1.f};
-    if (l2n) {
+    if constexpr (L2N) {
 #pragma unroll
         for (int o = 0; o < 2; ++o) {
             float sk = 0.f, sq = 0.f;
@@ -475,7 +475,7 @@ __device__ __forceinline__ void intra_item(
             if constexpr (!PER_DIM) {
                 a *= (jj <= ii) ? ex(grow[ii] - grow[jj]) : 0.f;
                 a2 *= (j2 <= i2) ? ex(grow[i2] - grow[j2]) : 0.f;
-                if (l2n) {  // raw q, k products: apply the row scales afterwards
+                if constexpr (L2N) {  // raw q, k products: apply the row scales afterwards
                     a *= knr[ii] * knr[jj];
                     a2 *= rq * knr[j2];
                 }
@@ -697,10 +697,10 @@ __device__ __forceinline__ void intra_item(
 
 // Persistent: workgroup b takes items b, b + gridDim.x, ... (item = slot * H + head) and
 // keeps its scratch in slot b, so the scratch of all workgroups stays cache-resident.
-template <int C, bool PER_DIM>
+template <int C, bool PER_DIM, bool L2N>
 __global__ __launch_bounds__(ITHREADS) void intra_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    const float* __restrict__ g, const float* __restrict__ beta, ChunkMap map, int H, int Hk, int l2n,
+    const float* __restrict__ g, const float* __restrict__ beta, ChunkMap map, int H, int Hk,
     float scale, Work ws, int nitems) {
     __shared__ __attribute__((aligned(16))) unsigned char smem[IntraShape<C>::BYTES];
     EIn ein;
@@ -708,13 +708,13 @@ __global__ __launch_bounds__(ITHREADS) void intra_kernel(
     for (int item = blockIdx.x; item < nitems; item += gridDim.x) {
         __syncthreads();  // the previous item is done with LDS
         const int next = item + (int)gridDim.x < nitems ? item + (int)gridDim.x : -1;
-        intra_item<C, PER_DIM>(q, k, v, g, beta, map, H, Hk, l2n != 0, scale, ws, smem, item / H, item % H,
+        intra_item<C, PER_DIM, L2N>(q, k, v, g, beta, map, H, Hk, scale, ws, smem, item / H, item % H,
                                blockIdx.x, ein, next);
     }
 }
 
 // Workgroups of this kernel that the current device holds at once (cached per device).
-template <int C, bool PER_DIM>
+template <int C, bool PER_DIM, bool L2N>
 static int resident_groups() {
     static std::atomic<int> cache[64];
     int dev = 0;
@@ -725,32 +725,40 @@ static int resident_groups() {
     }
     int ncu = 0, per_cu = 0;
     if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, intra_kernel<C, PER_DIM>, ITHREADS, 0) != hipSuccess)
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, intra_kernel<C, PER_DIM, L2N>, ITHREADS, 0) != hipSuccess)
         return 1;
     const int r = max(1, ncu * per_cu);
     if (dev >= 0 && dev < 64) cache[dev].store(r, std::memory_order_relaxed);
     return r;
 }
 
-template <int C, bool PER_DIM>
+template <int C, bool PER_DIM, bool L2N>
 static hipError_t launch_intra_t(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float* g,
-                                 const float* beta, const ChunkMap& map, int nslots, int H, int Hk, int l2n,
+                                 const float* beta, const ChunkMap& map, int nslots, int H, int Hk,
                                  float scale, const Work& ws, int nscratch, hipStream_t stream) {
     const int nitems = nslots * H;
-    const int grid = min(min(nitems, nscratch), resident_groups<C, PER_DIM>());
-    hipLaunchKernelGGL((intra_kernel<C, PER_DIM>), dim3(grid), dim3(ITHREADS), 0, stream, q, k, v, g, beta, map, H,
-                       Hk, l2n, scale, ws, nitems);
+    const int grid = min(min(nitems, nscratch), resident_groups<C, PER_DIM, L2N>());
+    hipLaunchKernelGGL((intra_kernel<C, PER_DIM, L2N>), dim3(grid), dim3(ITHREADS), 0, stream, q, k, v, g, beta, map,
+                       H, Hk, scale, ws, nitems);
     return hipGetLastError();
+}
+
+template <int C, bool PER_DIM>
+static hipError_t launch_intra_n(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float* g,
+                                 const float* beta, const ChunkMap& map, int nslots, int H, int Hk, int l2n,
+                                 float scale, const Work& ws, int nscratch, hipStream_t stream) {
+    return l2n ? launch_intra_t<C, PER_DIM, true>(q, k, v, g, beta, map, nslots, H, Hk, scale, ws, nscratch, stream)
+               : launch_intra_t<C, PER_DIM, false>(q, k, v, g, beta, map, nslots, H, Hk, scale, ws, nscratch, stream);
 }
 
 hipError_t launch_intra(int C, bool per_dim, const uint16_t* q, const uint16_t* k, const uint16_t* v,
                         const float* g, const float* beta, const ChunkMap& map, int nslots, int H, int Hk,
                         int l2n, float scale, const Work& ws, int nscratch, hipStream_t stream) {
     if (C == 64)
-        return per_dim ? launch_intra_t<64, true>(q, k, v, g, beta, map, nslots, H, Hk, l2n, scale, ws, nscratch, stream)
-                       : launch_intra_t<64, false>(q, k, v, g, beta, map, nslots, H, Hk, l2n, scale, ws, nscratch, stream);
-    return per_dim ? launch_intra_t<128, true>(q, k, v, g, beta, map, nslots, H, Hk, l2n, scale, ws, nscratch, stream)
-                   : launch_intra_t<128, false>(q, k, v, g, beta, map, nslots, H, Hk, l2n, scale, ws, nscratch, stream);
+        return per_dim ? launch_intra_n<64, true>(q, k, v, g, beta, map, nslots, H, Hk, l2n, scale, ws, nscratch, stream)
+                       : launch_intra_n<64, false>(q, k, v, g, beta, map, nslots, H, Hk, l2n, scale, ws, nscratch, stream);
+    return per_dim ? launch_intra_n<128, true>(q, k, v, g, beta, map, nslots, H, Hk, l2n, scale, ws, nscratch, stream)
+                   : launch_intra_n<128, false>(q, k, v, g, beta, map, nslots, H, Hk, l2n, scale, ws, nscratch, stream);
 }
 
 }  // namespace cdr
