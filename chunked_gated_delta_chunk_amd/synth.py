@@ -151,3 +151,116 @@ def workload_inputs(w: Workload, seed: int, **overrides) -> Inputs:
               chunk_size=w.chunk_size)
     kw.update(overrides)
     return make_inputs(w.B, w.T, w.H, w.K, w.V, seed=seed, **kw)
+
+
+# --------------------------------------------------------------------------- decode
+
+@dataclass(frozen=True)
+class DecodeWorkload:
+    """One step of batched decoding against a pool of recurrent states.
+
+    N sequences of ``T`` tokens each (or ``lengths``, packed), H query/key heads and HV value
+    heads, a state pool of ``num_slots`` entries.  ``index_cols == 0``: one state slot per
+    sequence, read and written in place.  ``index_cols > 0``: speculative decoding, a row of
+    ``index_cols`` slots per sequence (one per draft position) and a count of accepted tokens
+    that selects the slot the step starts from.
+    """
+    name: str
+    N: int
+    T: int
+    H: int
+    HV: int
+    num_slots: int
+    index_cols: int = 0
+    K: int = 128
+    V: int = 128
+    per_dim_gate: bool = True
+    qk_l2norm: bool = True
+    lengths: Optional[Sequence[int]] = None
+    description: str = ""
+
+    @property
+    def tokens(self) -> int:
+        return int(sum(self.lengths)) if self.lengths is not None else self.N * self.T
+
+
+#: Decode workloads: one step of a serving batch with KDA's head shape (H = 16, K = V = 128),
+#: raw q/k normalised in the kernel, and a pool larger than the batch.
+DECODE_WORKLOADS = {
+    "kda_decode_b256": DecodeWorkload(
+        "kda_decode_b256", N=256, T=1, H=16, HV=16, num_slots=1024,
+        description="KDA decode, 256 sequences x 1 token, H=HV=16 K=V=128, pool of 1024 states"),
+    "kda_spec_decode_b64x4": DecodeWorkload(
+        "kda_spec_decode_b64x4", N=64, T=4, H=16, HV=16, num_slots=1024, index_cols=4,
+        description="KDA speculative decode, 64 sequences x 4 draft tokens, H=HV=16, pool of 1024"),
+}
+
+
+@dataclass
+class DecodeInputs:
+    q: torch.Tensor
+    k: torch.Tensor
+    v: torch.Tensor
+    g: torch.Tensor
+    beta: torch.Tensor
+    cu_seqlens: Optional[torch.Tensor]
+    state_pool: torch.Tensor
+    ssm_state_indices: torch.Tensor
+    num_accepted_tokens: Optional[torch.Tensor]
+
+    def to(self, device):
+        mv = lambda t: None if t is None else t.to(device)  # noqa: E731
+        return DecodeInputs(mv(self.q), mv(self.k), mv(self.v), mv(self.g), mv(self.beta),
+                            mv(self.cu_seqlens), mv(self.state_pool), mv(self.ssm_state_indices),
+                            mv(self.num_accepted_tokens))
+
+
+def make_decode_inputs(N: int, T: int, H: int, HV: int, num_slots: int, *, seed: int,
+                       index_cols: int = 0, K: int = 128, V: int = 128,
+                       per_dim_gate: bool = True, normalise: bool = False,
+                       lengths: Optional[Sequence[int]] = None, padded: Sequence[int] = (),
+                       state_std: float = 0.1, gate_mean: float = 0.0,
+                       beta_mode: str = "sigmoid", gate: str = "logsigmoid",
+                       accepted: Optional[Sequence[int]] = None) -> DecodeInputs:
+    """Draw one seeded decode step.
+
+    Token inputs come from :func:`make_inputs` (B = N rows of T tokens, or one packed row of
+    ``lengths``) with ``normalise`` applied on the host; a second generator seeded with
+    ``seed + 1`` then draws, in order, the pool (``state_std`` x N(0, 1), [num_slots, HV, V, K]),
+    a random choice of distinct slots, and the accepted-token counts (uniform in
+    1..index_cols) unless ``accepted`` fixes them.  Sequences listed in ``padded`` get slot
+    index -1 everywhere (padding entries).
+    """
+    if lengths is not None:
+        inp = make_inputs(1, int(sum(lengths)), H, K, V, seed=seed, per_dim_gate=per_dim_gate,
+                          lengths=lengths, normalise=normalise, HV=HV, gate_mean=gate_mean,
+                          beta_mode=beta_mode, gate=gate)
+        N = len(lengths)
+    else:
+        inp = make_inputs(N, T, H, K, V, seed=seed, per_dim_gate=per_dim_gate,
+                          normalise=normalise, HV=HV, gate_mean=gate_mean,
+                          beta_mode=beta_mode, gate=gate)
+    gen = torch.Generator("cpu").manual_seed(int(seed) + 1)
+    pool = torch.randn(num_slots, HV, V, K, generator=gen, dtype=torch.float32) * state_std
+    cols = max(index_cols, 1)
+    if N * cols > num_slots:
+        raise ValueError("the pool must hold a distinct slot for every index")
+    slots = torch.randperm(num_slots, generator=gen)[:N * cols].to(torch.int32).reshape(N, cols)
+    acc = None
+    if index_cols > 0:
+        acc = torch.randint(1, index_cols + 1, (N,), generator=gen, dtype=torch.int32)
+        if accepted is not None:
+            acc = torch.tensor(list(accepted), dtype=torch.int32)
+    else:
+        slots = slots[:, 0].contiguous()
+    for n in padded:
+        slots[n] = -1
+    return DecodeInputs(inp.q, inp.k, inp.v, inp.g, inp.beta, inp.cu_seqlens, pool.contiguous(),
+                        slots.contiguous(), acc)
+
+
+def decode_workload_inputs(w: DecodeWorkload, seed: int, **overrides) -> DecodeInputs:
+    kw = dict(index_cols=w.index_cols, K=w.K, V=w.V, per_dim_gate=w.per_dim_gate,
+              normalise=not w.qk_l2norm, lengths=w.lengths)
+    kw.update(overrides)
+    return make_decode_inputs(w.N, w.T, w.H, w.HV, w.num_slots, seed=seed, **kw)

@@ -14,6 +14,10 @@ Two independent fp64 formulations, both written from the page
 * :func:`chunked_fwd` -- the chunked algorithm of sections M1-M4 of the same
   page, in numpy (``chunked.py``).  It is used to cross-check the recurrent
   form and shares no code with it.
+* :func:`recurrent_pool_fwd` -- the decode-side use of the same recurrence
+  (section 与其他 KDA 算子的关系): start states gathered from a state pool by
+  slot index, results scattered back in place, with the per-position states
+  of speculative decoding (``decode.py``).
 
 Pins (tests/test_oracle.py) tie both to facts that do not come from either
 implementation: closed forms (beta = 0, g = beta = 0, a single token, one-hot
@@ -133,3 +137,6 @@ def recurrent_fwd(q, k, v, g, beta, scale=None, initial_state=None, cu_seqlens=N
     if rc != 0:
         raise ValueError(f"oracle_recurrent_fwd failed with code {rc}")
     return o, s
+
+
+from .decode import recurrent_pool_fwd  # noqa: E402,F401  (re-export; needs recurrent_fwd above)
