@@ -95,6 +95,64 @@ def load_traffic(kernel, workload):
     return rec.get("hbm_bytes")
 
 
+def decode_bytes(w):
+    """Compulsory HBM bytes of one decode call: every state read once and written once per
+    stored position (64 KiB each at K = V = 128), the token inputs (q, k per key head; v, g,
+    beta per value head), o, and the slot indices."""
+    state = w.V * w.K * 4
+    writes = 1 if w.index_cols == 0 else min(w.T, w.index_cols)
+    per_tok = (w.H * w.K * 2 * 2
+               + w.HV * (w.V * 2 + (w.K * 4 if w.per_dim_gate else 4) + 4 + w.V * 2))
+    idx = w.N * max(w.index_cols, 1) * 4 + (w.N * 4 if w.index_cols else 0)
+    return w.N * w.HV * state * (1 + writes) + w.tokens * per_tok + idx
+
+
+def bench_decode(name, steps, warmup):
+    """Time one decode workload: a call is one kernel over the batch, the pool updated in
+    place.  Slot sets are rotated (disjoint, up to 4) so that a call does not find the
+    states of the previous call in cache."""
+    import torch
+    import chunked_gated_delta_chunk_amd as cdr
+    from chunked_gated_delta_chunk_amd.synth import DECODE_WORKLOADS, decode_workload_inputs
+    w = DECODE_WORKLOADS[name]
+    dev = torch.device("cuda:0")
+    host = decode_workload_inputs(w, seed=2000 + list(DECODE_WORKLOADS).index(name))
+    d = host.to(dev)
+    per = w.N * max(w.index_cols, 1)
+    nsets = max(1, min(4, w.num_slots // per))
+    perm = torch.randperm(w.num_slots, generator=torch.Generator().manual_seed(7)).to(torch.int32)
+    calls = []
+    for i in range(nsets):
+        idx = perm[i * per:(i + 1) * per].reshape(d.ssm_state_indices.shape).contiguous().to(dev)
+        calls.append(cdr.PreparedRecurrent(d.q, d.k, d.v, d.g, d.beta, cu_seqlens=d.cu_seqlens,
+                                           use_qk_l2norm_in_kernel=w.qk_l2norm,
+                                           state_pool=d.state_pool, ssm_state_indices=idx,
+                                           num_accepted_tokens=d.num_accepted_tokens))
+    for i in range(warmup):
+        calls[i % nsets]()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    t0 = time.perf_counter()
+    ev[0].record()
+    for i in range(steps):
+        calls[i % nsets]()
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / steps
+    us = sum(ev[i].elapsed_time(ev[i + 1]) for i in range(steps)) / steps * 1e3
+    nbytes = decode_bytes(w)
+    gbs = nbytes / (us * 1e-6) / 1e9
+    return {"workload": name, "us_per_call": round(us, 2), "wall_us_per_call": round(wall * 1e6, 2),
+            "tokens_per_s": round(w.tokens / (us * 1e-6), 1),
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                         "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                         "traffic": load_traffic("decode", name), "kernel": "decode_kernel",
+                         "algorithmic_bytes": nbytes},
+            "config": {"N": w.N, "T": w.T, "H": w.H, "HV": w.HV, "K": w.K, "V": w.V,
+                       "num_slots": w.num_slots, "index_cols": w.index_cols,
+                       "qk_l2norm": w.qk_l2norm, "slot_sets_rotated": nsets}}
+
+
 def cpu_baseline(inp, w, budget_s):
     """Time the fp64 oracle on the host: all heads, a prefix of the tokens sized to the
     time budget (all tokens when it fits)."""
@@ -130,6 +188,9 @@ def main():
     ap.add_argument("--workload", default="kda_t8192")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=8.0, help="seconds of oracle wall time")
+    ap.add_argument("--no-decode", action="store_true", help="skip the decode workloads")
+    ap.add_argument("--decode-only", default=None, metavar="NAME",
+                    help="time only this decode workload and print its JSON line")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (reference for the "
                          "HBM byte counters) and exit")
@@ -150,9 +211,18 @@ def main():
               file=sys.stderr)
         sys.exit(2)
 
+    if args.decode_only:
+        r = bench_decode(args.decode_only, args.steps, args.warmup)
+        r.update({"metric": "decode tokens/s + % HBM peak", "unit": "tokens/s",
+                  "value": r["tokens_per_s"], "higher_is_better": True, "n_gpus": 1,
+                  "steps": args.steps, "warmup": args.warmup, "dtype": "f32",
+                  "data": "synthetic"})
+        print(json.dumps(r), flush=True)
+        return
+
     import torch
     import chunked_gated_delta_chunk_amd as cdr
-    from chunked_gated_delta_chunk_amd.synth import WORKLOADS, workload_inputs
+    from chunked_gated_delta_chunk_amd.synth import WORKLOADS, DECODE_WORKLOADS, workload_inputs
 
     w = WORKLOADS[args.workload]
     seed = 1000 + list(WORKLOADS).index(args.workload) + 1
@@ -242,6 +312,12 @@ def main():
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(host_sets[0], w, args.cpu_budget)
 
+    decode = None
+    if not args.no_decode:
+        del calls, host_sets
+        torch.cuda.empty_cache()
+        decode = {n: bench_decode(n, args.steps, args.warmup) for n in DECODE_WORKLOADS}
+
     line = {
         "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": K, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
@@ -258,6 +334,7 @@ def main():
         "roofline": roof,
         "cpu_baseline": cpu,
         "parity_spot_check": spot,
+        "decode": decode,
     }
     print(json.dumps(line), flush=True)
 

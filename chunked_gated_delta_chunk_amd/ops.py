@@ -21,7 +21,8 @@ GATE_PER_DIM = 0
 GATE_PER_HEAD = 1
 
 EXPORTED = ("cdr_check", "cdr_workspace_bytes", "chunk_dr_fwd", "chunk_dr_fwd_stages",
-            "cdr_status_str", "cdr_version")
+            "cdr_recurrent_check", "chunk_dr_recurrent_fwd", "cdr_status_str", "cdr_version")
+STATE_SEPARATE, STATE_POOL, STATE_POOL_SPEC = 0, 1, 2
 STAGE_INTRA, STAGE_CHAIN, STAGE_OUTPUT, STAGE_ALL = 1, 2, 4, 7
 
 
@@ -32,6 +33,16 @@ class cdr_problem(ctypes.Structure):
                 ("scale", ctypes.c_float), ("has_initial_state", ctypes.c_int32),
                 ("output_final_state", ctypes.c_int32), ("varlen", ctypes.c_int32),
                 ("HV", ctypes.c_int32), ("qk_l2norm", ctypes.c_int32)]
+
+
+class cdr_recurrent_problem(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("T", ctypes.c_int32), ("H", ctypes.c_int32),
+                ("HV", ctypes.c_int32), ("K", ctypes.c_int32), ("V", ctypes.c_int32),
+                ("N", ctypes.c_int32), ("gate", ctypes.c_int32), ("scale", ctypes.c_float),
+                ("varlen", ctypes.c_int32), ("qk_l2norm", ctypes.c_int32),
+                ("state_mode", ctypes.c_int32), ("has_initial_state", ctypes.c_int32),
+                ("output_final_state", ctypes.c_int32), ("num_slots", ctypes.c_int32),
+                ("index_cols", ctypes.c_int32)]
 
 
 _lib = None
@@ -57,6 +68,11 @@ def load_library(path: str = LIB_PATH):
     lib.chunk_dr_fwd_stages.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t,
                                         ctypes.c_int32, vp]
     lib.chunk_dr_fwd_stages.restype = ctypes.c_int
+    R = ctypes.POINTER(cdr_recurrent_problem)
+    lib.cdr_recurrent_check.argtypes = [R]
+    lib.cdr_recurrent_check.restype = ctypes.c_int
+    lib.chunk_dr_recurrent_fwd.argtypes = [R] + [vp] * 13
+    lib.chunk_dr_recurrent_fwd.restype = ctypes.c_int
     lib.cdr_status_str.argtypes = [ctypes.c_int]
     lib.cdr_status_str.restype = ctypes.c_char_p
     lib.cdr_version.argtypes = []
@@ -228,3 +244,153 @@ def chunk_dr_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Ten
                            final_state_out=final_state_out,
                            use_qk_l2norm_in_kernel=use_qk_l2norm_in_kernel)
     return call(stages)
+
+
+class PreparedRecurrent:
+    """A validated call of the per-token forward whose arguments are marshalled once.
+
+    Takes the arguments of :func:`fused_recurrent_fwd`; each call queues the kernel on the
+    current stream with a single ctypes call and returns ``(o, S)``.  In the pool modes every
+    call updates the pool in place again.
+    """
+
+    def __init__(self, q, k, v, g, beta, scale=None, initial_state=None, output_final_state=False,
+                 cu_seqlens=None, use_qk_l2norm_in_kernel=False, state_pool=None,
+                 ssm_state_indices=None, num_accepted_tokens=None, out=None, final_state_out=None):
+        lib = load_library()
+        _need(q, "q", torch.bfloat16)
+        if q.dim() != 4:
+            raise ValueError("q must be [B, T, H, K]")
+        B, T, H, K = q.shape
+        _need(k, "k", torch.bfloat16, (B, T, H, K))
+        if v.dim() != 4 or tuple(v.shape[:2]) != (B, T) or v.shape[2] % H:
+            raise ValueError("v must be [B, T, HV, V] with HV a multiple of the q/k heads")
+        _need(v, "v", torch.bfloat16)
+        HV, V = v.shape[2], v.shape[3]
+        _need(g, "g", torch.float32)
+        if tuple(g.shape) == (B, T, HV, K):
+            per_dim = True
+        elif tuple(g.shape) == (B, T, HV):
+            per_dim = False
+        else:
+            raise ValueError(f"g must be [B,T,HV,K] or [B,T,HV], got {tuple(g.shape)}")
+        _need(beta, "beta", torch.float32, (B, T, HV))
+        if cu_seqlens is not None:
+            _need(cu_seqlens, "cu_seqlens", torch.int32)
+            if cu_seqlens.dim() != 1 or cu_seqlens.numel() < 2:
+                raise ValueError("cu_seqlens must be a 1-D tensor of N + 1 offsets")
+            N = cu_seqlens.numel() - 1
+        else:
+            N = B
+        if scale is None:
+            scale = K ** -0.5
+        num_slots, cols = 0, 0
+        if state_pool is not None:
+            if initial_state is not None or output_final_state:
+                raise ValueError("state_pool replaces initial_state and output_final_state")
+            _need(state_pool, "state_pool", torch.float32)
+            if state_pool.dim() != 4 or tuple(state_pool.shape[1:]) != (HV, V, K):
+                raise ValueError(f"state_pool must be [P, {HV}, {V}, {K}]")
+            if not state_pool.is_contiguous():
+                raise ValueError("state_pool must be contiguous (it is updated in place)")
+            if ssm_state_indices is None:
+                raise ValueError("state_pool needs ssm_state_indices")
+            _need(ssm_state_indices, "ssm_state_indices", torch.int32)
+            num_slots = state_pool.shape[0]
+            if ssm_state_indices.dim() == 1 and ssm_state_indices.shape[0] == N:
+                mode = STATE_POOL
+                if num_accepted_tokens is not None:
+                    raise ValueError("num_accepted_tokens needs ssm_state_indices of shape [N, L]")
+            elif ssm_state_indices.dim() == 2 and ssm_state_indices.shape[0] == N:
+                mode = STATE_POOL_SPEC
+                cols = ssm_state_indices.shape[1]
+                if num_accepted_tokens is not None:
+                    _need(num_accepted_tokens, "num_accepted_tokens", torch.int32, (N,))
+            else:
+                raise ValueError(f"ssm_state_indices must be [N] or [N, L] with N = {N}")
+        else:
+            mode = STATE_SEPARATE
+            if ssm_state_indices is not None or num_accepted_tokens is not None:
+                raise ValueError("ssm_state_indices and num_accepted_tokens need a state_pool")
+            if initial_state is not None:
+                _need(initial_state, "initial_state", torch.float32, (N, HV, V, K))
+        self.problem = cdr_recurrent_problem(
+            int(B), int(T), int(H), int(HV), int(K), int(V), int(N),
+            GATE_PER_DIM if per_dim else GATE_PER_HEAD, float(scale), int(cu_seqlens is not None),
+            int(bool(use_qk_l2norm_in_kernel)), mode, int(initial_state is not None),
+            int(bool(output_final_state)), int(num_slots), int(cols))
+        st = lib.cdr_recurrent_check(ctypes.byref(self.problem))
+        if st != CDR_OK:
+            _raise(st, "fused_recurrent_fwd")
+        device = q.device
+        if device.type != "cuda":
+            raise ValueError("inputs must be on a GPU device")
+        self.device = device
+        # keep references: the kernel reads these buffers when it runs
+        self.inputs = tuple(t.contiguous() for t in (q, k, v, g, beta))
+        self.s0 = initial_state.contiguous() if initial_state is not None else None
+        self.cu = cu_seqlens.contiguous() if cu_seqlens is not None else None
+        self.idx = ssm_state_indices.contiguous() if ssm_state_indices is not None else None
+        self.acc = num_accepted_tokens.contiguous() if num_accepted_tokens is not None else None
+        self.pool = state_pool
+        if out is None:
+            out = torch.empty((B, T, HV, V), dtype=torch.bfloat16, device=device)
+        else:
+            _need(out, "out", torch.bfloat16, (B, T, HV, V))
+        self.o = out
+        self.S = None
+        if mode == STATE_SEPARATE and output_final_state:
+            if final_state_out is None:
+                final_state_out = torch.empty((N, HV, V, K), dtype=torch.float32, device=device)
+            else:
+                _need(final_state_out, "final_state_out", torch.float32, (N, HV, V, K))
+            self.S = final_state_out
+        ptr = lambda t: None if t is None else _dev_ptr(t, device)  # noqa: E731
+        qq, kk, vv, gg, bb = self.inputs
+        self._args = (ctypes.byref(self.problem), ptr(qq), ptr(kk), ptr(vv), ptr(gg), ptr(bb),
+                      ptr(self.cu), ptr(self.s0), ptr(self.S), ptr(self.pool), ptr(self.idx),
+                      ptr(self.acc), ptr(self.o))
+        self._lib = lib
+
+    def __call__(self):
+        stream = torch.cuda.current_stream(self.device).cuda_stream
+        st = self._lib.chunk_dr_recurrent_fwd(*self._args, stream)
+        if st != CDR_OK:
+            _raise(st, "fused_recurrent_fwd")
+        return self.o, self.S
+
+
+def fused_recurrent_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
+                        beta: torch.Tensor, scale: Optional[float] = None,
+                        initial_state: Optional[torch.Tensor] = None,
+                        output_final_state: bool = False,
+                        cu_seqlens: Optional[torch.Tensor] = None,
+                        use_qk_l2norm_in_kernel: bool = False,
+                        state_pool: Optional[torch.Tensor] = None,
+                        ssm_state_indices: Optional[torch.Tensor] = None,
+                        num_accepted_tokens: Optional[torch.Tensor] = None,
+                        out: Optional[torch.Tensor] = None,
+                        final_state_out: Optional[torch.Tensor] = None,
+                        ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Per-token gated delta-rule forward on the GPU (the decode path).
+
+    q, k, v, g, beta, scale, cu_seqlens and use_qk_l2norm_in_kernel as :func:`chunk_dr_fwd`.
+
+    Without ``state_pool`` the states are separate, as in chunk_dr_fwd: initial_state
+    ``[N,HV,V,K]`` fp32 or None (zeros), and the final state is returned when
+    output_final_state (``final_state_out`` may be ``initial_state`` itself).
+
+    With ``state_pool`` ``[P,HV,V,K]`` fp32 the states are updated in place in the pool:
+    ``ssm_state_indices`` int32 ``[N]`` gives each sequence's slot (read, then written back);
+    ``[N,L]`` gives one slot per draft position (speculative decoding), the sequence starting
+    from slot ``idx[n, num_accepted_tokens[n] - 1]`` (``num_accepted_tokens`` int32 ``[N]`` or
+    None for 1) and writing its state after token t to ``idx[n, t]``.  Slot indices outside
+    ``[0, P)`` mark padding (see chunk_dr.h).  Returns ``(o, S)``: S is the final state in the
+    separate mode with output_final_state, else None (the pool holds the results).
+    """
+    return PreparedRecurrent(q, k, v, g, beta, scale=scale, initial_state=initial_state,
+                             output_final_state=output_final_state, cu_seqlens=cu_seqlens,
+                             use_qk_l2norm_in_kernel=use_qk_l2norm_in_kernel,
+                             state_pool=state_pool, ssm_state_indices=ssm_state_indices,
+                             num_accepted_tokens=num_accepted_tokens, out=out,
+                             final_state_out=final_state_out)()

@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define CDR_VERSION 2
+#define CDR_VERSION 3
 
 typedef enum {
     CDR_OK = 0,
@@ -157,6 +157,90 @@ cdr_status chunk_dr_fwd_stages(const cdr_problem* p,
                                void* o, float* final_state,
                                void* workspace, size_t workspace_bytes,
                                int32_t stages, void* stream);
+
+/* ------------------------------------------------------------------------------------------
+ * Per-token (recurrent) forward: the decode path.
+ *
+ * The decode-side companion of the chunked operator (page "PyPTO-Gym 的 chunk_kda 算子实战",
+ * section 与其他 KDA 算子的关系): the same update rule as above, applied token by token to an
+ * fp32 [HV, V, K] state per sequence, which may be kept in place in a pool of states addressed
+ * by slot indices (ssm_state_indices) and may keep one state per draft token for speculative
+ * decoding (num_accepted_tokens).  The page names these arguments without defining them; the
+ * reading implemented here:
+ *
+ *  CDR_STATE_SEPARATE  initial_state [N, HV, V, K] (or zeros) in, final_state [N, HV, V, K]
+ *                      out, exactly as chunk_dr_fwd.  initial_state and final_state may be the
+ *                      same buffer (the update is then in place).
+ *  CDR_STATE_POOL      state_pool [num_slots, HV, V, K] fp32, read and written in place;
+ *                      ssm_state_indices int32 [N]: sequence n starts from slot idx[n] and its
+ *                      state after its last token is written back to slot idx[n].
+ *  CDR_STATE_POOL_SPEC ssm_state_indices int32 [N, index_cols]: draft position t of sequence n
+ *                      owns slot idx[n, t].  The sequence starts from slot idx[n, a_n - 1], with
+ *                      a_n = num_accepted_tokens[n] (int32 [N]; NULL means a_n = 1), and its
+ *                      state after its own token t is written to slot idx[n, t] for every
+ *                      t < index_cols (later positions have no slot and are not stored).
+ *
+ * In both pool modes a slot index outside [0, num_slots) marks padding: a start index outside
+ * it (or a_n outside 1..index_cols) makes the sequence a padding entry, whose o rows are set to
+ * zero and which reads and writes no state; a write index outside it skips that one write.
+ * Indices are read on the device and never cause an access outside the pool.  Every start
+ * state is read before any state of the same sequence is written, so a sequence may write the
+ * slot it starts from; two sequences writing the same slot, or one writing a slot that another
+ * starts from, give an undefined result.
+ *
+ * No workspace: the kernels keep each state row in registers for the whole sequence.
+ * ------------------------------------------------------------------------------------------ */
+typedef enum {
+    CDR_STATE_SEPARATE = 0,
+    CDR_STATE_POOL = 1,
+    CDR_STATE_POOL_SPEC = 2
+} cdr_state_mode;
+
+typedef struct {
+    int32_t B;                  /* batch rows; must be 1 when varlen != 0 */
+    int32_t T;                  /* tokens per batch row (total packed tokens when varlen) */
+    int32_t H;                  /* query/key heads */
+    int32_t HV;                 /* value heads, a multiple of H; 0 means H */
+    int32_t K;                  /* must be 128 */
+    int32_t V;                  /* must be 128 */
+    int32_t N;                  /* sequences: B when varlen == 0, else len(cu_seqlens) - 1 */
+    int32_t gate;               /* cdr_gate */
+    float scale;                /* multiplies q */
+    int32_t varlen;             /* cu_seqlens is read when non-zero */
+    int32_t qk_l2norm;          /* normalise q and k per token inside the kernel, as chunk_dr_fwd */
+    int32_t state_mode;         /* cdr_state_mode */
+    int32_t has_initial_state;  /* CDR_STATE_SEPARATE: initial_state is read, else zeros */
+    int32_t output_final_state; /* CDR_STATE_SEPARATE: final_state is written */
+    int32_t num_slots;          /* pool modes: entries of state_pool (> 0) */
+    int32_t index_cols;         /* CDR_STATE_POOL_SPEC: columns of ssm_state_indices (> 0) */
+} cdr_recurrent_problem;
+
+/* Host-only validation of a recurrent problem description. */
+cdr_status cdr_recurrent_check(const cdr_recurrent_problem* p);
+
+/*
+ * Per-token forward.
+ *
+ *   q, k, v, g, beta, cu_seqlens, o   as chunk_dr_fwd (device pointers, same layouts)
+ *   initial_state, final_state        CDR_STATE_SEPARATE only (NULL allowed when the matching
+ *                                     flag is 0); ignored in the pool modes
+ *   state_pool                        pool modes: fp32 [num_slots, HV, V, K], updated in place
+ *   ssm_state_indices                 pool modes: int32 [N] (CDR_STATE_POOL) or
+ *                                     [N, index_cols] (CDR_STATE_POOL_SPEC), device
+ *   num_accepted_tokens               CDR_STATE_POOL_SPEC: int32 [N], device, or NULL
+ *   stream                            hipStream_t (NULL = default stream)
+ *
+ * One kernel is queued; nothing is allocated, copied to the host or synchronised.  Repeated
+ * calls on the same inputs give bit-identical results.  Returns CDR_OK after queueing, or an
+ * error status without launching anything (CDR_ERR_HIP if the launch failed).
+ */
+cdr_status chunk_dr_recurrent_fwd(const cdr_recurrent_problem* p,
+                                  const void* q, const void* k, const void* v,
+                                  const float* g, const float* beta, const int32_t* cu_seqlens,
+                                  const float* initial_state, float* final_state,
+                                  float* state_pool, const int32_t* ssm_state_indices,
+                                  const int32_t* num_accepted_tokens,
+                                  void* o, void* stream);
 
 /* Human-readable name of a status code (static storage). */
 const char* cdr_status_str(cdr_status s);

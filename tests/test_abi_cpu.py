@@ -33,7 +33,7 @@ def test_library_exports_every_declared_function():
 def test_problem_struct_matches_header():
     """The ctypes mirror lists the C struct's fields in order."""
     text = open(os.path.join(ROOT, "include", "chunk_dr.h")).read()
-    body = re.search(r"typedef struct \{(.*?)\} cdr_problem;", text, flags=re.S).group(1)
+    body = re.search(r"typedef struct \{([^{}]*)\} cdr_problem;", text).group(1)
     body = re.sub(r"/\*.*?\*/", "", body, flags=re.S)
     fields = re.findall(r"(?:int32_t|float)\s+(\w+);", body)
     assert fields == [f[0] for f in ops.cdr_problem._fields_]
@@ -126,3 +126,80 @@ def test_no_cpu_fallback_when_library_missing(monkeypatch, tmp_path):
     monkeypatch.setattr(ops, "_lib", None)
     with pytest.raises(RuntimeError, match="missing"):
         ops.load_library(str(tmp_path / "absent.so"))
+
+
+# ---------------------------------------------------------------------- recurrent entry point
+
+def test_recurrent_struct_matches_header():
+    text = open(os.path.join(ROOT, "include", "chunk_dr.h")).read()
+    body = re.search(r"typedef struct \{([^{}]*)\} cdr_recurrent_problem;", text).group(1)
+    body = re.sub(r"/\*.*?\*/", "", body, flags=re.S)
+    fields = re.findall(r"(?:int32_t|float)\s+(\w+);", body)
+    assert fields == [f[0] for f in ops.cdr_recurrent_problem._fields_]
+
+
+def _rp(**kw):
+    base = dict(B=2, T=1, H=2, HV=4, K=128, V=128, N=2, gate=0, scale=0.1, varlen=0,
+                qk_l2norm=1, state_mode=ops.STATE_POOL, has_initial_state=0,
+                output_final_state=0, num_slots=8, index_cols=0)
+    base.update(kw)
+    return ops.cdr_recurrent_problem(**base)
+
+
+@pytest.mark.parametrize("kw,status", [
+    ({}, 0),
+    (dict(state_mode=ops.STATE_SEPARATE, num_slots=0), 0),
+    (dict(state_mode=ops.STATE_POOL_SPEC, index_cols=4), 0),
+    (dict(state_mode=ops.STATE_POOL_SPEC, index_cols=0), 2),   # speculative rows need columns
+    (dict(num_slots=0), 2),                                      # a pool needs slots
+    (dict(HV=3), 2),                                             # whole groups of value heads
+    (dict(K=64), 3),
+    (dict(gate=2), 3),
+    (dict(state_mode=7), 3),
+    (dict(varlen=1), 4),                                         # varlen needs B == 1
+    (dict(N=3), 2),                                              # fixed length: N == B
+    (dict(B=1, N=3, varlen=1, T=5), 0),
+    (dict(T=-1), 2),
+])
+def test_recurrent_check_status(kw, status):
+    lib = cdr.load_library()
+    assert lib.cdr_recurrent_check(ctypes.byref(_rp(**kw))) == status
+
+
+def test_recurrent_rejects_missing_pointers_without_touching_device():
+    lib = cdr.load_library()
+    p = _rp()
+    fake = 1 << 20
+    args = [fake] * 5 + [None, None, None, None, None, None, fake, None]
+    assert lib.chunk_dr_recurrent_fwd(ctypes.byref(p), *args) == 1   # no pool, no indices
+    p = _rp(state_mode=ops.STATE_SEPARATE, has_initial_state=1)
+    args = [fake] * 5 + [None] * 7 + [fake, None]
+    assert lib.chunk_dr_recurrent_fwd(ctypes.byref(p), *args) == 1   # initial_state missing
+    p = _rp(K=64)
+    assert lib.chunk_dr_recurrent_fwd(ctypes.byref(p), *([None] * 13)) == 3
+
+
+def test_recurrent_binding_errors():
+    B, T, H, K = 2, 1, 2, 128
+    q = torch.zeros(B, T, H, K, dtype=torch.bfloat16)
+    v = torch.zeros(B, T, 4, K, dtype=torch.bfloat16)
+    g = torch.zeros(B, T, 4, K)
+    beta = torch.zeros(B, T, 4)
+    pool = torch.zeros(8, 4, K, K)
+    idx = torch.zeros(B, dtype=torch.int32)
+    with pytest.raises(ValueError):  # indices without a pool
+        cdr.fused_recurrent_fwd(q, q, v, g, beta, ssm_state_indices=idx)
+    with pytest.raises(ValueError):  # a pool without indices
+        cdr.fused_recurrent_fwd(q, q, v, g, beta, state_pool=pool)
+    with pytest.raises(ValueError):  # pool with the wrong head count
+        cdr.fused_recurrent_fwd(q, q, v, g, beta, state_pool=pool[:, :2], ssm_state_indices=idx)
+    with pytest.raises(TypeError):   # indices must be int32
+        cdr.fused_recurrent_fwd(q, q, v, g, beta, state_pool=pool, ssm_state_indices=idx.long())
+    with pytest.raises(ValueError):  # accepted counts need [N, L] indices
+        cdr.fused_recurrent_fwd(q, q, v, g, beta, state_pool=pool, ssm_state_indices=idx,
+                                num_accepted_tokens=idx)
+    with pytest.raises(ValueError):  # the pool replaces initial/final state
+        cdr.fused_recurrent_fwd(q, q, v, g, beta, state_pool=pool, ssm_state_indices=idx,
+                                output_final_state=True)
+    with pytest.raises(ValueError):  # host tensors: no CPU path exists
+        cdr.fused_recurrent_fwd(q, q, v, g, beta, state_pool=pool, ssm_state_indices=idx)
