@@ -10,10 +10,12 @@
 //     s <- s + k * beta (v_v - s . k)
 //     o_v = scale * (s . q)
 // so the state's rows are independent and a workgroup owns 32 of them for the whole
-// sequence, in registers.  Eight lanes share a row (16 columns each, as four 16-byte pieces
-// 32 columns apart, so that every load and store instruction covers whole 128-byte lines),
-// and the two dot products per token are 3-step butterflies across those eight lanes.  The
-// kernel is bound by streaming the state (64 KiB in and out per sequence and head).
+// sequence, in registers.  Eight lanes share a row group of two rows (16 columns each, as
+// four 16-byte pieces 32 columns apart, so that every load and store instruction covers whole
+// 128-byte lines), and the dot products per token are 3-step butterflies across those eight
+// lanes.  The kernel is bound by streaming the state (64 KiB in and 64 KiB out per sequence and
+// head, plus 64 KiB per stored draft position); state traffic uses non-temporal loads and
+// stores, since nothing reads a state twice within a call.
 #include "chunk_dr.h"
 #include "cdr_common.h"
 
@@ -22,7 +24,8 @@ namespace cdr {
 namespace {
 
 constexpr int DROWS = 32;                 // state rows per workgroup
-constexpr int DTHREADS = DROWS * 8;       // eight lanes per row
+constexpr int DRPL = 2;                   // rows per group of eight lanes
+constexpr int DTHREADS = DROWS / DRPL * 8;
 constexpr int DBLOCKS = VD / DROWS;       // workgroups per (sequence, value head)
 constexpr float DEC_L2N_EPS = 1e-6f;      // x / sqrt(|x|^2 + eps)
 
@@ -44,14 +47,15 @@ struct DecodeArgs {
     float scale;
 };
 
+// one token's inputs for a lane: its 16 columns of q, k (bf16) and g, beta, v of its rows
 struct TokIn {
     uint2 q[4], k[4];
     float4 g[4];
-    float b, v;
+    float b, v[DRPL];
 };
 
 template <bool PER_DIM>
-__device__ __forceinline__ void tok_load(TokIn& in, const DecodeArgs& a, int64_t tok, int hv, int hk, int row,
+__device__ __forceinline__ void tok_load(TokIn& in, const DecodeArgs& a, int64_t tok, int hv, int hk, int row0,
                                          int c0) {
     const size_t qk = ((size_t)tok * a.H + hk) * KD + c0;
     const size_t vh = (size_t)tok * a.HV + hv;
@@ -63,7 +67,8 @@ __device__ __forceinline__ void tok_load(TokIn& in, const DecodeArgs& a, int64_t
     }
     if constexpr (!PER_DIM) in.g[0].x = a.g[vh];
     in.b = a.beta[vh];
-    in.v = bf2f(a.v[vh * VD + row]);
+#pragma unroll
+    for (int r = 0; r < DRPL; ++r) in.v[r] = bf2f(a.v[vh * VD + row0 + r]);
 }
 
 __device__ __forceinline__ void unpack4(const uint2& p, float* f) {
@@ -73,7 +78,7 @@ __device__ __forceinline__ void unpack4(const uint2& p, float* f) {
     f[3] = __uint_as_float(p.y & 0xffff0000u);
 }
 
-// sum over the eight lanes of a row (lanes 8r .. 8r+7 of the wave)
+// sum over the eight lanes of a row group (lanes 8r .. 8r+7 of the wave)
 __device__ __forceinline__ float row_sum(float x) {
     x += __shfl_xor(x, 1, 64);
     x += __shfl_xor(x, 2, 64);
@@ -81,14 +86,26 @@ __device__ __forceinline__ float row_sum(float x) {
     return x;
 }
 
-__device__ __forceinline__ void load_rows(float4* s, const float* base) {
+typedef float f32x4v __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ void load_rows(float4 (&s)[DRPL][4], const float* base) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) s[i] = *reinterpret_cast<const float4*>(base + 32 * i);
+    for (int r = 0; r < DRPL; ++r)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const f32x4v x = __builtin_nontemporal_load(reinterpret_cast<const f32x4v*>(base + r * KD + 32 * i));
+            s[r][i] = make_float4(x.x, x.y, x.z, x.w);
+        }
 }
 
-__device__ __forceinline__ void store_rows(float* base, const float4* s) {
+__device__ __forceinline__ void store_rows(float* base, const float4 (&s)[DRPL][4]) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) *reinterpret_cast<float4*>(base + 32 * i) = s[i];
+    for (int r = 0; r < DRPL; ++r)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const f32x4v x = {s[r][i].x, s[r][i].y, s[r][i].z, s[r][i].w};
+            __builtin_nontemporal_store(x, reinterpret_cast<f32x4v*>(base + r * KD + 32 * i));
+        }
 }
 
 template <bool PER_DIM, bool L2N>
@@ -98,7 +115,7 @@ __global__ __launch_bounds__(DTHREADS) void decode_kernel(DecodeArgs a) {
     const int hv = (blk / DBLOCKS) % a.HV;
     const int n = blk / (DBLOCKS * a.HV);
     const int tid = threadIdx.x;
-    const int row = DROWS * rb + (tid >> 3);
+    const int row0 = DROWS * rb + DRPL * (tid >> 3);
     const int c0 = 4 * (tid & 7);
     const int hk = hv / (a.HV / a.H);
 
@@ -112,7 +129,7 @@ __global__ __launch_bounds__(DTHREADS) void decode_kernel(DecodeArgs a) {
         len = a.T;
     }
     const size_t state = (size_t)VD * KD;
-    const size_t in_row = (size_t)row * KD + c0;
+    const size_t in_row = (size_t)row0 * KD + c0;
 
     // start state
     int slot = -1;
@@ -126,73 +143,105 @@ __global__ __launch_bounds__(DTHREADS) void decode_kernel(DecodeArgs a) {
         if (slot < 0 || slot >= a.num_slots) {
             // padding entry: zero outputs, no state touched
             if ((tid & 7) == 0)
-                for (int t = 0; t < len; ++t) a.o[((size_t)(bos + t) * a.HV + hv) * VD + row] = 0;
+                for (int t = 0; t < len; ++t)
+#pragma unroll
+                    for (int r = 0; r < DRPL; ++r) a.o[((size_t)(bos + t) * a.HV + hv) * VD + row0 + r] = 0;
             return;
         }
     }
-    float4 s[4];
+    float4 s[DRPL][4];
     if (a.pool) {
         load_rows(s, a.s_in + ((size_t)slot * a.HV + hv) * state + in_row);
     } else if (a.s_in) {
         load_rows(s, a.s_in + ((size_t)n * a.HV + hv) * state + in_row);
     } else {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) s[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int r = 0; r < DRPL; ++r)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) s[r][i] = make_float4(0.f, 0.f, 0.f, 0.f);
     }
 
-    TokIn cur;
-    if (len > 0) tok_load<PER_DIM>(cur, a, bos, hv, hk, row, c0);
     for (int t = 0; t < len; ++t) {
-        TokIn nxt;
-        if (t + 1 < len) tok_load<PER_DIM>(nxt, a, bos + t + 1, hv, hk, row, c0);
-        float qf[16], kf[16];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            unpack4(cur.q[i], qf + 4 * i);
-            unpack4(cur.k[i], kf + 4 * i);
-        }
+        const int64_t tok = bos + t;
+        TokIn in;
+        tok_load<PER_DIM>(in, a, tok, hv, hk, row0, c0);
+        // q and k enter through their L2 scales: s.k = rk (s.k_raw), s.q = rq (s.q_raw)
+        float rq = 1.f, rk = 1.f;
         if constexpr (L2N) {
             float sq = 0.f, sk = 0.f;
 #pragma unroll
-            for (int j = 0; j < 16; ++j) {
-                sq += qf[j] * qf[j];
-                sk += kf[j] * kf[j];
+            for (int i = 0; i < 4; ++i) {
+                float qf[4], kf[4];
+                unpack4(in.q[i], qf);
+                unpack4(in.k[i], kf);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    sq += qf[e] * qf[e];
+                    sk += kf[e] * kf[e];
+                }
             }
-            const float rq = rsqrtf(row_sum(sq) + DEC_L2N_EPS), rk = rsqrtf(row_sum(sk) + DEC_L2N_EPS);
+            rq = rsqrtf(row_sum(sq) + DEC_L2N_EPS);
+            rk = rsqrtf(row_sum(sk) + DEC_L2N_EPS);
+        }
+        // decay, then the read s . k on the decayed state
+        float dot[DRPL];
 #pragma unroll
-            for (int j = 0; j < 16; ++j) {
-                qf[j] *= rq;
-                kf[j] *= rk;
+        for (int r = 0; r < DRPL; ++r) dot[r] = 0.f;
+        const float dh = PER_DIM ? 0.f : ex(in.g[0].x);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            float kf[4];
+            unpack4(in.k[i], kf);
+            float d[4];
+            if constexpr (PER_DIM) {
+                d[0] = ex(in.g[i].x);
+                d[1] = ex(in.g[i].y);
+                d[2] = ex(in.g[i].z);
+                d[3] = ex(in.g[i].w);
+            } else {
+                d[0] = d[1] = d[2] = d[3] = dh;
+            }
+#pragma unroll
+            for (int r = 0; r < DRPL; ++r) {
+                float* x = reinterpret_cast<float*>(&s[r][i]);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    x[e] *= d[e];
+                    dot[r] += x[e] * kf[e];
+                }
             }
         }
-        float* sf = reinterpret_cast<float*>(s);
-        if constexpr (PER_DIM) {
-            const float* gf = reinterpret_cast<const float*>(cur.g);
+        // s += k beta (v - s . k), then o = scale s . q
+        float u[DRPL], so[DRPL];
 #pragma unroll
-            for (int j = 0; j < 16; ++j) sf[j] *= ex(gf[j]);
-        } else {
-            const float d = ex(cur.g[0].x);
-#pragma unroll
-            for (int j = 0; j < 16; ++j) sf[j] *= d;
+        for (int r = 0; r < DRPL; ++r) {
+            u[r] = in.b * (in.v[r] - rk * row_sum(dot[r])) * rk;
+            so[r] = 0.f;
         }
-        float sk = 0.f;
 #pragma unroll
-        for (int j = 0; j < 16; ++j) sk += sf[j] * kf[j];
-        const float u = cur.b * (cur.v - row_sum(sk));
-        float so = 0.f;
+        for (int i = 0; i < 4; ++i) {
+            float qf[4], kf[4];
+            unpack4(in.q[i], qf);
+            unpack4(in.k[i], kf);
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-            sf[j] += kf[j] * u;
-            so += sf[j] * qf[j];
+            for (int r = 0; r < DRPL; ++r) {
+                float* x = reinterpret_cast<float*>(&s[r][i]);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    x[e] += kf[e] * u[r];
+                    so[r] += x[e] * qf[e];
+                }
+            }
         }
-        so = row_sum(so);
-        const int64_t tok = bos + t;
-        if ((tid & 7) == 0) a.o[((size_t)tok * a.HV + hv) * VD + row] = f2bf(a.scale * so);
+#pragma unroll
+        for (int r = 0; r < DRPL; ++r) {
+            const float ov = a.scale * rq * row_sum(so[r]);
+            if ((tid & 7) == 0) a.o[((size_t)tok * a.HV + hv) * VD + row0 + r] = f2bf(ov);
+        }
         if (a.pool && a.L > 0 && t < a.L) {
             const int w = a.idx[(size_t)n * a.L + t];
             if (w >= 0 && w < a.num_slots) store_rows(a.s_out + ((size_t)w * a.HV + hv) * state + in_row, s);
         }
-        cur = nxt;
     }
     if (a.pool) {
         if (a.L == 0) store_rows(a.s_out + ((size_t)slot * a.HV + hv) * state + in_row, s);
