@@ -12,6 +12,8 @@ hipError_t launch_output(int C, const ChunkMap& map, int nslots, int H, uint16_t
                          hipStream_t stream);
 }  // namespace cdr
 
+#include "cdr_bwd_api.h"
+
 namespace {
 
 constexpr size_t kAlign = 256;
@@ -65,6 +67,34 @@ Layout layout(const cdr_problem* p) {
         L.off[i] = at;
         at += align_up(bytes[i]);
     }
+    L.total = at;
+    return L;
+}
+
+struct BwdLayout {
+    size_t m, gcr, rq, rk, bet, dqp, dkp, total;
+};
+
+// backward workspace: NMAT fp32 128 x 128 matrices and four 128-vectors per (chunk slot, value
+// head), and per-value-head dq, dk partials when value heads are grouped
+BwdLayout bwd_layout(const cdr_problem* p) {
+    const size_t nch = (size_t)num_slots(p) * (size_t)value_heads(p);
+    const size_t tokens = (size_t)p->B * p->T;
+    BwdLayout L;
+    size_t at = 0;
+    auto take = [&](size_t bytes) {
+        const size_t o = at;
+        at += align_up(bytes);
+        return o;
+    };
+    L.m = take(nch * cdr::bwd_matrices() * 128 * 128 * sizeof(float));
+    L.gcr = take(nch * 128 * sizeof(float));
+    L.rq = take(nch * 128 * sizeof(float));
+    L.rk = take(nch * 128 * sizeof(float));
+    L.bet = take(nch * 128 * sizeof(float));
+    const bool grouped = value_heads(p) != p->H;
+    L.dqp = take(grouped ? tokens * value_heads(p) * p->K * sizeof(float) : 0);
+    L.dkp = take(grouped ? tokens * value_heads(p) * p->K * sizeof(float) : 0);
     L.total = at;
     return L;
 }
@@ -165,6 +195,62 @@ cdr_status chunk_dr_fwd(const cdr_problem* p, const void* q, const void* k, cons
                         float* final_state, void* workspace, size_t workspace_bytes, void* stream) {
     return chunk_dr_fwd_stages(p, q, k, v, g, beta, initial_state, cu_seqlens, o, final_state, workspace,
                                workspace_bytes, CDR_STAGE_ALL, stream);
+}
+
+size_t cdr_bwd_workspace_bytes(const cdr_problem* p) {
+    if (cdr_check(p) != CDR_OK) return 0;
+    return bwd_layout(p).total;
+}
+
+cdr_status chunk_dr_bwd(const cdr_problem* p, const void* q, const void* k, const void* v, const float* g,
+                        const float* beta, const float* initial_state, const int32_t* cu_seqlens, const void* d_o,
+                        const float* dht, float* dq, float* dk, float* dv, float* dg, float* dbeta, float* dh0,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+    const cdr_status st = cdr_check(p);
+    if (st != CDR_OK) return st;
+    const int64_t tokens = (int64_t)p->B * p->T;
+    if (tokens > 0 && (!q || !k || !v || !g || !beta || !d_o || !dq || !dk || !dv || !dg || !dbeta))
+        return CDR_ERR_NULL_ARG;
+    if (p->has_initial_state && (!initial_state || !dh0)) return CDR_ERR_NULL_ARG;
+    if (p->varlen && !cu_seqlens) return CDR_ERR_NULL_ARG;
+    const BwdLayout L = bwd_layout(p);
+    if (workspace == nullptr || workspace_bytes < L.total) return CDR_ERR_WORKSPACE;
+    if (reinterpret_cast<uintptr_t>(workspace) % kAlign != 0) return CDR_ERR_WORKSPACE;
+    const int nslots = tokens > 0 ? (int)num_slots(p) : 0;
+    char* wb = static_cast<char*>(workspace);
+    cdr::bwd::Work w;
+    w.M = reinterpret_cast<float*>(wb + L.m);
+    w.gcr = reinterpret_cast<float*>(wb + L.gcr);
+    w.rq = reinterpret_cast<float*>(wb + L.rq);
+    w.rk = reinterpret_cast<float*>(wb + L.rk);
+    w.bet = reinterpret_cast<float*>(wb + L.bet);
+    const bool grouped = value_heads(p) != p->H;
+    w.dqp = grouped ? reinterpret_cast<float*>(wb + L.dqp) : nullptr;
+    w.dkp = grouped ? reinterpret_cast<float*>(wb + L.dkp) : nullptr;
+    cdr::bwd::In in;
+    in.q = static_cast<const uint16_t*>(q);
+    in.k = static_cast<const uint16_t*>(k);
+    in.v = static_cast<const uint16_t*>(v);
+    in.g = g;
+    in.beta = beta;
+    in.dO = static_cast<const uint16_t*>(d_o);
+    in.dq = dq;
+    in.dk = dk;
+    in.dv = dv;
+    in.dg = dg;
+    in.dbeta = dbeta;
+    cdr::ChunkMap map;
+    map.cu = p->varlen ? cu_seqlens : nullptr;
+    map.T = p->T;
+    map.N = p->N;
+    map.C = p->chunk_size;
+    map.nchunk = (p->T + p->chunk_size - 1) / p->chunk_size;
+    const hipError_t e = cdr::bwd::launch(p->chunk_size, p->gate == CDR_GATE_PER_DIM, p->qk_l2norm != 0, in, map,
+                                          nslots, p->N, (int)value_heads(p), p->H, p->scale,
+                                          p->has_initial_state ? initial_state : nullptr, dht,
+                                          p->has_initial_state ? dh0 : nullptr, w, tokens,
+                                          static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? CDR_OK : CDR_ERR_HIP;
 }
 
 const char* cdr_status_str(cdr_status s) {

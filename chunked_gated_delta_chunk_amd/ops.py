@@ -21,6 +21,7 @@ GATE_PER_DIM = 0
 GATE_PER_HEAD = 1
 
 EXPORTED = ("cdr_check", "cdr_workspace_bytes", "chunk_dr_fwd", "chunk_dr_fwd_stages",
+            "cdr_bwd_workspace_bytes", "chunk_dr_bwd",
             "cdr_recurrent_check", "chunk_dr_recurrent_fwd", "cdr_status_str", "cdr_version")
 STATE_SEPARATE, STATE_POOL, STATE_POOL_SPEC = 0, 1, 2
 STAGE_INTRA, STAGE_CHAIN, STAGE_OUTPUT, STAGE_ALL = 1, 2, 4, 7
@@ -68,6 +69,10 @@ def load_library(path: str = LIB_PATH):
     lib.chunk_dr_fwd_stages.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t,
                                         ctypes.c_int32, vp]
     lib.chunk_dr_fwd_stages.restype = ctypes.c_int
+    lib.cdr_bwd_workspace_bytes.argtypes = [P]
+    lib.cdr_bwd_workspace_bytes.restype = ctypes.c_size_t
+    lib.chunk_dr_bwd.argtypes = [P] + [vp] * 16 + [ctypes.c_size_t, vp]
+    lib.chunk_dr_bwd.restype = ctypes.c_int
     R = ctypes.POINTER(cdr_recurrent_problem)
     lib.cdr_recurrent_check.argtypes = [R]
     lib.cdr_recurrent_check.restype = ctypes.c_int
@@ -244,6 +249,107 @@ def chunk_dr_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Ten
                            final_state_out=final_state_out,
                            use_qk_l2norm_in_kernel=use_qk_l2norm_in_kernel)
     return call(stages)
+
+
+def bwd_workspace_bytes(p: cdr_problem) -> int:
+    return load_library().cdr_bwd_workspace_bytes(ctypes.byref(p))
+
+
+class PreparedBackward:
+    """A validated call of the backward whose arguments are marshalled once.
+
+    Takes the arguments of :func:`chunk_dr_bwd`, allocates the gradients and the workspace
+    unless given, and queues the kernels on the current stream at each call, returning
+    ``(dq, dk, dv, dg, dbeta, dh0)``.
+    """
+
+    def __init__(self, q, k, v, g, beta, do, dht=None, scale=None, initial_state=None,
+                 cu_seqlens=None, chunk_size=64, use_qk_l2norm_in_kernel=False, workspace=None):
+        lib = load_library()
+        _need(q, "q", torch.bfloat16)
+        if q.dim() != 4:
+            raise ValueError("q must be [B, T, H, K]")
+        B, T, H, K = q.shape
+        _need(k, "k", torch.bfloat16, (B, T, H, K))
+        if v.dim() != 4 or tuple(v.shape[:2]) != (B, T) or v.shape[2] % H:
+            raise ValueError("v must be [B, T, HV, V] with HV a multiple of the q/k heads")
+        _need(v, "v", torch.bfloat16)
+        HV, V = v.shape[2], v.shape[3]
+        _need(g, "g", torch.float32)
+        if tuple(g.shape) == (B, T, HV, K):
+            per_dim = True
+        elif tuple(g.shape) == (B, T, HV):
+            per_dim = False
+        else:
+            raise ValueError(f"g must be [B,T,HV,K] or [B,T,HV], got {tuple(g.shape)}")
+        _need(beta, "beta", torch.float32, (B, T, HV))
+        _need(do, "do", torch.bfloat16, (B, T, HV, V))
+        if cu_seqlens is not None:
+            _need(cu_seqlens, "cu_seqlens", torch.int32)
+            if cu_seqlens.dim() != 1 or cu_seqlens.numel() < 2:
+                raise ValueError("cu_seqlens must be a 1-D tensor of N + 1 offsets")
+            N = cu_seqlens.numel() - 1
+        else:
+            N = B
+        if initial_state is not None:
+            _need(initial_state, "initial_state", torch.float32, (N, HV, V, K))
+        if dht is not None:
+            _need(dht, "dht", torch.float32, (N, HV, V, K))
+        if scale is None:
+            scale = K ** -0.5
+        self.problem = make_problem(B, T, H, K, V, N, per_dim, chunk_size, scale,
+                                    initial_state is not None, False, cu_seqlens is not None, HV,
+                                    use_qk_l2norm_in_kernel)
+        st = lib.cdr_check(ctypes.byref(self.problem))
+        if st != CDR_OK:
+            _raise(st, "chunk_dr_bwd")
+        device = q.device
+        if device.type != "cuda":
+            raise ValueError("inputs must be on a GPU device")
+        self.device = device
+        self.inputs = tuple(t.contiguous() for t in (q, k, v, g, beta, do))
+        self.s0 = initial_state.contiguous() if initial_state is not None else None
+        self.dht = dht.contiguous() if dht is not None else None
+        self.cu = cu_seqlens.contiguous() if cu_seqlens is not None else None
+        f32 = dict(dtype=torch.float32, device=device)
+        self.grads = (torch.empty((B, T, H, K), **f32), torch.empty((B, T, H, K), **f32),
+                      torch.empty((B, T, HV, V), **f32), torch.empty(tuple(g.shape), **f32),
+                      torch.empty((B, T, HV), **f32),
+                      torch.empty((N, HV, V, K), **f32) if initial_state is not None else None)
+        nbytes = lib.cdr_bwd_workspace_bytes(ctypes.byref(self.problem))
+        if workspace is None:
+            workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+        elif workspace.numel() * workspace.element_size() < nbytes:
+            raise ValueError("workspace too small")
+        self.workspace = workspace
+        ptr = lambda t: None if t is None else _dev_ptr(t, device)  # noqa: E731
+        qq, kk, vv, gg, bb, dd = self.inputs
+        self._args = (ctypes.byref(self.problem), ptr(qq), ptr(kk), ptr(vv), ptr(gg), ptr(bb),
+                      ptr(self.s0), ptr(self.cu), ptr(dd), ptr(self.dht),
+                      *(ptr(t) for t in self.grads), ptr(workspace),
+                      workspace.numel() * workspace.element_size())
+        self._lib = lib
+
+    def __call__(self):
+        stream = torch.cuda.current_stream(self.device).cuda_stream
+        st = self._lib.chunk_dr_bwd(*self._args, stream)
+        if st != CDR_OK:
+            _raise(st, "chunk_dr_bwd")
+        return self.grads
+
+
+def chunk_dr_bwd(q, k, v, g, beta, do, dht=None, scale=None, initial_state=None, cu_seqlens=None,
+                 chunk_size=64, use_qk_l2norm_in_kernel=False, workspace=None):
+    """Gradients of the chunked forward on the GPU.
+
+    Arguments as :func:`chunk_dr_fwd`, plus ``do`` ``[B,T,HV,V]`` bf16 (gradient of o) and
+    ``dht`` ``[N,HV,V,K]`` fp32 or None (gradient of the final state).  Returns fp32
+    ``(dq, dk, dv, dg, dbeta, dh0)`` with the shapes of q, k, v, g, beta and initial_state
+    (dh0 is None without an initial state); dq and dk sum over grouped value heads.
+    """
+    return PreparedBackward(q, k, v, g, beta, do, dht=dht, scale=scale, initial_state=initial_state,
+                            cu_seqlens=cu_seqlens, chunk_size=chunk_size,
+                            use_qk_l2norm_in_kernel=use_qk_l2norm_in_kernel, workspace=workspace)()
 
 
 class PreparedRecurrent:

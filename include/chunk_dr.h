@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define CDR_VERSION 3
+#define CDR_VERSION 4
 
 typedef enum {
     CDR_OK = 0,
@@ -157,6 +157,40 @@ cdr_status chunk_dr_fwd_stages(const cdr_problem* p,
                                void* o, float* final_state,
                                void* workspace, size_t workspace_bytes,
                                int32_t stages, void* stream);
+
+/* ------------------------------------------------------------------------------------------
+ * Backward of the chunked forward.
+ *
+ * The gradients of L = sum(o * do) + sum(final_state * dht) with respect to q, k, v, g, beta and
+ * initial_state, for the forward chunk_dr_fwd computes with the same problem p (the vector-
+ * Jacobian products of the per-token rule of the chunk_kda page, section 算子定位与算法背景).
+ * The backward recomputes what it needs from the inputs (nothing is kept from the forward call):
+ * per chunk the decayed blocks, the inverse of (I + A) and the chunk's affine state map, the
+ * chunk entry states by a forward chain, the gradients of the chunk exit states by a reverse
+ * chain, then all input gradients chunk by chunk.  Storage and the serial chains are fp32; the
+ * products run on split-bf16 MFMA (about 16 mantissa bits per operand).
+ *
+ *   q, k, v, g, beta, initial_state, cu_seqlens  as chunk_dr_fwd
+ *   d_o     bf16 [B*T, HV, V]      gradient of o
+ *   dht     fp32 [N, HV, V, K]     gradient of the final state, or NULL (zero)
+ *   dq, dk  fp32 [B*T, H, K]       written (summed over the value heads of a group)
+ *   dv      fp32 [B*T, HV, V]      written
+ *   dg      fp32, the shape of g   written
+ *   dbeta   fp32 [B*T, HV]         written
+ *   dh0     fp32 [N, HV, V, K]     written when p->has_initial_state, else may be NULL
+ *   workspace  at least cdr_bwd_workspace_bytes(p) bytes, 256-byte aligned, contents irrelevant
+ * Rows of padded or empty chunks are not written; every token of every sequence is.
+ * p->output_final_state is ignored.  Errors as chunk_dr_fwd.
+ * ------------------------------------------------------------------------------------------ */
+size_t cdr_bwd_workspace_bytes(const cdr_problem* p);
+
+cdr_status chunk_dr_bwd(const cdr_problem* p,
+                        const void* q, const void* k, const void* v,
+                        const float* g, const float* beta,
+                        const float* initial_state, const int32_t* cu_seqlens,
+                        const void* d_o, const float* dht,
+                        float* dq, float* dk, float* dv, float* dg, float* dbeta, float* dh0,
+                        void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------------------------
  * Per-token (recurrent) forward: the decode path.

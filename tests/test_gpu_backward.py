@@ -1,0 +1,138 @@
+"""Parity of the HIP backward with the fp64 gradient oracle, through the C interface.
+
+Bar (page "flash-linear-attention KCP 精度失效根因排查手册", section 验收标准): the norm
+ratio |x - ref| / |ref| of every gradient below 5e-3, per sequence, against the gradients of
+the per-token rule (``oracle.backward.recurrent_bwd``, fp64 autograd) on the same bits.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import chunked_gated_delta_chunk_amd as cdr
+from chunked_gated_delta_chunk_amd.synth import WORKLOADS, make_inputs, workload_inputs
+from oracle.backward import recurrent_bwd, norm_ratio
+
+pytestmark = pytest.mark.gpu
+
+TOL = 5e-3
+DEV = "cuda:0"
+NAMES = ("dq", "dk", "dv", "dg", "dbeta", "dh0")
+
+
+def note(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def upstream(inp, seed, dht=True):
+    gen = torch.Generator("cpu").manual_seed(seed)
+    B, T, HV, V = inp.v.shape
+    K = inp.q.shape[-1]
+    N = B if inp.cu_seqlens is None else inp.cu_seqlens.numel() - 1
+    do = torch.randn(B, T, HV, V, generator=gen).to(torch.bfloat16)
+    ht = (0.1 * torch.randn(N, HV, V, K, generator=gen)) if dht else None
+    return do, ht
+
+
+def run_gpu(inp, do, dht, l2n):
+    d = inp.to(DEV)
+    grads = cdr.chunk_dr_bwd(d.q, d.k, d.v, d.g, d.beta, do.to(DEV),
+                             dht=None if dht is None else dht.to(DEV),
+                             initial_state=d.initial_state, cu_seqlens=d.cu_seqlens,
+                             chunk_size=inp.chunk_size, use_qk_l2norm_in_kernel=l2n)
+    torch.cuda.synchronize()
+    return dict(zip(NAMES, (None if t is None else t.cpu().numpy() for t in grads)))
+
+
+def seq_slices(inp):
+    if inp.cu_seqlens is None:
+        return [(b, slice(None)) for b in range(inp.q.shape[0])]
+    cu = inp.cu_seqlens.tolist()
+    return [(0, slice(cu[n], cu[n + 1])) for n in range(len(cu) - 1)]
+
+
+def check(inp, label, l2n=False, dht=True, seed=1):
+    note(f"[bwd] {label} q{tuple(inp.q.shape)} v{tuple(inp.v.shape)} C={inp.chunk_size} l2n={l2n}")
+    do, ht = upstream(inp, seed, dht)
+    got = run_gpu(inp, do, ht, l2n)
+    ref = recurrent_bwd(inp.q, inp.k, inp.v, inp.g, inp.beta, do, dht=ht,
+                        initial_state=inp.initial_state, cu_seqlens=inp.cu_seqlens,
+                        use_qk_l2norm=l2n)
+    worst = {}
+    for name in NAMES:
+        if name == "dh0":
+            if inp.initial_state is None:
+                assert got["dh0"] is None
+                continue
+            for n in range(got["dh0"].shape[0]):
+                r = norm_ratio(got["dh0"][n], ref["dh0"][n])
+                worst[name] = max(worst.get(name, 0.0), r)
+            continue
+        assert np.isfinite(got[name]).all(), name
+        for b, sl in seq_slices(inp):
+            x, y = got[name][b, sl], ref[name][b, sl]
+            if y.size == 0:
+                continue
+            worst[name] = max(worst.get(name, 0.0), norm_ratio(x, y))
+    note(f"[bwd] {label}: " + "  ".join(f"{k} {v:.2e}" for k, v in worst.items()))
+    for k, v in worst.items():
+        assert v <= TOL, f"{k} norm ratio {v:.3e} > {TOL}"
+
+
+SMALL = [
+    # label, B, T, H, HV, C, per_dim, lengths, initial, gate_mean, l2n
+    ("kda_T64_one_chunk", 1, 64, 2, None, 64, True, None, True, 0.0, False),
+    ("kda_T37_tail", 1, 37, 1, None, 64, True, None, True, 0.0, False),
+    ("kda_T200_tail8_b2", 2, 200, 2, None, 64, True, None, True, 0.0, False),
+    ("kda_T300_C128_weak", 1, 300, 2, None, 128, True, None, True, 4.0, False),
+    ("kda_T256_C128_zero_state", 1, 256, 2, None, 128, True, None, False, 0.0, False),
+    ("gdn_T300_C64", 2, 300, 2, None, 64, False, None, True, 0.0, False),
+    ("gdn_T260_C128_weak", 1, 260, 1, None, 128, False, None, True, 3.0, False),
+    ("grouped_l2n_C64", 1, 150, 1, 2, 64, True, None, True, 1.0, True),
+    ("grouped_gdn_l2n_C128", 1, 200, 2, 4, 128, False, None, True, 0.0, True),
+    ("varlen_ragged_empty", 1, 259, 2, None, 64, True, (1, 0, 63, 65, 130), True, 0.0, False),
+    ("varlen_C128", 1, 400, 1, None, 128, True, (127, 129, 144), True, 1.0, True),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[c[0] for c in SMALL])
+def test_backward_parity(case):
+    label, B, T, H, HV, C, per_dim, lengths, init, gm, l2n = case
+    inp = make_inputs(B, T, H, seed=500 + T, per_dim_gate=per_dim, lengths=lengths,
+                      initial_state=init, chunk_size=C, gate_mean=gm, HV=HV, normalise=not l2n)
+    check(inp, label, l2n=l2n)
+
+
+def test_backward_without_final_state_gradient():
+    inp = make_inputs(1, 130, 2, seed=520, initial_state=True, chunk_size=64)
+    check(inp, "no_dht", dht=False)
+
+
+def test_backward_repeat_is_bit_identical():
+    inp = make_inputs(1, 260, 2, seed=521, initial_state=True, chunk_size=128, gate_mean=2.0)
+    do, ht = upstream(inp, 3)
+    a = run_gpu(inp, do, ht, False)
+    b = run_gpu(inp, do, ht, False)
+    for name in NAMES:
+        assert np.array_equal(a[name], b[name]), name
+
+
+@pytest.mark.parametrize("name", ["kda_t8192"])
+def test_backward_workload_one_head(name):
+    """The full workload on the GPU; the oracle on the first head (heads are independent)."""
+    w = WORKLOADS[name]
+    inp = workload_inputs(w, seed=1000 + list(WORKLOADS).index(name) + 1)
+    do, ht = upstream(inp, 7)
+    note(f"[bwd] {name} full size")
+    got = run_gpu(inp, do, ht, False)
+    one = lambda t: t[:, :, :1].contiguous()  # noqa: E731
+    ref = recurrent_bwd(one(inp.q), one(inp.k), one(inp.v), one(inp.g), one(inp.beta), one(do),
+                        dht=ht[:, :1].contiguous(), initial_state=inp.initial_state[:, :1].contiguous())
+    worst = {}
+    for nm in NAMES:
+        x = got[nm][:, :1] if nm == "dh0" else got[nm][:, :, :1]
+        worst[nm] = norm_ratio(x, ref[nm])
+    note(f"[bwd] {name} head 0: " + "  ".join(f"{k} {v:.2e}" for k, v in worst.items()))
+    for k, v in worst.items():
+        assert v <= TOL, f"{k} norm ratio {v:.3e} > {TOL}"
