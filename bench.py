@@ -73,6 +73,9 @@ def kernel_work(w, lengths):
 
 
 KERNEL_SOURCES = {"intra": ("cdr_intra.hip", "cdr_common.h"),
+                  "prep": ("cdr_bwd.hip", "cdr_common.h"),
+                  "chains": ("cdr_bwd.hip", "cdr_common.h"),
+                  "local": ("cdr_bwd.hip", "cdr_common.h"),
                   "chain": ("cdr_chain.hip", "cdr_common.h"),
                   "output": ("cdr_chain.hip", "cdr_common.h"),
                   "decode": ("cdr_decode.hip", "cdr_common.h")}
@@ -160,6 +163,73 @@ def bench_decode(name, steps, warmup):
                        "qk_l2norm": w.qk_l2norm, "slot_sets_rotated": nsets}}
 
 
+def backward_work(w, lengths):
+    """Per-stage flops of the backward (products counted once, as full products like the
+    forward's nominal count) and its compulsory bytes; n = rows of each chunk."""
+    K, V = w.K, w.V
+    fl = {"prep": 0.0, "chains": 0.0, "local": 0.0}
+    for L in lengths:
+        nchunks = (L + w.chunk_size - 1) // w.chunk_size
+        for c in range(nchunks):
+            n = min(w.chunk_size, L - c * w.chunk_size)
+            fl["prep"] += 2 * (2 * n * n * K + n ** 3 / 3 + n * n * K + n * n * V + n * K * K + n * K * V
+                               + n * n * V + 2 * n * K * V)
+            fl["chains"] += 2 * 2 * K * K * V
+            fl["local"] += 2 * (n * K * V + n * n * V + n * K * V + n * n * V + 3 * n * K * V + n * n * V
+                                + n * n * K + n * n * V + n * n * K + 2 * n ** 3 + 4 * n * n * K)
+    fl = {k: v * w.H for k, v in fl.items()}
+    per_tok = 4 * 2 * K + (4 * K if w.per_dim_gate else 4) + 4 + 4 * 4 * K + (4 * K if w.per_dim_gate else 4) + 4
+    nbytes = w.tokens * w.H * per_tok + (2 * len(lengths) * w.H * K * V * 4 if w.initial_state else 0)
+    return fl, nbytes
+
+
+def bench_backward(name, steps, warmup):
+    """Time the backward of one forward workload: one call is the three stages (prep, the two
+    state chains, local gradients), events between the stages on the launch stream."""
+    import torch
+    import chunked_gated_delta_chunk_amd as cdr
+    from chunked_gated_delta_chunk_amd.synth import WORKLOADS, workload_inputs
+    w = WORKLOADS[name]
+    dev = torch.device("cuda:0")
+    host = workload_inputs(w, seed=1000 + list(WORKLOADS).index(name) + 1)
+    gen = torch.Generator("cpu").manual_seed(7)
+    do = torch.randn(tuple(host.v.shape), generator=gen).to(torch.bfloat16)
+    N = w.N
+    dht = 0.1 * torch.randn(N, w.H, w.V, w.K, generator=gen)
+    d = host.to(dev)
+    call = cdr.PreparedBackward(d.q, d.k, d.v, d.g, d.beta, do.to(dev), dht=dht.to(dev),
+                                initial_state=d.initial_state, cu_seqlens=d.cu_seqlens,
+                                chunk_size=w.chunk_size)
+    stages = (cdr.BWD_PREP, cdr.BWD_CHAINS, cdr.BWD_LOCAL)
+    names = ("prep", "chains", "local")
+    for _ in range(warmup):
+        for st in stages:
+            call(st)
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        ev[i][0].record()
+        for j, st in enumerate(stages):
+            call(st)
+            ev[i][j + 1].record()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    kus = {nm: sum(ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(steps)) / steps * 1e3
+           for j, nm in enumerate(names)}
+    lengths = list(w.lengths) if w.lengths is not None else [w.T] * w.B
+    fl, nbytes = backward_work(w, lengths)
+    dom = max(names, key=lambda n: kus[n])
+    tf = fl[dom] / (kus[dom] * 1e-6) / 1e12
+    return {"workload": name, "ms_per_call": round(ms, 4), "tokens_per_s": round(w.tokens / (ms * 1e-3), 1),
+            "per_kernel_us": {k: round(v, 2) for k, v in kus.items()},
+            "gflop": {k: round(v / 1e9, 2) for k, v in fl.items()},
+            "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(tf / PEAK_BF16_TFLOPS, 4), "traffic": load_traffic(dom, name),
+                         "kernel": "bwd_" + dom, "duration_us": round(kus[dom], 2)},
+            "compulsory_bytes": nbytes}
+
+
 def cpu_baseline(inp, w, budget_s):
     """Time the fp64 oracle on the host: all heads, a prefix of the tokens sized to the
     time budget (all tokens when it fits)."""
@@ -196,6 +266,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=8.0, help="seconds of oracle wall time")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode workloads")
+    ap.add_argument("--no-backward", action="store_true", help="skip the backward")
+    ap.add_argument("--backward-only", action="store_true",
+                    help="time only the backward of the workload and print its JSON line")
     ap.add_argument("--decode-only", default=None, metavar="NAME",
                     help="time only this decode workload and print its JSON line")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -218,6 +291,13 @@ def main():
               file=sys.stderr)
         sys.exit(2)
 
+    if args.backward_only:
+        r = bench_backward(args.workload, args.steps, args.warmup)
+        r.update({"metric": "backward tokens/s", "unit": "tokens/s", "value": r["tokens_per_s"],
+                  "higher_is_better": True, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+                  "dtype": "bf16", "data": "synthetic"})
+        print(json.dumps(r), flush=True)
+        return
     if args.decode_only:
         r = bench_decode(args.decode_only, args.steps, args.warmup)
         r.update({"metric": "decode tokens/s + % HBM peak", "unit": "tokens/s",
@@ -325,6 +405,11 @@ def main():
         torch.cuda.empty_cache()
         decode = {n: bench_decode(n, args.steps, args.warmup) for n in DECODE_WORKLOADS}
 
+    backward = None
+    if not args.no_backward:
+        torch.cuda.empty_cache()
+        backward = bench_backward(args.workload, min(args.steps, 20), min(args.warmup, 3))
+
     line = {
         "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": K, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
@@ -342,6 +427,7 @@ def main():
         "cpu_baseline": cpu,
         "parity_spot_check": spot,
         "decode": decode,
+        "backward": backward,
     }
     print(json.dumps(line), flush=True)
 

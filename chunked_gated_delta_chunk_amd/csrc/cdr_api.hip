@@ -202,11 +202,13 @@ size_t cdr_bwd_workspace_bytes(const cdr_problem* p) {
     return bwd_layout(p).total;
 }
 
-cdr_status chunk_dr_bwd(const cdr_problem* p, const void* q, const void* k, const void* v, const float* g,
-                        const float* beta, const float* initial_state, const int32_t* cu_seqlens, const void* d_o,
-                        const float* dht, float* dq, float* dk, float* dv, float* dg, float* dbeta, float* dh0,
-                        void* workspace, size_t workspace_bytes, void* stream) {
+cdr_status chunk_dr_bwd_stages(const cdr_problem* p, const void* q, const void* k, const void* v, const float* g,
+                               const float* beta, const float* initial_state, const int32_t* cu_seqlens,
+                               const void* d_o, const float* dht, float* dq, float* dk, float* dv, float* dg,
+                               float* dbeta, float* dh0, void* workspace, size_t workspace_bytes, int32_t stages,
+                               void* stream) {
     const cdr_status st = cdr_check(p);
+    if (stages < 1 || stages > CDR_BWD_ALL) return CDR_ERR_UNSUPPORTED;
     if (st != CDR_OK) return st;
     const int64_t tokens = (int64_t)p->B * p->T;
     if (tokens > 0 && (!q || !k || !v || !g || !beta || !d_o || !dq || !dk || !dv || !dg || !dbeta))
@@ -248,9 +250,17 @@ cdr_status chunk_dr_bwd(const cdr_problem* p, const void* q, const void* k, cons
     const hipError_t e = cdr::bwd::launch(p->chunk_size, p->gate == CDR_GATE_PER_DIM, p->qk_l2norm != 0, in, map,
                                           nslots, p->N, (int)value_heads(p), p->H, p->scale,
                                           p->has_initial_state ? initial_state : nullptr, dht,
-                                          p->has_initial_state ? dh0 : nullptr, w, tokens,
+                                          p->has_initial_state ? dh0 : nullptr, w, tokens, stages,
                                           static_cast<hipStream_t>(stream));
     return e == hipSuccess ? CDR_OK : CDR_ERR_HIP;
+}
+
+cdr_status chunk_dr_bwd(const cdr_problem* p, const void* q, const void* k, const void* v, const float* g,
+                        const float* beta, const float* initial_state, const int32_t* cu_seqlens, const void* d_o,
+                        const float* dht, float* dq, float* dk, float* dv, float* dg, float* dbeta, float* dh0,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+    return chunk_dr_bwd_stages(p, q, k, v, g, beta, initial_state, cu_seqlens, d_o, dht, dq, dk, dv, dg, dbeta, dh0,
+                               workspace, workspace_bytes, CDR_BWD_ALL, stream);
 }
 
 const char* cdr_status_str(cdr_status s) {

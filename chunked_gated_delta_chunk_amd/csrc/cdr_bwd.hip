@@ -62,30 +62,55 @@ struct View {
     int ms, ks;
 };
 
+// A panel of M x 32 fp32 values moves global -> registers (issued early) -> LDS (split).
 template <int M>
-__device__ __forceinline__ void stage(const View& v, int k0, uint16_t* hi, uint16_t* lo, int tid) {
-    constexpr int NF4 = M * KB / 4;
-    if (v.ks == 1) {
-        for (int e = tid; e < NF4; e += BTHREADS) {
-            const int m = e >> 3, kk = (e & 7) * 4;
-            const float4 x = *reinterpret_cast<const float4*>(v.p + (size_t)m * v.ms + k0 + kk);
-            uint32_t h0, l0, h1, l1;
-            split_pk(x.x, x.y, h0, l0);
-            split_pk(x.z, x.w, h1, l1);
-            *reinterpret_cast<uint2*>(hi + m * LDP + kk) = make_uint2(h0, h1);
-            *reinterpret_cast<uint2*>(lo + m * LDP + kk) = make_uint2(l0, l1);
-        }
-    } else {
-        for (int e = tid; e < NF4; e += BTHREADS) {
-            const int kk = e / (M / 4), m = (e % (M / 4)) * 4;
-            const float4 x = *reinterpret_cast<const float4*>(v.p + (size_t)(k0 + kk) * v.ks + m);
-            const float xs[4] = {x.x, x.y, x.z, x.w};
+struct Panel {
+    static constexpr int NF4 = M * KB / 4;
+    static constexpr int PER = (NF4 + BTHREADS - 1) / BTHREADS;
+    float4 x[PER];
+};
+
+template <int M>
+__device__ __forceinline__ void panel_load(Panel<M>& r, const View& v, int k0, int tid) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                short h, l;
-                split_bf(xs[r], h, l);
-                hi[(m + r) * LDP + kk] = (uint16_t)h;
-                lo[(m + r) * LDP + kk] = (uint16_t)l;
+    for (int u = 0; u < Panel<M>::PER; ++u) {
+        const int e = tid + u * BTHREADS;
+        if (e < Panel<M>::NF4) {
+            if (v.ks == 1) {
+                const int m = e >> 3, kk = (e & 7) * 4;
+                r.x[u] = *reinterpret_cast<const float4*>(v.p + (size_t)m * v.ms + k0 + kk);
+            } else {
+                const int kk = e / (M / 4), m = (e % (M / 4)) * 4;
+                r.x[u] = *reinterpret_cast<const float4*>(v.p + (size_t)(k0 + kk) * v.ks + m);
+            }
+        }
+    }
+}
+
+template <int M>
+__device__ __forceinline__ void panel_store(const Panel<M>& r, const View& v, uint16_t* hi, uint16_t* lo, int tid) {
+#pragma unroll
+    for (int u = 0; u < Panel<M>::PER; ++u) {
+        const int e = tid + u * BTHREADS;
+        if (e < Panel<M>::NF4) {
+            const float4 x = r.x[u];
+            if (v.ks == 1) {
+                const int m = e >> 3, kk = (e & 7) * 4;
+                uint32_t h0, l0, h1, l1;
+                split_pk(x.x, x.y, h0, l0);
+                split_pk(x.z, x.w, h1, l1);
+                *reinterpret_cast<uint2*>(hi + m * LDP + kk) = make_uint2(h0, h1);
+                *reinterpret_cast<uint2*>(lo + m * LDP + kk) = make_uint2(l0, l1);
+            } else {
+                const int kk = e / (M / 4), m = (e % (M / 4)) * 4;
+                const float xs[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    short h, l;
+                    split_bf(xs[q], h, l);
+                    hi[(m + q) * LDP + kk] = (uint16_t)h;
+                    lo[(m + q) * LDP + kk] = (uint16_t)l;
+                }
             }
         }
     }
@@ -98,6 +123,7 @@ __device__ __forceinline__ f32x4 mfma3(const bf16x8& ah, const bf16x8& al, const
     return mfma32(ah, bl, acc);
 }
 
+// The next block's panels are loaded into registers while the current block's MFMAs run.
 template <int M, int N, class Epi>
 __device__ void gemm(const View a1, const View b1, int k1, const View a2, const View b2, int k2, float s2,
                      unsigned char* lds, Epi epi) {
@@ -110,37 +136,46 @@ __device__ void gemm(const View a1, const View b1, int k1, const View a2, const 
     f32x4 acc[TPW];
 #pragma unroll
     for (int t = 0; t < TPW; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int pass = 0; pass < 2; ++pass) {
-        const View a = pass ? a2 : a1, b = pass ? b2 : b1;
-        const int kd = pass ? k2 : k1;
-        if (kd == 0) continue;
-        const float sg = pass ? s2 : 1.f;
-        if (sg != 1.f) {
-#pragma unroll
-            for (int t = 0; t < TPW; ++t) acc[t] = f32x4{acc[t][0] * sg, acc[t][1] * sg, acc[t][2] * sg, acc[t][3] * sg};
+    // blocks of both passes in one sequence: block q < nb1 is pass 1
+    const int nb1 = k1 / KB, nb = nb1 + k2 / KB;
+    Panel<M> pa;
+    Panel<N> pb;
+    auto issue = [&](int q) {
+        if (q < nb1) {
+            panel_load<M>(pa, a1, q * KB, tid);
+            panel_load<N>(pb, b1, q * KB, tid);
+        } else {
+            panel_load<M>(pa, a2, (q - nb1) * KB, tid);
+            panel_load<N>(pb, b2, (q - nb1) * KB, tid);
         }
-        for (int k0 = 0; k0 < kd; k0 += KB) {
-            __syncthreads();
-            stage<M>(a, k0, ahi, alo, tid);
-            stage<N>(b, k0, bhi, blo, tid);
-            __syncthreads();
+    };
+    if (nb > 0) issue(0);
+    for (int q = 0; q < nb; ++q) {
+        if (q == nb1 && s2 != 1.f) {  // entering the second pair: D = X1 + s2 X2 with s2 = +-1
 #pragma unroll
-            for (int t = 0; t < TPW; ++t) {
-                const int tile = wave + BWAVES * t;
-                if (tile < NTL) {
-                    const int I = tile / NTN, J = tile % NTN;
-                    const int ro = (16 * I + (lane & 15)) * LDP + 8 * (lane >> 4);
-                    const int co = (16 * J + (lane & 15)) * LDP + 8 * (lane >> 4);
-                    acc[t] = mfma3(*reinterpret_cast<const bf16x8*>(ahi + ro), *reinterpret_cast<const bf16x8*>(alo + ro),
-                                   *reinterpret_cast<const bf16x8*>(bhi + co), *reinterpret_cast<const bf16x8*>(blo + co),
-                                   acc[t]);
-                }
+            for (int t = 0; t < TPW; ++t) acc[t] = f32x4{acc[t][0] * s2, acc[t][1] * s2, acc[t][2] * s2, acc[t][3] * s2};
+        }
+        __syncthreads();
+        panel_store<M>(pa, q < nb1 ? a1 : a2, ahi, alo, tid);
+        panel_store<N>(pb, q < nb1 ? b1 : b2, bhi, blo, tid);
+        if (q + 1 < nb) issue(q + 1);
+        __syncthreads();
+#pragma unroll
+        for (int t = 0; t < TPW; ++t) {
+            const int tile = wave + BWAVES * t;
+            if (tile < NTL) {
+                const int I = tile / NTN, J = tile % NTN;
+                const int ro = (16 * I + (lane & 15)) * LDP + 8 * (lane >> 4);
+                const int co = (16 * J + (lane & 15)) * LDP + 8 * (lane >> 4);
+                acc[t] = mfma3(*reinterpret_cast<const bf16x8*>(ahi + ro), *reinterpret_cast<const bf16x8*>(alo + ro),
+                               *reinterpret_cast<const bf16x8*>(bhi + co), *reinterpret_cast<const bf16x8*>(blo + co),
+                               acc[t]);
             }
         }
-        if (sg != 1.f) {  // sg is +-1: undo the sign applied before this pass
+    }
+    if (nb > nb1 && s2 != 1.f) {
 #pragma unroll
-            for (int t = 0; t < TPW; ++t) acc[t] = f32x4{acc[t][0] * sg, acc[t][1] * sg, acc[t][2] * sg, acc[t][3] * sg};
-        }
+        for (int t = 0; t < TPW; ++t) acc[t] = f32x4{acc[t][0] * s2, acc[t][1] * s2, acc[t][2] * s2, acc[t][3] * s2};
     }
 #pragma unroll
     for (int t = 0; t < TPW; ++t) {
@@ -205,6 +240,7 @@ __device__ __forceinline__ void stage_piv_rowmajor(const float* X, const float* 
 template <int PITCH>
 __device__ __forceinline__ void stage_piv_colmajor(const float* X, const float* gam, const float* piv, int sgn,
                                                    int jlo, int jhi, int nrows, uint16_t* hi, uint16_t* lo, int tid) {
+#pragma unroll 4
     for (int e = tid; e < nrows * 128; e += BTHREADS) {
         const int j = e >> 7, d = e & 127;
         float x = 0.f;
@@ -218,11 +254,11 @@ __device__ __forceinline__ void stage_piv_colmajor(const float* X, const float* 
 
 // ------------------------------------------------------------------------------------
 template <int C, bool PER_DIM, bool L2N>
-__global__ __launch_bounds__(BTHREADS) void bwd_prep_kernel(In in, ChunkMap map, int H, int Hk, float scale, Work w) {
+__global__ __launch_bounds__(BTHREADS) __attribute__((amdgpu_waves_per_eu(4))) void bwd_prep_kernel(In in, ChunkMap map, int H, int Hk, float scale, Work w) {
     constexpr int NT = C / 16;
     constexpr int P2 = 128 + 8;                     // pitch of pivot panels
-    constexpr int INV_BYTES = (2 * C * (C + 1) + 16 * C) * 4;   // A, T (pitch C + 1), X (16 x C)
-    constexpr int PIV_BYTES = (C * P2 * 2 + 2 * 16 * P2 * 2) * 2 + 128 * 4;
+    constexpr int INV_BYTES = (C * (C + 1) + 16 * C) * 4;   // A then T in place (pitch C + 1), X (16 x C)
+    constexpr int PIV_BYTES = 4 * 16 * P2 * 2 + 128 * 4;
     constexpr int GEMM_BYTES = 256 * LDP * 2 * 2;
     constexpr int SMEM = (INV_BYTES > PIV_BYTES ? (INV_BYTES > GEMM_BYTES ? INV_BYTES : GEMM_BYTES)
                                                 : (PIV_BYTES > GEMM_BYTES ? PIV_BYTES : GEMM_BYTES));
@@ -239,83 +275,102 @@ __global__ __launch_bounds__(BTHREADS) void bwd_prep_kernel(In in, ChunkMap map,
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     float* gam = mat(w, ch, GAM);
 
-    // ---- row scales, beta, gamma
-    if (tid < C) {
-        const int i = tid;
+    // ---- row scales and beta (a wave per row), gamma (a thread per key dimension)
+    for (int i = wave; i < C; i += BWAVES) {
         float rq = 1.f, rk = 1.f, b = 0.f;
         if (i < rows) {
             const size_t tok = tok0 + i;
             if (L2N) {
-                float sq = 0.f, sk = 0.f;
                 const uint16_t* qr = in.q + (tok * Hk + hk) * KD;
                 const uint16_t* kr = in.k + (tok * Hk + hk) * KD;
-                for (int d = 0; d < KD; ++d) {
-                    const float a = bf2f(qr[d]), c = bf2f(kr[d]);
-                    sq += a * a;
-                    sk += c * c;
+                const float q0 = bf2f(qr[lane]), q1 = bf2f(qr[lane + 64]);
+                const float k0 = bf2f(kr[lane]), k1 = bf2f(kr[lane + 64]);
+                float sq = q0 * q0 + q1 * q1, sk = k0 * k0 + k1 * k1;
+#pragma unroll
+                for (int m = 1; m < 64; m <<= 1) {
+                    sq += __shfl_xor(sq, m, 64);
+                    sk += __shfl_xor(sk, m, 64);
                 }
                 rq = rsqrtf(sq + EPS);
                 rk = rsqrtf(sk + EPS);
             }
             b = in.beta[tok * H + hv];
         }
-        sRq[i] = rq;
-        sRk[i] = rk;
-        sBeta[i] = b;
-        w.rq[ch * 128 + i] = rq;
-        w.rk[ch * 128 + i] = rk;
-        w.bet[ch * 128 + i] = b;
-    } else if (tid >= 128 && tid < 256) {
-        const int d = tid - 128;
+        if (lane == 0) {
+            sRq[i] = rq;
+            sRk[i] = rk;
+            sBeta[i] = b;
+            w.rq[ch * 128 + i] = rq;
+            w.rk[ch * 128 + i] = rk;
+            w.bet[ch * 128 + i] = b;
+        }
+    }
+    if (tid < 128) {
+        const int d = tid;
         float acc = 0.f;
-        for (int i = 0; i < C; ++i) {
-            float gi = 0.f;
-            if (i < rows) {
-                const size_t tok = tok0 + i;
-                gi = PER_DIM ? in.g[(tok * H + hv) * KD + d] : in.g[tok * H + hv];
+        for (int i0 = 0; i0 < C; i0 += 16) {  // 16 independent loads in flight per block
+            float gv[16];
+#pragma unroll
+            for (int u = 0; u < 16; ++u) {
+                const int i = i0 + u;
+                const size_t tok = tok0 + min(i, rows - 1);
+                const float x = PER_DIM ? in.g[(tok * H + hv) * KD + d] : in.g[tok * H + hv];
+                gv[u] = (i < rows) ? x : 0.f;
             }
-            acc += gi;
-            gam[i * 128 + d] = acc;
+#pragma unroll
+            for (int u = 0; u < 16; ++u) {
+                acc += gv[u];
+                gam[(i0 + u) * 128 + d] = acc;
+            }
         }
         sGC[d] = acc;
         w.gcr[ch * 128 + d] = acc;
     }
     __syncthreads();
 
-    // ---- inputs and their decayed forms
+    // ---- inputs and their decayed forms (four elements per thread per round, loads first)
     {
         float *KFp = mat(w, ch, KF), *QFp = mat(w, ch, QF), *VFp = mat(w, ch, VF), *DOp = mat(w, ch, DOF);
         float *QDp = mat(w, ch, QD), *KDp = mat(w, ch, KDM), *KGp = mat(w, ch, KG), *BKp = mat(w, ch, BKD);
         float* BVp = mat(w, ch, BV);
-        for (int e = tid; e < C * 128; e += BTHREADS) {
-            const int i = e >> 7, d = e & 127;
-            float kf = 0.f, qf = 0.f, vf = 0.f, df = 0.f;
-            if (i < rows) {
-                const size_t tok = tok0 + i;
-                kf = bf2f(in.k[(tok * Hk + hk) * KD + d]) * sRk[i];
-                qf = bf2f(in.q[(tok * Hk + hk) * KD + d]) * sRq[i];
-                vf = bf2f(in.v[(tok * H + hv) * VD + d]);
-                df = bf2f(in.dO[(tok * H + hv) * VD + d]);
+        for (int e0 = tid; e0 < C * 128; e0 += 4 * BTHREADS) {
+            float kf[4], qf[4], vf[4], df[4], gm[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int e = e0 + u * BTHREADS, i = e >> 7, d = e & 127;
+                const size_t tok = tok0 + min(i, rows - 1);
+                kf[u] = bf2f(in.k[(tok * Hk + hk) * KD + d]);
+                qf[u] = bf2f(in.q[(tok * Hk + hk) * KD + d]);
+                vf[u] = bf2f(in.v[(tok * H + hv) * VD + d]);
+                df[u] = bf2f(in.dO[(tok * H + hv) * VD + d]);
+                gm[u] = gam[e];
             }
-            const float gm = gam[e], eg = ex(gm), egc = ex(sGC[d] - gm), b = sBeta[i];
-            KFp[e] = kf;
-            QFp[e] = qf;
-            VFp[e] = vf;
-            DOp[e] = df;
-            QDp[e] = scale * qf * eg;
-            KDp[e] = kf * eg;
-            KGp[e] = kf * egc;
-            BKp[e] = b * kf * eg;
-            BVp[e] = b * vf;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int e = e0 + u * BTHREADS, i = e >> 7, d = e & 127;
+                const bool ok = i < rows;   // rows past the end are zero
+                const float k_ = ok ? kf[u] * sRk[i] : 0.f, q_ = ok ? qf[u] * sRq[i] : 0.f;
+                const float v_ = ok ? vf[u] : 0.f, d_ = ok ? df[u] : 0.f;
+                const float eg = ex(gm[u]), egc = ex(sGC[d] - gm[u]), b = sBeta[i];
+                KFp[e] = k_;
+                QFp[e] = q_;
+                VFp[e] = v_;
+                DOp[e] = d_;
+                QDp[e] = scale * q_ * eg;
+                KDp[e] = k_ * eg;
+                KGp[e] = k_ * egc;
+                BKp[e] = b * k_ * eg;
+                BVp[e] = b * v_;
+            }
         }
     }
     __syncthreads();
 
-    // ---- A-hat (strict) and A2 (inclusive) by row tiles: pivot p = gamma of row 16 I + 8
+    // ---- A-hat (strict) and A2 (inclusive) by row tiles: pivot p = gamma of row 16 I + 8.
+    // The tile rows' left factors (shared by the waves) are staged in LDS; wave J forms its
+    // right factor k_j e^(p - gamma_j) for its 16 rows in registers.
     {
-        uint16_t* bh = reinterpret_cast<uint16_t*>(smem);
-        uint16_t* bl = bh + C * P2;
-        uint16_t* kh = bl + C * P2;
+        uint16_t* kh = reinterpret_cast<uint16_t*>(smem);
         uint16_t* kl = kh + 16 * P2;
         uint16_t* qh = kl + 16 * P2;
         uint16_t* ql = qh + 16 * P2;
@@ -328,17 +383,15 @@ __global__ __launch_bounds__(BTHREADS) void bwd_prep_kernel(In in, ChunkMap map,
             __syncthreads();
             if (tid < 128) piv[tid] = gam[(16 * I + 8) * 128 + tid];
             __syncthreads();
-            // right factor k_j e^(p - gamma_j), j < 16 (I + 1)
-            stage_piv_rowmajor<P2>(KFp, gam, piv, 1, 0, 16 * (I + 1), 16 * (I + 1), bh, bl, tid);
-            // left factors k_i e^(gamma_i - p), q_i e^(gamma_i - p) of the tile rows
+#pragma unroll 4
             for (int e = tid; e < 16 * 128; e += BTHREADS) {
                 const int r = e >> 7, d = e & 127, i = 16 * I + r;
-                const float s = ex(gam[i * 128 + d] - piv[d]);
+                const float sc = ex(gam[i * 128 + d] - piv[d]);
                 short h, l;
-                split_bf(KFp[i * 128 + d] * s, h, l);
+                split_bf(KFp[i * 128 + d] * sc, h, l);
                 kh[r * P2 + d] = (uint16_t)h;
                 kl[r * P2 + d] = (uint16_t)l;
-                split_bf(QFp[i * 128 + d] * s, h, l);
+                split_bf(QFp[i * 128 + d] * sc, h, l);
                 qh[r * P2 + d] = (uint16_t)h;
                 ql[r * P2 + d] = (uint16_t)l;
             }
@@ -347,16 +400,35 @@ __global__ __launch_bounds__(BTHREADS) void bwd_prep_kernel(In in, ChunkMap map,
             if (J < NT) {
                 f32x4 ak = {0.f, 0.f, 0.f, 0.f}, aq = {0.f, 0.f, 0.f, 0.f};
                 if (J <= I) {
+                    const int j = 16 * J + (lane & 15);
+                    for (int s2 = 0; s2 < KD / 32; s2 += 2) {
+                        float4 kx[2][2], gx[2][2];
 #pragma unroll
-                    for (int s = 0; s < KD / 32; ++s) {
-                        const int ao = (lane & 15) * P2 + 32 * s + 8 * (lane >> 4);
-                        const int bo = (16 * J + (lane & 15)) * P2 + 32 * s + 8 * (lane >> 4);
-                        const bf16x8 b_h = *reinterpret_cast<const bf16x8*>(bh + bo);
-                        const bf16x8 b_l = *reinterpret_cast<const bf16x8*>(bl + bo);
-                        ak = mfma3(*reinterpret_cast<const bf16x8*>(kh + ao), *reinterpret_cast<const bf16x8*>(kl + ao),
-                                   b_h, b_l, ak);
-                        aq = mfma3(*reinterpret_cast<const bf16x8*>(qh + ao), *reinterpret_cast<const bf16x8*>(ql + ao),
-                                   b_h, b_l, aq);
+                        for (int t = 0; t < 2; ++t) {
+                            const int d0 = 32 * (s2 + t) + 8 * (lane >> 4);
+                            kx[t][0] = *reinterpret_cast<const float4*>(KFp + j * 128 + d0);
+                            kx[t][1] = *reinterpret_cast<const float4*>(KFp + j * 128 + d0 + 4);
+                            gx[t][0] = *reinterpret_cast<const float4*>(gam + j * 128 + d0);
+                            gx[t][1] = *reinterpret_cast<const float4*>(gam + j * 128 + d0 + 4);
+                        }
+#pragma unroll
+                        for (int t = 0; t < 2; ++t) {
+                            const int s = s2 + t, d0 = 32 * s + 8 * (lane >> 4);
+                            const float kk[8] = {kx[t][0].x, kx[t][0].y, kx[t][0].z, kx[t][0].w,
+                                                 kx[t][1].x, kx[t][1].y, kx[t][1].z, kx[t][1].w};
+                            const float gg[8] = {gx[t][0].x, gx[t][0].y, gx[t][0].z, gx[t][0].w,
+                                                 gx[t][1].x, gx[t][1].y, gx[t][1].z, gx[t][1].w};
+                            float bv[8];
+#pragma unroll
+                            for (int e = 0; e < 8; ++e) bv[e] = kk[e] * ex(piv[d0 + e] - gg[e]);
+                            bf16x8 b_h, b_l;
+                            split8(bv, b_h, b_l);
+                            const int ao = (lane & 15) * P2 + d0;
+                            ak = mfma3(*reinterpret_cast<const bf16x8*>(kh + ao), *reinterpret_cast<const bf16x8*>(kl + ao),
+                                       b_h, b_l, ak);
+                            aq = mfma3(*reinterpret_cast<const bf16x8*>(qh + ao), *reinterpret_cast<const bf16x8*>(ql + ao),
+                                       b_h, b_l, aq);
+                        }
                     }
                 }
 #pragma unroll
@@ -370,26 +442,37 @@ __global__ __launch_bounds__(BTHREADS) void bwd_prep_kernel(In in, ChunkMap map,
     }
     __syncthreads();
 
-    // ---- T = (I + A)^-1, A = beta_i A-hat (strictly lower), blocked by 16-row tiles in fp32
+    // ---- T = (I + A)^-1, A = beta_i A-hat (strictly lower), blocked by 16-row tiles in fp32,
+    // in place: each block of T replaces the block of A it is computed from (A_{I, <I} is last
+    // read to form X = A_{I, <I} T_{<I, <I}, and the diagonal block's column substitution
+    // only reads rows above the one it writes)
     {
         constexpr int LP = C + 1;
-        float* sA = reinterpret_cast<float*>(smem);
-        float* sT = sA + C * LP;
+        float* sT = reinterpret_cast<float*>(smem);
         float* sX = sT + C * LP;
         const float* AHp = mat(w, ch, AH);
         for (int e = tid; e < C * C; e += BTHREADS) {
             const int i = e / C, j = e % C;
-            sA[i * LP + j] = (j < i) ? sBeta[i] * AHp[i * 128 + j] : 0.f;
-            sT[i * LP + j] = 0.f;
+            sT[i * LP + j] = (j < i) ? sBeta[i] * AHp[i * 128 + j] : 0.f;
         }
         __syncthreads();
-        if (tid < C) {  // diagonal tile I = tid / 16, column c = tid % 16
+        if (tid < C) {
+            // diagonal tile I = tid / 16 (its 16 lanes are in one wave), column c = tid % 16, row by
+            // row: every lane reads row r of A before any lane overwrites it with row r of T
             const int I = tid >> 4, c = tid & 15, o = 16 * I;
-            sT[(o + c) * LP + o + c] = 1.f;
-            for (int r = c + 1; r < 16; ++r) {
+#pragma unroll
+            for (int r = 1; r < 16; ++r) {
+                float arow[16];
+#pragma unroll
+                for (int j = 0; j < 16; ++j) arow[j] = (j < r) ? sT[(o + r) * LP + o + j] : 0.f;
                 float s = 0.f;
-                for (int j = c; j < r; ++j) s += sA[(o + r) * LP + o + j] * sT[(o + j) * LP + o + c];
-                sT[(o + r) * LP + o + c] = -s;
+#pragma unroll
+                for (int j = 0; j < 16; ++j) {
+                    if (j == c) s += arow[j];                                   // A[r][c] T[c][c]
+                    else if (j > c && j < r) s += arow[j] * sT[(o + j) * LP + o + c];
+                }
+                asm volatile("" ::: "memory");  // no load of row r may move below the stores
+                if (c < r) sT[(o + r) * LP + o + c] = -s;
             }
         }
         __syncthreads();
@@ -397,15 +480,15 @@ __global__ __launch_bounds__(BTHREADS) void bwd_prep_kernel(In in, ChunkMap map,
             const int o = 16 * I;
             for (int e = tid; e < 16 * o; e += BTHREADS) {
                 const int r = e / o, col = e % o;
-                float s = 0.f;
-                for (int j = col; j < o; ++j) s += sA[(o + r) * LP + j] * sT[j * LP + col];
+                float s = sT[(o + r) * LP + col];             // A[o+r][col] * T[col][col] (= 1)
+                for (int j = col + 1; j < o; ++j) s += sT[(o + r) * LP + j] * sT[j * LP + col];
                 sX[r * C + col] = s;
             }
             __syncthreads();
             for (int e = tid; e < 16 * o; e += BTHREADS) {
                 const int r = e / o, col = e % o;
-                float s = 0.f;
-                for (int j = 0; j <= r; ++j) s += sT[(o + r) * LP + o + j] * sX[j * C + col];
+                float s = sX[r * C + col];                    // T[r][r] = 1
+                for (int j = 0; j < r; ++j) s += sT[(o + r) * LP + o + j] * sX[j * C + col];
                 sT[(o + r) * LP + col] = -s;
             }
             __syncthreads();
@@ -413,7 +496,7 @@ __global__ __launch_bounds__(BTHREADS) void bwd_prep_kernel(In in, ChunkMap map,
         float* TTp = mat(w, ch, TT);
         for (int e = tid; e < C * C; e += BTHREADS) {
             const int i = e / C, j = e % C;
-            TTp[i * 128 + j] = sT[i * LP + j];
+            TTp[i * 128 + j] = (j < i) ? sT[i * LP + j] : (j == i ? 1.f : 0.f);
         }
     }
     __syncthreads();
@@ -460,10 +543,13 @@ __global__ __launch_bounds__(BTHREADS) void bwd_prep_kernel(In in, ChunkMap map,
 // state entering every chunk; reverse: dS <- e^gamma_C dS - P^T dS + Q^T dO over the chunks
 // in reverse order, recording the gradient of every chunk's exit state.  One workgroup per
 // (sequence, value head, 16 value columns); thread (a, cg) owns row a, columns 4 cg .. + 3.
+// The chunk's 128 x 128 operand goes through LDS: the next chunk's is loaded into registers
+// while the current one is used, then stored into the other LDS buffer.
 template <bool REV>
 __global__ __launch_bounds__(BTHREADS) void bwd_chain_kernel(ChunkMap map, int H, const float* __restrict__ s0,
                                                               float* __restrict__ s_last, Work w) {
-    __shared__ __attribute__((aligned(16))) float sS[2][128][16];
+    __shared__ __attribute__((aligned(16))) float sP[2 * 128 * 128];   // two operand buffers
+    __shared__ __attribute__((aligned(16))) float sS[2 * 128 * 16];    // two published state blocks
     const int nh = blockIdx.x, vb = blockIdx.y;
     const int n = nh / H, hv = nh % H;
     int64_t bos;
@@ -477,27 +563,38 @@ __global__ __launch_bounds__(BTHREADS) void bwd_chain_kernel(ChunkMap map, int H
 #pragma unroll
         for (int e = 0; e < 4; ++e) s[e] = s0[(((size_t)n * H + hv) * VD + v0 + e) * KD + a];
     }
+    auto chunk = [&](int step) { return (size_t)(slot0 + (REV ? nch - 1 - step : step)) * H + hv; };
+    float4 pr[8];   // this thread's 8 float4 of the next operand: element (tid + 512 u) * 4
+    auto load = [&](int step) {
+        const float* Pm = mat(w, chunk(step), REV ? PP : PT);   // element (b, a) is (op P)[a][b]
+#pragma unroll
+        for (int u = 0; u < 8; ++u) pr[u] = *reinterpret_cast<const float4*>(Pm + (size_t)(tid + BTHREADS * u) * 4);
+    };
+    if (nch > 0) load(0);
     for (int step = 0; step < nch; ++step) {
-        const int c = REV ? nch - 1 - step : step;
-        const size_t ch = (size_t)(slot0 + c) * H + hv;
+        const size_t ch = chunk(step);
         const int buf = step & 1;
+        float* P = sP + buf * 128 * 128;
+        float* S = sS + buf * 128 * 16;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) *reinterpret_cast<float4*>(P + (tid + BTHREADS * u) * 4) = pr[u];
         float* rec = mat(w, ch, REV ? DS : SIN);
         *reinterpret_cast<float4*>(rec + a * 128 + v0) = make_float4(s[0], s[1], s[2], s[3]);
-        *reinterpret_cast<float4*>(&sS[buf][a][4 * cg]) = make_float4(s[0], s[1], s[2], s[3]);
+        *reinterpret_cast<float4*>(S + a * 16 + 4 * cg) = make_float4(s[0], s[1], s[2], s[3]);
+        const float gc = ex(w.gcr[ch * 128 + a]);
+        const float4 badd = *reinterpret_cast<const float4*>(mat(w, ch, REV ? BD : BB) + a * 128 + v0);
         __syncthreads();
-        const float* Pm = mat(w, ch, REV ? PP : PT);   // element (b, a) is (op P)[a][b]
+        if (step + 1 < nch) load(step + 1);
         float x[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 8
+#pragma unroll 16
         for (int b = 0; b < 128; ++b) {
-            const float p = Pm[b * 128 + a];
-            const float4 sb = *reinterpret_cast<const float4*>(&sS[buf][b][4 * cg]);
+            const float p = P[b * 128 + a];
+            const float4 sb = *reinterpret_cast<const float4*>(S + b * 16 + 4 * cg);
             x[0] += p * sb.x;
             x[1] += p * sb.y;
             x[2] += p * sb.z;
             x[3] += p * sb.w;
         }
-        const float gc = ex(w.gcr[ch * 128 + a]);
-        const float4 badd = *reinterpret_cast<const float4*>(mat(w, ch, REV ? BD : BB) + a * 128 + v0);
         s[0] = gc * s[0] - x[0] + badd.x;
         s[1] = gc * s[1] - x[1] + badd.y;
         s[2] = gc * s[2] - x[2] + badd.z;
@@ -511,10 +608,10 @@ __global__ __launch_bounds__(BTHREADS) void bwd_chain_kernel(ChunkMap map, int H
 
 // ------------------------------------------------------------------------------------
 template <int C, bool PER_DIM, bool L2N>
-__global__ __launch_bounds__(BTHREADS) void bwd_local_kernel(In in, ChunkMap map, int H, int Hk, float scale, Work w) {
+__global__ __launch_bounds__(BTHREADS) __attribute__((amdgpu_waves_per_eu(4))) void bwd_local_kernel(In in, ChunkMap map, int H, int Hk, float scale, Work w) {
     constexpr int NT = C / 16;
     constexpr int PC = C + 8;                          // pitch of [d][j] pivot panels
-    constexpr int PIV_BYTES = 128 * PC * 2 * 2 + 128 * 4;
+    constexpr int PIV_BYTES = (128 * PC * 2 + 2 * 16 * PC) * 2 + 128 * 4;
     constexpr int GEMM_BYTES = 256 * LDP * 2 * 2;
     constexpr int SMEM = PIV_BYTES > GEMM_BYTES ? PIV_BYTES : GEMM_BYTES;
     __shared__ __attribute__((aligned(16))) unsigned char smem[SMEM];
@@ -608,55 +705,57 @@ __global__ __launch_bounds__(BTHREADS) void bwd_local_kernel(In in, ChunkMap map
     }
     __syncthreads();
 
-    // ---- pair products with per-dimension decay
+    // ---- pair products with per-dimension decay.  Per row tile: the decayed right factor
+    // (all rows, [d][j] so that the contraction index is contiguous) and the tile's rows of the
+    // coefficient matrices are staged as hi/lo bf16 in LDS; wave w computes key dimensions
+    // 16 w .. 16 w + 15.
     uint16_t* bh = reinterpret_cast<uint16_t*>(smem);
     uint16_t* bl = bh + 128 * PC;
-    float* piv = reinterpret_cast<float*>(bl + 128 * PC);
+    uint16_t* m1h = bl + 128 * PC;          // [16][PC] the tile's rows of the coefficient matrix
+    uint16_t* m1l = m1h + 16 * PC;
+    float* piv = reinterpret_cast<float*>(m1l + 16 * PC);
     const float* KFp = mat(w, ch, KF);
     const float* QFp = mat(w, ch, QF);
-    // R_i = sum_j G_ij k_j e^(gamma_i - gamma_j), R2_i = sum_j dA2_ij k_j e^(...), by row tiles
-    {
-        const float* Gp = mat(w, ch, GG);
-        const float* DA2p = mat(w, ch, DA2);
-        float* Rp = mat(w, ch, RR);
-        float* R2p = mat(w, ch, R2);
+    auto stage_rows = [&](const float* Mx, int r0, int ncol, uint16_t* hi, uint16_t* lo) {
+        for (int e = tid; e < 16 * (ncol / 4); e += BTHREADS) {
+            const int r = e / (ncol / 4), c4 = (e % (ncol / 4)) * 4;
+            const float4 x = *reinterpret_cast<const float4*>(Mx + (r0 + r) * 128 + c4);
+            uint32_t h0, l0, h1, l1;
+            split_pk(x.x, x.y, h0, l0);
+            split_pk(x.z, x.w, h1, l1);
+            *reinterpret_cast<uint2*>(hi + r * PC + c4) = make_uint2(h0, h1);
+            *reinterpret_cast<uint2*>(lo + r * PC + c4) = make_uint2(l0, l1);
+        }
+    };
+    // R_i = sum_j G_ij k_j e^(gamma_i - gamma_j), R2_i = sum_j dA2_ij k_j e^(...), j <= i
+    for (int which = 0; which < 2; ++which) {
+        const float* Mx = mat(w, ch, which ? DA2 : GG);
+        float* Out = mat(w, ch, which ? R2 : RR);
         for (int I = 0; I < NT; ++I) {
             __syncthreads();
             if (tid < 128) piv[tid] = gam[(16 * I + 8) * 128 + tid];
             __syncthreads();
             const int nr = 16 * (I + 1), nrp = (nr + 31) & ~31;
             stage_piv_colmajor<PC>(KFp, gam, piv, 1, 0, nr, nrp, bh, bl, tid);
+            stage_rows(Mx, 16 * I, nrp, m1h, m1l);
             __syncthreads();
-            const int Dt = wave;   // 8 waves x 16 key dimensions
-            f32x4 r1 = {0.f, 0.f, 0.f, 0.f}, r2 = {0.f, 0.f, 0.f, 0.f};
-            const int i = 16 * I + (lane & 15);
+            const int Dt = wave;
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
             for (int s = 0; s < nrp / 32; ++s) {
                 const int jo = 32 * s + 8 * (lane >> 4);
-                float ga[8], da[8];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    ga[e] = Gp[i * 128 + jo + e];
-                    da[e] = DA2p[i * 128 + jo + e];
-                }
-                bf16x8 gh, gl, dh, dl;
-                split8(ga, gh, gl);
-                split8(da, dh, dl);
+                const int ao = (lane & 15) * PC + jo;
                 const int bo = (16 * Dt + (lane & 15)) * PC + jo;
-                const bf16x8 b_h = *reinterpret_cast<const bf16x8*>(bh + bo);
-                const bf16x8 b_l = *reinterpret_cast<const bf16x8*>(bl + bo);
-                r1 = mfma3(gh, gl, b_h, b_l, r1);
-                r2 = mfma3(dh, dl, b_h, b_l, r2);
+                acc = mfma3(*reinterpret_cast<const bf16x8*>(m1h + ao), *reinterpret_cast<const bf16x8*>(m1l + ao),
+                            *reinterpret_cast<const bf16x8*>(bh + bo), *reinterpret_cast<const bf16x8*>(bl + bo), acc);
             }
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int ii = 16 * I + 4 * (lane >> 4) + e, d = 16 * Dt + (lane & 15);
-                const float f = ex(gam[ii * 128 + d] - piv[d]);
-                Rp[ii * 128 + d] = f * r1[e];
-                R2p[ii * 128 + d] = f * r2[e];
+                Out[ii * 128 + d] = ex(gam[ii * 128 + d] - piv[d]) * acc[e];
             }
         }
     }
-    // Cc_j = sum_i G_ij k_i e^(gamma_i - gamma_j), C2_j = sum_i dA2_ij q_i e^(...), by row tiles
+    // Cc_j = sum_i G_ij k_i e^(gamma_i - gamma_j), C2_j = sum_i dA2_ij q_i e^(...), i >= j
     for (int which = 0; which < 2; ++which) {
         const float* Mt = mat(w, ch, which ? DA2T : GT);
         const float* X = which ? QFp : KFp;
@@ -667,20 +766,16 @@ __global__ __launch_bounds__(BTHREADS) void bwd_local_kernel(In in, ChunkMap map
             __syncthreads();
             const int i0 = (16 * J) & ~31;          // first contraction block
             stage_piv_colmajor<PC>(X, gam, piv, -1, 16 * J, C, C, bh, bl, tid);
+            stage_rows(Mt, 16 * J, C, m1h, m1l);
             __syncthreads();
             const int Dt = wave;
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            const int j = 16 * J + (lane & 15);
             for (int io = i0; io < C; io += 32) {
                 const int ii = io + 8 * (lane >> 4);
-                float ma[8];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) ma[e] = Mt[j * 128 + ii + e];
-                bf16x8 mh, ml;
-                split8(ma, mh, ml);
+                const int ao = (lane & 15) * PC + ii;
                 const int bo = (16 * Dt + (lane & 15)) * PC + ii;
-                acc = mfma3(mh, ml, *reinterpret_cast<const bf16x8*>(bh + bo), *reinterpret_cast<const bf16x8*>(bl + bo),
-                            acc);
+                acc = mfma3(*reinterpret_cast<const bf16x8*>(m1h + ao), *reinterpret_cast<const bf16x8*>(m1l + ao),
+                            *reinterpret_cast<const bf16x8*>(bh + bo), *reinterpret_cast<const bf16x8*>(bl + bo), acc);
             }
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -691,80 +786,144 @@ __global__ __launch_bounds__(BTHREADS) void bwd_local_kernel(In in, ChunkMap map
     }
     __syncthreads();
 
-    // ---- assembly: gradients of the normalised q, k and of gamma; dv
+    // ---- assembly: gradients of the normalised q, k and of gamma; dv (two elements per
+    // thread per round, loads first)
     {
         const float *Rp = mat(w, ch, RR), *Cp = mat(w, ch, CC), *R2p = mat(w, ch, R2), *C2p = mat(w, ch, C2);
         const float *DQDp = mat(w, ch, DQD), *DKGp = mat(w, ch, DKG), *DKTp = mat(w, ch, DKT), *DBTp = mat(w, ch, DBT);
         const float *QDp = mat(w, ch, QD), *KDp = mat(w, ch, KDM), *KGp = mat(w, ch, KG);
         float *DQHp = mat(w, ch, DQH), *DKHp = mat(w, ch, DKH), *DGMp = mat(w, ch, DGM);
-        for (int e = tid; e < C * 128; e += BTHREADS) {
-            const int i = e >> 7, d = e & 127;
-            const float gm = gam[e], eg = ex(gm), egc = ex(sGC[d] - gm);
-            const float kf = KFp[e], qf = QFp[e], b = sBeta[i];
-            const float dkd = b * DKTp[e];
-            const float dqd = DQDp[e], dkg = DKGp[e];
-            DQHp[e] = scale * R2p[e] + scale * eg * dqd;
-            DKHp[e] = Rp[e] + Cp[e] + scale * C2p[e] + eg * dkd + egc * dkg;
-            DGMp[e] = kf * Rp[e] - kf * Cp[e] + scale * (qf * R2p[e] - kf * C2p[e]) + QDp[e] * dqd + KDp[e] * dkd -
-                      KGp[e] * dkg;
-            if (i < rows) in.dv[((tok0 + i) * H + hv) * VD + d] = b * DBTp[e];
+        for (int e0 = tid; e0 < C * 128; e0 += 2 * BTHREADS) {
+            float gm[2], kf[2], qf[2], dkt[2], dqd[2], dkg[2], rr[2], cc[2], r2[2], c2[2], qd[2], kd[2], kg[2], dbt[2];
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const int e = e0 + u * BTHREADS;
+                gm[u] = gam[e];
+                kf[u] = KFp[e];
+                qf[u] = QFp[e];
+                dkt[u] = DKTp[e];
+                dqd[u] = DQDp[e];
+                dkg[u] = DKGp[e];
+                rr[u] = Rp[e];
+                cc[u] = Cp[e];
+                r2[u] = R2p[e];
+                c2[u] = C2p[e];
+                qd[u] = QDp[e];
+                kd[u] = KDp[e];
+                kg[u] = KGp[e];
+                dbt[u] = DBTp[e];
+            }
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const int e = e0 + u * BTHREADS, i = e >> 7, d = e & 127;
+                const float eg = ex(gm[u]), egc = ex(sGC[d] - gm[u]), b = sBeta[i];
+                const float dkd = b * dkt[u];
+                DQHp[e] = scale * r2[u] + scale * eg * dqd[u];
+                DKHp[e] = rr[u] + cc[u] + scale * c2[u] + eg * dkd + egc * dkg[u];
+                DGMp[e] = kf[u] * rr[u] - kf[u] * cc[u] + scale * (qf[u] * r2[u] - kf[u] * c2[u]) + qd[u] * dqd[u] +
+                          kd[u] * dkd - kg[u] * dkg[u];
+                if (i < rows) in.dv[((tok0 + i) * H + hv) * VD + d] = b * dbt[u];
+            }
         }
     }
     __syncthreads();
-    // ---- per row: dbeta, dq, dk (raw, through the normalisation);  per key dimension: dg
-    if (tid < C) {
-        const int i = tid;
-        if (i < rows) {
+    // ---- per row (a wave per row, two key dimensions per lane): dbeta, dq, dk (raw, through
+    // the normalisation)
+    {
+        const float *DBTp = mat(w, ch, DBT), *VFp = mat(w, ch, VF), *DKTp = mat(w, ch, DKT), *KDp = mat(w, ch, KDM);
+        const float *DAp = mat(w, ch, DAM), *AHp = mat(w, ch, AH);
+        const float *DQHp = mat(w, ch, DQH), *DKHp = mat(w, ch, DKH);
+        for (int i = wave; i < rows; i += BWAVES) {
             const size_t tok = tok0 + i;
-            const float *DBTp = mat(w, ch, DBT), *VFp = mat(w, ch, VF), *DKTp = mat(w, ch, DKT), *KDp = mat(w, ch, KDM);
-            const float *DAp = mat(w, ch, DAM), *AHp = mat(w, ch, AH);
-            float db = 0.f;
-            for (int d = 0; d < 128; ++d) db += DBTp[i * 128 + d] * VFp[i * 128 + d] + DKTp[i * 128 + d] * KDp[i * 128 + d];
-            for (int j = 0; j < i; ++j) db += DAp[i * 128 + j] * AHp[i * 128 + j];
-            in.dbeta[tok * H + hv] = db;
-            const float *DQHp = mat(w, ch, DQH), *DKHp = mat(w, ch, DKH);
-            float dotq = 0.f, dotk = 0.f;
-            const float rq = w.rq[ch * 128 + i], rk = w.rk[ch * 128 + i];
-            if (L2N) {
-                for (int d = 0; d < 128; ++d) {
-                    dotq += QFp[i * 128 + d] * DQHp[i * 128 + d];
-                    dotk += KFp[i * 128 + d] * DKHp[i * 128 + d];
+            const int r = i * 128;
+            float db = 0.f, dotq = 0.f, dotk = 0.f;
+            float gq[2], gk[2], qv[2], kv[2];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int d = lane + 64 * h;
+                db += DBTp[r + d] * VFp[r + d] + DKTp[r + d] * KDp[r + d];
+                if (d < i) db += DAp[r + d] * AHp[r + d];
+                gq[h] = DQHp[r + d];
+                gk[h] = DKHp[r + d];
+                qv[h] = QFp[r + d];
+                kv[h] = KFp[r + d];
+                dotq += qv[h] * gq[h];
+                dotk += kv[h] * gk[h];
+            }
+#pragma unroll
+            for (int m = 1; m < 64; m <<= 1) {
+                db += __shfl_xor(db, m, 64);
+                if (L2N) {
+                    dotq += __shfl_xor(dotq, m, 64);
+                    dotk += __shfl_xor(dotk, m, 64);
                 }
             }
+            if (lane == 0) in.dbeta[tok * H + hv] = db;
             float* dqo = w.dqp ? w.dqp + (tok * H + hv) * KD : in.dq + (tok * Hk + hk) * KD;
             float* dko = w.dkp ? w.dkp + (tok * H + hv) * KD : in.dk + (tok * Hk + hk) * KD;
-            for (int d = 0; d < 128; ++d) {
-                float gq = DQHp[i * 128 + d], gk = DKHp[i * 128 + d];
+            const float rq = w.rq[ch * 128 + i], rk = w.rk[ch * 128 + i];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                float xq = gq[h], xk = gk[h];
                 if (L2N) {
-                    gq = rq * (gq - QFp[i * 128 + d] * dotq);
-                    gk = rk * (gk - KFp[i * 128 + d] * dotk);
+                    xq = rq * (xq - qv[h] * dotq);
+                    xk = rk * (xk - kv[h] * dotk);
                 }
-                dqo[d] = gq;
-                dko[d] = gk;
+                dqo[lane + 64 * h] = xq;
+                dko[lane + 64 * h] = xk;
             }
         }
-    } else if (tid >= 128 && tid < 256) {
-        const int d = tid - 128;
+    }
+    // ---- per key dimension: dgamma_C and the reverse prefix sum of dgamma over the chunk rows
+    {
+        float (*sPart)[128] = reinterpret_cast<float (*)[128]>(smem);   // [4][128], pivot panels are done
+        float* sSd = reinterpret_cast<float*>(smem) + 4 * 128;
         const float *KGp = mat(w, ch, KG), *DKGp = mat(w, ch, DKG), *DGMp = mat(w, ch, DGM);
-        float dgc = 0.f, sd = 0.f;
-        for (int i = 0; i < C; ++i) dgc += KGp[i * 128 + d] * DKGp[i * 128 + d];
-        for (int v = 0; v < 128; ++v) sd += SINp[d * 128 + v] * DSp[d * 128 + v];
-        dgc += ex(sGC[d]) * sd;
+        // S_in . dS_out along the value columns of row d of both (a wave per row)
+        for (int d = wave; d < 128; d += BWAVES) {
+            float x = SINp[d * 128 + lane] * DSp[d * 128 + lane] + SINp[d * 128 + lane + 64] * DSp[d * 128 + lane + 64];
+#pragma unroll
+            for (int m = 1; m < 64; m <<= 1) x += __shfl_xor(x, m, 64);
+            if (lane == 0) sSd[d] = x;
+        }
+        // thread (d, part): rows part * C/4 .. + C/4 - 1
+        constexpr int SEG = C / 4;
+        const int d = tid & 127, part = tid >> 7, i0 = part * SEG;
+        float kgsum = 0.f, seg = 0.f;
+#pragma unroll 8
+        for (int u = 0; u < SEG; ++u) {
+            const int i = i0 + u;
+            kgsum += KGp[i * 128 + d] * DKGp[i * 128 + d];
+            seg += (i < rows) ? DGMp[i * 128 + d] : 0.f;
+        }
+        sPart[part][d] = kgsum;
+        __syncthreads();
+        const float dgc = sPart[0][d] + sPart[1][d] + sPart[2][d] + sPart[3][d] + ex(sGC[d]) * sSd[d];
+        __syncthreads();
+        sPart[part][d] = seg;
+        __syncthreads();
+        // suffix offset: later segments, plus dgamma_C (it enters at the last row, i.e. every row's sum)
         float acc = dgc;
+        for (int p2 = part + 1; p2 < 4; ++p2) acc += sPart[p2][d];
         float* DGSp = mat(w, ch, DGS);
-        for (int i = rows - 1; i >= 0; --i) {
-            acc += DGMp[i * 128 + d];
-            if (PER_DIM) in.dg[((tok0 + i) * H + hv) * KD + d] = acc;
-            else DGSp[i * 128 + d] = acc;
+#pragma unroll 8
+        for (int u = SEG - 1; u >= 0; --u) {
+            const int i = i0 + u;
+            acc += (i < rows) ? DGMp[i * 128 + d] : 0.f;
+            if (i < rows) {
+                if (PER_DIM) in.dg[((tok0 + i) * H + hv) * KD + d] = acc;
+                else DGSp[i * 128 + d] = acc;
+            }
         }
     }
     if (!PER_DIM) {
         __syncthreads();
-        if (tid < rows) {
-            const float* DGSp = mat(w, ch, DGS);
-            float s = 0.f;
-            for (int d = 0; d < 128; ++d) s += DGSp[tid * 128 + d];
-            in.dg[(tok0 + tid) * H + hv] = s;
+        const float* DGSp = mat(w, ch, DGS);
+        for (int i = wave; i < rows; i += BWAVES) {
+            float x = DGSp[i * 128 + lane] + DGSp[i * 128 + lane + 64];
+#pragma unroll
+            for (int m = 1; m < 64; m <<= 1) x += __shfl_xor(x, m, 64);
+            if (lane == 0) in.dg[(tok0 + i) * H + hv] = x;
         }
     }
 }
@@ -791,15 +950,20 @@ __global__ void bwd_group_kernel(int64_t tokens, int H, int Hk, const float* __r
 
 template <int C, bool PD, bool L2>
 hipError_t launch_t(const In& in, const ChunkMap& map, int nslots, int N, int H, int Hk, float scale,
-                    const float* h0, const float* dht, float* dh0, const Work& w, int64_t tokens, hipStream_t s) {
+                    const float* h0, const float* dht, float* dh0, const Work& w, int64_t tokens, int stages,
+                    hipStream_t s) {
     // with no chunk (no token) only the reverse chain runs: dh0 = dht (or zero)
-    if (nslots > 0) {
+    if ((stages & 1) && nslots > 0)
         hipLaunchKernelGGL((bwd_prep_kernel<C, PD, L2>), dim3(nslots, H), dim3(BTHREADS), 0, s, in, map, H, Hk, scale,
                            w);
-        hipLaunchKernelGGL((bwd_chain_kernel<false>), dim3(N * H, VD / 16), dim3(BTHREADS), 0, s, map, H, h0,
-                           (float*)nullptr, w);
+    if (stages & 2) {
+        if (nslots > 0)
+            hipLaunchKernelGGL((bwd_chain_kernel<false>), dim3(N * H, VD / 16), dim3(BTHREADS), 0, s, map, H,
+                               h0, (float*)nullptr, w);
+        hipLaunchKernelGGL((bwd_chain_kernel<true>), dim3(N * H, VD / 16), dim3(BTHREADS), 0, s, map, H, dht,
+                           dh0, w);
     }
-    hipLaunchKernelGGL((bwd_chain_kernel<true>), dim3(N * H, VD / 16), dim3(BTHREADS), 0, s, map, H, dht, dh0, w);
+    if (!(stages & 4)) return hipGetLastError();
     if (nslots > 0)
         hipLaunchKernelGGL((bwd_local_kernel<C, PD, L2>), dim3(nslots, H), dim3(BTHREADS), 0, s, in, map, H, Hk, scale,
                            w);
@@ -813,10 +977,10 @@ hipError_t launch_t(const In& in, const ChunkMap& map, int nslots, int N, int H,
 
 hipError_t launch(int C, bool per_dim, bool l2n, const In& in, const ChunkMap& map, int nslots, int N, int H, int Hk,
                   float scale, const float* h0, const float* dht, float* dh0, const Work& w, int64_t tokens,
-                  hipStream_t s) {
+                  int stages, hipStream_t s) {
 #define CDR_BWD_CASE(CC, PDV, L2V)                                                                    \
     if (C == CC && per_dim == PDV && l2n == L2V)                                                      \
-        return launch_t<CC, PDV, L2V>(in, map, nslots, N, H, Hk, scale, h0, dht, dh0, w, tokens, s);
+        return launch_t<CC, PDV, L2V>(in, map, nslots, N, H, Hk, scale, h0, dht, dh0, w, tokens, stages, s);
     CDR_BWD_CASE(64, true, false)
     CDR_BWD_CASE(64, true, true)
     CDR_BWD_CASE(64, false, false)

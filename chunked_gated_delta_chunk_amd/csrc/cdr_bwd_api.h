@@ -33,7 +33,7 @@ struct In {
 
 hipError_t launch(int C, bool per_dim, bool l2n, const In& in, const ChunkMap& map, int nslots, int N, int H, int Hk,
                   float scale, const float* h0, const float* dht, float* dh0, const Work& w, int64_t tokens,
-                  hipStream_t s);
+                  int stages, hipStream_t s);
 
 }  // namespace bwd
 

@@ -21,10 +21,11 @@ GATE_PER_DIM = 0
 GATE_PER_HEAD = 1
 
 EXPORTED = ("cdr_check", "cdr_workspace_bytes", "chunk_dr_fwd", "chunk_dr_fwd_stages",
-            "cdr_bwd_workspace_bytes", "chunk_dr_bwd",
+            "cdr_bwd_workspace_bytes", "chunk_dr_bwd", "chunk_dr_bwd_stages",
             "cdr_recurrent_check", "chunk_dr_recurrent_fwd", "cdr_status_str", "cdr_version")
 STATE_SEPARATE, STATE_POOL, STATE_POOL_SPEC = 0, 1, 2
 STAGE_INTRA, STAGE_CHAIN, STAGE_OUTPUT, STAGE_ALL = 1, 2, 4, 7
+BWD_PREP, BWD_CHAINS, BWD_LOCAL, BWD_ALL = 1, 2, 4, 7
 
 
 class cdr_problem(ctypes.Structure):
@@ -73,6 +74,8 @@ def load_library(path: str = LIB_PATH):
     lib.cdr_bwd_workspace_bytes.restype = ctypes.c_size_t
     lib.chunk_dr_bwd.argtypes = [P] + [vp] * 16 + [ctypes.c_size_t, vp]
     lib.chunk_dr_bwd.restype = ctypes.c_int
+    lib.chunk_dr_bwd_stages.argtypes = [P] + [vp] * 16 + [ctypes.c_size_t, ctypes.c_int32, vp]
+    lib.chunk_dr_bwd_stages.restype = ctypes.c_int
     R = ctypes.POINTER(cdr_recurrent_problem)
     lib.cdr_recurrent_check.argtypes = [R]
     lib.cdr_recurrent_check.restype = ctypes.c_int
@@ -330,9 +333,12 @@ class PreparedBackward:
                       workspace.numel() * workspace.element_size())
         self._lib = lib
 
-    def __call__(self):
+    def __call__(self, stages: int = BWD_ALL):
         stream = torch.cuda.current_stream(self.device).cuda_stream
-        st = self._lib.chunk_dr_bwd(*self._args, stream)
+        if stages == BWD_ALL:
+            st = self._lib.chunk_dr_bwd(*self._args, stream)
+        else:
+            st = self._lib.chunk_dr_bwd_stages(*self._args, int(stages), stream)
         if st != CDR_OK:
             _raise(st, "chunk_dr_bwd")
         return self.grads

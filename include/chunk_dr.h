@@ -192,6 +192,28 @@ cdr_status chunk_dr_bwd(const cdr_problem* p,
                         float* dq, float* dk, float* dv, float* dg, float* dbeta, float* dh0,
                         void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * The same backward split into its stages, for timing and profiling.  `stages` is a bit mask of
+ *   CDR_BWD_PREP   (1)  per chunk: decayed blocks, (I + A)^-1, w, u, the chunk's state map P, B
+ *                       and Q^T do
+ *   CDR_BWD_CHAINS (2)  the forward chain (chunk entry states) and the reverse chain (gradients
+ *                       of the chunk exit states, dh0)
+ *   CDR_BWD_LOCAL  (4)  per chunk: dq, dk, dv, dg, dbeta (and the sum over grouped value heads)
+ * Stages run in this order and read what earlier stages left in the workspace, as for
+ * chunk_dr_fwd_stages.  chunk_dr_bwd(...) is chunk_dr_bwd_stages(..., CDR_BWD_ALL, stream).
+ */
+#define CDR_BWD_PREP 1
+#define CDR_BWD_CHAINS 2
+#define CDR_BWD_LOCAL 4
+#define CDR_BWD_ALL 7
+cdr_status chunk_dr_bwd_stages(const cdr_problem* p,
+                               const void* q, const void* k, const void* v,
+                               const float* g, const float* beta,
+                               const float* initial_state, const int32_t* cu_seqlens,
+                               const void* d_o, const float* dht,
+                               float* dq, float* dk, float* dv, float* dg, float* dbeta, float* dh0,
+                               void* workspace, size_t workspace_bytes, int32_t stages, void* stream);
+
 /* ------------------------------------------------------------------------------------------
  * Per-token (recurrent) forward: the decode path.
  *
