@@ -225,7 +225,7 @@ def bench_backward(name, steps, warmup):
             "per_kernel_us": {k: round(v, 2) for k, v in kus.items()},
             "gflop": {k: round(v / 1e9, 2) for k, v in fl.items()},
             "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                         "frac": round(tf / PEAK_BF16_TFLOPS, 4), "traffic": load_traffic(dom, name),
+                         "frac": round(tf / PEAK_BF16_TFLOPS, 4), "traffic": load_traffic(dom, name + "_backward"),
                          "kernel": "bwd_" + dom, "duration_us": round(kus[dom], 2)},
             "compulsory_bytes": nbytes}
 
