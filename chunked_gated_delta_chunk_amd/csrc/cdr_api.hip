@@ -29,7 +29,7 @@ int64_t num_slots(const cdr_problem* p) {
     return (int64_t)p->B * ((p->T + p->chunk_size - 1) / p->chunk_size);
 }
 
-constexpr int kArrays = 14;
+constexpr int kArrays = 13;
 constexpr int64_t kScratchSlots = 512; // at most this many intra workgroups run at once
 
 size_t scratch_slots(const cdr_problem* p) {
@@ -46,8 +46,7 @@ Layout layout(const cdr_problem* p) {
     const size_t nch = (size_t)num_slots(p) * (size_t)value_heads(p), nsc = scratch_slots(p);
     const size_t C = (size_t)p->chunk_size, K = (size_t)p->K, V = (size_t)p->V;
     const size_t bytes[kArrays] = {
-        nch * K * K * 2,  // Pn_hi
-        nch * K * K * 2,  // Pn_lo
+        nch * K * K * 2,  // Pn
         nch * K * V * 4,  // Bm
         nch * C * K * 2,  // Qp
         nch * C * V * 2,  // Up
@@ -145,20 +144,19 @@ cdr_status chunk_dr_fwd_stages(const cdr_problem* p, const void* q, const void* 
 
     char* wb = static_cast<char*>(workspace);
     cdr::Work ws;
-    ws.Pn_hi = reinterpret_cast<uint16_t*>(wb + L.off[0]);
-    ws.Pn_lo = reinterpret_cast<uint16_t*>(wb + L.off[1]);
-    ws.Bm = reinterpret_cast<float*>(wb + L.off[2]);
-    ws.Qp = reinterpret_cast<uint16_t*>(wb + L.off[3]);
-    ws.Up = reinterpret_cast<uint16_t*>(wb + L.off[4]);
-    ws.gC = reinterpret_cast<float*>(wb + L.off[5]);
-    ws.Sc = reinterpret_cast<uint16_t*>(wb + L.off[6]);
-    ws.bwT_hi = reinterpret_cast<uint16_t*>(wb + L.off[7]);
-    ws.bwT_lo = reinterpret_cast<uint16_t*>(wb + L.off[8]);
-    ws.vT = reinterpret_cast<uint16_t*>(wb + L.off[9]);
-    ws.kgT_hi = reinterpret_cast<uint16_t*>(wb + L.off[10]);
-    ws.kgT_lo = reinterpret_cast<uint16_t*>(wb + L.off[11]);
-    ws.A2s = reinterpret_cast<uint16_t*>(wb + L.off[12]);
-    ws.qgs = reinterpret_cast<uint16_t*>(wb + L.off[13]);
+    ws.Pn = reinterpret_cast<uint16_t*>(wb + L.off[0]);
+    ws.Bm = reinterpret_cast<float*>(wb + L.off[1]);
+    ws.Qp = reinterpret_cast<uint16_t*>(wb + L.off[2]);
+    ws.Up = reinterpret_cast<uint16_t*>(wb + L.off[3]);
+    ws.gC = reinterpret_cast<float*>(wb + L.off[4]);
+    ws.Sc = reinterpret_cast<uint16_t*>(wb + L.off[5]);
+    ws.bwT_hi = reinterpret_cast<uint16_t*>(wb + L.off[6]);
+    ws.bwT_lo = reinterpret_cast<uint16_t*>(wb + L.off[7]);
+    ws.vT = reinterpret_cast<uint16_t*>(wb + L.off[8]);
+    ws.kgT_hi = reinterpret_cast<uint16_t*>(wb + L.off[9]);
+    ws.kgT_lo = reinterpret_cast<uint16_t*>(wb + L.off[10]);
+    ws.A2s = reinterpret_cast<uint16_t*>(wb + L.off[11]);
+    ws.qgs = reinterpret_cast<uint16_t*>(wb + L.off[12]);
 
     cdr::ChunkMap map;
     map.cu = p->varlen ? cu_seqlens : nullptr;

@@ -664,12 +664,9 @@ __device__ __forceinline__ void intra_item(
             pt[e] = p0[e] + p1[e];
             bt[e] = b0[e] + b1[e];
         }
-        uint2 ph, pl;
-        split_pk(-pt[0], -pt[1], ph.x, pl.x);
-        split_pk(-pt[2], -pt[3], ph.y, pl.y);
+        const uint2 ph = make_uint2(pack_bf2(-pt[0], -pt[1]), pack_bf2(-pt[2], -pt[3]));
         const size_t po = ch * KD * KD + frag(x, dt >> 1, KD / 32) + fragP(dt & 1, r16, q4);
-        st_nt(reinterpret_cast<uint2*>(ws.Pn_hi + po), ph);
-        st_nt(reinterpret_cast<uint2*>(ws.Pn_lo + po), pl);
+        st_nt(reinterpret_cast<uint2*>(ws.Pn + po), ph);
         st_nt(reinterpret_cast<float4*>(ws.Bm + ch * KD * VD + ((size_t)(x * (VD / 16) + dt) * 64 + lane) * 4),
               make_float4(bt[0], bt[1], bt[2], bt[3]));
     }

@@ -91,8 +91,8 @@ cdr_status cdr_check(const cdr_problem* p);
  * Bytes of device workspace chunk_dr_fwd needs for problem p (0 if p is invalid).
  * The size depends only on the shape fields (B, T, H, HV, K, V, N, chunk_size): it
  * holds the per-chunk intermediates (w, u, decayed keys and queries, the in-chunk
- * attention block, the chunk-entry states and the corrected values), about
- * 290 KiB per chunk and head at chunk_size 128.
+ * attention block, the chunk-entry states and the chunk's state map), about 190 KiB per
+ * chunk and head at chunk_size 128, plus up to 512 per-workgroup scratch slots of 224 KiB.
  */
 size_t cdr_workspace_bytes(const cdr_problem* p);
 
