@@ -230,6 +230,38 @@ def bench_backward(name, steps, warmup):
             "compulsory_bytes": nbytes}
 
 
+def bench_context_parallel(name, ranks, steps, warmup):
+    """One rank's share of the workload when its sequence is split over `ranks` ranks: the
+    segment summary (M, X) of T / ranks tokens, and the merge of `ranks` summaries."""
+    import torch
+    import chunked_gated_delta_chunk_amd as cdr
+    from chunked_gated_delta_chunk_amd.synth import WORKLOADS, make_inputs
+    w = WORKLOADS[name]
+    seg = w.T // ranks
+    inp = make_inputs(1, seg, w.H, w.K, w.V, seed=77, chunk_size=w.chunk_size).to("cuda:0")
+    p = cdr.make_problem(1, seg, w.H, w.K, w.V, 1, True, w.chunk_size, w.K ** -0.5, False, True, False)
+    ws = torch.empty(cdr.workspace_bytes(p), dtype=torch.uint8, device="cuda:0")
+    for _ in range(warmup):
+        M, X = cdr.segment_map(inp.q, inp.k, inp.v, inp.g, inp.beta, chunk_size=w.chunk_size, workspace=ws)
+    Ms, Xs = M.expand(ranks, -1, -1, -1).contiguous(), X.expand(ranks, -1, -1, -1).contiguous()
+    for _ in range(warmup):
+        cdr.merge_states(Ms, Xs)
+    torch.cuda.synchronize()
+    e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    e[0].record()
+    for _ in range(steps):
+        cdr.segment_map(inp.q, inp.k, inp.v, inp.g, inp.beta, chunk_size=w.chunk_size, workspace=ws)
+    e[1].record()
+    for _ in range(steps):
+        cdr.merge_states(Ms, Xs)
+    e[2].record()
+    torch.cuda.synchronize()
+    return {"workload": f"{name}, one of {ranks} ranks ({seg} tokens x {w.H} heads)",
+            "segment_map_us": round(e[0].elapsed_time(e[1]) / steps * 1e3, 2),
+            "merge_us": round(e[1].elapsed_time(e[2]) / steps * 1e3, 2),
+            "summary_bytes_per_rank": w.H * (w.K * w.K + w.V * w.K) * 4}
+
+
 def cpu_baseline(inp, w, budget_s):
     """Time the fp64 oracle on the host: all heads, a prefix of the tokens sized to the
     time budget (all tokens when it fits)."""
@@ -405,6 +437,10 @@ def main():
         torch.cuda.empty_cache()
         decode = {n: bench_decode(n, args.steps, args.warmup) for n in DECODE_WORKLOADS}
 
+    cp = None
+    if not args.no_decode:
+        cp = bench_context_parallel(args.workload, 8, args.steps, args.warmup)
+
     backward = None
     if not args.no_backward:
         torch.cuda.empty_cache()
@@ -428,6 +464,7 @@ def main():
         "parity_spot_check": spot,
         "decode": decode,
         "backward": backward,
+        "context_parallel": cp,
     }
     print(json.dumps(line), flush=True)
 

@@ -10,6 +10,9 @@ hipError_t launch_chain(const ChunkMap& map, int N, int H, const float* s0, floa
                         hipStream_t stream);
 hipError_t launch_output(int C, const ChunkMap& map, int nslots, int H, uint16_t* o, const Work& ws,
                          hipStream_t stream);
+hipError_t launch_chain_map(const ChunkMap& map, int N, int H, float* m_out, const Work& ws, hipStream_t stream);
+hipError_t launch_merge(int R, int HV, const float* M, const float* X, const float* s0, float* s_in,
+                        hipStream_t stream);
 }  // namespace cdr
 
 #include "cdr_bwd_api.h"
@@ -134,7 +137,7 @@ cdr_status chunk_dr_fwd_stages(const cdr_problem* p, const void* q, const void* 
     if (stages < 1 || stages > CDR_STAGE_ALL) return CDR_ERR_UNSUPPORTED;
     if (st != CDR_OK) return st;
     const int64_t tokens = (int64_t)p->B * p->T;
-    if (tokens > 0 && (!q || !k || !v || !g || !beta || !o)) return CDR_ERR_NULL_ARG;
+    if (tokens > 0 && (!q || !k || !v || !g || !beta || ((stages & CDR_STAGE_OUTPUT) && !o))) return CDR_ERR_NULL_ARG;
     if (p->has_initial_state && !initial_state) return CDR_ERR_NULL_ARG;
     if (p->output_final_state && !final_state) return CDR_ERR_NULL_ARG;
     if (p->varlen && !cu_seqlens) return CDR_ERR_NULL_ARG;
@@ -193,6 +196,48 @@ cdr_status chunk_dr_fwd(const cdr_problem* p, const void* q, const void* k, cons
                         float* final_state, void* workspace, size_t workspace_bytes, void* stream) {
     return chunk_dr_fwd_stages(p, q, k, v, g, beta, initial_state, cu_seqlens, o, final_state, workspace,
                                workspace_bytes, CDR_STAGE_ALL, stream);
+}
+
+cdr_status chunk_dr_segment_map(const cdr_problem* p, const void* q, const void* k, const void* v, const float* g,
+                                const float* beta, const int32_t* cu_seqlens, float* M, float* X, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+    const cdr_status st = cdr_check(p);
+    if (st != CDR_OK) return st;
+    if (!M || !X) return CDR_ERR_NULL_ARG;
+    // the offsets X: the forward's final state from a zero start (no output written)
+    cdr_problem pz = *p;
+    pz.has_initial_state = 0;
+    pz.output_final_state = 1;
+    const cdr_status s1 = chunk_dr_fwd_stages(&pz, q, k, v, g, beta, nullptr, cu_seqlens, nullptr, X, workspace,
+                                              workspace_bytes, CDR_STAGE_INTRA | CDR_STAGE_CHAIN, stream);
+    if (s1 != CDR_OK) return s1;
+    // the linear part M: the same chunk maps, from the identity and without their offsets
+    const Layout L = layout(p);
+    char* wb = static_cast<char*>(workspace);
+    cdr::Work ws;
+    ws.Pn = reinterpret_cast<uint16_t*>(wb + L.off[0]);
+    ws.Bm = reinterpret_cast<float*>(wb + L.off[1]);
+    ws.gC = reinterpret_cast<float*>(wb + L.off[4]);
+    ws.Sc = reinterpret_cast<uint16_t*>(wb + L.off[5]);
+    cdr::ChunkMap map;
+    map.cu = p->varlen ? cu_seqlens : nullptr;
+    map.T = p->T;
+    map.N = p->N;
+    map.C = p->chunk_size;
+    map.nchunk = (p->T + p->chunk_size - 1) / p->chunk_size;
+    if (cdr::launch_chain_map(map, p->N, (int)value_heads(p), M, ws, static_cast<hipStream_t>(stream)) != hipSuccess)
+        return CDR_ERR_HIP;
+    return CDR_OK;
+}
+
+cdr_status chunk_dr_merge_states(int32_t R, int32_t HV, int32_t K, int32_t V, const float* M, const float* X,
+                                 const float* initial_state, float* s_in, void* stream) {
+    if (R <= 0 || HV <= 0 || K <= 0 || V <= 0) return CDR_ERR_BAD_SHAPE;
+    if (K != 128 || V != 128) return CDR_ERR_UNSUPPORTED;
+    if (!M || !X || !s_in) return CDR_ERR_NULL_ARG;
+    return cdr::launch_merge(R, HV, M, X, initial_state, s_in, static_cast<hipStream_t>(stream)) == hipSuccess
+               ? CDR_OK
+               : CDR_ERR_HIP;
 }
 
 size_t cdr_bwd_workspace_bytes(const cdr_problem* p) {

@@ -36,17 +36,20 @@ struct ChainOps {
     float4 gc;      // exp(gamma_C) of the wave's state rows
 };
 
+template <bool MAP>
 __device__ __forceinline__ void chain_load(ChainOps& op, const Work& ws, size_t ch, int x, int lane, int q4, int vb) {
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
         const size_t off = ch * KD * KD + frag(x, s, KS) + lane * 8;
         op.ph[s] = *reinterpret_cast<const uint4*>(ws.Pn + off);
     }
-    op.b = *reinterpret_cast<const float4*>(ws.Bm + ch * KD * VD + ((size_t)(x * (VD / 16) + vb) * 64 + lane) * 4);
+    op.b = MAP ? make_float4(0.f, 0.f, 0.f, 0.f)
+               : *reinterpret_cast<const float4*>(ws.Bm + ch * KD * VD + ((size_t)(x * (VD / 16) + vb) * 64 + lane) * 4);
     op.gc = *reinterpret_cast<const float4*>(ws.gC + ch * KD + 16 * x + 4 * q4);
 }
 
 // sbuf: one published state, [2 (high, low)][KS fragments][512] bf16
+template <bool MAP>
 __device__ __forceinline__ void chain_step(const ChainOps& op, f32x4& S, const Work& ws, size_t ch, int x, int lane,
                                            int r16, int q4, int vb, uint16_t* sbuf) {
     // 1. publish the state: pi-order fragment x / 2 of the B operand, half x % 2
@@ -56,7 +59,7 @@ __device__ __forceinline__ void chain_step(const ChainOps& op, f32x4& S, const W
     const int so = frag(0, x >> 1, KS) + fragP(x & 1, r16, q4);
     *reinterpret_cast<uint2*>(sbuf + so) = sh;
     *reinterpret_cast<uint2*>(sbuf + KS * 512 + so) = sl;
-    *reinterpret_cast<uint2*>(ws.Sc + ch * VD * KD + frag(vb, x >> 1, KS) + fragP(x & 1, r16, q4)) = sh;
+    if (!MAP) *reinterpret_cast<uint2*>(ws.Sc + ch * VD * KD + frag(vb, x >> 1, KS) + fragP(x & 1, r16, q4)) = sh;
     lds_barrier();
     // 2. S = exp(gamma_C) S + B - P S
     f32x4 a0 = {op.gc.x * S[0] + op.b.x, op.gc.y * S[1] + op.b.y, op.gc.z * S[2] + op.b.z, op.gc.w * S[3] + op.b.w};
@@ -72,6 +75,10 @@ __device__ __forceinline__ void chain_step(const ChainOps& op, f32x4& S, const W
     for (int e = 0; e < 4; ++e) S[e] = a0[e] + a2[e];
 }
 
+// MAP: the chunk maps without their offsets, S <- (exp(gamma_C) - P) S from S = I, which
+// leaves the sequence's linear map (the final state is S_in M + X, X being the final state
+// from a zero start); no chunk-entry states are written.
+template <bool MAP>
 __global__ __launch_bounds__(CTHREADS) void chain_kernel(ChunkMap map, int H, const float* __restrict__ s0,
                                                           float* __restrict__ s_out, Work ws) {
     __shared__ __attribute__((aligned(16))) uint16_t sbuf[2][2 * KS * 512];  // two published states
@@ -92,7 +99,10 @@ __global__ __launch_bounds__(CTHREADS) void chain_kernel(ChunkMap map, int H, co
     const size_t srow = (((size_t)n * H + h) * VD + 16 * vb + r16) * KD + 16 * x + 4 * q4;
 
     f32x4 S = {0.f, 0.f, 0.f, 0.f};
-    if (s0 != nullptr) {
+    if (MAP) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) S[e] = (16 * x + 4 * q4 + e == 16 * vb + r16) ? 1.f : 0.f;
+    } else if (s0 != nullptr) {
         const float4 v = *reinterpret_cast<const float4*>(s0 + srow);
         S = f32x4{v.x, v.y, v.z, v.w};
     }
@@ -105,12 +115,12 @@ __global__ __launch_bounds__(CTHREADS) void chain_kernel(ChunkMap map, int H, co
     const int last = nchunks - 1;
     auto chunk_of = [&](int c) { return (size_t)(slot0 + max(min(c, last), 0)) * H + h; };
     auto step = [&](ChainOps& next, int cload, const ChainOps& cur, int c, int buf) {
-        chain_load(next, ws, chunk_of(cload), x, lane, q4, vb);
-        chain_step(cur, S, ws, chunk_of(c), x, lane, r16, q4, vb, sbuf[buf]);
+        chain_load<MAP>(next, ws, chunk_of(cload), x, lane, q4, vb);
+        chain_step<MAP>(cur, S, ws, chunk_of(c), x, lane, r16, q4, vb, sbuf[buf]);
     };
     if (nchunks > 0) {
-        chain_load(op0, ws, chunk_of(0), x, lane, q4, vb);
-        chain_load(op1, ws, chunk_of(1), x, lane, q4, vb);
+        chain_load<MAP>(op0, ws, chunk_of(0), x, lane, q4, vb);
+        chain_load<MAP>(op1, ws, chunk_of(1), x, lane, q4, vb);
     }
     for (int c = 0; c < nchunks; c += 6) {
         step(op2, c + 2, op0, c, 0);
@@ -181,7 +191,14 @@ __global__ __launch_bounds__(CTHREADS) void output_kernel(ChunkMap map, int H, u
 hipError_t launch_chain(const ChunkMap& map, int N, int H, const float* s0, float* s_out, const Work& ws,
                         hipStream_t stream) {
     const int groups = (N * H + NXCD - 1) / NXCD;
-    hipLaunchKernelGGL(chain_kernel, dim3(groups * NXCD * NVB), dim3(CTHREADS), 0, stream, map, H, s0, s_out, ws);
+    hipLaunchKernelGGL(chain_kernel<false>, dim3(groups * NXCD * NVB), dim3(CTHREADS), 0, stream, map, H, s0, s_out, ws);
+    return hipGetLastError();
+}
+
+hipError_t launch_chain_map(const ChunkMap& map, int N, int H, float* m_out, const Work& ws, hipStream_t stream) {
+    const int groups = (N * H + NXCD - 1) / NXCD;
+    hipLaunchKernelGGL(chain_kernel<true>, dim3(groups * NXCD * NVB), dim3(CTHREADS), 0, stream, map, H,
+                       (const float*)nullptr, m_out, ws);
     return hipGetLastError();
 }
 

@@ -22,6 +22,7 @@ GATE_PER_HEAD = 1
 
 EXPORTED = ("cdr_check", "cdr_workspace_bytes", "chunk_dr_fwd", "chunk_dr_fwd_stages",
             "cdr_bwd_workspace_bytes", "chunk_dr_bwd", "chunk_dr_bwd_stages",
+            "chunk_dr_segment_map", "chunk_dr_merge_states",
             "cdr_recurrent_check", "chunk_dr_recurrent_fwd", "cdr_status_str", "cdr_version")
 STATE_SEPARATE, STATE_POOL, STATE_POOL_SPEC = 0, 1, 2
 STAGE_INTRA, STAGE_CHAIN, STAGE_OUTPUT, STAGE_ALL = 1, 2, 4, 7
@@ -76,6 +77,10 @@ def load_library(path: str = LIB_PATH):
     lib.chunk_dr_bwd.restype = ctypes.c_int
     lib.chunk_dr_bwd_stages.argtypes = [P] + [vp] * 16 + [ctypes.c_size_t, ctypes.c_int32, vp]
     lib.chunk_dr_bwd_stages.restype = ctypes.c_int
+    lib.chunk_dr_segment_map.argtypes = [P] + [vp] * 8 + [ctypes.c_size_t, vp]
+    lib.chunk_dr_segment_map.restype = ctypes.c_int
+    lib.chunk_dr_merge_states.argtypes = [ctypes.c_int32] * 4 + [vp] * 5
+    lib.chunk_dr_merge_states.restype = ctypes.c_int
     R = ctypes.POINTER(cdr_recurrent_problem)
     lib.cdr_recurrent_check.argtypes = [R]
     lib.cdr_recurrent_check.restype = ctypes.c_int
@@ -119,6 +124,14 @@ def _need(t, name, dtype, shape=None):
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
     if shape is not None and tuple(t.shape) != tuple(shape):
         raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _aligned(t: Optional[torch.Tensor]) -> Optional[torch.Tensor]:
+    """t as a contiguous tensor whose data is 16-byte aligned (a copy when a view is not)."""
+    if t is None:
+        return None
+    t = t.contiguous()
+    return t if t.data_ptr() % 16 == 0 else t.clone()
 
 
 def _dev_ptr(t: torch.Tensor, device) -> int:
@@ -181,9 +194,9 @@ class PreparedForward:
             raise ValueError("inputs must be on a GPU device")
         self.device = device
         # keep references: the library reads these buffers when the kernels run
-        self.inputs = tuple(t.contiguous() for t in (q, k, v, g, beta))
-        self.s0 = initial_state.contiguous() if initial_state is not None else None
-        self.cu = cu_seqlens.contiguous() if cu_seqlens is not None else None
+        self.inputs = tuple(_aligned(t) for t in (q, k, v, g, beta))
+        self.s0 = _aligned(initial_state)
+        self.cu = _aligned(cu_seqlens)
         if out is None:
             out = torch.empty((B, T, HV, V), dtype=torch.bfloat16, device=device)
         else:
@@ -254,6 +267,71 @@ def chunk_dr_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Ten
     return call(stages)
 
 
+def segment_map(q, k, v, g, beta, cu_seqlens=None, chunk_size=64, scale=None,
+                use_qk_l2norm_in_kernel=False, workspace=None):
+    """Affine summary of every sequence (segment): ``final = initial @ M + X``.
+
+    Arguments as :func:`chunk_dr_fwd`.  Returns fp32 ``M [N,HV,K,K]`` and ``X [N,HV,V,K]``.
+    """
+    lib = load_library()
+    B, T, H, K = q.shape
+    HV, V = v.shape[2], v.shape[3]
+    _need(q, "q", torch.bfloat16)
+    _need(k, "k", torch.bfloat16, (B, T, H, K))
+    _need(v, "v", torch.bfloat16)
+    _need(g, "g", torch.float32)
+    _need(beta, "beta", torch.float32, (B, T, HV))
+    per_dim = g.dim() == 4
+    N = cu_seqlens.numel() - 1 if cu_seqlens is not None else B
+    p = make_problem(B, T, H, K, V, N, per_dim, chunk_size, K ** -0.5 if scale is None else scale,
+                     False, True, cu_seqlens is not None, HV, use_qk_l2norm_in_kernel)
+    st = lib.cdr_check(ctypes.byref(p))
+    if st != CDR_OK:
+        _raise(st, "chunk_dr_segment_map")
+    device = q.device
+    if device.type != "cuda":
+        raise ValueError("inputs must be on a GPU device")
+    nbytes = lib.cdr_workspace_bytes(ctypes.byref(p))
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+    M = torch.empty((N, HV, K, K), dtype=torch.float32, device=device)
+    X = torch.empty((N, HV, V, K), dtype=torch.float32, device=device)
+    ins = [_aligned(t) for t in (q, k, v, g, beta)]
+    cu = _aligned(cu_seqlens)
+    ptr = lambda t: None if t is None else _dev_ptr(t, device)  # noqa: E731
+    stream = torch.cuda.current_stream(device).cuda_stream
+    st = lib.chunk_dr_segment_map(ctypes.byref(p), *(ptr(t) for t in ins), ptr(cu), ptr(M), ptr(X),
+                                  ptr(workspace), workspace.numel() * workspace.element_size(), stream)
+    if st != CDR_OK:
+        _raise(st, "chunk_dr_segment_map")
+    return M, X
+
+
+def merge_states(M, X, initial_state=None):
+    """States entering R consecutive segments from their maps: ``s_in[0] = initial_state``,
+    ``s_in[r+1] = s_in[r] @ M[r] + X[r]``.  M ``[R,HV,K,K]``, X ``[R,HV,V,K]``, initial_state
+    ``[HV,V,K]`` or None (zeros).  Returns ``s_in [R+1,HV,V,K]`` (the last is the final state)."""
+    lib = load_library()
+    _need(M, "M", torch.float32)
+    _need(X, "X", torch.float32)
+    R, HV, K, _ = M.shape
+    V = X.shape[2]
+    if tuple(X.shape) != (R, HV, V, K):
+        raise ValueError("X must be [R, HV, V, K]")
+    if initial_state is not None:
+        _need(initial_state, "initial_state", torch.float32, (HV, V, K))
+    device = M.device
+    s_in = torch.empty((R + 1, HV, V, K), dtype=torch.float32, device=device)
+    Mc, Xc = _aligned(M), _aligned(X)          # referenced until the call returns
+    s0 = _aligned(initial_state)
+    ptr = lambda t: None if t is None else _dev_ptr(t, device)  # noqa: E731
+    stream = torch.cuda.current_stream(device).cuda_stream
+    st = lib.chunk_dr_merge_states(R, HV, K, V, ptr(Mc), ptr(Xc), ptr(s0), ptr(s_in), stream)
+    if st != CDR_OK:
+        _raise(st, "chunk_dr_merge_states")
+    return s_in
+
+
 def bwd_workspace_bytes(p: cdr_problem) -> int:
     return load_library().cdr_bwd_workspace_bytes(ctypes.byref(p))
 
@@ -310,10 +388,10 @@ class PreparedBackward:
         if device.type != "cuda":
             raise ValueError("inputs must be on a GPU device")
         self.device = device
-        self.inputs = tuple(t.contiguous() for t in (q, k, v, g, beta, do))
-        self.s0 = initial_state.contiguous() if initial_state is not None else None
-        self.dht = dht.contiguous() if dht is not None else None
-        self.cu = cu_seqlens.contiguous() if cu_seqlens is not None else None
+        self.inputs = tuple(_aligned(t) for t in (q, k, v, g, beta, do))
+        self.s0 = _aligned(initial_state)
+        self.dht = _aligned(dht)
+        self.cu = _aligned(cu_seqlens)
         f32 = dict(dtype=torch.float32, device=device)
         self.grads = (torch.empty((B, T, H, K), **f32), torch.empty((B, T, H, K), **f32),
                       torch.empty((B, T, HV, V), **f32), torch.empty(tuple(g.shape), **f32),
@@ -439,11 +517,11 @@ class PreparedRecurrent:
             raise ValueError("inputs must be on a GPU device")
         self.device = device
         # keep references: the kernel reads these buffers when it runs
-        self.inputs = tuple(t.contiguous() for t in (q, k, v, g, beta))
-        self.s0 = initial_state.contiguous() if initial_state is not None else None
-        self.cu = cu_seqlens.contiguous() if cu_seqlens is not None else None
-        self.idx = ssm_state_indices.contiguous() if ssm_state_indices is not None else None
-        self.acc = num_accepted_tokens.contiguous() if num_accepted_tokens is not None else None
+        self.inputs = tuple(_aligned(t) for t in (q, k, v, g, beta))
+        self.s0 = _aligned(initial_state)
+        self.cu = _aligned(cu_seqlens)
+        self.idx = _aligned(ssm_state_indices)
+        self.acc = _aligned(num_accepted_tokens)
         self.pool = state_pool
         if out is None:
             out = torch.empty((B, T, HV, V), dtype=torch.bfloat16, device=device)

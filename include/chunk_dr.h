@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define CDR_VERSION 4
+#define CDR_VERSION 5
 
 typedef enum {
     CDR_OK = 0,
@@ -157,6 +157,36 @@ cdr_status chunk_dr_fwd_stages(const cdr_problem* p,
                                void* o, float* final_state,
                                void* workspace, size_t workspace_bytes,
                                int32_t stages, void* stream);
+
+/* ------------------------------------------------------------------------------------------
+ * Context parallelism, the part one device computes (page "flash-linear-attention KCP 精度失效
+ * 根因排查手册": a sequence split over ranks, each rank summarising its segment, the summaries
+ * exchanged and merged so that each rank learns the state entering its segment).
+ *
+ * The forward of a segment is affine in its initial state: in the [V, K] layout of the states,
+ * final = initial M + X, where X is the final state from a zero start and M ([K, K]) is the
+ * product of the segment's chunk maps (exp(gamma_C) - P per chunk, transposed to this layout).
+ *
+ * chunk_dr_segment_map: M [N, HV, K, K] and X [N, HV, V, K] of every sequence of problem p
+ *   (each sequence is one segment).  Arguments as chunk_dr_fwd; p->has_initial_state and
+ *   p->output_final_state are ignored.  Uses the forward workspace (cdr_workspace_bytes(p)).
+ * chunk_dr_merge_states: given the maps of R consecutive segments of one sequence (M
+ *   [R, HV, K, K], X [R, HV, V, K], in order) and the state entering the first (initial_state
+ *   [HV, V, K], or NULL for zeros), writes s_in [R + 1, HV, V, K]: s_in[0] = initial_state,
+ *   s_in[r + 1] = s_in[r] M[r] + X[r], the state entering segment r + 1; s_in[R] is the final
+ *   state.  Running segment r's forward from s_in[r] gives the outputs of the unsplit sequence.
+ * On several devices the (M, X) pairs would be all-gathered between the two calls; here they are
+ * in one device's memory.
+ * ------------------------------------------------------------------------------------------ */
+cdr_status chunk_dr_segment_map(const cdr_problem* p,
+                                const void* q, const void* k, const void* v,
+                                const float* g, const float* beta, const int32_t* cu_seqlens,
+                                float* M, float* X,
+                                void* workspace, size_t workspace_bytes, void* stream);
+
+cdr_status chunk_dr_merge_states(int32_t R, int32_t HV, int32_t K, int32_t V,
+                                 const float* M, const float* X, const float* initial_state,
+                                 float* s_in, void* stream);
 
 /* ------------------------------------------------------------------------------------------
  * Backward of the chunked forward.
