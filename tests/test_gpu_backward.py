@@ -136,3 +136,14 @@ def test_backward_workload_one_head(name):
     note(f"[bwd] {name} head 0: " + "  ".join(f"{k} {v:.2e}" for k, v in worst.items()))
     for k, v in worst.items():
         assert v <= TOL, f"{k} norm ratio {v:.3e} > {TOL}"
+
+
+def test_backward_single_token_and_no_tokens():
+    """One token (a pure-tail chunk), and a varlen batch whose sequences are all empty: then
+    the only gradient is dh0 = dht."""
+    inp = make_inputs(1, 1, 1, seed=530, initial_state=True, chunk_size=64)
+    check(inp, "T1")
+    empty = make_inputs(1, 0, 2, seed=531, lengths=(0, 0), initial_state=True, chunk_size=64)
+    do, ht = upstream(empty, 4)
+    got = run_gpu(empty, do, ht, False)
+    assert np.array_equal(got["dh0"], ht.numpy())
