@@ -32,7 +32,7 @@ int64_t num_slots(const cdr_problem* p) {
     return (int64_t)p->B * ((p->T + p->chunk_size - 1) / p->chunk_size);
 }
 
-constexpr int kArrays = 13;
+constexpr int kArrays = 11;
 constexpr int64_t kScratchSlots = 512; // at most this many intra workgroups run at once
 
 size_t scratch_slots(const cdr_problem* p) {
@@ -60,8 +60,6 @@ Layout layout(const cdr_problem* p) {
         nsc * V * C * 2,  // vT
         nsc * K * C * 2,  // kgT_hi
         nsc * K * C * 2,  // kgT_lo
-        nsc * C * C * 2,  // A2s
-        nsc * C * K * 2,  // qgs
     };
     Layout L;
     size_t at = 0;
@@ -158,8 +156,6 @@ cdr_status chunk_dr_fwd_stages(const cdr_problem* p, const void* q, const void* 
     ws.vT = reinterpret_cast<uint16_t*>(wb + L.off[8]);
     ws.kgT_hi = reinterpret_cast<uint16_t*>(wb + L.off[9]);
     ws.kgT_lo = reinterpret_cast<uint16_t*>(wb + L.off[10]);
-    ws.A2s = reinterpret_cast<uint16_t*>(wb + L.off[11]);
-    ws.qgs = reinterpret_cast<uint16_t*>(wb + L.off[12]);
 
     cdr::ChunkMap map;
     map.cu = p->varlen ? cu_seqlens : nullptr;

@@ -229,8 +229,6 @@ struct Work {
     uint16_t* vT;      // (V, C) frag    bf16   v
     uint16_t* kgT_hi;  // (K, C) frag pi bf16   exp(gamma_C - gamma) * k, high part
     uint16_t* kgT_lo;  // (K, C) frag pi bf16   low part
-    uint16_t* A2s;     // (C, C) frag pi bf16   in-chunk output block (j <= i), lower fragments
-    uint16_t* qgs;     // D tiles        bf16   (scale * q * exp(gamma))^T, (C/16) x (K/16) tiles
 };
 
 }  // namespace cdr

@@ -21,16 +21,21 @@
 //        raw q, k (exact bf16 products) and apply the scalar decay afterwards.  Tile rows w
 //        and NT-1-w form one list of NT+1 tiles shared by waves w and w+4.  qg (scratch) is
 //        produced on the diagonal tiles.
-//   INV  T = (I + A)^-1 by block-triangular inversion: the 16x16 diagonal blocks by
-//        forward substitution in fp32, then blocks are merged 16->32->64->128 with
-//        T21 = -T22 (A21 T11), two tile-parallel steps per level on split-bf16 MFMAs.
-//   WU   w = T' (exp(gamma) k) and u = T' v with T' = T diag(beta), split-bf16 MFMAs; wave
-//        w keeps 16 columns of each in registers, as accumulator tiles.
+//   INV  the 16x16 diagonal blocks T_RR = (I + A_RR)^-1 by forward substitution in fp32
+//        (wave R), then M_RJ = T_RR A_RJ (J < R) and T'_RR = T_RR diag(beta) on split-bf16
+//        MFMAs, kept split in LDS.
+//   WU   w = (I + A)^-1 diag(beta) exp(gamma) k and u = (I + A)^-1 diag(beta) v by blocked
+//        forward substitution, Z_R = T'_RR Y_R - sum_{J<R} M_RJ Z_J, on split-bf16 MFMAs:
+//        wave w owns 16 columns of each and keeps the Z tiles in registers, so the solve
+//        runs without barriers.
 //   PQ   the factors of the re-associated chunk step (section M4):
-//          P = kg^T w, B = kg^T u          (split-bf16, they carry the state)
+//          B = kg^T u                      (split-bf16: it enters the state additively)
+//          P = kg^T w                      (single bf16: it is stored with one rounding)
 //          Q = qg - A2 w, U = A2 u         (single bf16, they only reach the output)
 //        The w and u tiles are used as MFMA operands straight from registers (pi order),
-//        kg^T and A2 are staged in LDS by direct global-to-LDS loads issued during WU.
+//        kg^T comes back from scratch at the start of INV and goes to LDS once the A
+//        tiles there are consumed; the A2 and qg tiles stay in registers from AA2 and go to
+//        LDS after the solve.
 #include "cdr_common.h"
 
 #include <atomic>
@@ -54,37 +59,22 @@ struct IntraShape {
     static constexpr int TILE_SZ = 16 * TILE_LD;
     static constexpr int NS = C / 32;                  // 32-wide steps along the chunk
     // LDS regions (bytes)
-    static constexpr int R1 = C * EP_LD * 4;           // Ep; later A tiles and merge scratch
-    static constexpr int R2 = 2 * C * COL_LD * 2;      // column operands; later T tiles
+    static constexpr int R1 = C * EP_LD * 4;           // Ep; later A tiles, then kg^T
+    static constexpr int R2 = 2 * C * COL_LD * 2;      // column operands; later the solve, A2
     static constexpr int RF = (NOFF > NT ? NOFF : NT) * KD * 4;  // tile totals, later F
     static constexpr int RG = 2 * NT * KD * 4;         // gamma and exp(gamma) at tile middles
     static constexpr int RMISC = 3 * C * 4;            // beta, per-head gamma, key row scales
     static constexpr int BYTES = R1 + R2 + RF + RG + RMISC;
-    static_assert((NPAIR + (NT / 2) * (NT / 2)) * TILE_SZ * 4 <= R1, "A tiles + merge scratch");
-    static_assert(NPAIR * TILE_SZ * 4 <= R2, "T tiles");
+    // phase INV/WU in R2: T_RR (fp32 tiles), then -M_RJ (J < R) and T'_RR split into bf16
+    // high and low parts, 1 KiB per tile
+    static constexpr int TD_BYTES = NT * TILE_SZ * 4;
+    static constexpr int SOLVE_BYTES = TD_BYTES + (NOFF + NT) * 1024;
+    static_assert(NPAIR * TILE_SZ * 4 <= R1, "A tiles");
+    static_assert(SOLVE_BYTES <= R2, "solve operands");
     static_assert(BYTES <= 160 * 1024, "LDS budget");
 };
 
 __device__ __forceinline__ int tri(int R, int J) { return R * (R + 1) / 2 + J; }  // J <= R
-
-// 16x16x16 split-bf16 product accumulate: acc += A_tile(fp32, LDS, row-major) * B_tile(fp32, LDS)
-__device__ __forceinline__ void tile_mma(f32x4& acc, const float* At, const float* Bt, int r16, int q4, int ld) {
-    const float4 av = *reinterpret_cast<const float4*>(At + r16 * ld + 4 * q4);
-    const float bb[4] = {Bt[(4 * q4 + 0) * ld + r16], Bt[(4 * q4 + 1) * ld + r16], Bt[(4 * q4 + 2) * ld + r16],
-                         Bt[(4 * q4 + 3) * ld + r16]};
-    uint32_t ah[2], al[2], bh[2], bl[2];
-    split_pk(av.x, av.y, ah[0], al[0]);
-    split_pk(av.z, av.w, ah[1], al[1]);
-    split_pk(bb[0], bb[1], bh[0], bl[0]);
-    split_pk(bb[2], bb[3], bh[1], bl[1]);
-    const bf16x4 Ah = __builtin_bit_cast(bf16x4, make_uint2(ah[0], ah[1]));
-    const bf16x4 Al = __builtin_bit_cast(bf16x4, make_uint2(al[0], al[1]));
-    const bf16x4 Bh = __builtin_bit_cast(bf16x4, make_uint2(bh[0], bh[1]));
-    const bf16x4 Bl = __builtin_bit_cast(bf16x4, make_uint2(bl[0], bl[1]));
-    acc = mfma16(Ah, Bh, acc);
-    acc = mfma16(Al, Bh, acc);
-    acc = mfma16(Ah, Bl, acc);
-}
 
 __device__ __forceinline__ void tile_store(float* Tt, const f32x4& v, float sgn, int r16, int q4, int ld) {
 #pragma unroll
@@ -174,8 +164,6 @@ __device__ __forceinline__ void intra_item(
     float* grow = bet + C;                                                        // [C] per-head gamma
     float* knr = grow + C;                                                        // [C] key row scales
     float* Atile = reinterpret_cast<float*>(smem);                                // after AA2
-    float* Pscr = Atile + S::NPAIR * S::TILE_SZ;                                  // merge scratch
-    float* Ttile = reinterpret_cast<float*>(smem + S::R1);
 
     // laundered so that the per-thread offsets derived from it are recomputed for every item
     // instead of being hoisted out of the item loop and held in registers across it
@@ -196,7 +184,10 @@ __device__ __forceinline__ void intra_item(
     const size_t basek = (size_t)tok0 * rsk + (size_t)(h / (H / Hk)) * KD;
 
     // Row operands of phase AA2 (raw k and q rows of the wave's two tile rows), loaded
-    // before phase E so that their latency is hidden behind it.
+    // before phase E so that their latency is hidden behind it.  The loads are unconditional
+    // (rows past the end read the last row) and rows past the end are zeroed after phase E:
+    // a load that only some lanes need would be issued under a branch, and the wait count
+    // the compiler derives after such a branch covers every load in flight.
     // waves w and w + 4 share tile rows cp = w % 4 and NT-1-cp: NT+1 tiles, HF for the first
     const int cp = wave & 3, part = wave >> 2;
     const bool aa_active = cp < NT / 2;
@@ -206,11 +197,9 @@ __device__ __forceinline__ void intra_item(
     for (int o = 0; o < 2; ++o)
 #pragma unroll
         for (int ks = 0; ks < KD / 32; ++ks) {
-            const int i = 16 * Rown[o] + r16, ic = min(max(i, 0), rows - 1);
-            const uint4 kx = *reinterpret_cast<const uint4*>(k + basek + (size_t)ic * rsk + 32 * ks + 8 * q4);
-            const uint4 qx = *reinterpret_cast<const uint4*>(q + basek + (size_t)ic * rsk + 32 * ks + 8 * q4);
-            kfr[o][ks] = (i < rows) ? kx : make_uint4(0, 0, 0, 0);
-            qfr[o][ks] = (i < rows) ? qx : make_uint4(0, 0, 0, 0);
+            const int ic = min(16 * Rown[o] + r16, rows - 1);
+            kfr[o][ks] = *reinterpret_cast<const uint4*>(k + basek + (size_t)ic * rsk + 32 * ks + 8 * q4);
+            qfr[o][ks] = *reinterpret_cast<const uint4*>(q + basek + (size_t)ic * rsk + 32 * ks + 8 * q4);
         }
     // ------------------------------------------------------------------ phase E
     {
@@ -358,6 +347,15 @@ __device__ __forceinline__ void intra_item(
     lds_barrier();
 
     // ------------------------------------------------------------------ phase AA2
+#pragma unroll
+    for (int o = 0; o < 2; ++o)
+        if (16 * Rown[o] + r16 >= rows) {
+#pragma unroll
+            for (int ks = 0; ks < KD / 32; ++ks) {
+                kfr[o][ks] = make_uint4(0u, 0u, 0u, 0u);
+                qfr[o][ks] = make_uint4(0u, 0u, 0u, 0u);
+            }
+        }
     // L2 scales of the wave's own q and k rows: lanes r16 + 16 q4 (q4 = 0..3) share a row
     float rk2[2] = {1.f, 1.f}, rq2[2] = {1.f, 1.f};
     if constexpr (L2N) {
@@ -383,10 +381,17 @@ __device__ __forceinline__ void intra_item(
             rq2[o] = rsqrtf(sq + L2N_EPS);
         }
     }
+    // A tiles go to LDS after the phase; the A2 fragments and the qg tile of the wave's
+    // diagonal tile stay in registers until phase PQ (no scratch round trip)
     f32x4 accA[S::SMAX];
+    uint2 a2keep[S::SMAX];
+    uint4 qgkeep[KD / 32];
+#pragma unroll
+    for (int ks = 0; ks < KD / 32; ++ks) qgkeep[ks] = make_uint4(0u, 0u, 0u, 0u);
 #pragma unroll
     for (int s = 0; s < S::SMAX; ++s) {
         accA[s] = f32x4{0.f, 0.f, 0.f, 0.f};
+        a2keep[s] = make_uint2(0u, 0u);
         const int p = (part ? S::HF : 0) + s;  // position in the row pair's tile list
         if (!aa_active || p >= NT + 1 || (part == 0 && s >= S::HF)) continue;
         const int o = (p <= cp) ? 0 : 1;
@@ -428,7 +433,7 @@ __device__ __forceinline__ void intra_item(
                     pq.y = pack_bf2(scale * qf[2] * ep[2] * eg[2], scale * qf[3] * ep[3] * eg[3]);
                     pq.z = pack_bf2(scale * qf[4] * ep[4] * eg[4], scale * qf[5] * ep[5] * eg[5]);
                     pq.w = pack_bf2(scale * qf[6] * ep[6] * eg[6], scale * qf[7] * ep[7] * eg[7]);
-                    store_qg(ws.qgs + sc * C * KD, R, ks, r16, q4, pq);
+                    qgkeep[ks] = pq;
                 }
                 uint4 ah, al, aq;
                 split_pk(kf[0] * ep[0], kf[1] * ep[1], ah.x, al.x);
@@ -458,7 +463,7 @@ __device__ __forceinline__ void intra_item(
                     pq.y = pack_bf2(f * qf[2], f * qf[3]);
                     pq.z = pack_bf2(f * qf[4], f * qf[5]);
                     pq.w = pack_bf2(f * qf[6], f * qf[7]);
-                    store_qg(ws.qgs + sc * C * KD, R, ks, r16, q4, pq);
+                    qgkeep[ks] = pq;
                 }
                 acc = mfma32(as_bf16x8(krv), b, acc);
                 acc2 = mfma32(b, as_bf16x8(qrv), acc2);   // A2^T tile: rows j, columns i
@@ -483,13 +488,10 @@ __device__ __forceinline__ void intra_item(
             accA[s][rr] = (jj < ii) ? a * bet[ii] : 0.f;
             a2v[rr] = (j2 <= i2) ? a2 * scale : 0.f;
         }
-        uint16_t* a2f = ws.A2s + sc * C * C + frag(R, J >> 1, C / 32);
-        *reinterpret_cast<uint2*>(a2f + fragP(J & 1, r16, q4)) = make_uint2(pack_bf2(a2v[0], a2v[1]), pack_bf2(a2v[2], a2v[3]));
-        // tile (R, R + 1) shares the fragment of an even diagonal tile and is zero
-        if (J == R && (R & 1) == 0) *reinterpret_cast<uint2*>(a2f + fragP(1, r16, q4)) = make_uint2(0u, 0u);
+        a2keep[s] = make_uint2(pack_bf2(a2v[0], a2v[1]), pack_bf2(a2v[2], a2v[3]));
     }
-    // the global stores of phases E and AA2 complete before the barrier: from here on the
-    // whole workgroup reads them back
+    // the global stores of phase E complete before the barrier: from here on the whole
+    // workgroup reads them back
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     lds_barrier();
 
@@ -503,6 +505,21 @@ __device__ __forceinline__ void intra_item(
         bwl_f[s] = *reinterpret_cast<const uint4*>(ws.bwT_lo + off);
         vt_f[s] = *reinterpret_cast<const uint4*>(ws.vT + off);
     }
+    // kg^T fragments (high, then low) of phase PQ, the same number per wave; they go to LDS
+    // (R1) once the A tiles there are no longer read
+    constexpr int NKG = 2 * (KD / 16) * NS;
+    constexpr int KPW = NKG / 2 / IWAVES;  // fragments of each part per wave
+    static_assert(NKG % (2 * IWAVES) == 0, "kg^T fragments per wave");
+    static_assert(NKG * 1024 <= S::R1, "kg^T staging");
+    u32x4v kgr[2][KPW];  // a vector type: a struct copy would go through private memory
+#pragma unroll
+    for (int hl = 0; hl < 2; ++hl)
+#pragma unroll
+        for (int i = 0; i < KPW; ++i) {
+            const int f = wave + IWAVES * i;  // fragment (f / NS, f % NS) of the part
+            const uint16_t* src = (hl ? ws.kgT_lo : ws.kgT_hi) + sc * KD * C + frag(f / NS, f % NS, C / 32);
+            kgr[hl][i] = *reinterpret_cast<const u32x4v*>(src + lane * 8);
+        }
 #pragma unroll
     for (int s = 0; s < S::SMAX; ++s) {
         const int p = (part ? S::HF : 0) + s;
@@ -513,157 +530,189 @@ __device__ __forceinline__ void intra_item(
         tile_store(Atile + tri(R, J) * S::TILE_SZ, accA[s], 1.f, r16, q4, S::TILE_LD);
     }
     lds_barrier();
-    {   // diagonal blocks: T_RR = (I + A_RR)^-1, wave R, lane r16 owns column r16
+    // R2 (the column operands of AA2) is free from here on
+    float* Tdg = reinterpret_cast<float*>(smem + S::R1);                        // T_RR, fp32 tiles
+    uint16_t* Mpre = reinterpret_cast<uint16_t*>(smem + S::R1 + S::TD_BYTES);  // -M_RJ split, J < R
+    uint16_t* Tpre = Mpre + S::NOFF * 512;                                      // T'_RR split
+    {   // wave R: T_RR = (I + A_RR)^-1, then M_RJ = T_RR A_RJ for J < R and T'_RR = T_RR diag(beta)
         const int R = wave;
-        if (q4 == 0 && R < NT) {
-            const float* Ad = Atile + tri(R, R) * S::TILE_SZ;
-            const int jc = r16;
-            float t[16];
+        if (R < NT) {
+            float* Td = Tdg + R * S::TILE_SZ;
+            if (q4 == 0) {  // forward substitution, lane r16 owns column r16
+                const float* Ad = Atile + tri(R, R) * S::TILE_SZ;
+                const int jc = r16;
+                float t[16];
 #pragma unroll
-            for (int ii = 0; ii < 16; ++ii) {
-                float acc = 0.f;
+                for (int ii = 0; ii < 16; ++ii) {
+                    float acc = 0.f;
 #pragma unroll
-                for (int m = 0; m < ii; ++m) acc += Ad[ii * S::TILE_LD + m] * t[m];
-                t[ii] = (ii < jc) ? 0.f : ((ii == jc) ? 1.f : -acc);
+                    for (int m = 0; m < ii; ++m) acc += Ad[ii * S::TILE_LD + m] * t[m];
+                    t[ii] = (ii < jc) ? 0.f : ((ii == jc) ? 1.f : -acc);
+                }
+#pragma unroll
+                for (int ii = 0; ii < 16; ++ii) Td[ii * S::TILE_LD + jc] = t[ii];
             }
-            float* Td = Ttile + tri(R, R) * S::TILE_SZ;
-#pragma unroll
-            for (int ii = 0; ii < 16; ++ii) Td[ii * S::TILE_LD + jc] = t[ii];
+            wave_lds_sync();
+            // lane (r16, q4): row r16, columns 4 q4 .. + 3 of T_RR, the B operand of
+            // M_RJ^T = A_RJ^T T_RR^T on the 16x16x16 instruction
+            const float4 tr = *reinterpret_cast<const float4*>(Td + r16 * S::TILE_LD + 4 * q4);
+            uint2 bh, bl;
+            split_pk(tr.x, tr.y, bh.x, bl.x);
+            split_pk(tr.z, tr.w, bh.y, bl.y);
+            const bf16x4 Bh = __builtin_bit_cast(bf16x4, bh), Bl = __builtin_bit_cast(bf16x4, bl);
+            {   // T'_RR: column c of T_RR times beta of chunk row 16 R + c; row r keeps its 16 high
+                // parts, then its 16 low parts
+                const float* br = bet + 16 * R + 4 * q4;
+                uint2 h, l;
+                split_pk(tr.x * br[0], tr.y * br[1], h.x, l.x);
+                split_pk(tr.z * br[2], tr.w * br[3], h.y, l.y);
+                *reinterpret_cast<uint2*>(Tpre + R * 512 + r16 * 32 + 4 * q4) = h;
+                *reinterpret_cast<uint2*>(Tpre + R * 512 + r16 * 32 + 16 + 4 * q4) = l;
+            }
+            for (int J = 0; J < R; ++J) {
+                // A operand: column r16 of A_RJ, rows 4 q4 .. + 3
+                const float* Aj = Atile + tri(R, J) * S::TILE_SZ + 4 * q4 * S::TILE_LD + r16;
+                uint2 ah, al;
+                split_pk(Aj[0], Aj[S::TILE_LD], ah.x, al.x);
+                split_pk(Aj[2 * S::TILE_LD], Aj[3 * S::TILE_LD], ah.y, al.y);
+                const bf16x4 Ah = __builtin_bit_cast(bf16x4, ah), Al = __builtin_bit_cast(bf16x4, al);
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+                acc = mfma16(Ah, Bh, acc);
+                acc = mfma16(Al, Bh, acc);
+                acc = mfma16(Ah, Bl, acc);
+                // acc[e] = M_RJ[r16][4 q4 + e]; kept negated, high parts then low parts
+                uint2 h, l;
+                split_pk(-acc[0], -acc[1], h.x, l.x);
+                split_pk(-acc[2], -acc[3], h.y, l.y);
+                uint16_t* mp = Mpre + (R * (R - 1) / 2 + J) * 512 + r16 * 16 + 4 * q4;
+                *reinterpret_cast<uint2*>(mp) = h;
+                *reinterpret_cast<uint2*>(mp + 256) = l;
+            }
         }
     }
     lds_barrier();
-    // merge levels: blocks of m tiles, pairs (2p, 2p+1): T21 = -T22 (A21 T11)
-#pragma unroll
-    for (int m = 1; m < NT; m *= 2) {
-        const int npair = NT / (2 * m);
-        const int ntile = npair * m * m;      // output tiles per step
-        // step 1: P[r][c] = sum_{x >= c} A21[r][x] T11[x][c]
-        for (int t = wave; t < ntile; t += IWAVES) {
-            const int p = t / (m * m), rc = t % (m * m);
-            const int r = (rc / m + rc % m) % m, c = rc % m;   // spread the long sums over waves
-            const int b1 = 2 * p * m, b2 = b1 + m;
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            for (int x = c; x < m; ++x)
-                tile_mma(acc, Atile + tri(b2 + r, b1 + x) * S::TILE_SZ, Ttile + tri(b1 + x, b1 + c) * S::TILE_SZ,
-                         r16, q4, S::TILE_LD);
-            tile_store(Pscr + (p * m * m + r * m + c) * S::TILE_SZ, acc, 1.f, r16, q4, S::TILE_LD);
-        }
-        lds_barrier();
-        // step 2: T21[r][c] = -sum_{x <= r} T22[r][x] P[x][c]
-        for (int t = wave; t < ntile; t += IWAVES) {
-            const int p = t / (m * m), rc = t % (m * m);
-            const int r = rc / m, c = (rc / m + rc % m) % m;
-            const int b1 = 2 * p * m, b2 = b1 + m;
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            for (int x = 0; x <= r; ++x)
-                tile_mma(acc, Ttile + tri(b2 + r, b2 + x) * S::TILE_SZ, Pscr + (p * m * m + x * m + c) * S::TILE_SZ,
-                         r16, q4, S::TILE_LD);
-            tile_store(Ttile + tri(b2 + r, b1 + c) * S::TILE_SZ, acc, -1.f, r16, q4, S::TILE_LD);
-        }
-        lds_barrier();
-    }
 
     // ------------------------------------------------------------------ phase WU
-    // kg^T and A2 to LDS (R1 is free since the last merge barrier)
-    constexpr int NKG = 2 * (KD / 16) * NS;       // kg^T fragments (high, then low)
     constexpr int NA2 = NT + (NT / 2) * (NT / 2 - 1);  // lower A2 fragments
-    uint16_t* kgL = reinterpret_cast<uint16_t*>(smem);                              // R1: dead after INV
-    uint16_t* a2L = reinterpret_cast<uint16_t*>(smem + S::R1 + S::NPAIR * S::TILE_SZ * 4);  // R2 after the T tiles
-    static_assert(NKG * 1024 <= S::R1, "kg^T staging");
-    static_assert(S::NPAIR * S::TILE_SZ * 4 + NA2 * 1024 <= S::R2, "A2 staging");
-    for (int f = wave; f < NKG + NA2; f += IWAVES) {
-        if (f < NKG) {
-            const int hl = f / (NKG / 2), x = (f % (NKG / 2)) / NS, s = f % NS;
-            const uint16_t* src = (hl ? ws.kgT_lo : ws.kgT_hi) + sc * KD * C + frag(x, s, C / 32);
-            frag_to_lds(src, kgL + f * 512, lane);
-        } else {
-            int I = 0;
-            while (I + 1 < NT && a2_slot(I + 1, 0) <= f - NKG) ++I;
-            const int s = f - NKG - a2_slot(I, 0);
-            frag_to_lds(ws.A2s + sc * C * C + frag(I, s, C / 32), a2L + (f - NKG) * 512, lane);
-        }
-    }
-    // accw[R]: w tile (rows 16 R + 4 q4 + e, column 16 dt + r16); accu[R] the same for u
-    f32x4 accw[NT], accu[NT];
+    uint16_t* kgL = reinterpret_cast<uint16_t*>(smem);  // kg^T over the A tiles (R1)
+#pragma unroll
+    for (int hl = 0; hl < 2; ++hl)
+#pragma unroll
+        for (int i = 0; i < KPW; ++i)
+            *reinterpret_cast<u32x4v*>(kgL + (hl * (NKG / 2) + wave + IWAVES * i) * 512 + lane * 8) = kgr[hl][i];
+    // Blocked forward substitution for [w | u] = (I + A)^-1 diag(beta) [exp(gamma) k | v], wave
+    // dt producing columns 16 dt .. + 15 of each:  Z_R = T'_RR Y_R - sum_{J<R} M_RJ Z_J.  The Z
+    // tiles stay in registers, split, in the D layout (lane (r16, q4), element e: row
+    // 16 R + 4 q4 + e, column 16 dt + r16), which two at a time are the pi-order B operand of
+    // the 16x16x32 instruction.
+    uint2 wzh[NT], wzl[NT], uzh[NT], uzl[NT];
 #pragma unroll
     for (int R = 0; R < NT; ++R) {
-        accw[R] = f32x4{0.f, 0.f, 0.f, 0.f};
-        accu[R] = f32x4{0.f, 0.f, 0.f, 0.f};
+        f32x4 aw = {0.f, 0.f, 0.f, 0.f}, au = aw;
+        {   // T'_RR Y_R: Y rows 32 (R / 2) + 8 q4 + i in the normal-order fragment R / 2
+            uint4 th = make_uint4(0u, 0u, 0u, 0u), tl = th;
+            if ((q4 >> 1) == (R & 1)) {
+                const uint4* tp = reinterpret_cast<const uint4*>(Tpre + R * 512 + r16 * 32);
+                th = tp[q4 & 1];
+                tl = tp[2 + (q4 & 1)];
+            }
+            const bf16x8 thi = as_bf16x8(th), tlo = as_bf16x8(tl);
+            const int s = R >> 1;
+            aw = mfma32(thi, as_bf16x8(bwh_f[s]), aw);
+            aw = mfma32(tlo, as_bf16x8(bwh_f[s]), aw);
+            aw = mfma32(thi, as_bf16x8(bwl_f[s]), aw);
+            au = mfma32(thi, as_bf16x8(vt_f[s]), au);
+            au = mfma32(tlo, as_bf16x8(vt_f[s]), au);
+        }
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
-            if (2 * s > R) break;
-            const int J = 2 * s + (q4 >> 1);
-            const int jb = 32 * s + 8 * q4;
-            float tv[8];
-            if (J <= R) {
-                const float4* tp = reinterpret_cast<const float4*>(Ttile + tri(R, J) * S::TILE_SZ + r16 * S::TILE_LD +
-                                                                   8 * (q4 & 1));
-                const float4 t0 = tp[0], t1 = tp[1];
-                tv[0] = t0.x; tv[1] = t0.y; tv[2] = t0.z; tv[3] = t0.w;
-                tv[4] = t1.x; tv[5] = t1.y; tv[6] = t1.z; tv[7] = t1.w;
-            } else {
-#pragma unroll
-                for (int e = 0; e < 8; ++e) tv[e] = 0.f;
-            }
-            uint4 th, tl;
-            split_pk(tv[0] * bet[jb + 0], tv[1] * bet[jb + 1], th.x, tl.x);
-            split_pk(tv[2] * bet[jb + 2], tv[3] * bet[jb + 3], th.y, tl.y);
-            split_pk(tv[4] * bet[jb + 4], tv[5] * bet[jb + 5], th.z, tl.z);
-            split_pk(tv[6] * bet[jb + 6], tv[7] * bet[jb + 7], th.w, tl.w);
-            const bf16x8 thi = as_bf16x8(th), tlo = as_bf16x8(tl);
-            const bf16x8 bwh = as_bf16x8(bwh_f[s]), bwl = as_bf16x8(bwl_f[s]), vv = as_bf16x8(vt_f[s]);
-            accw[R] = mfma32(thi, bwh, accw[R]);
-            accw[R] = mfma32(tlo, bwh, accw[R]);
-            accw[R] = mfma32(thi, bwl, accw[R]);
-            accu[R] = mfma32(thi, vv, accu[R]);
-            accu[R] = mfma32(tlo, vv, accu[R]);
+            if (2 * s >= R) break;
+            // pi-order pair (2 s, 2 s + 1); the second half is zero when 2 s + 1 = R
+            const bool two = 2 * s + 1 < R;
+            const uint16_t* m0 = Mpre + (R * (R - 1) / 2 + 2 * s) * 512 + r16 * 16 + 4 * q4;
+            const uint2 z2 = make_uint2(0u, 0u);
+            const uint2 mh0 = *reinterpret_cast<const uint2*>(m0);
+            const uint2 ml0 = *reinterpret_cast<const uint2*>(m0 + 256);
+            const uint2 mh1 = two ? *reinterpret_cast<const uint2*>(m0 + 512) : z2;
+            const uint2 ml1 = two ? *reinterpret_cast<const uint2*>(m0 + 768) : z2;
+            const bf16x8 Mh = as_bf16x8(make_uint4(mh0.x, mh0.y, mh1.x, mh1.y));
+            const bf16x8 Ml = as_bf16x8(make_uint4(ml0.x, ml0.y, ml1.x, ml1.y));
+            const uint2 wh1 = two ? wzh[2 * s + 1] : z2, wl1 = two ? wzl[2 * s + 1] : z2;
+            const uint2 uh1 = two ? uzh[2 * s + 1] : z2, ul1 = two ? uzl[2 * s + 1] : z2;
+            const bf16x8 Zwh = as_bf16x8(make_uint4(wzh[2 * s].x, wzh[2 * s].y, wh1.x, wh1.y));
+            const bf16x8 Zwl = as_bf16x8(make_uint4(wzl[2 * s].x, wzl[2 * s].y, wl1.x, wl1.y));
+            const bf16x8 Zuh = as_bf16x8(make_uint4(uzh[2 * s].x, uzh[2 * s].y, uh1.x, uh1.y));
+            const bf16x8 Zul = as_bf16x8(make_uint4(uzl[2 * s].x, uzl[2 * s].y, ul1.x, ul1.y));
+            aw = mfma32(Mh, Zwh, aw);
+            aw = mfma32(Ml, Zwh, aw);
+            aw = mfma32(Mh, Zwl, aw);
+            au = mfma32(Mh, Zuh, au);
+            au = mfma32(Ml, Zuh, au);
+            au = mfma32(Mh, Zul, au);
         }
+        split_pk(aw[0], aw[1], wzh[R].x, wzl[R].x);
+        split_pk(aw[2], aw[3], wzh[R].y, wzl[R].y);
+        split_pk(au[0], au[1], uzh[R].x, uzl[R].x);
+        split_pk(au[2], au[3], uzh[R].y, uzl[R].y);
     }
 
     // ------------------------------------------------------------------ phase PQ
-    uint2 qgv[NT];  // (qg)^T tiles (I, dt) used after the P, B loop
+    lds_barrier();  // every wave is done with the solve operands in R2
+    // the A2 fragments and qg tiles kept since phase AA2 go to R2
+    uint16_t* a2L = reinterpret_cast<uint16_t*>(smem + S::R1);  // lower A2 fragments, pi order
+    uint16_t* qgL = a2L + NA2 * 512;                             // (qg)^T D tiles
+    static_assert(NA2 * 1024 + C * KD * 2 <= S::R2, "A2 and qg staging");
 #pragma unroll
-    for (int I = 0; I < NT; ++I)
-        qgv[I] = *reinterpret_cast<const uint2*>(ws.qgs + sc * C * KD + ((size_t)(I * (KD / 16) + dt) * 64 + lane) * 4);
-    e_load<C, PER_DIM>(ein, k, v, g, beta, map, H, Hk, next_item, tid);  // next item, in flight through PQ
-    // w and u as pi-order operands: tiles 2s and 2s+1 give the 32 contracted rows of step s
-    uint4 wh[NS], wl[NS], uh[NS], ul[NS];
+    for (int s = 0; s < S::SMAX; ++s) {
+        const int p = (part ? S::HF : 0) + s;
+        if (!aa_active || p >= NT + 1 || (part == 0 && s >= S::HF)) continue;
+        const int o = (p <= cp) ? 0 : 1;
+        const int R = Rown[o];
+        const int J = (o == 0) ? p : p - cp - 1;
+        uint16_t* f = a2L + a2_slot(R, J >> 1) * 512;
+        *reinterpret_cast<uint2*>(f + fragP(J & 1, r16, q4)) = a2keep[s];
+        // tile (R, R + 1) shares the fragment of an even diagonal tile and is zero
+        if (J == R && (R & 1) == 0) *reinterpret_cast<uint2*>(f + fragP(1, r16, q4)) = make_uint2(0u, 0u);
+    }
+    if (aa_active) {  // each active wave owns one diagonal tile: tile row cp (first part) or NT-1-cp
+        const int Rd = part ? NT - 1 - cp : cp;
+#pragma unroll
+        for (int ks = 0; ks < KD / 32; ++ks) store_qg(qgL, Rd, ks, r16, q4, qgkeep[ks]);
+    }
+    // w and u as pi-order operands: tiles 2s and 2s+1 give the 32 contracted rows of step s.
+    // w only reaches P and Q, both formed from its high part; u keeps its split for B.
+    uint4 wh[NS], uh[NS], ul[NS];
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
-        split_pk(accw[2 * s][0], accw[2 * s][1], wh[s].x, wl[s].x);
-        split_pk(accw[2 * s][2], accw[2 * s][3], wh[s].y, wl[s].y);
-        split_pk(accw[2 * s + 1][0], accw[2 * s + 1][1], wh[s].z, wl[s].z);
-        split_pk(accw[2 * s + 1][2], accw[2 * s + 1][3], wh[s].w, wl[s].w);
-        split_pk(accu[2 * s][0], accu[2 * s][1], uh[s].x, ul[s].x);
-        split_pk(accu[2 * s][2], accu[2 * s][3], uh[s].y, ul[s].y);
-        split_pk(accu[2 * s + 1][0], accu[2 * s + 1][1], uh[s].z, ul[s].z);
-        split_pk(accu[2 * s + 1][2], accu[2 * s + 1][3], uh[s].w, ul[s].w);
+        wh[s] = make_uint4(wzh[2 * s].x, wzh[2 * s].y, wzh[2 * s + 1].x, wzh[2 * s + 1].y);
+        uh[s] = make_uint4(uzh[2 * s].x, uzh[2 * s].y, uzh[2 * s + 1].x, uzh[2 * s + 1].y);
+        ul[s] = make_uint4(uzl[2 * s].x, uzl[2 * s].y, uzl[2 * s + 1].x, uzl[2 * s + 1].y);
     }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // direct-to-LDS copies of this wave
-    __syncthreads();  // staged kg^T and A2 have landed in LDS
+    lds_barrier();  // staged kg^T, A2 and qg are in LDS
+    uint2 qgv[NT];    // (qg)^T tiles (I, dt)
+#pragma unroll
+    for (int I = 0; I < NT; ++I) qgv[I] = *reinterpret_cast<const uint2*>(qgL + ((I * (KD / 16) + dt) * 64 + lane) * 4);
+    // the next item's phase E inputs, in flight through the rest of PQ (issued after the wait
+    // above, which would otherwise take them in)
+    e_load<C, PER_DIM>(ein, k, v, g, beta, map, H, Hk, next_item, tid);
     // P^T tile (rows d in block dt, columns k in block x) = w^T kg; B tile (rows k in x,
     // columns v in dt) = kg^T u.  -P goes out in pi order as the A operand of -P S.
 #pragma unroll 1
     for (int x = 0; x < KD / 16; ++x) {
-        // four independent accumulation chains
-        f32x4 p0 = {0.f, 0.f, 0.f, 0.f}, p1 = p0, b0 = p0, b1 = p0;
+        // P (stored with one bf16 rounding) from the high parts only; B split
+        f32x4 pt = {0.f, 0.f, 0.f, 0.f}, b0 = pt, b1 = pt;
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
             const bf16x8 kh = as_bf16x8(*reinterpret_cast<const uint4*>(kgL + (x * NS + s) * 512 + lane * 8));
             const bf16x8 kl = as_bf16x8(*reinterpret_cast<const uint4*>(kgL + (NKG / 2 + x * NS + s) * 512 + lane * 8));
-            p0 = mfma32(as_bf16x8(wh[s]), kh, p0);
+            pt = mfma32(as_bf16x8(wh[s]), kh, pt);
             b0 = mfma32(kh, as_bf16x8(uh[s]), b0);
-            p1 = mfma32(as_bf16x8(wl[s]), kh, p1);
             b1 = mfma32(kl, as_bf16x8(uh[s]), b1);
-            p1 = mfma32(as_bf16x8(wh[s]), kl, p1);
             b1 = mfma32(kh, as_bf16x8(ul[s]), b1);
         }
-        f32x4 pt, bt;
+        f32x4 bt;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            pt[e] = p0[e] + p1[e];
-            bt[e] = b0[e] + b1[e];
-        }
+        for (int e = 0; e < 4; ++e) bt[e] = b0[e] + b1[e];
         const uint2 ph = make_uint2(pack_bf2(-pt[0], -pt[1]), pack_bf2(-pt[2], -pt[3]));
         const size_t po = ch * KD * KD + frag(x, dt >> 1, KD / 32) + fragP(dt & 1, r16, q4);
         st_nt(reinterpret_cast<uint2*>(ws.Pn + po), ph);
