@@ -9,7 +9,8 @@
 //        issues all of its loads (g, k, v) at once.  gamma = prefix sum of g inside the tile
 //        plus the totals of the tiles above (through LDS).  Per-element decay factors
 //        relative to the tile's middle row m, and the element-wise outputs: exp(gamma_C),
-//        kg = exp(gamma_C - gamma) k (split), exp(gamma) k (split) and v, fragment-major
+//        kg = exp(gamma_C - gamma) k (split), exp(gamma) k (single bf16: w only reaches P
+//        and Q, which are formed from its own single bf16 rounding) and v, fragment-major
 //        (scratch read back by this workgroup).
 //   AA2  16x16 tiles of A (strictly lower, times beta) and A2 (lower incl. diagonal, times
 //        scale) on bf16 MFMA.  Per-dimension gates enter the operands through the tile
@@ -279,7 +280,7 @@ __device__ __forceinline__ void intra_item(
 #pragma unroll
             for (int hh = 0; hh < 2; ++hh) {
                 // column-major outputs of rows 16R + 8hh .. +7, two bf16 (consecutive rows) per register
-                uint32_t bwh[2][4], bwl[2][4], kgh[2][4], kgl[2][4], vtp[2][4];
+                uint32_t bwh[2][4], kgh[2][4], kgl[2][4], vtp[2][4];
 #pragma unroll
                 for (int e2 = 0; e2 < 4; ++e2) {
                     float kf[2][2], ep[2][2], em[2][2];   // [row of the pair][column]
@@ -292,7 +293,7 @@ __device__ __forceinline__ void intra_item(
                         for (int c = 0; c < 2; ++c) {
                             const float x = gm2[ii][c] - gmv[c];
                             ep[rr][c] = ex(x);     // exp(gamma_i - gamma_m)
-                            em[rr][c] = ex(-x);    // exp(gamma_m - gamma_i)
+                            em[rr][c] = __builtin_amdgcn_rcpf(ep[rr][c]);  // exp(gamma_m - gamma_i)
                         }
                         if constexpr (PER_DIM) {
                             const int i = 16 * R + ii;
@@ -306,7 +307,7 @@ __device__ __forceinline__ void intra_item(
 #pragma unroll
                     for (int c = 0; c < 2; ++c) {
                         // exp(gamma_i) k (beta enters through T diag(beta)) and exp(gamma_C - gamma_i) k
-                        split_pk(kf[0][c] * (e_gm[c] * ep[0][c]), kf[1][c] * (e_gm[c] * ep[1][c]), bwh[c][e2], bwl[c][e2]);
+                        bwh[c][e2] = pack_bf2(kf[0][c] * (e_gm[c] * ep[0][c]), kf[1][c] * (e_gm[c] * ep[1][c]));
                         split_pk(kf[0][c] * (em[0][c] * e_cm[c]), kf[1][c] * (em[1][c] * e_cm[c]), kgh[c][e2], kgl[c][e2]);
                     }
                     const uint32_t v0 = vr[8 * hh + 2 * e2], v1 = vr[8 * hh + 2 * e2 + 1];
@@ -319,8 +320,7 @@ __device__ __forceinline__ void intra_item(
                     // are exactly the 16-byte slot of lane (d % 16) + 16 (2 (R % 2) + hh)
                     const int d = d0 + c;
                     const size_t tcol = sc * KD * C + frag(d >> 4, R >> 1, C / 32) + ((d & 15) + 16 * (2 * (R & 1) + hh)) * 8;
-                    *reinterpret_cast<uint4*>(ws.bwT_hi + tcol) = make_uint4(bwh[c][0], bwh[c][1], bwh[c][2], bwh[c][3]);
-                    *reinterpret_cast<uint4*>(ws.bwT_lo + tcol) = make_uint4(bwl[c][0], bwl[c][1], bwl[c][2], bwl[c][3]);
+                    *reinterpret_cast<uint4*>(ws.bwT + tcol) = make_uint4(bwh[c][0], bwh[c][1], bwh[c][2], bwh[c][3]);
                     // kg^T in pi order: rows 16 R + 4 q .. + 3 go to lane (d % 16) + 16 q, half R % 2
                     const size_t pcol = sc * KD * C + frag(d >> 4, R >> 1, C / 32);
                     *reinterpret_cast<uint2*>(ws.kgT_hi + pcol + fragP(R & 1, d & 15, 2 * hh)) = make_uint2(kgh[c][0], kgh[c][1]);
@@ -497,12 +497,11 @@ __device__ __forceinline__ void intra_item(
 
     // ------------------------------------------------------------------ phase INV
     const int dt = wave;  // 16-block of K (for w) and of V (for u) this wave produces in WU
-    uint4 bwh_f[NS], bwl_f[NS], vt_f[NS];
+    uint4 bwh_f[NS], vt_f[NS];
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
         const size_t off = sc * KD * C + frag(dt, s, C / 32) + lane * 8;
-        bwh_f[s] = *reinterpret_cast<const uint4*>(ws.bwT_hi + off);
-        bwl_f[s] = *reinterpret_cast<const uint4*>(ws.bwT_lo + off);
+        bwh_f[s] = *reinterpret_cast<const uint4*>(ws.bwT + off);
         vt_f[s] = *reinterpret_cast<const uint4*>(ws.vT + off);
     }
     // kg^T fragments (high, then low) of phase PQ, the same number per wave; they go to LDS
@@ -609,7 +608,8 @@ __device__ __forceinline__ void intra_item(
 #pragma unroll
     for (int R = 0; R < NT; ++R) {
         f32x4 aw = {0.f, 0.f, 0.f, 0.f}, au = aw;
-        {   // T'_RR Y_R: Y rows 32 (R / 2) + 8 q4 + i in the normal-order fragment R / 2
+        {   // T'_RR Y_R (Y single bf16 for both): Y rows 32 (R / 2) + 8 q4 + i in the normal-order
+            // fragment R / 2
             uint4 th = make_uint4(0u, 0u, 0u, 0u), tl = th;
             if ((q4 >> 1) == (R & 1)) {
                 const uint4* tp = reinterpret_cast<const uint4*>(Tpre + R * 512 + r16 * 32);
@@ -620,7 +620,6 @@ __device__ __forceinline__ void intra_item(
             const int s = R >> 1;
             aw = mfma32(thi, as_bf16x8(bwh_f[s]), aw);
             aw = mfma32(tlo, as_bf16x8(bwh_f[s]), aw);
-            aw = mfma32(thi, as_bf16x8(bwl_f[s]), aw);
             au = mfma32(thi, as_bf16x8(vt_f[s]), au);
             au = mfma32(tlo, as_bf16x8(vt_f[s]), au);
         }
@@ -657,6 +656,9 @@ __device__ __forceinline__ void intra_item(
     }
 
     // ------------------------------------------------------------------ phase PQ
+    // the next item's phase E inputs, in flight through PQ (nothing below waits on the
+    // vector memory counter before the next item uses them)
+    e_load<C, PER_DIM>(ein, k, v, g, beta, map, H, Hk, next_item, tid);
     lds_barrier();  // every wave is done with the solve operands in R2
     // the A2 fragments and qg tiles kept since phase AA2 go to R2
     uint16_t* a2L = reinterpret_cast<uint16_t*>(smem + S::R1);  // lower A2 fragments, pi order
@@ -692,9 +694,6 @@ __device__ __forceinline__ void intra_item(
     uint2 qgv[NT];    // (qg)^T tiles (I, dt)
 #pragma unroll
     for (int I = 0; I < NT; ++I) qgv[I] = *reinterpret_cast<const uint2*>(qgL + ((I * (KD / 16) + dt) * 64 + lane) * 4);
-    // the next item's phase E inputs, in flight through the rest of PQ (issued after the wait
-    // above, which would otherwise take them in)
-    e_load<C, PER_DIM>(ein, k, v, g, beta, map, H, Hk, next_item, tid);
     // P^T tile (rows d in block dt, columns k in block x) = w^T kg; B tile (rows k in x,
     // columns v in dt) = kg^T u.  -P goes out in pi order as the A operand of -P S.
 #pragma unroll 1
