@@ -195,6 +195,18 @@ __device__ __forceinline__ void slot_chunk(const ChunkMap& m, int slot, int64_t&
 // 32-blocks b (nb of them) keeps fragment (a, b) at element ((a * nb + b) * 512).
 // ---------------------------------------------------------------------------------------
 __device__ __forceinline__ size_t frag(int a, int b, int nb) { return ((size_t)a * nb + b) * 512; }
+__device__ __forceinline__ uint32_t frag32(int a, int b, int nb) { return (uint32_t)(a * nb + b) * 512u; }
+
+// base + a 32-bit byte offset.  With a wave-uniform base the access takes the scalar-base +
+// 32-bit vector-offset form, with no 64-bit address arithmetic per lane.
+template <typename T>
+__device__ __forceinline__ const T* cptr(const void* base, uint32_t bytes) {
+    return reinterpret_cast<const T*>(static_cast<const char*>(base) + bytes);
+}
+template <typename T>
+__device__ __forceinline__ T* mptr(void* base, uint32_t bytes) {
+    return reinterpret_cast<T*>(static_cast<char*>(base) + bytes);
+}
 // Element offset, inside a fragment, of the four values a D-layout tile lane (r, q) holds
 // when the tile is the transpose of the operand (tile rows = contracted index 16 t + 4 q + e
 // within the fragment's 32, tile column = non-contracted index r): four consecutive slots.

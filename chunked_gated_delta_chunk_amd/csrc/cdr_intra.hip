@@ -122,25 +122,29 @@ __device__ __forceinline__ void e_load(EIn& in, const uint16_t* __restrict__ k, 
     int64_t tok0;
     int rows;
     slot_chunk(map, slot, tok0, rows);
-    const int last = max(rows - 1, 0);
-    // value head h reads key head h / (H / Hk); v and g have H heads
-    const size_t rs = (size_t)H * KD, rsk = (size_t)Hk * KD;
-    const size_t base = (size_t)tok0 * rs + (size_t)h * KD;
-    const size_t basek = (size_t)tok0 * rsk + (size_t)(h / (H / Hk)) * KD;
-    const int R = min(tid >> 6, C / 16 - 1), d0 = 2 * (tid & 63);
-    in.b = beta[(size_t)(tok0 + min(tid, last)) * H + h];
+    const uint32_t last = (uint32_t)max(rows - 1, 0);
+    // value head h reads key head h / (H / Hk); v and g have H heads.  Item bases are
+    // uniform; per lane only 32-bit byte offsets of rows min(16 R + ii, last) are formed.
+    const uint32_t rs = (uint32_t)H * KD, rsk = (uint32_t)Hk * KD;
+    const uint16_t* kb = k + ((size_t)tok0 * rsk + (size_t)(h / (H / Hk)) * KD);
+    const uint16_t* vb = v + ((size_t)tok0 * rs + (size_t)h * KD);
+    const uint32_t R = (uint32_t)min(tid >> 6, C / 16 - 1), d0 = 2u * (uint32_t)(tid & 63);
+    in.b = *cptr<float>(beta + ((size_t)tok0 * H + h), min((uint32_t)tid, last) * (uint32_t)H * 4u);
     {
+        const uint32_t r0 = 16u * R;
+        const uint32_t ok0 = (r0 * rsk + d0) * 2u, okl = (last * rsk + d0) * 2u;   // k bytes
+        const uint32_t ov0 = (r0 * rs + d0) * 2u, ovl = (last * rs + d0) * 2u;     // v bytes
 #pragma unroll
         for (int ii = 0; ii < 16; ++ii) {
-            const int ic = min(16 * R + ii, last);
             if constexpr (PER_DIM) {
-                in.g[ii] = *reinterpret_cast<const float2*>(g + base + (size_t)ic * rs + d0);
+                // g rows have the byte offsets of v rows, doubled
+                in.g[ii] = *cptr<float2>(g + ((size_t)tok0 * rs + (size_t)h * KD), 2u * min(ov0 + ii * rs * 2u, ovl));
             } else {
-                const float s1 = g[(size_t)(tok0 + ic) * H + h];
+                const float s1 = *cptr<float>(g + ((size_t)tok0 * H + h), min(r0 + ii, last) * (uint32_t)H * 4u);
                 in.g[ii] = make_float2(s1, s1);
             }
-            in.k[ii] = *reinterpret_cast<const uint32_t*>(k + basek + (size_t)ic * rsk + d0);
-            in.v[ii] = *reinterpret_cast<const uint32_t*>(v + base + (size_t)ic * rs + d0);
+            in.k[ii] = *cptr<uint32_t>(kb, min(ok0 + ii * rsk * 2u, okl));
+            in.v[ii] = *cptr<uint32_t>(vb, min(ov0 + ii * rs * 2u, ovl));
         }
     }
 }
@@ -178,11 +182,18 @@ __device__ __forceinline__ void intra_item(
         return;
     }
     const size_t ch = (size_t)slot * H + h;
+    // the workgroup's scratch slot
+    uint16_t* bwS = ws.bwT + sc * KD * C;
+    uint16_t* vS = ws.vT + sc * VD * C;
+    uint16_t* kgS_hi = ws.kgT_hi + sc * KD * C;
+    uint16_t* kgS_lo = ws.kgT_lo + sc * KD * C;
     const int lane = tid & 63, wave = tid >> 6;
     const int r16 = lane & 15, q4 = lane >> 4;
-    // q and k: key head h / (H / Hk) of Hk
-    const size_t rsk = (size_t)Hk * KD;
+    // q and k: key head h / (H / Hk) of Hk; uniform item bases, 32-bit byte offsets per lane
+    const uint32_t rsk = (uint32_t)Hk * KD;
     const size_t basek = (size_t)tok0 * rsk + (size_t)(h / (H / Hk)) * KD;
+    const uint16_t* kbase = k + basek;
+    const uint16_t* qbase = q + basek;
 
     // Row operands of phase AA2 (raw k and q rows of the wave's two tile rows), loaded
     // before phase E so that their latency is hidden behind it.  The loads are unconditional
@@ -195,13 +206,14 @@ __device__ __forceinline__ void intra_item(
     const int Rown[2] = {cp, NT - 1 - cp};
     uint4 kfr[2][KD / 32], qfr[2][KD / 32];
 #pragma unroll
-    for (int o = 0; o < 2; ++o)
+    for (int o = 0; o < 2; ++o) {
+        const uint32_t ro = ((uint32_t)min(16 * Rown[o] + r16, rows - 1) * rsk + 8u * q4) * 2u;
 #pragma unroll
         for (int ks = 0; ks < KD / 32; ++ks) {
-            const int ic = min(16 * Rown[o] + r16, rows - 1);
-            kfr[o][ks] = *reinterpret_cast<const uint4*>(k + basek + (size_t)ic * rsk + 32 * ks + 8 * q4);
-            qfr[o][ks] = *reinterpret_cast<const uint4*>(q + basek + (size_t)ic * rsk + 32 * ks + 8 * q4);
+            kfr[o][ks] = *cptr<uint4>(kbase, ro + 64u * ks);
+            qfr[o][ks] = *cptr<uint4>(qbase, ro + 64u * ks);
         }
+    }
     // ------------------------------------------------------------------ phase E
     {
         const int R = tid >> 6, d0 = 2 * (tid & 63);  // tile row R, columns d0, d0 + 1
@@ -270,7 +282,7 @@ __device__ __forceinline__ void intra_item(
             }
             *reinterpret_cast<float2*>(gmid + R * KD + d0) = make_float2(gmv[0], gmv[1]);
             *reinterpret_cast<float2*>(egm + R * KD + d0) = make_float2(e_gm[0], e_gm[1]);
-            if (R == 0) st_nt(reinterpret_cast<float2*>(ws.gC + ch * KD + d0), make_float2(ex(gcl[0]), ex(gcl[1])));
+            if (R == 0) st_nt(mptr<float2>(ws.gC + ch * KD, d0 * 4u), make_float2(ex(gcl[0]), ex(gcl[1])));
             if constexpr (!PER_DIM) {
                 if ((tid & 63) == 0) {
 #pragma unroll
@@ -319,15 +331,17 @@ __device__ __forceinline__ void intra_item(
                     // (K, C) / (V, C) fragment (d / 16, R / 2): rows 16 R + 8 hh .. +7 of column d
                     // are exactly the 16-byte slot of lane (d % 16) + 16 (2 (R % 2) + hh)
                     const int d = d0 + c;
-                    const size_t tcol = sc * KD * C + frag(d >> 4, R >> 1, C / 32) + ((d & 15) + 16 * (2 * (R & 1) + hh)) * 8;
-                    *reinterpret_cast<uint4*>(ws.bwT + tcol) = make_uint4(bwh[c][0], bwh[c][1], bwh[c][2], bwh[c][3]);
+                    // byte offsets inside the workgroup's scratch slot (uniform bases)
+                    const uint32_t fo = frag32(d >> 4, R >> 1, C / 32);
+                    const uint32_t tcol = (fo + ((d & 15) + 16 * (2 * (R & 1) + hh)) * 8) * 2u;
+                    *mptr<uint4>(bwS, tcol) = make_uint4(bwh[c][0], bwh[c][1], bwh[c][2], bwh[c][3]);
                     // kg^T in pi order: rows 16 R + 4 q .. + 3 go to lane (d % 16) + 16 q, half R % 2
-                    const size_t pcol = sc * KD * C + frag(d >> 4, R >> 1, C / 32);
-                    *reinterpret_cast<uint2*>(ws.kgT_hi + pcol + fragP(R & 1, d & 15, 2 * hh)) = make_uint2(kgh[c][0], kgh[c][1]);
-                    *reinterpret_cast<uint2*>(ws.kgT_hi + pcol + fragP(R & 1, d & 15, 2 * hh + 1)) = make_uint2(kgh[c][2], kgh[c][3]);
-                    *reinterpret_cast<uint2*>(ws.kgT_lo + pcol + fragP(R & 1, d & 15, 2 * hh)) = make_uint2(kgl[c][0], kgl[c][1]);
-                    *reinterpret_cast<uint2*>(ws.kgT_lo + pcol + fragP(R & 1, d & 15, 2 * hh + 1)) = make_uint2(kgl[c][2], kgl[c][3]);
-                    *reinterpret_cast<uint4*>(ws.vT + tcol) = make_uint4(vtp[c][0], vtp[c][1], vtp[c][2], vtp[c][3]);
+                    const uint32_t p0 = (fo + fragP(R & 1, d & 15, 2 * hh)) * 2u, p1 = (fo + fragP(R & 1, d & 15, 2 * hh + 1)) * 2u;
+                    *mptr<uint2>(kgS_hi, p0) = make_uint2(kgh[c][0], kgh[c][1]);
+                    *mptr<uint2>(kgS_hi, p1) = make_uint2(kgh[c][2], kgh[c][3]);
+                    *mptr<uint2>(kgS_lo, p0) = make_uint2(kgl[c][0], kgl[c][1]);
+                    *mptr<uint2>(kgS_lo, p1) = make_uint2(kgl[c][2], kgl[c][3]);
+                    *mptr<uint4>(vS, tcol) = make_uint4(vtp[c][0], vtp[c][1], vtp[c][2], vtp[c][3]);
                 }
             }
         }
@@ -452,7 +466,7 @@ __device__ __forceinline__ void intra_item(
                 acc = mfma32(ahi, blo, acc);
                 acc2 = mfma32(bhi, aqv, acc2);   // A2^T tile: rows j, columns i
             } else {
-                const uint4 kx = *reinterpret_cast<const uint4*>(k + basek + (size_t)min(j, rows - 1) * rsk + dd);
+                const uint4 kx = *cptr<uint4>(kbase, ((uint32_t)min(j, rows - 1) * rsk + dd) * 2u);
                 const bf16x8 b = as_bf16x8((j < rows) ? kx : make_uint4(0, 0, 0, 0));
                 if (J == R) {
                     float qf[8];
@@ -500,9 +514,9 @@ __device__ __forceinline__ void intra_item(
     uint4 bwh_f[NS], vt_f[NS];
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
-        const size_t off = sc * KD * C + frag(dt, s, C / 32) + lane * 8;
-        bwh_f[s] = *reinterpret_cast<const uint4*>(ws.bwT + off);
-        vt_f[s] = *reinterpret_cast<const uint4*>(ws.vT + off);
+        const uint32_t off = (frag32(dt, s, C / 32) + lane * 8) * 2u;
+        bwh_f[s] = *cptr<uint4>(bwS, off);
+        vt_f[s] = *cptr<uint4>(vS, off);
     }
     // kg^T fragments (high, then low) of phase PQ, the same number per wave; they go to LDS
     // (R1) once the A tiles there are no longer read
@@ -516,8 +530,7 @@ __device__ __forceinline__ void intra_item(
 #pragma unroll
         for (int i = 0; i < KPW; ++i) {
             const int f = wave + IWAVES * i;  // fragment (f / NS, f % NS) of the part
-            const uint16_t* src = (hl ? ws.kgT_lo : ws.kgT_hi) + sc * KD * C + frag(f / NS, f % NS, C / 32);
-            kgr[hl][i] = *reinterpret_cast<const u32x4v*>(src + lane * 8);
+            kgr[hl][i] = *cptr<u32x4v>(hl ? kgS_lo : kgS_hi, (frag32(f / NS, f % NS, C / 32) + lane * 8) * 2u);
         }
 #pragma unroll
     for (int s = 0; s < S::SMAX; ++s) {
@@ -696,6 +709,11 @@ __device__ __forceinline__ void intra_item(
     for (int I = 0; I < NT; ++I) qgv[I] = *reinterpret_cast<const uint2*>(qgL + ((I * (KD / 16) + dt) * 64 + lane) * 4);
     // P^T tile (rows d in block dt, columns k in block x) = w^T kg; B tile (rows k in x,
     // columns v in dt) = kg^T u.  -P goes out in pi order as the A operand of -P S.
+    // Outputs of the item through uniform bases and 32-bit byte offsets.
+    uint16_t* PnI = ws.Pn + ch * KD * KD;
+    float* BmI = ws.Bm + ch * KD * VD;
+    uint16_t* QpI = ws.Qp + ch * C * KD;
+    uint16_t* UpI = ws.Up + ch * C * VD;
 #pragma unroll 1
     for (int x = 0; x < KD / 16; ++x) {
         // P (stored with one bf16 rounding) from the high parts only; B split
@@ -713,10 +731,8 @@ __device__ __forceinline__ void intra_item(
 #pragma unroll
         for (int e = 0; e < 4; ++e) bt[e] = b0[e] + b1[e];
         const uint2 ph = make_uint2(pack_bf2(-pt[0], -pt[1]), pack_bf2(-pt[2], -pt[3]));
-        const size_t po = ch * KD * KD + frag(x, dt >> 1, KD / 32) + fragP(dt & 1, r16, q4);
-        st_nt(reinterpret_cast<uint2*>(ws.Pn + po), ph);
-        st_nt(reinterpret_cast<float4*>(ws.Bm + ch * KD * VD + ((size_t)(x * (VD / 16) + dt) * 64 + lane) * 4),
-              make_float4(bt[0], bt[1], bt[2], bt[3]));
+        st_nt(mptr<uint2>(PnI, (frag32(x, dt >> 1, KD / 32) + fragP(dt & 1, r16, q4)) * 2u), ph);
+        st_nt(mptr<float4>(BmI, ((x * (VD / 16) + dt) * 64 + lane) * 16u), make_float4(bt[0], bt[1], bt[2], bt[3]));
     }
     // Q^T tile (rows d in dt, columns i in I) = (qg)^T - w^T A2^T; U^T tile (rows v in dt,
     // columns i in I) = u^T A2^T.  A2 fragment (I, s) is the B operand of both.
@@ -733,10 +749,9 @@ __device__ __forceinline__ void intra_item(
             qt = mfma32(as_bf16x8(neg_bf16x8(wh[s])), a2, qt);
             ut = mfma32(as_bf16x8(uh[s]), a2, ut);
         }
-        st_nt(reinterpret_cast<uint2*>(ws.Qp + ch * C * KD + frag(I, dt >> 1, KD / 32) + fragP(dt & 1, r16, q4)),
+        st_nt(mptr<uint2>(QpI, (frag32(I, dt >> 1, KD / 32) + fragP(dt & 1, r16, q4)) * 2u),
               make_uint2(pack_bf2(qt[0], qt[1]), pack_bf2(qt[2], qt[3])));
-        st_nt(reinterpret_cast<uint2*>(ws.Up + ch * C * VD + ((size_t)(I * (VD / 16) + dt) * 64 + lane) * 4),
-              make_uint2(pack_bf2(ut[0], ut[1]), pack_bf2(ut[2], ut[3])));
+        st_nt(mptr<uint2>(UpI, ((I * (VD / 16) + dt) * 64 + lane) * 8u), make_uint2(pack_bf2(ut[0], ut[1]), pack_bf2(ut[2], ut[3])));
     }
 }
 
