@@ -236,8 +236,6 @@ struct Work {
     float* gC;         // [K]            fp32   exp(gamma_C)
     uint16_t* Sc;      // (V, K) frag pi bf16   state entering the chunk; A operand of (Q S)^T
     // scratch of the intra kernel (written and read back by the same workgroup)
-    uint16_t* bwT;     // (K, C) frag    bf16   exp(gamma) * k
-    uint16_t* vT;      // (V, C) frag    bf16   v
     uint16_t* kgT_hi;  // (K, C) frag pi bf16   exp(gamma_C - gamma) * k, high part
     uint16_t* kgT_lo;  // (K, C) frag pi bf16   low part
 };

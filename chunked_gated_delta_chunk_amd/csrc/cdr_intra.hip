@@ -9,9 +9,10 @@
 //        issues all of its loads (g, k, v) at once.  gamma = prefix sum of g inside the tile
 //        plus the totals of the tiles above (through LDS).  Per-element decay factors
 //        relative to the tile's middle row m, and the element-wise outputs: exp(gamma_C),
-//        kg = exp(gamma_C - gamma) k (split), exp(gamma) k (single bf16: w only reaches P
-//        and Q, which are formed from its own single bf16 rounding) and v, fragment-major
-//        (scratch read back by this workgroup).
+//        kg = exp(gamma_C - gamma) k (split; fragment-major scratch read back by this
+//        workgroup in INV), exp(gamma) k (single bf16: w only reaches P and Q, which are
+//        formed from its own single bf16 rounding) and v, both as fragment slots kept in
+//        registers until LDS is free for them after INV.
 //   AA2  16x16 tiles of A (strictly lower, times beta) and A2 (lower incl. diagonal, times
 //        scale) on bf16 MFMA.  Per-dimension gates enter the operands through the tile
 //        pivots: for rows i in tile R and columns j in tile J <= R,
@@ -183,8 +184,6 @@ __device__ __forceinline__ void intra_item(
     }
     const size_t ch = (size_t)slot * H + h;
     // the workgroup's scratch slot
-    uint16_t* bwS = ws.bwT + sc * KD * C;
-    uint16_t* vS = ws.vT + sc * VD * C;
     uint16_t* kgS_hi = ws.kgT_hi + sc * KD * C;
     uint16_t* kgS_lo = ws.kgT_lo + sc * KD * C;
     const int lane = tid & 63, wave = tid >> 6;
@@ -214,6 +213,9 @@ __device__ __forceinline__ void intra_item(
             qfr[o][ks] = *cptr<uint4>(qbase, ro + 64u * ks);
         }
     }
+    // exp(gamma) k and v of the thread's phase E block as 16-byte fragment slots [hh][c],
+    // kept in registers until the A tiles leave LDS, then staged there for the solve
+    uint4 xs[2][2], vs[2][2];
     // ------------------------------------------------------------------ phase E
     {
         const int R = tid >> 6, d0 = 2 * (tid & 63);  // tile row R, columns d0, d0 + 1
@@ -333,15 +335,14 @@ __device__ __forceinline__ void intra_item(
                     const int d = d0 + c;
                     // byte offsets inside the workgroup's scratch slot (uniform bases)
                     const uint32_t fo = frag32(d >> 4, R >> 1, C / 32);
-                    const uint32_t tcol = (fo + ((d & 15) + 16 * (2 * (R & 1) + hh)) * 8) * 2u;
-                    *mptr<uint4>(bwS, tcol) = make_uint4(bwh[c][0], bwh[c][1], bwh[c][2], bwh[c][3]);
+                    xs[hh][c] = make_uint4(bwh[c][0], bwh[c][1], bwh[c][2], bwh[c][3]);
                     // kg^T in pi order: rows 16 R + 4 q .. + 3 go to lane (d % 16) + 16 q, half R % 2
                     const uint32_t p0 = (fo + fragP(R & 1, d & 15, 2 * hh)) * 2u, p1 = (fo + fragP(R & 1, d & 15, 2 * hh + 1)) * 2u;
                     *mptr<uint2>(kgS_hi, p0) = make_uint2(kgh[c][0], kgh[c][1]);
                     *mptr<uint2>(kgS_hi, p1) = make_uint2(kgh[c][2], kgh[c][3]);
                     *mptr<uint2>(kgS_lo, p0) = make_uint2(kgl[c][0], kgl[c][1]);
                     *mptr<uint2>(kgS_lo, p1) = make_uint2(kgl[c][2], kgl[c][3]);
-                    *mptr<uint4>(vS, tcol) = make_uint4(vtp[c][0], vtp[c][1], vtp[c][2], vtp[c][3]);
+                    vs[hh][c] = make_uint4(vtp[c][0], vtp[c][1], vtp[c][2], vtp[c][3]);
                 }
             }
         }
@@ -511,13 +512,6 @@ __device__ __forceinline__ void intra_item(
 
     // ------------------------------------------------------------------ phase INV
     const int dt = wave;  // 16-block of K (for w) and of V (for u) this wave produces in WU
-    uint4 bwh_f[NS], vt_f[NS];
-#pragma unroll
-    for (int s = 0; s < NS; ++s) {
-        const uint32_t off = (frag32(dt, s, C / 32) + lane * 8) * 2u;
-        bwh_f[s] = *cptr<uint4>(bwS, off);
-        vt_f[s] = *cptr<uint4>(vS, off);
-    }
     // kg^T fragments (high, then low) of phase PQ, the same number per wave; they go to LDS
     // (R1) once the A tiles there are no longer read
     constexpr int NKG = 2 * (KD / 16) * NS;
@@ -606,12 +600,23 @@ __device__ __forceinline__ void intra_item(
 
     // ------------------------------------------------------------------ phase WU
     constexpr int NA2 = NT + (NT / 2) * (NT / 2 - 1);  // lower A2 fragments
-    uint16_t* kgL = reinterpret_cast<uint16_t*>(smem);  // kg^T over the A tiles (R1)
+    // exp(gamma) k and v fragments over the A tiles (R1)
+    uint16_t* xL = reinterpret_cast<uint16_t*>(smem);
+    uint16_t* vL = xL + KD * C;
+    static_assert((KD + VD) * C * 2 <= S::R1, "solve operand staging");
+    if ((tid >> 6) < NT) {
+        const int R = tid >> 6, d0 = 2 * (tid & 63);
 #pragma unroll
-    for (int hl = 0; hl < 2; ++hl)
+        for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
-        for (int i = 0; i < KPW; ++i)
-            *reinterpret_cast<u32x4v*>(kgL + (hl * (NKG / 2) + wave + IWAVES * i) * 512 + lane * 8) = kgr[hl][i];
+            for (int c = 0; c < 2; ++c) {
+                const int d = d0 + c;
+                const uint32_t o = frag32(d >> 4, R >> 1, C / 32) + ((d & 15) + 16 * (2 * (R & 1) + hh)) * 8;
+                *reinterpret_cast<uint4*>(xL + o) = xs[hh][c];
+                *reinterpret_cast<uint4*>(vL + o) = vs[hh][c];
+            }
+    }
+    lds_barrier();
     // Blocked forward substitution for [w | u] = (I + A)^-1 diag(beta) [exp(gamma) k | v], wave
     // dt producing columns 16 dt .. + 15 of each:  Z_R = T'_RR Y_R - sum_{J<R} M_RJ Z_J.  The Z
     // tiles stay in registers, split, in the D layout (lane (r16, q4), element e: row
@@ -630,11 +635,13 @@ __device__ __forceinline__ void intra_item(
                 tl = tp[2 + (q4 & 1)];
             }
             const bf16x8 thi = as_bf16x8(th), tlo = as_bf16x8(tl);
-            const int s = R >> 1;
-            aw = mfma32(thi, as_bf16x8(bwh_f[s]), aw);
-            aw = mfma32(tlo, as_bf16x8(bwh_f[s]), aw);
-            au = mfma32(thi, as_bf16x8(vt_f[s]), au);
-            au = mfma32(tlo, as_bf16x8(vt_f[s]), au);
+            const uint32_t fo = frag32(dt, R >> 1, C / 32) + lane * 8;
+            const bf16x8 xf = as_bf16x8(*reinterpret_cast<const uint4*>(xL + fo));
+            const bf16x8 vf = as_bf16x8(*reinterpret_cast<const uint4*>(vL + fo));
+            aw = mfma32(thi, xf, aw);
+            aw = mfma32(tlo, xf, aw);
+            au = mfma32(thi, vf, au);
+            au = mfma32(tlo, vf, au);
         }
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
@@ -673,7 +680,13 @@ __device__ __forceinline__ void intra_item(
     // vector memory counter before the next item uses them)
     e_load<C, PER_DIM>(ein, k, v, g, beta, map, H, Hk, next_item, tid);
     lds_barrier();  // every wave is done with the solve operands in R2
-    // the A2 fragments and qg tiles kept since phase AA2 go to R2
+    // kg^T to R1; the A2 fragments and qg tiles kept since phase AA2 to R2
+    uint16_t* kgL = reinterpret_cast<uint16_t*>(smem);
+#pragma unroll
+    for (int hl = 0; hl < 2; ++hl)
+#pragma unroll
+        for (int i = 0; i < KPW; ++i)
+            *reinterpret_cast<u32x4v*>(kgL + (hl * (NKG / 2) + wave + IWAVES * i) * 512 + lane * 8) = kgr[hl][i];
     uint16_t* a2L = reinterpret_cast<uint16_t*>(smem + S::R1);  // lower A2 fragments, pi order
     uint16_t* qgL = a2L + NA2 * 512;                             // (qg)^T D tiles
     static_assert(NA2 * 1024 + C * KD * 2 <= S::R2, "A2 and qg staging");
