@@ -32,7 +32,7 @@ int64_t num_slots(const cdr_problem* p) {
     return (int64_t)p->B * ((p->T + p->chunk_size - 1) / p->chunk_size);
 }
 
-constexpr int kArrays = 8;
+constexpr int kArrays = 7;
 constexpr int64_t kScratchSlots = 512; // at most this many intra workgroups run at once
 
 size_t scratch_slots(const cdr_problem* p) {
@@ -55,8 +55,7 @@ Layout layout(const cdr_problem* p) {
         nch * C * V * 2,  // Up
         nch * K * 4,      // gC
         nch * V * K * 2,  // Sc
-        nsc * K * C * 2,  // kgT_hi
-        nsc * K * C * 2,  // kgT_lo
+        nsc * K * C * 2,  // kgT
     };
     Layout L;
     size_t at = 0;
@@ -148,8 +147,7 @@ cdr_status chunk_dr_fwd_stages(const cdr_problem* p, const void* q, const void* 
     ws.Up = reinterpret_cast<uint16_t*>(wb + L.off[3]);
     ws.gC = reinterpret_cast<float*>(wb + L.off[4]);
     ws.Sc = reinterpret_cast<uint16_t*>(wb + L.off[5]);
-    ws.kgT_hi = reinterpret_cast<uint16_t*>(wb + L.off[6]);
-    ws.kgT_lo = reinterpret_cast<uint16_t*>(wb + L.off[7]);
+    ws.kgT = reinterpret_cast<uint16_t*>(wb + L.off[6]);
 
     cdr::ChunkMap map;
     map.cu = p->varlen ? cu_seqlens : nullptr;

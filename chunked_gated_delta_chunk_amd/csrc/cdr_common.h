@@ -236,8 +236,8 @@ struct Work {
     float* gC;         // [K]            fp32   exp(gamma_C)
     uint16_t* Sc;      // (V, K) frag pi bf16   state entering the chunk; A operand of (Q S)^T
     // scratch of the intra kernel (written and read back by the same workgroup)
-    uint16_t* kgT_hi;  // (K, C) frag pi bf16   exp(gamma_C - gamma) * k, high part
-    uint16_t* kgT_lo;  // (K, C) frag pi bf16   low part
+    uint16_t* kgT;     // (K, C) frag pi bf16   exp(gamma_C - gamma) * k, high part (the low part
+                       //                       stays in registers)
 };
 
 }  // namespace cdr

@@ -184,8 +184,7 @@ __device__ __forceinline__ void intra_item(
     }
     const size_t ch = (size_t)slot * H + h;
     // the workgroup's scratch slot
-    uint16_t* kgS_hi = ws.kgT_hi + sc * KD * C;
-    uint16_t* kgS_lo = ws.kgT_lo + sc * KD * C;
+    uint16_t* kgS = ws.kgT + sc * KD * C;
     const int lane = tid & 63, wave = tid >> 6;
     const int r16 = lane & 15, q4 = lane >> 4;
     // q and k: key head h / (H / Hk) of Hk; uniform item bases, 32-bit byte offsets per lane
@@ -216,6 +215,7 @@ __device__ __forceinline__ void intra_item(
     // exp(gamma) k and v of the thread's phase E block as 16-byte fragment slots [hh][c],
     // kept in registers until the A tiles leave LDS, then staged there for the solve
     uint4 xs[2][2], vs[2][2];
+    uint4 kls[2][2];  // low part of kg^T, the two pi-order halves of each slot, to LDS after the solve
     // ------------------------------------------------------------------ phase E
     {
         const int R = tid >> 6, d0 = 2 * (tid & 63);  // tile row R, columns d0, d0 + 1
@@ -338,10 +338,9 @@ __device__ __forceinline__ void intra_item(
                     xs[hh][c] = make_uint4(bwh[c][0], bwh[c][1], bwh[c][2], bwh[c][3]);
                     // kg^T in pi order: rows 16 R + 4 q .. + 3 go to lane (d % 16) + 16 q, half R % 2
                     const uint32_t p0 = (fo + fragP(R & 1, d & 15, 2 * hh)) * 2u, p1 = (fo + fragP(R & 1, d & 15, 2 * hh + 1)) * 2u;
-                    *mptr<uint2>(kgS_hi, p0) = make_uint2(kgh[c][0], kgh[c][1]);
-                    *mptr<uint2>(kgS_hi, p1) = make_uint2(kgh[c][2], kgh[c][3]);
-                    *mptr<uint2>(kgS_lo, p0) = make_uint2(kgl[c][0], kgl[c][1]);
-                    *mptr<uint2>(kgS_lo, p1) = make_uint2(kgl[c][2], kgl[c][3]);
+                    *mptr<uint2>(kgS, p0) = make_uint2(kgh[c][0], kgh[c][1]);
+                    *mptr<uint2>(kgS, p1) = make_uint2(kgh[c][2], kgh[c][3]);
+                    kls[hh][c] = make_uint4(kgl[c][0], kgl[c][1], kgl[c][2], kgl[c][3]);
                     vs[hh][c] = make_uint4(vtp[c][0], vtp[c][1], vtp[c][2], vtp[c][3]);
                 }
             }
@@ -512,20 +511,18 @@ __device__ __forceinline__ void intra_item(
 
     // ------------------------------------------------------------------ phase INV
     const int dt = wave;  // 16-block of K (for w) and of V (for u) this wave produces in WU
-    // kg^T fragments (high, then low) of phase PQ, the same number per wave; they go to LDS
-    // (R1) once the A tiles there are no longer read
-    constexpr int NKG = 2 * (KD / 16) * NS;
-    constexpr int KPW = NKG / 2 / IWAVES;  // fragments of each part per wave
+    // high part of kg^T for phase PQ from scratch, the same number of fragments per wave; it
+    // goes to LDS (R1) after the solve
+    constexpr int NKG = 2 * (KD / 16) * NS;  // kg^T fragments in LDS (high, then low)
+    constexpr int KPW = NKG / 2 / IWAVES;    // high fragments per wave
     static_assert(NKG % (2 * IWAVES) == 0, "kg^T fragments per wave");
     static_assert(NKG * 1024 <= S::R1, "kg^T staging");
-    u32x4v kgr[2][KPW];  // a vector type: a struct copy would go through private memory
+    u32x4v kgr[KPW];  // a vector type: a struct copy would go through private memory
 #pragma unroll
-    for (int hl = 0; hl < 2; ++hl)
-#pragma unroll
-        for (int i = 0; i < KPW; ++i) {
-            const int f = wave + IWAVES * i;  // fragment (f / NS, f % NS) of the part
-            kgr[hl][i] = *cptr<u32x4v>(hl ? kgS_lo : kgS_hi, (frag32(f / NS, f % NS, C / 32) + lane * 8) * 2u);
-        }
+    for (int i = 0; i < KPW; ++i) {
+        const int f = wave + IWAVES * i;  // fragment (f / NS, f % NS)
+        kgr[i] = *cptr<u32x4v>(kgS, (frag32(f / NS, f % NS, C / 32) + lane * 8) * 2u);
+    }
 #pragma unroll
     for (int s = 0; s < S::SMAX; ++s) {
         const int p = (part ? S::HF : 0) + s;
@@ -680,13 +677,24 @@ __device__ __forceinline__ void intra_item(
     // vector memory counter before the next item uses them)
     e_load<C, PER_DIM>(ein, k, v, g, beta, map, H, Hk, next_item, tid);
     lds_barrier();  // every wave is done with the solve operands in R2
-    // kg^T to R1; the A2 fragments and qg tiles kept since phase AA2 to R2
+    // kg^T to R1 (high part from scratch, low part kept since phase E); the A2 fragments and
+    // qg tiles kept since phase AA2 to R2
     uint16_t* kgL = reinterpret_cast<uint16_t*>(smem);
 #pragma unroll
-    for (int hl = 0; hl < 2; ++hl)
+    for (int i = 0; i < KPW; ++i)
+        *reinterpret_cast<u32x4v*>(kgL + (wave + IWAVES * i) * 512 + lane * 8) = kgr[i];
+    if ((tid >> 6) < NT) {
+        const int R = tid >> 6, d0 = 2 * (tid & 63);
 #pragma unroll
-        for (int i = 0; i < KPW; ++i)
-            *reinterpret_cast<u32x4v*>(kgL + (hl * (NKG / 2) + wave + IWAVES * i) * 512 + lane * 8) = kgr[hl][i];
+        for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+            for (int c = 0; c < 2; ++c) {
+                const int d = d0 + c;
+                uint16_t* fl = kgL + (NKG / 2) * 512 + frag32(d >> 4, R >> 1, C / 32);
+                *reinterpret_cast<uint2*>(fl + fragP(R & 1, d & 15, 2 * hh)) = make_uint2(kls[hh][c].x, kls[hh][c].y);
+                *reinterpret_cast<uint2*>(fl + fragP(R & 1, d & 15, 2 * hh + 1)) = make_uint2(kls[hh][c].z, kls[hh][c].w);
+            }
+    }
     uint16_t* a2L = reinterpret_cast<uint16_t*>(smem + S::R1);  // lower A2 fragments, pi order
     uint16_t* qgL = a2L + NA2 * 512;                             // (qg)^T D tiles
     static_assert(NA2 * 1024 + C * KD * 2 <= S::R2, "A2 and qg staging");
