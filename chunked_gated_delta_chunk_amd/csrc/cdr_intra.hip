@@ -78,6 +78,19 @@ struct IntraShape {
 
 __device__ __forceinline__ int tri(int R, int J) { return R * (R + 1) / 2 + J; }  // J <= R
 
+// x = hi + lo as split_pk, with the two high parts converted by one packed conversion whose
+// halves give them back as floats.  The packed value passes through an empty asm statement
+// (no instruction is emitted) so that the compiler does not convert each value on its own
+// (two conversions, two shifts and a permute per pair instead of one, one, one).  The
+// conversion itself stays compiler-generated: an instruction inside inline asm is outside the
+// compiler's hazard checks, and reading an MFMA result that way returns stale values.
+__device__ __forceinline__ void split2(float a, float b, uint32_t& hi, uint32_t& lo) {
+    uint32_t h = pack_bf2(a, b);
+    asm("" : "+v"(h));
+    hi = h;
+    lo = pack_bf2(a - __uint_as_float(h << 16), b - __uint_as_float(h & 0xffff0000u));
+}
+
 __device__ __forceinline__ void tile_store(float* Tt, const f32x4& v, float sgn, int r16, int q4, int ld) {
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) Tt[(4 * q4 + rr) * ld + r16] = sgn * v[rr];
@@ -313,7 +326,7 @@ __device__ __forceinline__ void intra_item(
                             const int i = 16 * R + ii;
                             *reinterpret_cast<float2*>(Ep + i * S::EP_LD + d0) = make_float2(ep[rr][0], ep[rr][1]);
                             uint32_t chv, clv;
-                            split_pk(kf[rr][0] * em[rr][0], kf[rr][1] * em[rr][1], chv, clv);
+                            split2(kf[rr][0] * em[rr][0], kf[rr][1] * em[rr][1], chv, clv);
                             *reinterpret_cast<uint32_t*>(colh + i * S::COL_LD + d0) = chv;
                             *reinterpret_cast<uint32_t*>(coll + i * S::COL_LD + d0) = clv;
                         }
@@ -322,7 +335,7 @@ __device__ __forceinline__ void intra_item(
                     for (int c = 0; c < 2; ++c) {
                         // exp(gamma_i) k (beta enters through T diag(beta)) and exp(gamma_C - gamma_i) k
                         bwh[c][e2] = pack_bf2(kf[0][c] * (e_gm[c] * ep[0][c]), kf[1][c] * (e_gm[c] * ep[1][c]));
-                        split_pk(kf[0][c] * (em[0][c] * e_cm[c]), kf[1][c] * (em[1][c] * e_cm[c]), kgh[c][e2], kgl[c][e2]);
+                        split2(kf[0][c] * (em[0][c] * e_cm[c]), kf[1][c] * (em[1][c] * e_cm[c]), kgh[c][e2], kgl[c][e2]);
                     }
                     const uint32_t v0 = vr[8 * hh + 2 * e2], v1 = vr[8 * hh + 2 * e2 + 1];
                     vtp[0][e2] = (v0 & 0xffffu) | (v1 << 16);
@@ -450,10 +463,10 @@ __device__ __forceinline__ void intra_item(
                     qgkeep[ks] = pq;
                 }
                 uint4 ah, al, aq;
-                split_pk(kf[0] * ep[0], kf[1] * ep[1], ah.x, al.x);
-                split_pk(kf[2] * ep[2], kf[3] * ep[3], ah.y, al.y);
-                split_pk(kf[4] * ep[4], kf[5] * ep[5], ah.z, al.z);
-                split_pk(kf[6] * ep[6], kf[7] * ep[7], ah.w, al.w);
+                split2(kf[0] * ep[0], kf[1] * ep[1], ah.x, al.x);
+                split2(kf[2] * ep[2], kf[3] * ep[3], ah.y, al.y);
+                split2(kf[4] * ep[4], kf[5] * ep[5], ah.z, al.z);
+                split2(kf[6] * ep[6], kf[7] * ep[7], ah.w, al.w);
                 aq.x = pack_bf2(qf[0] * ep[0], qf[1] * ep[1]);
                 aq.y = pack_bf2(qf[2] * ep[2], qf[3] * ep[3]);
                 aq.z = pack_bf2(qf[4] * ep[4], qf[5] * ep[5]);
@@ -560,15 +573,15 @@ __device__ __forceinline__ void intra_item(
             // M_RJ^T = A_RJ^T T_RR^T on the 16x16x16 instruction
             const float4 tr = *reinterpret_cast<const float4*>(Td + r16 * S::TILE_LD + 4 * q4);
             uint2 bh, bl;
-            split_pk(tr.x, tr.y, bh.x, bl.x);
-            split_pk(tr.z, tr.w, bh.y, bl.y);
+            split2(tr.x, tr.y, bh.x, bl.x);
+            split2(tr.z, tr.w, bh.y, bl.y);
             const bf16x4 Bh = __builtin_bit_cast(bf16x4, bh), Bl = __builtin_bit_cast(bf16x4, bl);
             {   // T'_RR: column c of T_RR times beta of chunk row 16 R + c; row r keeps its 16 high
                 // parts, then its 16 low parts
                 const float* br = bet + 16 * R + 4 * q4;
                 uint2 h, l;
-                split_pk(tr.x * br[0], tr.y * br[1], h.x, l.x);
-                split_pk(tr.z * br[2], tr.w * br[3], h.y, l.y);
+                split2(tr.x * br[0], tr.y * br[1], h.x, l.x);
+                split2(tr.z * br[2], tr.w * br[3], h.y, l.y);
                 *reinterpret_cast<uint2*>(Tpre + R * 512 + r16 * 32 + 4 * q4) = h;
                 *reinterpret_cast<uint2*>(Tpre + R * 512 + r16 * 32 + 16 + 4 * q4) = l;
             }
@@ -576,8 +589,8 @@ __device__ __forceinline__ void intra_item(
                 // A operand: column r16 of A_RJ, rows 4 q4 .. + 3
                 const float* Aj = Atile + tri(R, J) * S::TILE_SZ + 4 * q4 * S::TILE_LD + r16;
                 uint2 ah, al;
-                split_pk(Aj[0], Aj[S::TILE_LD], ah.x, al.x);
-                split_pk(Aj[2 * S::TILE_LD], Aj[3 * S::TILE_LD], ah.y, al.y);
+                split2(Aj[0], Aj[S::TILE_LD], ah.x, al.x);
+                split2(Aj[2 * S::TILE_LD], Aj[3 * S::TILE_LD], ah.y, al.y);
                 const bf16x4 Ah = __builtin_bit_cast(bf16x4, ah), Al = __builtin_bit_cast(bf16x4, al);
                 f32x4 acc = {0.f, 0.f, 0.f, 0.f};
                 acc = mfma16(Ah, Bh, acc);
@@ -585,8 +598,8 @@ __device__ __forceinline__ void intra_item(
                 acc = mfma16(Ah, Bl, acc);
                 // acc[e] = M_RJ[r16][4 q4 + e]; kept negated, high parts then low parts
                 uint2 h, l;
-                split_pk(-acc[0], -acc[1], h.x, l.x);
-                split_pk(-acc[2], -acc[3], h.y, l.y);
+                split2(-acc[0], -acc[1], h.x, l.x);
+                split2(-acc[2], -acc[3], h.y, l.y);
                 uint16_t* mp = Mpre + (R * (R - 1) / 2 + J) * 512 + r16 * 16 + 4 * q4;
                 *reinterpret_cast<uint2*>(mp) = h;
                 *reinterpret_cast<uint2*>(mp + 256) = l;
@@ -666,10 +679,10 @@ __device__ __forceinline__ void intra_item(
             au = mfma32(Ml, Zuh, au);
             au = mfma32(Mh, Zul, au);
         }
-        split_pk(aw[0], aw[1], wzh[R].x, wzl[R].x);
-        split_pk(aw[2], aw[3], wzh[R].y, wzl[R].y);
-        split_pk(au[0], au[1], uzh[R].x, uzl[R].x);
-        split_pk(au[2], au[3], uzh[R].y, uzl[R].y);
+        split2(aw[0], aw[1], wzh[R].x, wzl[R].x);
+        split2(aw[2], aw[3], wzh[R].y, wzl[R].y);
+        split2(au[0], au[1], uzh[R].x, uzl[R].x);
+        split2(au[2], au[3], uzh[R].y, uzl[R].y);
     }
 
     // ------------------------------------------------------------------ phase PQ
@@ -787,7 +800,11 @@ __global__ __launch_bounds__(ITHREADS) void intra_kernel(
     EIn ein;
     e_load<C, PER_DIM>(ein, k, v, g, beta, map, H, Hk, blockIdx.x < nitems ? (int)blockIdx.x : -1, threadIdx.x);
     for (int item = blockIdx.x; item < nitems; item += gridDim.x) {
-        __syncthreads();  // the previous item is done with LDS
+        // the previous item is done with LDS.  An LDS-only barrier: __syncthreads() would also
+        // wait for every load and store in flight (this item's inputs, prefetched during the
+        // previous item, and the previous item's results); the only global data read back
+        // across waves, the kg^T scratch, is ordered by the wait at the end of phase AA2
+        lds_barrier();
         const int next = item + (int)gridDim.x < nitems ? item + (int)gridDim.x : -1;
         intra_item<C, PER_DIM, L2N>(q, k, v, g, beta, map, H, Hk, scale, ws, smem, item / H, item % H,
                                blockIdx.x, ein, next);
