@@ -55,7 +55,7 @@ Layout layout(const cdr_problem* p) {
         nch * C * V * 2,  // Up
         nch * K * 4,      // gC
         nch * V * K * 2,  // Sc
-        nsc * K * C * 2,  // kgT
+        nsc * K * C * 2 + nsc * 1024 * 4,  // kgT, then the pad area of each slot (intra kernel)
     };
     Layout L;
     size_t at = 0;

@@ -163,13 +163,30 @@ __device__ __forceinline__ void e_load(EIn& in, const uint16_t* __restrict__ k, 
     }
 }
 
+// Issues as many vector-memory operations as phase PQ issues after its next-item loads (N
+// stores of zero into the workgroup's pad area), on the paths into an item that do not pass
+// through PQ.  Where phase E first uses those loads, the compiler waits with the smallest count
+// of younger operations over all paths into the item loop; with this the count includes PQ's
+// result stores, so phase E waits for its inputs only, not for the previous item's stores too.
+// A lane stores at distinct addresses 16 words apart (no store is merged or dropped, and all
+// offsets fit the instruction's immediate field); lanes of the workgroup overlap, all storing
+// zero; nothing reads the pad.
+constexpr int PAD_WORDS = 1024;  // per workgroup: ITHREADS + 16 * (N - 1) words for N <= 32
+template <int N>
+__device__ __forceinline__ void vm_pad(uint32_t* p) {
+    static_assert(ITHREADS + 16 * (N - 1) <= PAD_WORDS, "pad area");
+#pragma unroll
+    for (int i = 0; i < N; ++i) p[16 * i] = 0u;
+}
+
 // One (chunk slot, head) item.  sc is the workgroup's scratch slot; ein holds the item's
 // phase E inputs on entry and those of next_item (-1: none) on exit.
 template <int C, bool PER_DIM, bool L2N>
 __device__ __forceinline__ void intra_item(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const float* __restrict__ g, const float* __restrict__ beta, const ChunkMap& map, int H, int Hk,
-    float scale, const Work& ws, unsigned char* smem, int slot, int h, size_t sc, EIn& ein, int next_item) {
+    float scale, const Work& ws, unsigned char* smem, int slot, int h, size_t sc, EIn& ein, int next_item,
+    uint32_t* pad) {
     using S = IntraShape<C>;
     constexpr int NT = S::NT, NS = S::NS;
     float* Ep = reinterpret_cast<float*>(smem);                                   // [C][EP_LD]
@@ -193,6 +210,7 @@ __device__ __forceinline__ void intra_item(
     slot_chunk(map, slot, tok0, rows);
     if (rows == 0) {
         e_load<C, PER_DIM>(ein, k, v, g, beta, map, H, Hk, next_item, tid);
+        vm_pad<2 * (KD / 16) + 2 * NT>(pad);
         return;
     }
     const size_t ch = (size_t)slot * H + h;
@@ -795,10 +813,12 @@ template <int C, bool PER_DIM, bool L2N>
 __global__ __launch_bounds__(ITHREADS) void intra_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const float* __restrict__ g, const float* __restrict__ beta, ChunkMap map, int H, int Hk,
-    float scale, Work ws, int nitems) {
+    float scale, Work ws, int nitems, uint32_t* __restrict__ pad_all) {
     __shared__ __attribute__((aligned(16))) unsigned char smem[IntraShape<C>::BYTES];
+    uint32_t* pad = pad_all + blockIdx.x * PAD_WORDS + threadIdx.x;
     EIn ein;
     e_load<C, PER_DIM>(ein, k, v, g, beta, map, H, Hk, blockIdx.x < nitems ? (int)blockIdx.x : -1, threadIdx.x);
+    vm_pad<2 * (KD / 16) + 2 * (C / 16)>(pad);
     for (int item = blockIdx.x; item < nitems; item += gridDim.x) {
         // the previous item is done with LDS.  An LDS-only barrier: __syncthreads() would also
         // wait for every load and store in flight (this item's inputs, prefetched during the
@@ -807,7 +827,7 @@ __global__ __launch_bounds__(ITHREADS) void intra_kernel(
         lds_barrier();
         const int next = item + (int)gridDim.x < nitems ? item + (int)gridDim.x : -1;
         intra_item<C, PER_DIM, L2N>(q, k, v, g, beta, map, H, Hk, scale, ws, smem, item / H, item % H,
-                               blockIdx.x, ein, next);
+                               blockIdx.x, ein, next, pad);
     }
 }
 
@@ -836,8 +856,10 @@ static hipError_t launch_intra_t(const uint16_t* q, const uint16_t* k, const uin
                                  float scale, const Work& ws, int nscratch, hipStream_t stream) {
     const int nitems = nslots * H;
     const int grid = min(min(nitems, nscratch), resident_groups<C, PER_DIM, L2N>());
+    // the pad areas of the scratch slots, after the kg^T planes
+    uint32_t* pad = reinterpret_cast<uint32_t*>(ws.kgT + (size_t)nscratch * KD * C);
     hipLaunchKernelGGL((intra_kernel<C, PER_DIM, L2N>), dim3(grid), dim3(ITHREADS), 0, stream, q, k, v, g, beta, map,
-                       H, Hk, scale, ws, nitems);
+                       H, Hk, scale, ws, nitems, pad);
     return hipGetLastError();
 }
 
