@@ -21,7 +21,8 @@
 //              forward substitution in fp32), W, U, P, B and Q^T dO.
 //   bwd_chain  per (sequence, value head, 16 value columns): the chunk entry states S_in
 //              (forward direction) and the chunk exit gradients dS_out (reverse direction),
-//              in fp32; the reverse direction ends with dh0.
+//              fp32 states and records, -P (-P^T) with one bf16 rounding on MFMA as in the
+//              forward chain; the reverse direction ends with dh0.
 //   bwd_local  per (chunk, value head): all input gradients of the chunk.
 //   bwd_group  sums dq, dk over the value heads of a group (grouped value heads only).
 #include "chunk_dr.h"
@@ -50,6 +51,20 @@ enum Mat {
 
 __device__ __forceinline__ float* mat(const Work& w, size_t ch, int id) {
     return w.M + (ch * NMAT + id) * (size_t)MSZ;
+}
+
+// Operand layouts of the state chains, kept in the first half of a matrix slot (PP, PT) or in
+// all of it (BB, BD):
+// element (m, k) of a 128 x 128 MFMA A operand stored as bf16 pi-order fragments (rows m,
+// contracted index k), the layout of the forward chain's -P
+__device__ __forceinline__ int pi_elem(int m, int k) {
+    const int kl = k & 31;
+    return (int)frag(m >> 4, k >> 5, 4) + fragP(kl >> 4, m & 15, (kl & 15) >> 2) + (kl & 3);
+}
+// element (m, n) of a 128 x 128 fp32 matrix stored as 16x16 accumulator tiles (the D layout:
+// lane (r, q) of tile (m / 16, n / 16) holds rows 4 q .. 4 q + 3 of column r)
+__device__ __forceinline__ int dtile_elem(int m, int n) {
+    return ((((m >> 4) * 8 + (n >> 4)) * 64 + (n & 15) + 16 * ((m & 15) >> 2)) << 2) + (m & 3);
 }
 
 // ------------------------------------------------------------------------------------
@@ -512,19 +527,21 @@ __global__ __launch_bounds__(BTHREADS) __attribute__((amdgpu_waves_per_eu(4))) v
                       [&](int m, int n, float x) { Up[m * 128 + n] = x; });
     }
     __syncthreads();
-    // ---- P = kg^T W (and P^T), B = kg^T U, Y = A2^T dO
+    // ---- P = kg^T W, B = kg^T U, Y = A2^T dO.  -P and -P^T go out with one bf16 rounding as
+    // the A operands of the chains (pi-order fragments), B as accumulator tiles.
     {
-        float* Pp = mat(w, ch, PP);
-        float* PTp = mat(w, ch, PT);
+        uint16_t* Pp = reinterpret_cast<uint16_t*>(mat(w, ch, PP));
+        uint16_t* PTp = reinterpret_cast<uint16_t*>(mat(w, ch, PT));
         float* Bp = mat(w, ch, BB);
         float* Yp = mat(w, ch, YY);
         const float* KGp = mat(w, ch, KG);
         gemm1<128, 128>(vw(KGp, 1, 128), vw(mat(w, ch, WW), 1, 128), C, smem, [&](int m, int n, float x) {
-            Pp[m * 128 + n] = x;
-            PTp[n * 128 + m] = x;
+            const uint16_t nb = f2bf(-x);
+            Pp[pi_elem(m, n)] = nb;
+            PTp[pi_elem(n, m)] = nb;
         });
         gemm1<128, 128>(vw(KGp, 1, 128), vw(mat(w, ch, UU), 1, 128), C, smem,
-                        [&](int m, int n, float x) { Bp[m * 128 + n] = x; });
+                        [&](int m, int n, float x) { Bp[dtile_elem(m, n)] = x; });
         gemm1<C, 128>(vw(mat(w, ch, A2M), 1, 128), vw(mat(w, ch, DOF), 1, 128), C, smem,
                       [&](int m, int n, float x) { Yp[m * 128 + n] = x; });
     }
@@ -534,76 +551,120 @@ __global__ __launch_bounds__(BTHREADS) __attribute__((amdgpu_waves_per_eu(4))) v
         float* BDp = mat(w, ch, BD);
         gemm<128, 128>(vw(mat(w, ch, QD), 1, 128), vw(mat(w, ch, DOF), 1, 128), C, vw(mat(w, ch, WW), 1, 128),
                        vw(mat(w, ch, YY), 1, 128), C, -1.f, smem,
-                       [&](int m, int n, float x) { BDp[m * 128 + n] = x; });
+                       [&](int m, int n, float x) { BDp[dtile_elem(m, n)] = x; });
     }
 }
 
 // ------------------------------------------------------------------------------------
-// State chains in fp32.  Forward (REV = false): S <- e^gamma_C S - P S + B, recording the
-// state entering every chunk; reverse: dS <- e^gamma_C dS - P^T dS + Q^T dO over the chunks
-// in reverse order, recording the gradient of every chunk's exit state.  One workgroup per
-// (sequence, value head, 16 value columns); thread (a, cg) owns row a, columns 4 cg .. + 3.
-// The chunk's 128 x 128 operand goes through LDS: the next chunk's is loaded into registers
-// while the current one is used, then stored into the other LDS buffer.
+// State chains, the forward chain's scheme: forward (REV = false) S <- e^gamma_C S - P S + B,
+// recording the state entering every chunk; reverse dS <- e^gamma_C dS - P^T dS + Q^T dO over
+// the chunks in reverse order, recording the gradient of every chunk's exit state.  One
+// workgroup of 8 waves per (sequence, value head, 16 value columns); wave x keeps rows
+// 16 x .. 16 x + 15 of the fp32 slice in registers (accumulator layout).  Per chunk the slice
+// is recorded (fp32), published in LDS as hi + lo bf16 (the B operand of the product), and
+// -P (or -P^T), stored by bwd_prep with one bf16 rounding, multiplies both halves: two MFMAs
+// per 32-step.  The operands of the next two chunks are in flight in a ring of three
+// register buffers; the value blocks of one (sequence, head) are numbered onto one XCD.
+constexpr int CH_NXCD = 8;          // workgroups are dealt to the 8 XCDs round-robin
+constexpr int CH_NVB = VD / 16;     // value blocks per (sequence, head)
+constexpr int CH_KS = KD / 32;      // 32-wide contraction steps over the state rows
+
+struct ChainOps {
+    uint4 ph[CH_KS];  // -P (or -P^T) fragments (x, s)
+    float4 b;         // B (or Q^T dO) tile (x, value block)
+    float4 gl;        // gamma_C of the wave's rows (log domain)
+};
+
+template <bool REV>
+__device__ __forceinline__ void chain_load(ChainOps& op, const Work& w, size_t ch, int x, int lane, int q4, int vb) {
+    const uint16_t* Pm = reinterpret_cast<const uint16_t*>(mat(w, ch, REV ? PT : PP));
+#pragma unroll
+    for (int s = 0; s < CH_KS; ++s) op.ph[s] = *reinterpret_cast<const uint4*>(Pm + frag(x, s, CH_KS) + lane * 8);
+    op.b = *reinterpret_cast<const float4*>(mat(w, ch, REV ? BD : BB) + ((x * 8 + vb) * 64 + lane) * 4);
+    op.gl = *reinterpret_cast<const float4*>(w.gcr + ch * 128 + 16 * x + 4 * q4);
+}
+
+template <bool REV>
+__device__ __forceinline__ void chain_step(const ChainOps& op, f32x4& S, const Work& w, size_t ch, int x, int lane,
+                                           int r16, int q4, int vb, uint16_t* sb) {
+    // record: rows 16 x + 4 q4 + e, column 16 vb + r16 of the [k][v] matrix
+    float* rec = mat(w, ch, REV ? DS : SIN) + (16 * x + 4 * q4) * 128 + 16 * vb + r16;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) rec[e * 128] = S[e];
+    // publish: pi-order fragment x / 2 of the B operand, half x % 2
+    uint2 sh, sl;
+    split_pk(S[0], S[1], sh.x, sl.x);
+    split_pk(S[2], S[3], sh.y, sl.y);
+    const int so = (int)frag(0, x >> 1, CH_KS) + fragP(x & 1, r16, q4);
+    *reinterpret_cast<uint2*>(sb + so) = sh;
+    *reinterpret_cast<uint2*>(sb + CH_KS * 512 + so) = sl;
+    lds_barrier();
+    f32x4 a0 = {ex(op.gl.x) * S[0] + op.b.x, ex(op.gl.y) * S[1] + op.b.y, ex(op.gl.z) * S[2] + op.b.z,
+                ex(op.gl.w) * S[3] + op.b.w};
+    f32x4 a2 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < CH_KS; ++s) {
+        const bf16x8 bh = as_bf16x8(*reinterpret_cast<const uint4*>(sb + s * 512 + lane * 8));
+        const bf16x8 bl = as_bf16x8(*reinterpret_cast<const uint4*>(sb + (CH_KS + s) * 512 + lane * 8));
+        a0 = mfma32(as_bf16x8(op.ph[s]), bh, a0);
+        a2 = mfma32(as_bf16x8(op.ph[s]), bl, a2);
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) S[e] = a0[e] + a2[e];
+}
+
 template <bool REV>
 __global__ __launch_bounds__(BTHREADS) void bwd_chain_kernel(ChunkMap map, int H, const float* __restrict__ s0,
                                                               float* __restrict__ s_last, Work w) {
-    __shared__ __attribute__((aligned(16))) float sP[2 * 128 * 128];   // two operand buffers
-    __shared__ __attribute__((aligned(16))) float sS[2 * 128 * 16];    // two published state blocks
-    const int nh = blockIdx.x, vb = blockIdx.y;
+    __shared__ __attribute__((aligned(16))) uint16_t sbuf[2][2 * CH_KS * 512];  // two published states
+    const int b = blockIdx.x;
+    const int xcd = b % CH_NXCD, j = b / CH_NXCD;
+    const int vb = j % CH_NVB, nh = (j / CH_NVB) * CH_NXCD + xcd;
+    if (nh >= map.N * H) return;
     const int n = nh / H, hv = nh % H;
     int64_t bos;
     int len, slot0;
     seq_info(map, n, bos, len, slot0);
     const int nch = (len + map.C - 1) / map.C;
-    const int tid = threadIdx.x, a = tid & 127, cg = tid >> 7;
-    const int v0 = 16 * vb + 4 * cg;
-    float s[4] = {0.f, 0.f, 0.f, 0.f};
+    const int tid = threadIdx.x, lane = tid & 63, x = tid >> 6;
+    const int r16 = lane & 15, q4 = lane >> 4;
+    // state tile: rows k = 16 x + 4 q4 + e, column v = 16 vb + r16; [N][H][V][K] in memory
+    const size_t srow = (((size_t)n * H + hv) * VD + 16 * vb + r16) * KD + 16 * x + 4 * q4;
+    f32x4 S = {0.f, 0.f, 0.f, 0.f};
     if (s0 != nullptr) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) s[e] = s0[(((size_t)n * H + hv) * VD + v0 + e) * KD + a];
+        const float4 v = *reinterpret_cast<const float4*>(s0 + srow);
+        S = f32x4{v.x, v.y, v.z, v.w};
     }
-    auto chunk = [&](int step) { return (size_t)(slot0 + (REV ? nch - 1 - step : step)) * H + hv; };
-    float4 pr[8];   // this thread's 8 float4 of the next operand: element (tid + 512 u) * 4
-    auto load = [&](int step) {
-        const float* Pm = mat(w, chunk(step), REV ? PP : PT);   // element (b, a) is (op P)[a][b]
-#pragma unroll
-        for (int u = 0; u < 8; ++u) pr[u] = *reinterpret_cast<const float4*>(Pm + (size_t)(tid + BTHREADS * u) * 4);
+    // step c uses ring buffer c % 3 and publishes into LDS buffer c % 2; loads are issued
+    // unconditionally (clamped to the last chunk) two steps ahead
+    const int last = nch - 1;
+    auto chunk_of = [&](int step) {
+        const int c = max(min(step, last), 0);
+        return (size_t)(slot0 + (REV ? last - c : c)) * H + hv;
     };
-    if (nch > 0) load(0);
-    for (int step = 0; step < nch; ++step) {
-        const size_t ch = chunk(step);
-        const int buf = step & 1;
-        float* P = sP + buf * 128 * 128;
-        float* S = sS + buf * 128 * 16;
-#pragma unroll
-        for (int u = 0; u < 8; ++u) *reinterpret_cast<float4*>(P + (tid + BTHREADS * u) * 4) = pr[u];
-        float* rec = mat(w, ch, REV ? DS : SIN);
-        *reinterpret_cast<float4*>(rec + a * 128 + v0) = make_float4(s[0], s[1], s[2], s[3]);
-        *reinterpret_cast<float4*>(S + a * 16 + 4 * cg) = make_float4(s[0], s[1], s[2], s[3]);
-        const float gc = ex(w.gcr[ch * 128 + a]);
-        const float4 badd = *reinterpret_cast<const float4*>(mat(w, ch, REV ? BD : BB) + a * 128 + v0);
-        __syncthreads();
-        if (step + 1 < nch) load(step + 1);
-        float x[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 16
-        for (int b = 0; b < 128; ++b) {
-            const float p = P[b * 128 + a];
-            const float4 sb = *reinterpret_cast<const float4*>(S + b * 16 + 4 * cg);
-            x[0] += p * sb.x;
-            x[1] += p * sb.y;
-            x[2] += p * sb.z;
-            x[3] += p * sb.w;
-        }
-        s[0] = gc * s[0] - x[0] + badd.x;
-        s[1] = gc * s[1] - x[1] + badd.y;
-        s[2] = gc * s[2] - x[2] + badd.z;
-        s[3] = gc * s[3] - x[3] + badd.w;
+    ChainOps op0, op1, op2;
+    auto step = [&](ChainOps& next, int cload, const ChainOps& cur, int c, int buf) {
+        chain_load<REV>(next, w, chunk_of(cload), x, lane, q4, vb);
+        chain_step<REV>(cur, S, w, chunk_of(c), x, lane, r16, q4, vb, sbuf[buf]);
+    };
+    if (nch > 0) {
+        chain_load<REV>(op0, w, chunk_of(0), x, lane, q4, vb);
+        chain_load<REV>(op1, w, chunk_of(1), x, lane, q4, vb);
     }
-    if (s_last != nullptr) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) s_last[(((size_t)n * H + hv) * VD + v0 + e) * KD + a] = s[e];
+    for (int c = 0; c < nch; c += 6) {
+        step(op2, c + 2, op0, c, 0);
+        if (c + 1 >= nch) break;
+        step(op0, c + 3, op1, c + 1, 1);
+        if (c + 2 >= nch) break;
+        step(op1, c + 4, op2, c + 2, 0);
+        if (c + 3 >= nch) break;
+        step(op2, c + 5, op0, c + 3, 1);
+        if (c + 4 >= nch) break;
+        step(op0, c + 6, op1, c + 4, 0);
+        if (c + 5 >= nch) break;
+        step(op1, c + 7, op2, c + 5, 1);
     }
+    if (s_last != nullptr) *reinterpret_cast<float4*>(s_last + srow) = make_float4(S[0], S[1], S[2], S[3]);
 }
 
 // ------------------------------------------------------------------------------------
@@ -957,11 +1018,12 @@ hipError_t launch_t(const In& in, const ChunkMap& map, int nslots, int N, int H,
         hipLaunchKernelGGL((bwd_prep_kernel<C, PD, L2>), dim3(nslots, H), dim3(BTHREADS), 0, s, in, map, H, Hk, scale,
                            w);
     if (stages & 2) {
+        const int groups = (N * H + CH_NXCD - 1) / CH_NXCD;
         if (nslots > 0)
-            hipLaunchKernelGGL((bwd_chain_kernel<false>), dim3(N * H, VD / 16), dim3(BTHREADS), 0, s, map, H,
+            hipLaunchKernelGGL((bwd_chain_kernel<false>), dim3(groups * CH_NXCD * CH_NVB), dim3(BTHREADS), 0, s, map, H,
                                h0, (float*)nullptr, w);
-        hipLaunchKernelGGL((bwd_chain_kernel<true>), dim3(N * H, VD / 16), dim3(BTHREADS), 0, s, map, H, dht,
-                           dh0, w);
+        hipLaunchKernelGGL((bwd_chain_kernel<true>), dim3(groups * CH_NXCD * CH_NVB), dim3(BTHREADS), 0, s, map, H,
+                           dht, dh0, w);
     }
     if (!(stages & 4)) return hipGetLastError();
     if (nslots > 0)
