@@ -315,7 +315,7 @@ __device__ __forceinline__ void intra_item(
             }
             *reinterpret_cast<float2*>(gmid + R * KD + d0) = make_float2(gmv[0], gmv[1]);
             *reinterpret_cast<float2*>(egm + R * KD + d0) = make_float2(e_gm[0], e_gm[1]);
-            if (R == 0) st_nt(mptr<float2>(ws.gC + ch * KD, d0 * 4u), make_float2(ex(gcl[0]), ex(gcl[1])));
+            if (R == 0) *mptr<float2>(ws.gC + ch * KD, d0 * 4u) = make_float2(ex(gcl[0]), ex(gcl[1]));
             if constexpr (!PER_DIM) {
                 if ((tid & 63) == 0) {
 #pragma unroll
@@ -783,8 +783,8 @@ __device__ __forceinline__ void intra_item(
 #pragma unroll
         for (int e = 0; e < 4; ++e) bt[e] = b0[e] + b1[e];
         const uint2 ph = make_uint2(pack_bf2(-pt[0], -pt[1]), pack_bf2(-pt[2], -pt[3]));
-        st_nt(mptr<uint2>(PnI, (frag32(x, dt >> 1, KD / 32) + fragP(dt & 1, r16, q4)) * 2u), ph);
-        st_nt(mptr<float4>(BmI, ((x * (VD / 16) + dt) * 64 + lane) * 16u), make_float4(bt[0], bt[1], bt[2], bt[3]));
+        *mptr<uint2>(PnI, (frag32(x, dt >> 1, KD / 32) + fragP(dt & 1, r16, q4)) * 2u) = ph;
+        *mptr<float4>(BmI, ((x * (VD / 16) + dt) * 64 + lane) * 16u) = make_float4(bt[0], bt[1], bt[2], bt[3]);
     }
     // Q^T tile (rows d in dt, columns i in I) = (qg)^T - w^T A2^T; U^T tile (rows v in dt,
     // columns i in I) = u^T A2^T.  A2 fragment (I, s) is the B operand of both.
@@ -801,9 +801,9 @@ __device__ __forceinline__ void intra_item(
             qt = mfma32(as_bf16x8(neg_bf16x8(wh[s])), a2, qt);
             ut = mfma32(as_bf16x8(uh[s]), a2, ut);
         }
-        st_nt(mptr<uint2>(QpI, (frag32(I, dt >> 1, KD / 32) + fragP(dt & 1, r16, q4)) * 2u),
-              make_uint2(pack_bf2(qt[0], qt[1]), pack_bf2(qt[2], qt[3])));
-        st_nt(mptr<uint2>(UpI, ((I * (VD / 16) + dt) * 64 + lane) * 8u), make_uint2(pack_bf2(ut[0], ut[1]), pack_bf2(ut[2], ut[3])));
+        *mptr<uint2>(QpI, (frag32(I, dt >> 1, KD / 32) + fragP(dt & 1, r16, q4)) * 2u) =
+            make_uint2(pack_bf2(qt[0], qt[1]), pack_bf2(qt[2], qt[3]));
+        *mptr<uint2>(UpI, ((I * (VD / 16) + dt) * 64 + lane) * 8u) = make_uint2(pack_bf2(ut[0], ut[1]), pack_bf2(ut[2], ut[3]));
     }
 }
 
