@@ -5,8 +5,9 @@
 //
 // One workgroup of 8 waves per (chunk slot, head); the LDS it needs leaves room for one
 // workgroup per CU, so the two waves per SIMD are what hides latency.  Phases:
-//   E    every thread owns a 16-row x 2-column block of the chunk (one 16-row tile) and
-//        issues all of its loads (g, k, v) at once.  gamma = prefix sum of g inside the tile
+//   E    every thread owns a 16-row x 2-column block of the chunk (one 16-row tile); its
+//        loads are issued one item ahead (g and beta when the previous item's solve starts,
+//        k and v at its phase PQ).  gamma = prefix sum of g inside the tile
 //        plus the totals of the tiles above (through LDS).  Per-element decay factors
 //        relative to the tile's middle row m, and the element-wise outputs: exp(gamma_C),
 //        kg = exp(gamma_C - gamma) k (split; fragment-major scratch read back by this
@@ -18,7 +19,9 @@
 //        pivots: for rows i in tile R and columns j in tile J <= R,
 //          exp(g_i - g_j) = [exp(g_i - g_m(R)) exp(g_m(R) - g_m(J))] * exp(g_m(J) - g_j)
 //        so no factor exceeds exp(half a tile's gate span) and the product never
-//        overflows.  A uses hi/lo split operands (three MFMAs); A2 feeds only the output
+//        overflows.  The row operands times exp(g_i - g_m(R)) are formed once per row and
+//        32-column step; a tile below the diagonal multiplies them by the pivot ratio
+//        only.  A uses hi/lo split operands (three MFMAs); A2 feeds only the output
 //        and uses single bf16 operands (stored transposed, scratch).  Per-head gates use
 //        raw q, k (exact bf16 products) and apply the scalar decay afterwards.  Tile rows w
 //        and NT-1-w form one list of NT+1 tiles shared by waves w and w+4.  qg (scratch) is
@@ -116,50 +119,68 @@ __device__ __forceinline__ uint4 neg_bf16x8(const uint4& a) {
 }
 
 // Phase E inputs of one item, held in registers: thread (R = wave, d0 = 2 (lane)) owns rows
-// 16 R .. 16 R + 15 and columns d0, d0 + 1; loaded one item ahead.  Rows past the end of
-// the sequence read its last row (masked when used), so the loads stay unconditional.
+// 16 R .. 16 R + 15 and columns d0, d0 + 1; loaded one item ahead, the gates and beta early
+// (when the solve starts) and k and v later (at phase PQ), so that each workgroup's loads
+// reach memory in two smaller bursts and ahead of its result stores.  Rows past the end of the sequence read its last row (masked
+// when used), so the loads stay unconditional.
 struct EIn {
     float2 g[16];
     uint32_t k[16], v[16];
     float b;
 };
 
-template <int C, bool PER_DIM>
-__device__ __forceinline__ void e_load(EIn& in, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-                                       const float* __restrict__ g, const float* __restrict__ beta,
-                                       const ChunkMap& map, int H, int Hk, int item, int tid) {
-    // Every register is written on every path (no item or an empty chunk slot load token 0,
-    // which exists whenever there are items), so the previous contents are dead once this
-    // is called and nothing has to be kept alive across the item.
-    item = max(item, 0);
-    const int slot = item / H, h = item % H;
+// Where an item's rows are.  Every item exists when this is called with item >= 0; no item
+// (-1) reads token 0 of item 0, which exists whenever there are items, so that the loads
+// stay unconditional and every register of EIn is written on every path.
+struct ELoc {
     int64_t tok0;
-    int rows;
-    slot_chunk(map, slot, tok0, rows);
-    const uint32_t last = (uint32_t)max(rows - 1, 0);
-    // value head h reads key head h / (H / Hk); v and g have H heads.  Item bases are
-    // uniform; per lane only 32-bit byte offsets of rows min(16 R + ii, last) are formed.
-    const uint32_t rs = (uint32_t)H * KD, rsk = (uint32_t)Hk * KD;
-    const uint16_t* kb = k + ((size_t)tok0 * rsk + (size_t)(h / (H / Hk)) * KD);
-    const uint16_t* vb = v + ((size_t)tok0 * rs + (size_t)h * KD);
+    int rows, h;
+};
+
+__device__ __forceinline__ ELoc e_locate(const ChunkMap& map, int H, int item) {
+    item = max(item, 0);
+    ELoc l;
+    l.h = item % H;
+    slot_chunk(map, item / H, l.tok0, l.rows);
+    return l;
+}
+
+template <int C, bool PER_DIM>
+__device__ __forceinline__ void e_load_g(EIn& in, const float* g, const float* beta, const ELoc& l, int H, int tid) {
+    // per lane only 32-bit byte offsets of rows min(16 R + ii, last) from uniform item bases
+    const uint32_t last = (uint32_t)max(l.rows - 1, 0);
+    const uint32_t rs = (uint32_t)H * KD;
     const uint32_t R = (uint32_t)min(tid >> 6, C / 16 - 1), d0 = 2u * (uint32_t)(tid & 63);
-    in.b = *cptr<float>(beta + ((size_t)tok0 * H + h), min((uint32_t)tid, last) * (uint32_t)H * 4u);
-    {
-        const uint32_t r0 = 16u * R;
-        const uint32_t ok0 = (r0 * rsk + d0) * 2u, okl = (last * rsk + d0) * 2u;   // k bytes
-        const uint32_t ov0 = (r0 * rs + d0) * 2u, ovl = (last * rs + d0) * 2u;     // v bytes
+    in.b = *cptr<float>(beta + ((size_t)l.tok0 * H + l.h), min((uint32_t)tid, last) * (uint32_t)H * 4u);
+    const uint32_t r0 = 16u * R;
+    const uint32_t og0 = (r0 * rs + d0) * 4u, ogl = (last * rs + d0) * 4u;   // g bytes (per dimension)
 #pragma unroll
-        for (int ii = 0; ii < 16; ++ii) {
-            if constexpr (PER_DIM) {
-                // g rows have the byte offsets of v rows, doubled
-                in.g[ii] = *cptr<float2>(g + ((size_t)tok0 * rs + (size_t)h * KD), 2u * min(ov0 + ii * rs * 2u, ovl));
-            } else {
-                const float s1 = *cptr<float>(g + ((size_t)tok0 * H + h), min(r0 + ii, last) * (uint32_t)H * 4u);
-                in.g[ii] = make_float2(s1, s1);
-            }
-            in.k[ii] = *cptr<uint32_t>(kb, min(ok0 + ii * rsk * 2u, okl));
-            in.v[ii] = *cptr<uint32_t>(vb, min(ov0 + ii * rs * 2u, ovl));
+    for (int ii = 0; ii < 16; ++ii) {
+        if constexpr (PER_DIM) {
+            in.g[ii] = *cptr<float2>(g + ((size_t)l.tok0 * rs + (size_t)l.h * KD), min(og0 + ii * rs * 4u, ogl));
+        } else {
+            const float s1 = *cptr<float>(g + ((size_t)l.tok0 * H + l.h), min(r0 + ii, last) * (uint32_t)H * 4u);
+            in.g[ii] = make_float2(s1, s1);
         }
+    }
+}
+
+template <int C>
+__device__ __forceinline__ void e_load_kv(EIn& in, const uint16_t* k, const uint16_t* v, const ELoc& l, int H, int Hk,
+                                          int tid) {
+    // value head h reads key head h / (H / Hk); v has H heads
+    const uint32_t last = (uint32_t)max(l.rows - 1, 0);
+    const uint32_t rs = (uint32_t)H * KD, rsk = (uint32_t)Hk * KD;
+    const uint16_t* kb = k + ((size_t)l.tok0 * rsk + (size_t)(l.h / (H / Hk)) * KD);
+    const uint16_t* vb = v + ((size_t)l.tok0 * rs + (size_t)l.h * KD);
+    const uint32_t R = (uint32_t)min(tid >> 6, C / 16 - 1), d0 = 2u * (uint32_t)(tid & 63);
+    const uint32_t r0 = 16u * R;
+    const uint32_t ok0 = (r0 * rsk + d0) * 2u, okl = (last * rsk + d0) * 2u;   // k bytes
+    const uint32_t ov0 = (r0 * rs + d0) * 2u, ovl = (last * rs + d0) * 2u;     // v bytes
+#pragma unroll
+    for (int ii = 0; ii < 16; ++ii) {
+        in.k[ii] = *cptr<uint32_t>(kb, min(ok0 + ii * rsk * 2u, okl));
+        in.v[ii] = *cptr<uint32_t>(vb, min(ov0 + ii * rs * 2u, ovl));
     }
 }
 
@@ -175,6 +196,9 @@ constexpr int PAD_WORDS = 1024;  // per workgroup: ITHREADS + 16 * (N - 1) words
 template <int N>
 __device__ __forceinline__ void vm_pad(uint32_t* p) {
     static_assert(ITHREADS + 16 * (N - 1) <= PAD_WORDS, "pad area");
+    // the stores must follow the loads issued before: without this the compiler is free to
+    // move them ahead (they touch no input), and then they pad nothing
+    asm volatile("" ::: "memory");
 #pragma unroll
     for (int i = 0; i < N; ++i) p[16 * i] = 0u;
 }
@@ -183,8 +207,8 @@ __device__ __forceinline__ void vm_pad(uint32_t* p) {
 // phase E inputs on entry and those of next_item (-1: none) on exit.
 template <int C, bool PER_DIM, bool L2N>
 __device__ __forceinline__ void intra_item(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    const float* __restrict__ g, const float* __restrict__ beta, const ChunkMap& map, int H, int Hk,
+    const uint16_t* q, const uint16_t* k, const uint16_t* v,
+    const float* g, const float* beta, const ChunkMap& map, int H, int Hk,
     float scale, const Work& ws, unsigned char* smem, int slot, int h, size_t sc, EIn& ein, int next_item,
     uint32_t* pad) {
     using S = IntraShape<C>;
@@ -209,7 +233,9 @@ __device__ __forceinline__ void intra_item(
     int rows;
     slot_chunk(map, slot, tok0, rows);
     if (rows == 0) {
-        e_load<C, PER_DIM>(ein, k, v, g, beta, map, H, Hk, next_item, tid);
+        const ELoc nl = e_locate(map, H, next_item);
+        e_load_g<C, PER_DIM>(ein, g, beta, nl, H, tid);
+        e_load_kv<C>(ein, k, v, nl, H, Hk, tid);
         vm_pad<2 * (KD / 16) + 2 * NT>(pad);
         return;
     }
@@ -431,72 +457,113 @@ __device__ __forceinline__ void intra_item(
     f32x4 accA[S::SMAX];
     uint2 a2keep[S::SMAX];
     uint4 qgkeep[KD / 32];
+    f32x4 acc1[S::SMAX], acc2[S::SMAX];
 #pragma unroll
     for (int ks = 0; ks < KD / 32; ++ks) qgkeep[ks] = make_uint4(0u, 0u, 0u, 0u);
 #pragma unroll
     for (int s = 0; s < S::SMAX; ++s) {
-        accA[s] = f32x4{0.f, 0.f, 0.f, 0.f};
-        a2keep[s] = make_uint2(0u, 0u);
-        const int p = (part ? S::HF : 0) + s;  // position in the row pair's tile list
-        if (!aa_active || p >= NT + 1 || (part == 0 && s >= S::HF)) continue;
-        const int o = (p <= cp) ? 0 : 1;
-        const int R = Rown[o];
-        const int J = (o == 0) ? p : p - cp - 1;
-        const int i = 16 * R + r16, j = 16 * J + r16;
-        const float rk = o ? rk2[1] : rk2[0], rq = o ? rq2[1] : rq2[0];
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f}, acc2 = {0.f, 0.f, 0.f, 0.f};
+        acc1[s] = f32x4{0.f, 0.f, 0.f, 0.f};
+        acc2[s] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    // the wave's tiles: positions p in [plo, phi) of the row pair's list; p <= cp is tile
+    // (cp, p) of the first row, p > cp tile (NT-1-cp, p-cp-1) of the second
+    const int plo = part ? S::HF : 0, phi = part ? NT + 1 : S::HF;
+    if constexpr (PER_DIM) {
+        // Row by row: the row's operands times exp(gamma_i - gamma_m(R)) (and its L2 scale)
+        // are formed once per 32-column step and reused by every tile of the row; a tile
+        // below the diagonal multiplies them by F = exp(gamma_m(R) - gamma_m(J)) only.
 #pragma unroll
-        for (int ks = 0; ks < KD / 32; ++ks) {
-            const int dd = 32 * ks + 8 * q4;
-            const uint4 krv = o ? kfr[1][ks] : kfr[0][ks];
-            const uint4 qrv = o ? qfr[1][ks] : qfr[0][ks];
-            if constexpr (PER_DIM) {
-                float kf[8], qf[8], ep[8];
-                unpack8(krv, kf);
-                unpack8(qrv, qf);
+        for (int o = 0; o < 2; ++o) {
+            const bool has = aa_active && (o == 0 ? plo <= cp : phi - 1 > cp);
+            if (!has) continue;
+            const int R = Rown[o];
+            const int i = 16 * R + r16;
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    kf[e] *= rk;
-                    qf[e] *= rq;
+            for (int ks = 0; ks < KD / 32; ++ks) {
+                const int dd = 32 * ks + 8 * q4;
+                float kE[8], qE[8];
+                unpack8(kfr[o][ks], kE);
+                unpack8(qfr[o][ks], qE);
+                {
+                    const float4* epp = reinterpret_cast<const float4*>(Ep + i * S::EP_LD + dd);
+                    const float4 e0 = epp[0], e1 = epp[1];
+                    const float ep[8] = {e0.x, e0.y, e0.z, e0.w, e1.x, e1.y, e1.z, e1.w};
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        kE[e] *= (L2N ? rk2[o] : 1.f) * ep[e];
+                        qE[e] *= (L2N ? rq2[o] : 1.f) * ep[e];
+                    }
                 }
-                const float4* epp = reinterpret_cast<const float4*>(Ep + i * S::EP_LD + dd);
-                const float4 e0 = epp[0], e1 = epp[1];
-                ep[0] = e0.x; ep[1] = e0.y; ep[2] = e0.z; ep[3] = e0.w;
-                ep[4] = e1.x; ep[5] = e1.y; ep[6] = e1.z; ep[7] = e1.w;
-                if (J < R) {
-                    const float4* fp = reinterpret_cast<const float4*>(F + (R * (R - 1) / 2 + J) * KD + dd);
-                    const float4 f0 = fp[0], f1 = fp[1];
-                    ep[0] *= f0.x; ep[1] *= f0.y; ep[2] *= f0.z; ep[3] *= f0.w;
-                    ep[4] *= f1.x; ep[5] *= f1.y; ep[6] *= f1.z; ep[7] *= f1.w;
-                } else {
-                    // qg = scale q exp(gamma) = scale q Ep exp(gamma_m): (C, K) fragment (R, ks)
-                    const float4* gp = reinterpret_cast<const float4*>(egm + R * KD + dd);
-                    const float4 g0 = gp[0], g1 = gp[1];
-                    const float eg[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
-                    uint4 pq;
-                    pq.x = pack_bf2(scale * qf[0] * ep[0] * eg[0], scale * qf[1] * ep[1] * eg[1]);
-                    pq.y = pack_bf2(scale * qf[2] * ep[2] * eg[2], scale * qf[3] * ep[3] * eg[3]);
-                    pq.z = pack_bf2(scale * qf[4] * ep[4] * eg[4], scale * qf[5] * ep[5] * eg[5]);
-                    pq.w = pack_bf2(scale * qf[6] * ep[6] * eg[6], scale * qf[7] * ep[7] * eg[7]);
-                    qgkeep[ks] = pq;
+#pragma unroll
+                for (int s = 0; s < S::SMAX; ++s) {
+                    const int p = plo + s;
+                    if (p >= phi || (p <= cp) != (o == 0)) continue;
+                    const int J = (o == 0) ? p : p - cp - 1;
+                    const int j = 16 * J + r16;
+                    uint4 ah, al, aq;
+                    if (J < R) {
+                        const float4* fp = reinterpret_cast<const float4*>(F + (R * (R - 1) / 2 + J) * KD + dd);
+                        const float4 f0 = fp[0], f1 = fp[1];
+                        const float f[8] = {f0.x, f0.y, f0.z, f0.w, f1.x, f1.y, f1.z, f1.w};
+                        float rk[8], rq[8];
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) {
+                            rk[e] = kE[e] * f[e];
+                            rq[e] = qE[e] * f[e];
+                        }
+                        split2(rk[0], rk[1], ah.x, al.x);
+                        split2(rk[2], rk[3], ah.y, al.y);
+                        split2(rk[4], rk[5], ah.z, al.z);
+                        split2(rk[6], rk[7], ah.w, al.w);
+                        aq.x = pack_bf2(rq[0], rq[1]);
+                        aq.y = pack_bf2(rq[2], rq[3]);
+                        aq.z = pack_bf2(rq[4], rq[5]);
+                        aq.w = pack_bf2(rq[6], rq[7]);
+                    } else {
+                        // qg = scale q exp(gamma) = scale (q Ep) exp(gamma_m): (C, K) fragment (R, ks)
+                        const float4* gp = reinterpret_cast<const float4*>(egm + R * KD + dd);
+                        const float4 g0 = gp[0], g1 = gp[1];
+                        const float eg[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+                        uint4 pq;
+                        pq.x = pack_bf2(scale * qE[0] * eg[0], scale * qE[1] * eg[1]);
+                        pq.y = pack_bf2(scale * qE[2] * eg[2], scale * qE[3] * eg[3]);
+                        pq.z = pack_bf2(scale * qE[4] * eg[4], scale * qE[5] * eg[5]);
+                        pq.w = pack_bf2(scale * qE[6] * eg[6], scale * qE[7] * eg[7]);
+                        qgkeep[ks] = pq;
+                        split2(kE[0], kE[1], ah.x, al.x);
+                        split2(kE[2], kE[3], ah.y, al.y);
+                        split2(kE[4], kE[5], ah.z, al.z);
+                        split2(kE[6], kE[7], ah.w, al.w);
+                        aq.x = pack_bf2(qE[0], qE[1]);
+                        aq.y = pack_bf2(qE[2], qE[3]);
+                        aq.z = pack_bf2(qE[4], qE[5]);
+                        aq.w = pack_bf2(qE[6], qE[7]);
+                    }
+                    const bf16x8 ahi = as_bf16x8(ah), alo = as_bf16x8(al), aqv = as_bf16x8(aq);
+                    const bf16x8 bhi = as_bf16x8(*reinterpret_cast<const uint4*>(colh + j * S::COL_LD + dd));
+                    const bf16x8 blo = as_bf16x8(*reinterpret_cast<const uint4*>(coll + j * S::COL_LD + dd));
+                    acc1[s] = mfma32(ahi, bhi, acc1[s]);
+                    acc1[s] = mfma32(alo, bhi, acc1[s]);
+                    acc1[s] = mfma32(ahi, blo, acc1[s]);
+                    acc2[s] = mfma32(bhi, aqv, acc2[s]);   // A2^T tile: rows j, columns i
                 }
-                uint4 ah, al, aq;
-                split2(kf[0] * ep[0], kf[1] * ep[1], ah.x, al.x);
-                split2(kf[2] * ep[2], kf[3] * ep[3], ah.y, al.y);
-                split2(kf[4] * ep[4], kf[5] * ep[5], ah.z, al.z);
-                split2(kf[6] * ep[6], kf[7] * ep[7], ah.w, al.w);
-                aq.x = pack_bf2(qf[0] * ep[0], qf[1] * ep[1]);
-                aq.y = pack_bf2(qf[2] * ep[2], qf[3] * ep[3]);
-                aq.z = pack_bf2(qf[4] * ep[4], qf[5] * ep[5]);
-                aq.w = pack_bf2(qf[6] * ep[6], qf[7] * ep[7]);
-                const bf16x8 ahi = as_bf16x8(ah), alo = as_bf16x8(al), aqv = as_bf16x8(aq);
-                const bf16x8 bhi = as_bf16x8(*reinterpret_cast<const uint4*>(colh + j * S::COL_LD + dd));
-                const bf16x8 blo = as_bf16x8(*reinterpret_cast<const uint4*>(coll + j * S::COL_LD + dd));
-                acc = mfma32(ahi, bhi, acc);
-                acc = mfma32(alo, bhi, acc);
-                acc = mfma32(ahi, blo, acc);
-                acc2 = mfma32(bhi, aqv, acc2);   // A2^T tile: rows j, columns i
-            } else {
+            }
+        }
+    } else {
+#pragma unroll
+        for (int s = 0; s < S::SMAX; ++s) {
+            const int p = plo + s;
+            if (!aa_active || p >= phi) continue;
+            const int o = (p <= cp) ? 0 : 1;
+            const int R = Rown[o];
+            const int J = (o == 0) ? p : p - cp - 1;
+            const int i = 16 * R + r16, j = 16 * J + r16;
+            const float rq = o ? rq2[1] : rq2[0];
+#pragma unroll
+            for (int ks = 0; ks < KD / 32; ++ks) {
+                const int dd = 32 * ks + 8 * q4;
+                const uint4 krv = o ? kfr[1][ks] : kfr[0][ks];
+                const uint4 qrv = o ? qfr[1][ks] : qfr[0][ks];
                 const uint4 kx = *cptr<uint4>(kbase, ((uint32_t)min(j, rows - 1) * rsk + dd) * 2u);
                 const bf16x8 b = as_bf16x8((j < rows) ? kx : make_uint4(0, 0, 0, 0));
                 if (J == R) {
@@ -510,10 +577,21 @@ __device__ __forceinline__ void intra_item(
                     pq.w = pack_bf2(f * qf[6], f * qf[7]);
                     qgkeep[ks] = pq;
                 }
-                acc = mfma32(as_bf16x8(krv), b, acc);
-                acc2 = mfma32(b, as_bf16x8(qrv), acc2);   // A2^T tile: rows j, columns i
+                acc1[s] = mfma32(as_bf16x8(krv), b, acc1[s]);
+                acc2[s] = mfma32(b, as_bf16x8(qrv), acc2[s]);   // A2^T tile: rows j, columns i
             }
         }
+    }
+#pragma unroll
+    for (int s = 0; s < S::SMAX; ++s) {
+        accA[s] = f32x4{0.f, 0.f, 0.f, 0.f};
+        a2keep[s] = make_uint2(0u, 0u);
+        const int p = plo + s;
+        if (!aa_active || p >= phi) continue;
+        const int o = (p <= cp) ? 0 : 1;
+        const int R = Rown[o];
+        const int J = (o == 0) ? p : p - cp - 1;
+        const float rq = o ? rq2[1] : rq2[0];
         // A tile: rows i = 16 R + 4 q4 + rr, column j = 16 J + r16
         // A2^T tile: rows j = 16 J + 4 q4 + rr, column i = 16 R + r16
         float a2v[4];
@@ -521,7 +599,7 @@ __device__ __forceinline__ void intra_item(
         for (int rr = 0; rr < 4; ++rr) {
             const int ii = 16 * R + 4 * q4 + rr, jj = 16 * J + r16;
             const int i2 = 16 * R + r16, j2 = 16 * J + 4 * q4 + rr;
-            float a = acc[rr], a2 = acc2[rr];
+            float a = acc1[s][rr], a2 = acc2[s][rr];
             if constexpr (!PER_DIM) {
                 a *= (jj <= ii) ? ex(grow[ii] - grow[jj]) : 0.f;
                 a2 *= (j2 <= i2) ? ex(grow[i2] - grow[j2]) : 0.f;
@@ -554,6 +632,8 @@ __device__ __forceinline__ void intra_item(
         const int f = wave + IWAVES * i;  // fragment (f / NS, f % NS)
         kgr[i] = *cptr<u32x4v>(kgS, (frag32(f / NS, f % NS, C / 32) + lane * 8) * 2u);
     }
+    // the gates and beta of the next item (phase E inputs), in flight from here on
+    const ELoc nl = e_locate(map, H, next_item);
 #pragma unroll
     for (int s = 0; s < S::SMAX; ++s) {
         const int p = (part ? S::HF : 0) + s;
@@ -645,6 +725,8 @@ __device__ __forceinline__ void intra_item(
             }
     }
     lds_barrier();
+    // the gates and beta of the next item (phase E inputs), in flight from here on
+    e_load_g<C, PER_DIM>(ein, g, beta, nl, H, tid);
     // Blocked forward substitution for [w | u] = (I + A)^-1 diag(beta) [exp(gamma) k | v], wave
     // dt producing columns 16 dt .. + 15 of each:  Z_R = T'_RR Y_R - sum_{J<R} M_RJ Z_J.  The Z
     // tiles stay in registers, split, in the D layout (lane (r16, q4), element e: row
@@ -704,9 +786,9 @@ __device__ __forceinline__ void intra_item(
     }
 
     // ------------------------------------------------------------------ phase PQ
-    // the next item's phase E inputs, in flight through PQ (nothing below waits on the
-    // vector memory counter before the next item uses them)
-    e_load<C, PER_DIM>(ein, k, v, g, beta, map, H, Hk, next_item, tid);
+    // k and v of the next item (the rest of its phase E inputs), in flight through PQ (nothing
+    // below waits on the vector memory counter before the next item uses them)
+    e_load_kv<C>(ein, k, v, nl, H, Hk, tid);
     lds_barrier();  // every wave is done with the solve operands in R2
     // kg^T to R1 (high part from scratch, low part kept since phase E); the A2 fragments and
     // qg tiles kept since phase AA2 to R2
@@ -766,7 +848,7 @@ __device__ __forceinline__ void intra_item(
     float* BmI = ws.Bm + ch * KD * VD;
     uint16_t* QpI = ws.Qp + ch * C * KD;
     uint16_t* UpI = ws.Up + ch * C * VD;
-#pragma unroll 1
+#pragma unroll
     for (int x = 0; x < KD / 16; ++x) {
         // P (stored with one bf16 rounding) from the high parts only; B split
         f32x4 pt = {0.f, 0.f, 0.f, 0.f}, b0 = pt, b1 = pt;
@@ -811,13 +893,17 @@ __device__ __forceinline__ void intra_item(
 // keeps its scratch in slot b, so the scratch of all workgroups stays cache-resident.
 template <int C, bool PER_DIM, bool L2N>
 __global__ __launch_bounds__(ITHREADS) void intra_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    const float* __restrict__ g, const float* __restrict__ beta, ChunkMap map, int H, int Hk,
-    float scale, Work ws, int nitems, uint32_t* __restrict__ pad_all) {
+    const uint16_t* q, const uint16_t* k, const uint16_t* v,
+    const float* g, const float* beta, ChunkMap map, int H, int Hk,
+    float scale, Work ws, int nitems, uint32_t* pad_all) {
     __shared__ __attribute__((aligned(16))) unsigned char smem[IntraShape<C>::BYTES];
     uint32_t* pad = pad_all + blockIdx.x * PAD_WORDS + threadIdx.x;
     EIn ein;
-    e_load<C, PER_DIM>(ein, k, v, g, beta, map, H, Hk, blockIdx.x < nitems ? (int)blockIdx.x : -1, threadIdx.x);
+    {
+        const ELoc l0 = e_locate(map, H, blockIdx.x < nitems ? (int)blockIdx.x : -1);
+        e_load_g<C, PER_DIM>(ein, g, beta, l0, H, threadIdx.x);
+        e_load_kv<C>(ein, k, v, l0, H, Hk, threadIdx.x);
+    }
     vm_pad<2 * (KD / 16) + 2 * (C / 16)>(pad);
     for (int item = blockIdx.x; item < nitems; item += gridDim.x) {
         // the previous item is done with LDS.  An LDS-only barrier: __syncthreads() would also
