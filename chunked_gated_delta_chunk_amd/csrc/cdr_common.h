@@ -144,13 +144,21 @@ struct ChunkMap {
     int32_t nchunk;     // ceil(T / C), fixed length only
 };
 
+// cu_seqlens entries, read at wave-uniform indices through the constant address space: they
+// become scalar loads (scalar cache, waited on apart from the vector memory operations, so a
+// lookup does not wait for the loads and stores a kernel keeps in flight)
+__device__ __forceinline__ int cu_at(const ChunkMap& m, int i) {
+    typedef const int32_t __attribute__((address_space(4))) cint32;
+    return ((const cint32*)m.cu)[i];
+}
+
 __device__ __forceinline__ void seq_info(const ChunkMap& m, int n, int64_t& bos, int& len, int& slot0) {
     if (m.cu == nullptr) {
         bos = (int64_t)n * m.T;
         len = m.T;
         slot0 = n * m.nchunk;
     } else {
-        const int a = m.cu[n], b = m.cu[n + 1];
+        const int a = cu_at(m, n), b = cu_at(m, n + 1);
         bos = a;
         len = b - a;
         slot0 = a / m.C + n;
@@ -167,10 +175,10 @@ __device__ __forceinline__ void slot_chunk(const ChunkMap& m, int slot, int64_t&
         int lo = 0, hi = m.N - 1;  // largest n with cu[n]/C + n <= slot
         while (lo < hi) {
             const int mid = (lo + hi + 1) >> 1;
-            if (m.cu[mid] / m.C + mid <= slot) lo = mid; else hi = mid - 1;
+            if (cu_at(m, mid) / m.C + mid <= slot) lo = mid; else hi = mid - 1;
         }
         n = lo;
-        c = slot - (m.cu[n] / m.C + n);
+        c = slot - (cu_at(m, n) / m.C + n);
     }
     int64_t bos;
     int len, slot0;

@@ -259,14 +259,17 @@ __device__ __forceinline__ void intra_item(
     const int cp = wave & 3, part = wave >> 2;
     const bool aa_active = cp < NT / 2;
     const int Rown[2] = {cp, NT - 1 - cp};
+    // The second wave of a pair has no tile in the first row (its tiles start at HF > cp), so
+    // only the first wave loads that row.
     uint4 kfr[2][KD / 32], qfr[2][KD / 32];
 #pragma unroll
-    for (int o = 0; o < 2; ++o) {
+    for (int o = 1; o >= 0; --o) {
         const uint32_t ro = ((uint32_t)min(16 * Rown[o] + r16, rows - 1) * rsk + 8u * q4) * 2u;
+        const bool need = o == 1 || part == 0;
 #pragma unroll
         for (int ks = 0; ks < KD / 32; ++ks) {
-            kfr[o][ks] = *cptr<uint4>(kbase, ro + 64u * ks);
-            qfr[o][ks] = *cptr<uint4>(qbase, ro + 64u * ks);
+            kfr[o][ks] = need ? *cptr<uint4>(kbase, ro + 64u * ks) : make_uint4(0u, 0u, 0u, 0u);
+            qfr[o][ks] = need ? *cptr<uint4>(qbase, ro + 64u * ks) : make_uint4(0u, 0u, 0u, 0u);
         }
     }
     // exp(gamma) k and v of the thread's phase E block as 16-byte fragment slots [hh][c],
