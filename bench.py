@@ -273,9 +273,11 @@ def cpu_baseline(inp, w, budget_s):
 
     def run(tsub):
         sl = lambda t: None if t is None else t[:, :tsub].contiguous()  # noqa: E731
+        # packed sequences: the prefix ends every sequence at token tsub (later ones empty)
+        cu = None if inp.cu_seqlens is None else inp.cu_seqlens.clamp(max=tsub)
         t0 = time.perf_counter()
         oracle.recurrent_fwd(sl(inp.q), sl(inp.k), sl(inp.v), sl(inp.g), sl(inp.beta),
-                             initial_state=inp.initial_state)
+                             initial_state=inp.initial_state, cu_seqlens=cu)
         return time.perf_counter() - t0
 
     probe = min(T, 512)

@@ -7,10 +7,11 @@ hipError_t launch_intra(int C, bool per_dim, const uint16_t* q, const uint16_t* 
                         const float* g, const float* beta, const ChunkMap& map, int nslots, int H, int Hk,
                         int l2n, float scale, const Work& ws, int nscratch, hipStream_t stream);
 hipError_t launch_chain(const ChunkMap& map, int N, int H, const float* s0, float* s_out, const Work& ws,
-                        hipStream_t stream);
+                        int32_t* order_ws, hipStream_t stream);
 hipError_t launch_output(int C, const ChunkMap& map, int nslots, int H, uint16_t* o, const Work& ws,
                          hipStream_t stream);
-hipError_t launch_chain_map(const ChunkMap& map, int N, int H, float* m_out, const Work& ws, hipStream_t stream);
+hipError_t launch_chain_map(const ChunkMap& map, int N, int H, float* m_out, const Work& ws, int32_t* order_ws,
+                            hipStream_t stream);
 hipError_t launch_merge(int R, int HV, const float* M, const float* X, const float* s0, float* s_in,
                         hipStream_t stream);
 }  // namespace cdr
@@ -32,7 +33,7 @@ int64_t num_slots(const cdr_problem* p) {
     return (int64_t)p->B * ((p->T + p->chunk_size - 1) / p->chunk_size);
 }
 
-constexpr int kArrays = 7;
+constexpr int kArrays = 8;
 constexpr int64_t kScratchSlots = 512; // at most this many intra workgroups run at once
 
 size_t scratch_slots(const cdr_problem* p) {
@@ -56,6 +57,7 @@ Layout layout(const cdr_problem* p) {
         nch * K * 4,      // gC
         nch * V * K * 2,  // Sc
         nsc * K * C * 2 + nsc * 1024 * 4,  // kgT, then the pad area of each slot (intra kernel)
+        p->varlen ? (size_t)p->N * 4 : 0,  // chain order of packed sequences (longest first)
     };
     Layout L;
     size_t at = 0;
@@ -170,7 +172,10 @@ cdr_status chunk_dr_fwd_stages(const cdr_problem* p, const void* q, const void* 
             return CDR_ERR_HIP;
     }
     if (stages & CDR_STAGE_CHAIN) {
-        if (cdr::launch_chain(map, p->N, (int)value_heads(p), s0, s_out, ws, s) != hipSuccess) return CDR_ERR_HIP;
+        int32_t* order_ws = reinterpret_cast<int32_t*>(wb + L.off[7]);
+        if (cdr::launch_chain(map, p->N, (int)value_heads(p), s0, s_out, ws, p->varlen ? order_ws : nullptr, s) !=
+            hipSuccess)
+            return CDR_ERR_HIP;
     }
     if ((stages & CDR_STAGE_OUTPUT) && nslots > 0) {
         if (cdr::launch_output(C, map, nslots, (int)value_heads(p), static_cast<uint16_t*>(o), ws, s) != hipSuccess)
@@ -213,7 +218,9 @@ cdr_status chunk_dr_segment_map(const cdr_problem* p, const void* q, const void*
     map.N = p->N;
     map.C = p->chunk_size;
     map.nchunk = (p->T + p->chunk_size - 1) / p->chunk_size;
-    if (cdr::launch_chain_map(map, p->N, (int)value_heads(p), M, ws, static_cast<hipStream_t>(stream)) != hipSuccess)
+    int32_t* order_ws = p->varlen ? reinterpret_cast<int32_t*>(wb + L.off[7]) : nullptr;
+    if (cdr::launch_chain_map(map, p->N, (int)value_heads(p), M, ws, order_ws, static_cast<hipStream_t>(stream)) !=
+        hipSuccess)
         return CDR_ERR_HIP;
     return CDR_OK;
 }

@@ -80,7 +80,8 @@ __device__ __forceinline__ void chain_step(const ChainOps& op, f32x4& S, const W
 // from a zero start); no chunk-entry states are written.
 template <bool MAP>
 __global__ __launch_bounds__(CTHREADS) void chain_kernel(ChunkMap map, int H, const float* __restrict__ s0,
-                                                          float* __restrict__ s_out, Work ws) {
+                                                          float* __restrict__ s_out, Work ws,
+                                                          const int32_t* __restrict__ order) {
     __shared__ __attribute__((aligned(16))) uint16_t sbuf[2][2 * KS * 512];  // two published states
 
     // workgroup b runs on XCD b % 8; the value blocks of chain nh all get the same XCD
@@ -88,7 +89,8 @@ __global__ __launch_bounds__(CTHREADS) void chain_kernel(ChunkMap map, int H, co
     const int xcd = b % NXCD, j = b / NXCD;
     const int vb = j % NVB, nh = (j / NVB) * NXCD + xcd;
     if (nh >= map.N * H) return;
-    const int n = nh / H, h = nh % H;
+    // order (varlen): sequences by decreasing length, so the longest chains start first
+    const int n = order ? order[nh / H] : nh / H, h = nh % H;
     int64_t bos;
     int len, slot0;
     seq_info(map, n, bos, len, slot0);
@@ -142,13 +144,27 @@ __global__ __launch_bounds__(CTHREADS) void chain_kernel(ChunkMap map, int H, co
 // One workgroup of 8 waves per (chunk, head).  The chunk-entry state (A operand, shared by
 // all waves) is copied into LDS in its fragment-major order; Q fragments (B operand) are read
 // straight from memory and U^T initialises the accumulators.
+// One workgroup of OWAVES waves per 64 rows of a (chunk, head): wave w takes row tile
+// OWAVES part + w and all value tiles.  The parts of one (chunk, head) are 8 workgroups
+// apart in launch order, so they run on the same XCD and the second finds the staged state in
+// that XCD's L2.  More, smaller workgroups than the CUs hold at once, so that some load while
+// others store.
+constexpr int OWAVES = 4;
+constexpr int OTHREADS = 64 * OWAVES;
+
 template <int C>
-__global__ __launch_bounds__(CTHREADS) void output_kernel(ChunkMap map, int H, uint16_t* __restrict__ o, Work ws) {
+__global__ __launch_bounds__(OTHREADS) void output_kernel(ChunkMap map, int nslots, int H, uint16_t* __restrict__ o,
+                                                           Work ws) {
     constexpr int NT = C / 16;                     // row tiles of the chunk
-    constexpr int VTW = (VD / 16) * NT / CWAVES;   // value tiles per wave
+    constexpr int NPART = NT / OWAVES;             // workgroups per (chunk, head)
+    constexpr int VTW = VD / 16;                   // value tiles per wave
     constexpr int NSF = (VD / 16) * KS;            // state fragments
+    static_assert(NT % OWAVES == 0, "row tiles per workgroup");
     __shared__ __attribute__((aligned(16))) uint16_t sS[NSF * 512];
-    const int slot = blockIdx.x, h = blockIdx.y;
+    const int b = blockIdx.x, h = blockIdx.y;
+    const int grp = b / (8 * NPART), r = b % (8 * NPART);
+    const int part = r / 8, slot = grp * 8 + r % 8;
+    if (slot >= nslots) return;
     int64_t tok0;
     int rows;
     slot_chunk(map, slot, tok0, rows);
@@ -156,15 +172,15 @@ __global__ __launch_bounds__(CTHREADS) void output_kernel(ChunkMap map, int H, u
     const size_t ch = (size_t)slot * H + h;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int r16 = lane & 15, q4 = lane >> 4;
-    const int it = wave % NT, vt0 = (wave / NT) * VTW;
-    for (int f = wave; f < NSF; f += CWAVES) frag_to_lds(ws.Sc + ch * VD * KD + f * 512, sS + f * 512, lane);
+    const int it = part * OWAVES + wave;
+    for (int f = wave; f < NSF; f += OWAVES) frag_to_lds(ws.Sc + ch * VD * KD + f * 512, sS + f * 512, lane);
     uint4 qf[KS];
 #pragma unroll
     for (int s = 0; s < KS; ++s) qf[s] = *reinterpret_cast<const uint4*>(ws.Qp + ch * C * KD + frag(it, s, KS) + lane * 8);
     f32x4 acc[VTW];
 #pragma unroll
     for (int t = 0; t < VTW; ++t) {
-        const uint2 u = *reinterpret_cast<const uint2*>(ws.Up + ch * C * VD + ((size_t)(it * (VD / 16) + vt0 + t) * 64 + lane) * 4);
+        const uint2 u = *reinterpret_cast<const uint2*>(ws.Up + ch * C * VD + ((size_t)(it * (VD / 16) + t) * 64 + lane) * 4);
         acc[t] = f32x4{__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u), __uint_as_float(u.y << 16),
                        __uint_as_float(u.y & 0xffff0000u)};
     }
@@ -174,39 +190,72 @@ __global__ __launch_bounds__(CTHREADS) void output_kernel(ChunkMap map, int H, u
     for (int s = 0; s < KS; ++s)
 #pragma unroll
         for (int t = 0; t < VTW; ++t) {
-            const bf16x8 a = as_bf16x8(*reinterpret_cast<const uint4*>(sS + frag(vt0 + t, s, KS) + lane * 8));
+            const bf16x8 a = as_bf16x8(*reinterpret_cast<const uint4*>(sS + frag(t, s, KS) + lane * 8));
             acc[t] = mfma32(a, as_bf16x8(qf[s]), acc[t]);
         }
-    // acc[t]: rows v = 16 (vt0 + t) + 4 q4 + e, column i = 16 it + r16
+    // acc[t]: rows v = 16 t + 4 q4 + e, column i = 16 it + r16
     const int i = 16 * it + r16;
     if (i < rows) {
         uint16_t* orow = o + ((size_t)(tok0 + i) * H + h) * VD;
 #pragma unroll
         for (int t = 0; t < VTW; ++t)
-            *reinterpret_cast<uint2*>(orow + 16 * (vt0 + t) + 4 * q4) =
+            *reinterpret_cast<uint2*>(orow + 16 * t + 4 * q4) =
                 make_uint2(pack_bf2(acc[t][0], acc[t][1]), pack_bf2(acc[t][2], acc[t][3]));
     }
 }
 
+// Packed sequences of unequal lengths: the chain of the longest sequence bounds the kernel,
+// so its workgroups should be dispatched first.  order[r] = the sequence of rank r by
+// decreasing length (ties by index), from a single workgroup (N <= SEQ_ORDER_MAX).
+constexpr int SEQ_ORDER_MAX = 1024;
+
+__global__ __launch_bounds__(SEQ_ORDER_MAX) void seq_order_kernel(ChunkMap map, int32_t* __restrict__ order) {
+    __shared__ int len[SEQ_ORDER_MAX];
+    const int N = map.N;
+    for (int n = threadIdx.x; n < N; n += SEQ_ORDER_MAX) len[n] = map.cu[n + 1] - map.cu[n];
+    __syncthreads();
+    for (int n = threadIdx.x; n < N; n += SEQ_ORDER_MAX) {
+        const int ln = len[n];
+        int r = 0;
+        for (int m = 0; m < N; ++m) r += (len[m] > ln) || (len[m] == ln && m < n);
+        order[r] = n;
+    }
+}
+
+// the chain order for this map: NULL (sequence order) unless it is packed with N <= SEQ_ORDER_MAX
+static const int32_t* chain_order(const ChunkMap& map, int N, int32_t* order_ws, hipStream_t stream) {
+    if (map.cu == nullptr || order_ws == nullptr || N < 2 || N > SEQ_ORDER_MAX) return nullptr;
+    hipLaunchKernelGGL(seq_order_kernel, dim3(1), dim3(SEQ_ORDER_MAX), 0, stream, map, order_ws);
+    return order_ws;
+}
+
 hipError_t launch_chain(const ChunkMap& map, int N, int H, const float* s0, float* s_out, const Work& ws,
-                        hipStream_t stream) {
+                        int32_t* order_ws, hipStream_t stream) {
     const int groups = (N * H + NXCD - 1) / NXCD;
-    hipLaunchKernelGGL(chain_kernel<false>, dim3(groups * NXCD * NVB), dim3(CTHREADS), 0, stream, map, H, s0, s_out, ws);
+    const int32_t* order = chain_order(map, N, order_ws, stream);
+    hipLaunchKernelGGL(chain_kernel<false>, dim3(groups * NXCD * NVB), dim3(CTHREADS), 0, stream, map, H,
+                       s0, s_out, ws, order);
     return hipGetLastError();
 }
 
-hipError_t launch_chain_map(const ChunkMap& map, int N, int H, float* m_out, const Work& ws, hipStream_t stream) {
+hipError_t launch_chain_map(const ChunkMap& map, int N, int H, float* m_out, const Work& ws, int32_t* order_ws,
+                            hipStream_t stream) {
     const int groups = (N * H + NXCD - 1) / NXCD;
+    const int32_t* order = chain_order(map, N, order_ws, stream);
     hipLaunchKernelGGL(chain_kernel<true>, dim3(groups * NXCD * NVB), dim3(CTHREADS), 0, stream, map, H,
-                       (const float*)nullptr, m_out, ws);
+                       (const float*)nullptr, m_out, ws, order);
     return hipGetLastError();
 }
 
 hipError_t launch_output(int C, const ChunkMap& map, int nslots, int H, uint16_t* o, const Work& ws,
                          hipStream_t stream) {
-    dim3 grid(nslots, H);
-    if (C == 64) hipLaunchKernelGGL((output_kernel<64>), grid, dim3(CTHREADS), 0, stream, map, H, o, ws);
-    else hipLaunchKernelGGL((output_kernel<128>), grid, dim3(CTHREADS), 0, stream, map, H, o, ws);
+    const int groups = (nslots + 7) / 8;  // 8 slots, then their other parts
+    if (C == 64)
+        hipLaunchKernelGGL((output_kernel<64>), dim3(groups * 8 * (64 / 16 / OWAVES), H), dim3(OTHREADS), 0, stream, map,
+                           nslots, H, o, ws);
+    else
+        hipLaunchKernelGGL((output_kernel<128>), dim3(groups * 8 * (128 / 16 / OWAVES), H), dim3(OTHREADS), 0, stream,
+                           map, nslots, H, o, ws);
     return hipGetLastError();
 }
 
