@@ -24,7 +24,7 @@
 //        only.  A uses hi/lo split operands (three MFMAs); A2 feeds only the output
 //        and uses single bf16 operands (stored transposed, scratch).  Per-head gates use
 //        raw q, k (exact bf16 products) and apply the scalar decay afterwards.  Tile rows w
-//        and NT-1-w form one list of NT+1 tiles shared by waves w and w+4.  qg (scratch) is
+//        and NT-1-w form one list of NT+1 tiles shared by waves w and w+NT/2.  qg (scratch) is
 //        produced on the diagonal tiles.
 //   INV  the 16x16 diagonal blocks T_RR = (I + A_RR)^-1 by forward substitution in fp32
 //        (wave R), then M_RJ = T_RR A_RJ (J < R) and T'_RR = T_RR diag(beta) on split-bf16
@@ -255,9 +255,11 @@ __device__ __forceinline__ void intra_item(
     // (rows past the end read the last row) and rows past the end are zeroed after phase E:
     // a load that only some lanes need would be issued under a branch, and the wait count
     // the compiler derives after such a branch covers every load in flight.
-    // waves w and w + 4 share tile rows cp = w % 4 and NT-1-cp: NT+1 tiles, HF for the first
-    const int cp = wave & 3, part = wave >> 2;
-    const bool aa_active = cp < NT / 2;
+    // waves w and w + NT/2 share tile rows cp = w % (NT/2) and NT-1-cp: NT+1 tiles, HF for the
+    // first.  The NT active waves are consecutive, so at C = 64 they are spread over the four
+    // SIMDs (one each) instead of sharing two.
+    const int cp = wave % (NT / 2), part = wave / (NT / 2);
+    const bool aa_active = wave < NT;
     const int Rown[2] = {cp, NT - 1 - cp};
     // The second wave of a pair has no tile in the first row (its tiles start at HF > cp), so
     // only the first wave loads that row.

@@ -61,6 +61,7 @@ def check(inp, heads=None, label="", l2n=False):
 
 
 # ---------------------------------------------------------------- small shapes, all rows
+_L1100 = tuple((7 * i) % 5 for i in range(1100))  # lengths 0..4, empty sequences included
 SMALL = [
     # label, B, T, H, C, per_dim, lengths, initial, gate_mean
     ("kda_T64_one_chunk", 1, 64, 2, 64, True, None, False, 0.0),
@@ -76,6 +77,10 @@ SMALL = [
     ("varlen_ragged_empty", 1, 259, 2, 64, True, (1, 0, 63, 65, 130), True, 0.0),
     ("varlen_C128_ragged", 1, 700, 2, 128, True, (127, 129, 1, 443), True, 1.0),
     ("varlen_gdn", 1, 500, 2, 64, False, (100, 0, 400), True, 0.0),
+    # equal lengths: the chain order ranks ties by sequence index
+    ("varlen_equal_lengths", 1, 390, 2, 64, True, (130, 130, 130), True, 1.0),
+    # more packed sequences than the chain ordering handles (1100 > 1024): sequence order
+    ("varlen_1100_short", 1, sum(_L1100), 1, 64, True, _L1100, True, 1.0),
 ]
 
 
