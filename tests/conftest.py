@@ -15,7 +15,7 @@ def pytest_configure(config):
 
 def pytest_collection_modifyitems(config, items):
     # GPU tests cannot run without a device; skip them with a reason instead of failing
-    # at import time. The round-end GPU run selects them with -m gpu on a real MI355X.
+    # at import time. On an MI355X they are selected with -m gpu.
     try:
         import torch
         has_gpu = torch.cuda.is_available()
