@@ -141,14 +141,13 @@ __global__ __launch_bounds__(CTHREADS) void chain_kernel(ChunkMap map, int H, co
     if (s_out != nullptr) *reinterpret_cast<float4*>(s_out + srow) = make_float4(S[0], S[1], S[2], S[3]);
 }
 
-// One workgroup of 8 waves per (chunk, head).  The chunk-entry state (A operand, shared by
-// all waves) is copied into LDS in its fragment-major order; Q fragments (B operand) are read
-// straight from memory and U^T initialises the accumulators.
 // One workgroup of OWAVES waves per 64 rows of a (chunk, head): wave w takes row tile
-// OWAVES part + w and all value tiles.  The parts of one (chunk, head) are 8 workgroups
-// apart in launch order, so they run on the same XCD and the second finds the staged state in
-// that XCD's L2.  More, smaller workgroups than the CUs hold at once, so that some load while
-// others store.
+// OWAVES part + w and all value tiles.  The chunk-entry state (A operand, shared by all
+// waves) is copied into LDS in its fragment-major order; Q fragments (B operand) are read
+// straight from memory and U^T initialises the accumulators.  The parts of one (chunk, head)
+// are 8 workgroups apart in launch order, so they run on the same XCD and the second finds
+// the staged state in that XCD's L2.  More, smaller workgroups than the CUs hold at once, so
+// that some load while others store.
 constexpr int OWAVES = 4;
 constexpr int OTHREADS = 64 * OWAVES;
 
