@@ -40,7 +40,8 @@
 //        The w and u tiles are used as MFMA operands straight from registers (pi order),
 //        kg^T comes back from scratch at the start of INV and goes to LDS once the A
 //        tiles there are consumed; the A2 and qg tiles stay in registers from AA2 and go to
-//        LDS after the solve.
+//        LDS after the solve.  -P and B are written with ordinary stores (the chain reads
+//        them next), Q and U with non-temporal ones (only the output kernel reads them).
 #include "cdr_common.h"
 
 #include <atomic>
@@ -888,9 +889,11 @@ __device__ __forceinline__ void intra_item(
             qt = mfma32(as_bf16x8(neg_bf16x8(wh[s])), a2, qt);
             ut = mfma32(as_bf16x8(uh[s]), a2, ut);
         }
-        *mptr<uint2>(QpI, (frag32(I, dt >> 1, KD / 32) + fragP(dt & 1, r16, q4)) * 2u) =
-            make_uint2(pack_bf2(qt[0], qt[1]), pack_bf2(qt[2], qt[3]));
-        *mptr<uint2>(UpI, ((I * (VD / 16) + dt) * 64 + lane) * 8u) = make_uint2(pack_bf2(ut[0], ut[1]), pack_bf2(ut[2], ut[3]));
+        // Q and U are read only by the output kernel, after the chain: streamed past the caches,
+        // so that they do not displace -P and B, which the chain reads next
+        st_nt(mptr<uint2>(QpI, (frag32(I, dt >> 1, KD / 32) + fragP(dt & 1, r16, q4)) * 2u),
+              make_uint2(pack_bf2(qt[0], qt[1]), pack_bf2(qt[2], qt[3])));
+        st_nt(mptr<uint2>(UpI, ((I * (VD / 16) + dt) * 64 + lane) * 8u), make_uint2(pack_bf2(ut[0], ut[1]), pack_bf2(ut[2], ut[3])));
     }
 }
 
