@@ -158,7 +158,9 @@ __device__ __forceinline__ void e_load_g(EIn& in, const float* g, const float* b
 #pragma unroll
     for (int ii = 0; ii < 16; ++ii) {
         if constexpr (PER_DIM) {
-            in.g[ii] = *cptr<float2>(g + ((size_t)l.tok0 * rs + (size_t)l.h * KD), min(og0 + ii * rs * 4u, ogl));
+            // the gates (the largest input, read once) past the caches: they leave the
+            // memory-side cache to -P and B, which the chain reads next
+            in.g[ii] = ld_nt(cptr<float2>(g + ((size_t)l.tok0 * rs + (size_t)l.h * KD), min(og0 + ii * rs * 4u, ogl)));
         } else {
             const float s1 = *cptr<float>(g + ((size_t)l.tok0 * H + l.h), min(r0 + ii, last) * (uint32_t)H * 4u);
             in.g[ii] = make_float2(s1, s1);
