@@ -265,7 +265,9 @@ __device__ __forceinline__ void intra_item(
     const bool aa_active = wave < NT;
     const int Rown[2] = {cp, NT - 1 - cp};
     // The second wave of a pair has no tile in the first row (its tiles start at HF > cp), so
-    // only the first wave loads that row.
+    // only the first wave loads that row.  The condition is wave-uniform; phase E's wait counts
+    // then follow the shorter path, so the waves that do load also wait for 8 of the previous
+    // item's stores, which costs less than the loads saved (measured).
     uint4 kfr[2][KD / 32], qfr[2][KD / 32];
 #pragma unroll
     for (int o = 1; o >= 0; --o) {
