@@ -50,7 +50,7 @@ Layout layout(const cdr_problem* p) {
     const size_t nch = (size_t)num_slots(p) * (size_t)value_heads(p), nsc = scratch_slots(p);
     const size_t C = (size_t)p->chunk_size, K = (size_t)p->K, V = (size_t)p->V;
     const size_t bytes[kArrays] = {
-        nch * K * K * 2,  // Pn
+        nch * K * K * 4,  // Pn (high and low bf16 parts)
         nch * K * V * 4,  // Bm
         nch * C * K * 2,  // Qp
         nch * C * V * 2,  // Up

@@ -9,9 +9,9 @@
 // registers (value columns of the state evolve independently).  Per chunk:
 //   1. the state is split into bf16 hi + lo and published in LDS (B operand of P S) and,
 //      as bf16, to the workspace as the chunk-entry state of the output kernel;
-//   2. S = exp(gamma_C) S + B - P S with two MFMA chains, P S hi and P S lo: P is stored
-//      with one bf16 rounding (it halves the operand stream each step must receive), the
-//      state keeps its 16-bit-mantissa split.
+//   2. S = exp(gamma_C) S + B - P S with three MFMA chains, P_hi S_hi, P_lo S_hi and
+//      P_hi S_lo: -P and the state both keep a 16-bit mantissa as bf16 high + low parts (the
+//      product of the two low parts is below fp32 rounding of the sum).
 // One LDS barrier per chunk: the published state alternates between two buffers.  The
 // operands of the next chunks (-P, B, exp(gamma_C)) do not depend on the state and are
 // loaded two chunks ahead into a ring of three register buffers.  Workgroups are numbered
@@ -31,7 +31,8 @@ constexpr int NVB = VD / BV;
 constexpr int KS = KD / 32; // 32-wide contraction steps over the state rows
 
 struct ChainOps {
-    uint4 ph[KS];   // -P fragments (x, s)
+    uint4 ph[KS];   // -P fragments (x, s), high bf16 parts
+    uint4 pl[KS];   // and low parts
     float4 b;       // B tile (x, value block)
     float4 gc;      // exp(gamma_C) of the wave's state rows
 };
@@ -40,8 +41,9 @@ template <bool MAP>
 __device__ __forceinline__ void chain_load(ChainOps& op, const Work& ws, size_t ch, int x, int lane, int q4, int vb) {
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
-        const size_t off = ch * KD * KD + frag(x, s, KS) + lane * 8;
+        const size_t off = ch * 2 * KD * KD + frag(x, s, KS) + lane * 8;
         op.ph[s] = *reinterpret_cast<const uint4*>(ws.Pn + off);
+        op.pl[s] = *reinterpret_cast<const uint4*>(ws.Pn + off + KD * KD);
     }
     op.b = MAP ? make_float4(0.f, 0.f, 0.f, 0.f)
                : *reinterpret_cast<const float4*>(ws.Bm + ch * KD * VD + ((size_t)(x * (VD / 16) + vb) * 64 + lane) * 4);
@@ -63,16 +65,17 @@ __device__ __forceinline__ void chain_step(const ChainOps& op, f32x4& S, const W
     lds_barrier();
     // 2. S = exp(gamma_C) S + B - P S
     f32x4 a0 = {op.gc.x * S[0] + op.b.x, op.gc.y * S[1] + op.b.y, op.gc.z * S[2] + op.b.z, op.gc.w * S[3] + op.b.w};
-    f32x4 a2 = {0.f, 0.f, 0.f, 0.f};
+    f32x4 a1 = {0.f, 0.f, 0.f, 0.f}, a2 = a1;
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
         const bf16x8 bh = as_bf16x8(*reinterpret_cast<const uint4*>(sbuf + s * 512 + lane * 8));
         const bf16x8 bl = as_bf16x8(*reinterpret_cast<const uint4*>(sbuf + (KS + s) * 512 + lane * 8));
         a0 = mfma32(as_bf16x8(op.ph[s]), bh, a0);
+        a1 = mfma32(as_bf16x8(op.pl[s]), bh, a1);
         a2 = mfma32(as_bf16x8(op.ph[s]), bl, a2);
     }
 #pragma unroll
-    for (int e = 0; e < 4; ++e) S[e] = a0[e] + a2[e];
+    for (int e = 0; e < 4; ++e) S[e] = a0[e] + (a1[e] + a2[e]);
 }
 
 // MAP: the chunk maps without their offsets, S <- (exp(gamma_C) - P) S from S = I, which

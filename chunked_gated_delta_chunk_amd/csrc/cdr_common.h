@@ -235,7 +235,8 @@ __device__ __forceinline__ int fragP(int t, int r, int q) { return (r + 16 * q) 
 // output as  o = Q S + U  with Q = qg - A2 w and U = A2 u, so the sequential kernel only
 // needs P, B and exp(gamma_C).
 struct Work {
-    uint16_t* Pn;      // (K, K) frag pi bf16   -P (one bf16 rounding); A operand of -P S
+    uint16_t* Pn;      // 2 x (K, K) frag pi bf16   -P split into high then low bf16 parts; A
+                       //                       operands of -P S
     float* Bm;         // D tiles        fp32   B = kg^T u, (K/16) x (V/16) tiles of 64 lanes x 4
                        //                       rows, the layout of the state accumulator
     uint16_t* Qp;      // (C, K) frag pi bf16   Q = qg - A2 w; B operand of (Q S)^T

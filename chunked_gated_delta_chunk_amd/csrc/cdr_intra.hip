@@ -50,6 +50,11 @@ namespace cdr {
 
 constexpr int IWAVES = 8;
 constexpr float L2N_EPS = 1e-6f;  // in-kernel q/k normalisation: x / sqrt(|x|^2 + eps)
+// Largest gate span (|gamma_i - gamma_m| over a 16-row tile and its middle row m) for which the
+// tile-middle pivot factors exp(+-(gamma_i - gamma_m)) are used: they stay below e^64, so the
+// decayed operands, even times a large key, and their products stay finite in fp32.  A chunk
+// with a wider tile takes pivots that make every factor <= 1 and exact diagonal tiles.
+constexpr float SAFE_SPAN = 64.f;
 constexpr int ITHREADS = 64 * IWAVES;
 
 template <int C>
@@ -206,6 +211,65 @@ __device__ __forceinline__ void vm_pad(uint32_t* p) {
     for (int i = 0; i < N; ++i) p[16 * i] = 0u;
 }
 
+// Exact decayed products of the diagonal tile (R, R), for chunks whose gates are too wide for
+// pivot factors: one exponential per pair and dimension, exp(-|gamma_a - gamma_b|), which for
+// g <= 0 is the decay exp(gamma_i - gamma_j) of the pair's later row i over its earlier row j.
+// Lane (r16, q4) returns, in the accumulator layouts of phase AA2 (a = 16 R + r16,
+// b = 16 R + 4 q4 + e),
+//     dA[e] = sum_d k_b k_a decay      (A tile: row b, column a)
+//     dQ[e] = sum_d q_a k_b decay      (A2^T tile: row b, column a)
+// with the L2 scales of the rows applied (knr for keys, rq for the lane's query row) and rows at
+// or past `rows` taken as zero; the caller applies the triangle masks, beta and scale.  gam holds
+// gamma by row, row stride ld floats.
+template <bool L2N>
+__device__ __forceinline__ void diag_exact(const float* gam, int ld, const uint16_t* kbase, const uint16_t* qbase,
+                                           uint32_t rsk, int rows, int R, int r16, int q4, const float* knr,
+                                           float rq, f32x4& dA, f32x4& dQ) {
+    const int a = 16 * R + r16;
+    const uint32_t oa = (uint32_t)min(a, rows - 1) * rsk * 2u;
+    const float sk = a < rows ? (L2N ? knr[a] : 1.f) : 0.f, sq = a < rows ? rq : 0.f;
+    uint32_t ob[4];
+    float sb[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const int b = 16 * R + 4 * q4 + e;
+        ob[e] = (uint32_t)min(b, rows - 1) * rsk * 2u;
+        sb[e] = b < rows ? (L2N ? knr[b] : 1.f) : 0.f;
+        dA[e] = 0.f;
+        dQ[e] = 0.f;
+    }
+    for (int dc = 0; dc < KD / 8; ++dc) {
+        float ka[8], qa[8];
+        unpack8(*cptr<uint4>(kbase, oa + 16u * dc), ka);
+        unpack8(*cptr<uint4>(qbase, oa + 16u * dc), qa);
+        const float4* gpa = reinterpret_cast<const float4*>(gam + a * ld + 8 * dc);
+        const float4 a0 = gpa[0], a1 = gpa[1];
+        const float ga[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            float kb[8];
+            unpack8(*cptr<uint4>(kbase, ob[e] + 16u * dc), kb);
+            const float4* gpb = reinterpret_cast<const float4*>(gam + (16 * R + 4 * q4 + e) * ld + 8 * dc);
+            const float4 b0 = gpb[0], b1 = gpb[1];
+            const float gb[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+            float sA = 0.f, sQ = 0.f;
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+                const float kd = kb[t] * ex(-fabsf(ga[t] - gb[t]));
+                sA += kd * ka[t];
+                sQ += kd * qa[t];
+            }
+            dA[e] += sA;
+            dQ[e] += sQ;
+        }
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        dA[e] *= sb[e] * sk;
+        dQ[e] *= sb[e] * sq;
+    }
+}
+
 // One (chunk slot, head) item.  sc is the workgroup's scratch slot; ein holds the item's
 // phase E inputs on entry and those of next_item (-1: none) on exit.
 template <int C, bool PER_DIM, bool L2N>
@@ -281,8 +345,11 @@ __device__ __forceinline__ void intra_item(
     }
     // exp(gamma) k and v of the thread's phase E block as 16-byte fragment slots [hh][c],
     // kept in registers until the A tiles leave LDS, then staged there for the solve
-    uint4 xs[2][2], vs[2][2];
+    uint4 xs[2][2], xls[2][2], vs[2][2];  // exp(gamma) k split into high (xs) and low parts
     uint4 kls[2][2];  // low part of kg^T, the two pi-order halves of each slot, to LDS after the solve
+    // per-dimension gates too wide for the tile-middle pivots somewhere in the chunk (same value in
+    // every thread of the workgroup after phase E's first barrier)
+    bool wide = false;
     // ------------------------------------------------------------------ phase E
     {
         const int R = tid >> 6, d0 = 2 * (tid & 63);  // tile row R, columns d0, d0 + 1
@@ -305,6 +372,17 @@ __device__ __forceinline__ void intra_item(
                 gm2[ii][1] += gm2[ii - 1][1];
             }
             *reinterpret_cast<float2*>(ttot + R * KD + d0) = make_float2(gm2[15][0], gm2[15][1]);
+            if constexpr (PER_DIM) {
+                // gate span of the tile on either side of its middle row, the exponent of the
+                // largest pivot factor; a wave flags its tile when it exceeds SAFE_SPAN
+                float span = 0.f;
+#pragma unroll
+                for (int ii = 0; ii < 16; ++ii)
+#pragma unroll
+                    for (int c = 0; c < 2; ++c) span = fmaxf(span, fabsf(gm2[ii][c] - gm2[8][c]));
+                const bool wflag = __ballot(!(span <= SAFE_SPAN)) != 0;
+                if ((tid & 63) == 0) reinterpret_cast<int*>(grow)[R] = wflag ? 1 : 0;
+            }
         }
         // in-kernel L2 normalisation of keys: k / sqrt(|k|^2 + eps) per token, the row sum of
         // squares reduced across the wave (the 64 lanes hold the row's 128 columns)
@@ -326,6 +404,10 @@ __device__ __forceinline__ void intra_item(
             }
         }
         lds_barrier();
+        if constexpr (PER_DIM) {
+#pragma unroll
+            for (int Rp = 0; Rp < NT; ++Rp) wide |= reinterpret_cast<const int*>(grow)[Rp] != 0;
+        }
         if (act) {
             float off[2] = {0.f, 0.f}, gcl[2] = {0.f, 0.f};
             for (int Rp = 0; Rp < NT; ++Rp) {
@@ -342,14 +424,18 @@ __device__ __forceinline__ void intra_item(
                 gm2[ii][0] += off[0];
                 gm2[ii][1] += off[1];
             }
-            float gmv[2], e_gm[2], e_cm[2];
+            // pivots of the tile: gpr for its rows, gpc for its columns.  Narrow gates: both the
+            // middle row's gamma.  Wide gates: gamma before the tile's first row (off) for the rows
+            // and at its last row for the columns, so that every factor is <= 1 for g <= 0
+            float gpr[2], gpc[2], e_gm[2], e_cm[2];
 #pragma unroll
             for (int c = 0; c < 2; ++c) {
-                gmv[c] = gm2[8][c];
-                e_gm[c] = ex(gmv[c]);            // exp(gamma_m)
-                e_cm[c] = ex(gcl[c] - gmv[c]);   // exp(gamma_C - gamma_m) <= 1
+                gpr[c] = wide ? off[c] : gm2[8][c];
+                gpc[c] = wide ? gm2[15][c] : gm2[8][c];
+                e_gm[c] = ex(gpr[c]);            // exp(gamma at the row pivot) <= 1
+                e_cm[c] = ex(gcl[c] - gpc[c]);   // exp(gamma_C - gamma at the column pivot) <= 1
             }
-            *reinterpret_cast<float2*>(gmid + R * KD + d0) = make_float2(gmv[0], gmv[1]);
+            *reinterpret_cast<float2*>(gmid + R * KD + d0) = make_float2(gpr[0], gpr[1]);
             *reinterpret_cast<float2*>(egm + R * KD + d0) = make_float2(e_gm[0], e_gm[1]);
             if (R == 0) *mptr<float2>(ws.gC + ch * KD, d0 * 4u) = make_float2(ex(gcl[0]), ex(gcl[1]));
             if constexpr (!PER_DIM) {
@@ -361,35 +447,51 @@ __device__ __forceinline__ void intra_item(
 #pragma unroll
             for (int hh = 0; hh < 2; ++hh) {
                 // column-major outputs of rows 16R + 8hh .. +7, two bf16 (consecutive rows) per register
-                uint32_t bwh[2][4], kgh[2][4], kgl[2][4], vtp[2][4];
+                uint32_t bwh[2][4], bwl[2][4], kgh[2][4], kgl[2][4], vtp[2][4];
 #pragma unroll
                 for (int e2 = 0; e2 < 4; ++e2) {
-                    float kf[2][2], ep[2][2], em[2][2];   // [row of the pair][column]
+                    // kf: the key; fx, fk: its factors exp(gamma_i) (for w; beta enters through
+                    // T diag(beta)) and exp(gamma_C - gamma_i) (for kg)
+                    float kf[2][2], fx[2][2], fk[2][2];   // [row of the pair][column]
 #pragma unroll
                     for (int rr = 0; rr < 2; ++rr) {
                         const int ii = 8 * hh + 2 * e2 + rr;
                         kf[rr][0] = __uint_as_float(kr[ii] << 16) * rnk[ii];
                         kf[rr][1] = __uint_as_float(kr[ii] & 0xffff0000u) * rnk[ii];
-#pragma unroll
-                        for (int c = 0; c < 2; ++c) {
-                            const float x = gm2[ii][c] - gmv[c];
-                            ep[rr][c] = ex(x);     // exp(gamma_i - gamma_m)
-                            em[rr][c] = __builtin_amdgcn_rcpf(ep[rr][c]);  // exp(gamma_m - gamma_i)
-                        }
                         if constexpr (PER_DIM) {
+                            float ep[2], em[2];
+#pragma unroll
+                            for (int c = 0; c < 2; ++c) {
+                                ep[c] = ex(gm2[ii][c] - gpr[c]);   // exp(gamma_i - row pivot)
+                                // exp(column pivot - gamma_i): the reciprocal when the pivots agree
+                                em[c] = wide ? ex(gpc[c] - gm2[ii][c]) : __builtin_amdgcn_rcpf(ep[c]);
+                                fx[rr][c] = e_gm[c] * ep[c];
+                                fk[rr][c] = em[c] * e_cm[c];
+                            }
                             const int i = 16 * R + ii;
-                            *reinterpret_cast<float2*>(Ep + i * S::EP_LD + d0) = make_float2(ep[rr][0], ep[rr][1]);
+                            // row factors of phase AA2; with wide gates gamma itself, from which AA2
+                            // forms them and the diagonal tiles their exact pair decays
+                            *reinterpret_cast<float2*>(Ep + i * S::EP_LD + d0) =
+                                wide ? make_float2(gm2[ii][0], gm2[ii][1]) : make_float2(ep[0], ep[1]);
                             uint32_t chv, clv;
-                            split2(kf[rr][0] * em[rr][0], kf[rr][1] * em[rr][1], chv, clv);
+                            split2(kf[rr][0] * em[0], kf[rr][1] * em[1], chv, clv);
                             *reinterpret_cast<uint32_t*>(colh + i * S::COL_LD + d0) = chv;
                             *reinterpret_cast<uint32_t*>(coll + i * S::COL_LD + d0) = clv;
+                        } else {
+                            // one gate per token: both factors directly, each <= 1 for g <= 0
+                            const float xg = ex(gm2[ii][0]), kgf = ex(gcl[0] - gm2[ii][0]);
+#pragma unroll
+                            for (int c = 0; c < 2; ++c) {
+                                fx[rr][c] = xg;
+                                fk[rr][c] = kgf;
+                            }
                         }
                     }
 #pragma unroll
                     for (int c = 0; c < 2; ++c) {
-                        // exp(gamma_i) k (beta enters through T diag(beta)) and exp(gamma_C - gamma_i) k
-                        bwh[c][e2] = pack_bf2(kf[0][c] * (e_gm[c] * ep[0][c]), kf[1][c] * (e_gm[c] * ep[1][c]));
-                        split2(kf[0][c] * (em[0][c] * e_cm[c]), kf[1][c] * (em[1][c] * e_cm[c]), kgh[c][e2], kgl[c][e2]);
+                        // exp(gamma_i) k and exp(gamma_C - gamma_i) k
+                        split2(kf[0][c] * fx[0][c], kf[1][c] * fx[1][c], bwh[c][e2], bwl[c][e2]);
+                        split2(kf[0][c] * fk[0][c], kf[1][c] * fk[1][c], kgh[c][e2], kgl[c][e2]);
                     }
                     const uint32_t v0 = vr[8 * hh + 2 * e2], v1 = vr[8 * hh + 2 * e2 + 1];
                     vtp[0][e2] = (v0 & 0xffffu) | (v1 << 16);
@@ -403,6 +505,7 @@ __device__ __forceinline__ void intra_item(
                     // byte offsets inside the workgroup's scratch slot (uniform bases)
                     const uint32_t fo = frag32(d >> 4, R >> 1, C / 32);
                     xs[hh][c] = make_uint4(bwh[c][0], bwh[c][1], bwh[c][2], bwh[c][3]);
+                    xls[hh][c] = make_uint4(bwl[c][0], bwl[c][1], bwl[c][2], bwl[c][3]);
                     // kg^T in pi order: rows 16 R + 4 q .. + 3 go to lane (d % 16) + 16 q, half R % 2
                     const uint32_t p0 = (fo + fragP(R & 1, d & 15, 2 * hh)) * 2u, p1 = (fo + fragP(R & 1, d & 15, 2 * hh + 1)) * 2u;
                     *mptr<uint2>(kgS, p0) = make_uint2(kgh[c][0], kgh[c][1]);
@@ -414,13 +517,15 @@ __device__ __forceinline__ void intra_item(
         }
         lds_barrier();
         if constexpr (PER_DIM) {
-            // strictly lower pairs p = R(R-1)/2 + J: F = exp(gamma_m(R) - gamma_m(J)) <= 1
+            // strictly lower pairs p = R(R-1)/2 + J: F = exp(row pivot of R - column pivot of J) <= 1.
+            // The column pivot of J is its row pivot, or with wide gates gamma at its last row, which
+            // is the row pivot of J + 1 <= R
             for (int e = 4 * tid; e < S::NOFF * KD; e += 4 * ITHREADS) {
                 const int p = e / KD, d = e % KD;
                 const int R = (int)((1.f + __builtin_sqrtf(8.f * p + 1.f)) * 0.5f);  // R(R-1)/2 <= p < R(R+1)/2
                 const int J = p - R * (R - 1) / 2;
                 const float4 a = *reinterpret_cast<const float4*>(gmid + R * KD + d);
-                const float4 b = *reinterpret_cast<const float4*>(gmid + J * KD + d);
+                const float4 b = *reinterpret_cast<const float4*>(gmid + (J + (wide ? 1 : 0)) * KD + d);
                 *reinterpret_cast<float4*>(F + e) = make_float4(ex(a.x - b.x), ex(a.y - b.y), ex(a.z - b.z), ex(a.w - b.w));
             }
         }
@@ -479,9 +584,9 @@ __device__ __forceinline__ void intra_item(
     // (cp, p) of the first row, p > cp tile (NT-1-cp, p-cp-1) of the second
     const int plo = part ? S::HF : 0, phi = part ? NT + 1 : S::HF;
     if constexpr (PER_DIM) {
-        // Row by row: the row's operands times exp(gamma_i - gamma_m(R)) (and its L2 scale)
+        // Row by row: the row's operands times exp(gamma_i - row pivot of R) (and its L2 scale)
         // are formed once per 32-column step and reused by every tile of the row; a tile
-        // below the diagonal multiplies them by F = exp(gamma_m(R) - gamma_m(J)) only.
+        // below the diagonal multiplies them by F = exp(row pivot of R - column pivot of J) only.
 #pragma unroll
         for (int o = 0; o < 2; ++o) {
             const bool has = aa_active && (o == 0 ? plo <= cp : phi - 1 > cp);
@@ -497,7 +602,14 @@ __device__ __forceinline__ void intra_item(
                 {
                     const float4* epp = reinterpret_cast<const float4*>(Ep + i * S::EP_LD + dd);
                     const float4 e0 = epp[0], e1 = epp[1];
-                    const float ep[8] = {e0.x, e0.y, e0.z, e0.w, e1.x, e1.y, e1.z, e1.w};
+                    float ep[8] = {e0.x, e0.y, e0.z, e0.w, e1.x, e1.y, e1.z, e1.w};
+                    if (wide) {  // Ep holds gamma: the factor against the row pivot, <= 1
+                        const float4* gp = reinterpret_cast<const float4*>(gmid + R * KD + dd);
+                        const float4 p0 = gp[0], p1 = gp[1];
+                        const float pv[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) ep[e] = ex(ep[e] - pv[e]);
+                    }
 #pragma unroll
                     for (int e = 0; e < 8; ++e) {
                         kE[e] *= (L2N ? rk2[o] : 1.f) * ep[e];
@@ -559,7 +671,14 @@ __device__ __forceinline__ void intra_item(
                 }
             }
         }
-    } else {
+    }
+    // wide gates: the wave's diagonal tile exactly (its pivot products above are finite but not the
+    // pair decays); tile row cp for the first wave of a pair, NT-1-cp for the second
+    f32x4 dA = {0.f, 0.f, 0.f, 0.f}, dQ = dA;
+    if (PER_DIM && wide && aa_active)
+        diag_exact<L2N>(Ep, S::EP_LD, kbase, qbase, rsk, rows, part ? NT - 1 - cp : cp, r16, q4, knr,
+                        L2N ? (part ? rq2[1] : rq2[0]) : 1.f, dA, dQ);
+    if constexpr (!PER_DIM) {
 #pragma unroll
         for (int s = 0; s < S::SMAX; ++s) {
             const int p = plo + s;
@@ -610,7 +729,12 @@ __device__ __forceinline__ void intra_item(
             const int ii = 16 * R + 4 * q4 + rr, jj = 16 * J + r16;
             const int i2 = 16 * R + r16, j2 = 16 * J + 4 * q4 + rr;
             float a = acc1[s][rr], a2 = acc2[s][rr];
-            if constexpr (!PER_DIM) {
+            if constexpr (PER_DIM) {
+                if (wide && J == R) {
+                    a = dA[rr];
+                    a2 = dQ[rr];
+                }
+            } else {
                 a *= (jj <= ii) ? ex(grow[ii] - grow[jj]) : 0.f;
                 a2 *= (j2 <= i2) ? ex(grow[i2] - grow[j2]) : 0.f;
                 if constexpr (L2N) {  // raw q, k products: apply the row scales afterwards
@@ -722,6 +846,9 @@ __device__ __forceinline__ void intra_item(
     uint16_t* xL = reinterpret_cast<uint16_t*>(smem);
     uint16_t* vL = xL + KD * C;
     static_assert((KD + VD) * C * 2 <= S::R1, "solve operand staging");
+    // the low parts of exp(gamma) k after the solve's own operands (R2 and the free F and pivot areas)
+    uint16_t* xlL = reinterpret_cast<uint16_t*>(smem + S::R1 + S::SOLVE_BYTES);
+    static_assert(S::SOLVE_BYTES + KD * C * 2 <= S::R2 + S::RF + S::RG, "solve operand staging");
     if ((tid >> 6) < NT) {
         const int R = tid >> 6, d0 = 2 * (tid & 63);
 #pragma unroll
@@ -731,6 +858,7 @@ __device__ __forceinline__ void intra_item(
                 const int d = d0 + c;
                 const uint32_t o = frag32(d >> 4, R >> 1, C / 32) + ((d & 15) + 16 * (2 * (R & 1) + hh)) * 8;
                 *reinterpret_cast<uint4*>(xL + o) = xs[hh][c];
+                *reinterpret_cast<uint4*>(xlL + o) = xls[hh][c];
                 *reinterpret_cast<uint4*>(vL + o) = vs[hh][c];
             }
     }
@@ -746,8 +874,8 @@ __device__ __forceinline__ void intra_item(
 #pragma unroll
     for (int R = 0; R < NT; ++R) {
         f32x4 aw = {0.f, 0.f, 0.f, 0.f}, au = aw;
-        {   // T'_RR Y_R (Y single bf16 for both): Y rows 32 (R / 2) + 8 q4 + i in the normal-order
-            // fragment R / 2
+        {   // T'_RR Y_R (Y = exp(gamma) k split, v exact in bf16): Y rows 32 (R / 2) + 8 q4 + i in
+            // the normal-order fragment R / 2
             uint4 th = make_uint4(0u, 0u, 0u, 0u), tl = th;
             if ((q4 >> 1) == (R & 1)) {
                 const uint4* tp = reinterpret_cast<const uint4*>(Tpre + R * 512 + r16 * 32);
@@ -757,9 +885,11 @@ __device__ __forceinline__ void intra_item(
             const bf16x8 thi = as_bf16x8(th), tlo = as_bf16x8(tl);
             const uint32_t fo = frag32(dt, R >> 1, C / 32) + lane * 8;
             const bf16x8 xf = as_bf16x8(*reinterpret_cast<const uint4*>(xL + fo));
+            const bf16x8 xlf = as_bf16x8(*reinterpret_cast<const uint4*>(xlL + fo));
             const bf16x8 vf = as_bf16x8(*reinterpret_cast<const uint4*>(vL + fo));
             aw = mfma32(thi, xf, aw);
             aw = mfma32(tlo, xf, aw);
+            aw = mfma32(thi, xlf, aw);
             au = mfma32(thi, vf, au);
             au = mfma32(tlo, vf, au);
         }
@@ -839,11 +969,12 @@ __device__ __forceinline__ void intra_item(
         for (int ks = 0; ks < KD / 32; ++ks) store_qg(qgL, Rd, ks, r16, q4, qgkeep[ks]);
     }
     // w and u as pi-order operands: tiles 2s and 2s+1 give the 32 contracted rows of step s.
-    // w only reaches P and Q, both formed from its high part; u keeps its split for B.
-    uint4 wh[NS], uh[NS], ul[NS];
+    // Both keep their split for P and B; Q and U take the high parts.
+    uint4 wh[NS], wl[NS], uh[NS], ul[NS];
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
         wh[s] = make_uint4(wzh[2 * s].x, wzh[2 * s].y, wzh[2 * s + 1].x, wzh[2 * s + 1].y);
+        wl[s] = make_uint4(wzl[2 * s].x, wzl[2 * s].y, wzl[2 * s + 1].x, wzl[2 * s + 1].y);
         uh[s] = make_uint4(uzh[2 * s].x, uzh[2 * s].y, uzh[2 * s + 1].x, uzh[2 * s + 1].y);
         ul[s] = make_uint4(uzl[2 * s].x, uzl[2 * s].y, uzl[2 * s + 1].x, uzl[2 * s + 1].y);
     }
@@ -854,28 +985,39 @@ __device__ __forceinline__ void intra_item(
     // P^T tile (rows d in block dt, columns k in block x) = w^T kg; B tile (rows k in x,
     // columns v in dt) = kg^T u.  -P goes out in pi order as the A operand of -P S.
     // Outputs of the item through uniform bases and 32-bit byte offsets.
-    uint16_t* PnI = ws.Pn + ch * KD * KD;
+    uint16_t* PnI = ws.Pn + ch * 2 * KD * KD;
     float* BmI = ws.Bm + ch * KD * VD;
     uint16_t* QpI = ws.Qp + ch * C * KD;
     uint16_t* UpI = ws.Up + ch * C * VD;
 #pragma unroll
     for (int x = 0; x < KD / 16; ++x) {
-        // P (stored with one bf16 rounding) from the high parts only; B split
-        f32x4 pt = {0.f, 0.f, 0.f, 0.f}, b0 = pt, b1 = pt;
+        // P and B from split operands (three MFMAs each): the state goes through P in every
+        // chunk, so a single bf16 rounding of w or kg grows into its error where it persists
+        f32x4 pt = {0.f, 0.f, 0.f, 0.f}, p1 = pt, b0 = pt, b1 = pt;
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
             const bf16x8 kh = as_bf16x8(*reinterpret_cast<const uint4*>(kgL + (x * NS + s) * 512 + lane * 8));
             const bf16x8 kl = as_bf16x8(*reinterpret_cast<const uint4*>(kgL + (NKG / 2 + x * NS + s) * 512 + lane * 8));
             pt = mfma32(as_bf16x8(wh[s]), kh, pt);
+            p1 = mfma32(as_bf16x8(wl[s]), kh, p1);
+            p1 = mfma32(as_bf16x8(wh[s]), kl, p1);
             b0 = mfma32(kh, as_bf16x8(uh[s]), b0);
             b1 = mfma32(kl, as_bf16x8(uh[s]), b1);
             b1 = mfma32(kh, as_bf16x8(ul[s]), b1);
         }
         f32x4 bt;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) bt[e] = b0[e] + b1[e];
-        const uint2 ph = make_uint2(pack_bf2(-pt[0], -pt[1]), pack_bf2(-pt[2], -pt[3]));
-        *mptr<uint2>(PnI, (frag32(x, dt >> 1, KD / 32) + fragP(dt & 1, r16, q4)) * 2u) = ph;
+        for (int e = 0; e < 4; ++e) {
+            bt[e] = b0[e] + b1[e];
+            pt[e] += p1[e];
+        }
+        // -P split into bf16 high and low parts, for the same reason
+        uint2 ph, pl;
+        split2(-pt[0], -pt[1], ph.x, pl.x);
+        split2(-pt[2], -pt[3], ph.y, pl.y);
+        const uint32_t po = (frag32(x, dt >> 1, KD / 32) + fragP(dt & 1, r16, q4)) * 2u;
+        *mptr<uint2>(PnI, po) = ph;
+        *mptr<uint2>(PnI, po + KD * KD * 2u) = pl;
         *mptr<float4>(BmI, ((x * (VD / 16) + dt) * 64 + lane) * 16u) = make_float4(bt[0], bt[1], bt[2], bt[3]);
     }
     // Q^T tile (rows d in dt, columns i in I) = (qg)^T - w^T A2^T; U^T tile (rows v in dt,

@@ -96,7 +96,8 @@ def make_inputs(B: int, T: int, H: int, K: int = 128, V: int = 128, *, seed: int
                 initial_state: bool = False, chunk_size: int = 64,
                 gate_mean: float = 0.0, gate: str = "logsigmoid",
                 beta_mode: str = "sigmoid", state_std: float = 0.1,
-                normalise: bool = True, HV: Optional[int] = None) -> Inputs:
+                normalise: bool = True, HV: Optional[int] = None,
+                spike_prob: float = 0.0, spike_value: float = -40.0) -> Inputs:
     """Draw one seeded batch.
 
     gate: "logsigmoid" -> g = logsigmoid(N(gate_mean, 1)); "zero" -> g = 0.
@@ -104,6 +105,9 @@ def make_inputs(B: int, T: int, H: int, K: int = 128, V: int = 128, *, seed: int
     With ``lengths`` the batch is packed (B must be 1, T = sum(lengths)) and
     ``cu_seqlens`` is the int32 prefix sum of the lengths.  ``HV`` (a multiple of H)
     gives v, g, beta and the initial state HV value heads while q and k keep H.
+    ``spike_prob`` > 0 sets the whole gate of a (token, head) to ``spike_value`` with that
+    probability (isolated strong forgetting); the mask is drawn after everything else, so
+    the other tensors are those of the same seed without spikes.
     """
     if lengths is not None:
         if B != 1 or T != sum(lengths):
@@ -137,6 +141,9 @@ def make_inputs(B: int, T: int, H: int, K: int = 128, V: int = 128, *, seed: int
         beta = torch.ones(B, T, Hv)
     else:
         raise ValueError(beta_mode)
+    if spike_prob > 0:
+        hit = torch.rand(B, T, Hv, generator=gen) < spike_prob
+        g = torch.where(hit[..., None] if per_dim_gate else hit, torch.tensor(float(spike_value)), g)
     cu = None
     if lengths is not None:
         cu = torch.zeros(len(lengths) + 1, dtype=torch.int32)
@@ -144,6 +151,47 @@ def make_inputs(B: int, T: int, H: int, K: int = 128, V: int = 128, *, seed: int
     return Inputs(q.to(torch.bfloat16), k.to(torch.bfloat16), v.to(torch.bfloat16),
                   g.contiguous(), beta.contiguous(),
                   None if s0 is None else s0.contiguous(), cu, chunk_size)
+
+
+def make_teacher_inputs(T: int, H: int, K: int = 128, V: int = 128, *, seed: int, chunk_size: int = 64,
+                        state_scale: float = 1.0, noise: float = 1e-2,
+                        key_scale: Sequence[float] = (1.0, 1.0), gate: str = "zero",
+                        gate_mean: float = 0.0, beta_mode: str = "sigmoid") -> Inputs:
+    """One sequence (B = 1) whose values come from a linear teacher that the initial state
+    already holds, the input family of the page's ``cancellation_stress`` mode (section
+    test_inputs.py对抗性: inputs aimed at the cancellation in v - w S).
+
+    Drawn in order from one generator seeded with ``seed``: q, k ~ N(0, 1) normalised over K;
+    the teacher W = state_scale * N(0, 1) of shape [H, V, K], which is also the initial state;
+    per chunk of ``chunk_size`` tokens a key scale drawn log-uniformly from ``key_scale``;
+    noise ~ N(0, 1); gates and beta as :func:`make_inputs`.  Then k is scaled per chunk,
+    rounded to bf16, and v_t = W k_t + noise * N(0, 1) (in fp32 from the rounded keys) is
+    rounded to bf16.  A state that has learnt W predicts every value up to the noise, so the
+    correction each chunk applies is a small difference of large terms.
+    """
+    gen = torch.Generator("cpu").manual_seed(int(seed))
+    randn = lambda *shape: torch.randn(*shape, generator=gen, dtype=torch.float32)  # noqa: E731
+    q = l2_normalise(randn(1, T, H, K))
+    k = l2_normalise(randn(1, T, H, K))
+    W = randn(H, V, K) * state_scale
+    nch = (T + chunk_size - 1) // chunk_size
+    lo, hi = float(key_scale[0]), float(key_scale[1])
+    u = torch.rand(nch, generator=gen)
+    a = torch.exp(torch.log(torch.tensor(lo)) + u * (torch.log(torch.tensor(hi)) - torch.log(torch.tensor(lo))))
+    eps = randn(1, T, H, V)
+    g0 = randn(1, T, H, K)
+    b0 = randn(1, T, H)
+    k = (k * a.repeat_interleave(chunk_size)[:T].view(1, T, 1, 1)).to(torch.bfloat16)
+    v = (torch.einsum("hvk,bthk->bthv", W, k.float()) + noise * eps).to(torch.bfloat16)
+    if gate == "logsigmoid":
+        g = F.logsigmoid(g0 + gate_mean)
+    elif gate == "zero":
+        g = torch.zeros(1, T, H, K)
+    else:
+        raise ValueError(gate)
+    beta = {"sigmoid": torch.sigmoid(b0), "one": torch.ones(1, T, H)}[beta_mode]
+    return Inputs(q.to(torch.bfloat16), k, v, g.contiguous(), beta.contiguous(),
+                  W.unsqueeze(0).contiguous(), None, chunk_size)
 
 
 def workload_inputs(w: Workload, seed: int, **overrides) -> Inputs:

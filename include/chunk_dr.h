@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define CDR_VERSION 5
+#define CDR_VERSION 6
 
 typedef enum {
     CDR_OK = 0,
@@ -82,17 +82,23 @@ typedef struct {
 } cdr_problem;
 
 /*
- * Host-only validation of a problem description; never touches the device.
- * Returns CDR_OK or the first violated rule (see cdr_status).
+ * Host-only validation of a problem description; never touches the device.  The rules are the
+ * input checks of the chunk_kda page's host wrapper (section 主机侧 wrapper 与输入校验: K = V =
+ * 128, a batch of one with cu_seqlens, shapes that agree), with the page's fixed-length
+ * T % 128 == 0 relaxed: any T is accepted, a short last chunk being zero-filled as the page does
+ * for varlen tails.  Dtypes are not described here (the interface is untyped); the Python
+ * binding checks them.  Returns CDR_OK or the first violated rule (see cdr_status).
  */
 cdr_status cdr_check(const cdr_problem* p);
 
 /*
- * Bytes of device workspace chunk_dr_fwd needs for problem p (0 if p is invalid).
- * The size depends only on the shape fields (B, T, H, HV, K, V, N, chunk_size): it
- * holds the per-chunk intermediates (w, u, decayed keys and queries, the in-chunk
- * attention block, the chunk-entry states and the chunk's state map), about 190 KiB per
- * chunk and head at chunk_size 128, plus up to 512 per-workgroup scratch slots of 224 KiB.
+ * Bytes of device workspace chunk_dr_fwd needs for problem p (0 if p is invalid).  The
+ * workspace replaces the intermediate tensors of the page's wrapper (section 主机侧 wrapper 与
+ * 输入校验 allocates them per call); here the caller owns it.  The size depends only on the
+ * shape fields (B, T, H, HV, K, V, N, chunk_size): per chunk and value head the factors of the
+ * chunk step (-P split in two bf16 parts, B in fp32, Q, U, exp(gamma_C)) and the chunk-entry
+ * state, 224.5 KiB at chunk_size 128 and 192.5 KiB at 64, plus up to 512 per-workgroup scratch
+ * slots of 36 KiB (20 KiB at 64).
  */
 size_t cdr_workspace_bytes(const cdr_problem* p);
 
@@ -102,7 +108,13 @@ size_t cdr_workspace_bytes(const cdr_problem* p);
  *   q, k          bf16 [B*T, H, K]   queries and keys
  *   v             bf16 [B*T, HV, V]  values (HV value heads, see cdr_problem)
  *   g             fp32 [B*T, HV, K] (CDR_GATE_PER_DIM) or [B*T, HV] (CDR_GATE_PER_HEAD);
- *                 log-domain forget gate, expected <= 0
+ *                 log-domain forget gate.  Supported: every finite g <= 0 (the page's gates
+ *                 are logsigmoid values); the in-chunk sums of g must be finite in fp32.
+ *                 A chunk in which a per-dimension gate sums to more than 64 in magnitude
+ *                 over half a 16-token tile takes an exact path for its diagonal 16 x 16
+ *                 blocks (one exponential per pair and dimension), about as slow again as
+ *                 the rest of the chunk's work; other chunks are unaffected.  g > 0 is
+ *                 outside the contract (the state can then grow without bound).
  *   beta          fp32 [B*T, HV]     delta-rule step size
  *   initial_state fp32 [N, HV, V, K] read when p->has_initial_state, else may be NULL
  *   cu_seqlens    int32 [N + 1]      device array of sequence offsets into the packed token

@@ -34,8 +34,9 @@ def _as_f64(x):
     return x.detach().cpu().double().numpy()
 
 
-def _chunk(q, k, v, g, beta, S, scale):
-    """One chunk of one head. q, k, g: [n, K]; v: [n, V]; beta: [n]; S: [K, V]."""
+def _chunk(q, k, v, g, beta, S, scale, detail=False):
+    """One chunk of one head. q, k, g: [n, K]; v: [n, V]; beta: [n]; S: [K, V].
+    Returns (o, S_next), and also u and v_new when ``detail``."""
     n, K = k.shape
     gam = np.cumsum(g, axis=0)                                   # M1
     diff = gam[:, None, :] - gam[None, :, :]                     # [i, j, d]
@@ -53,6 +54,8 @@ def _chunk(q, k, v, g, beta, S, scale):
     o = (scale * q * np.exp(gam)) @ S + A2 @ v_new
     g_last = gam[-1]
     S_next = np.exp(g_last)[:, None] * S + (np.exp(g_last[None, :] - gam) * k).T @ v_new
+    if detail:
+        return o, S_next, u, v_new
     return o, S_next
 
 
@@ -94,3 +97,26 @@ def chunked_fwd(q, k, v, g, beta, scale=None, initial_state=None, cu_seqlens=Non
                 o[b, c0:c1, h] = oc
             S_out[n, h] = S.T
     return o, S_out
+
+
+def cancellation(q, k, v, g, beta, initial_state, chunk_size=64, scale=None):
+    """How much the state's prediction cancels in section M4's v_new = u - w S, per chunk:
+    ``|v_new| / |u|`` (Frobenius norms over the chunk), fp64, shape [H, chunks], for one
+    fixed-length sequence (B = 1) without grouped heads.  Used to choose adversarial inputs
+    (the page's cancellation_stress mode); it defines no expected value."""
+    q, k, v, g, beta = (_as_f64(x)[0] for x in (q, k, v, g, beta))
+    T, H, K = q.shape
+    if scale is None:
+        scale = K ** -0.5
+    s0 = _as_f64(initial_state)[0]
+    out = []
+    for h in range(H):
+        S = s0[h].T.copy()
+        row = []
+        for c0 in range(0, T, chunk_size):
+            c1 = min(c0 + chunk_size, T)
+            _, S, u, vn = _chunk(q[c0:c1, h], k[c0:c1, h], v[c0:c1, h], g[c0:c1, h], beta[c0:c1, h],
+                                 S, scale, detail=True)
+            row.append(np.linalg.norm(vn) / max(np.linalg.norm(u), 1e-300))
+        out.append(row)
+    return np.asarray(out)

@@ -334,3 +334,29 @@ def test_chunked_matches_recurrent_grouped_and_normalised(per_dim):
                            chunk_size=64, use_qk_l2norm=True)
     for x, y in zip(a, b):
         np.testing.assert_allclose(x, y, rtol=1e-9, atol=1e-9)
+
+
+# ---------------------------------------------------------------- input generators used by the GPU suite
+def test_spike_gates_leave_other_inputs_unchanged():
+    """spike_prob draws its mask after every other tensor: the rest is the unspiked batch."""
+    from chunked_gated_delta_chunk_amd.synth import make_inputs
+    a = make_inputs(1, 256, 2, seed=3, spike_prob=0.125, initial_state=True)
+    b = make_inputs(1, 256, 2, seed=3, initial_state=True)
+    for x, y in ((a.q, b.q), (a.k, b.k), (a.v, b.v), (a.beta, b.beta), (a.initial_state, b.initial_state)):
+        assert torch.equal(x, y)
+    hit = (a.g == -40.0).all(-1)
+    assert 0.05 < hit.float().mean().item() < 0.2
+    assert torch.equal(a.g[~hit], b.g[~hit])
+
+
+def test_teacher_inputs_are_predicted_by_the_initial_state():
+    """Values of the cancellation inputs are the initial state's prediction up to the noise and
+    the bf16 rounding of v; the keys carry one scale per chunk."""
+    from chunked_gated_delta_chunk_amd.synth import make_teacher_inputs
+    t = make_teacher_inputs(256, 2, seed=4, chunk_size=64, key_scale=(0.3, 1.2), noise=1e-3)
+    pred = torch.einsum("hvk,bthk->bthv", t.initial_state[0], t.k.float())
+    err = (t.v.float() - pred).abs()
+    assert err.max().item() <= 1e-3 * 6 + 2 ** -8 * pred.abs().max().item()
+    norms = t.k.float().norm(dim=-1)[0, :, 0].view(4, 64)
+    assert ((norms - norms[:, :1]).abs() < 0.02).all()        # one scale per chunk
+    assert norms.min().item() >= 0.29 and norms.max().item() <= 1.21
