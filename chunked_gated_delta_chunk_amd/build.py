@@ -11,7 +11,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libchunkdr.so")
-SOURCES = ["cdr_api.hip", "cdr_intra.hip", "cdr_chain.hip", "cdr_decode.hip", "cdr_bwd.hip", "cdr_cp.hip"]
+SOURCES = ["cdr_api.hip", "cdr_intra.hip", "cdr_chain.hip", "cdr_decode.hip", "cdr_bwd.hip", "cdr_cp.hip",
+           "cdr_noalloc.hip"]
 ARCH = os.environ.get("CDR_OFFLOAD_ARCH", "gfx950")
 
 

@@ -310,6 +310,7 @@ const char* cdr_status_str(cdr_status s) {
         case CDR_ERR_VARLEN_BATCH: return "cu_seqlens requires B == 1";
         case CDR_ERR_WORKSPACE: return "workspace missing, too small or not 256-byte aligned";
         case CDR_ERR_HIP: return "HIP kernel launch failed";
+        case CDR_ERR_SCRATCH_LIMIT: return "problem needs more workspace than the no-allocation entry point's static array";
     }
     return "unknown status";
 }

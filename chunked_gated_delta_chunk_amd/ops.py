@@ -16,16 +16,18 @@ LIB_PATH = os.path.join(_HERE, "libchunkdr.so")
 
 CDR_OK = 0
 _STATUS_EXC = {1: ValueError, 2: ValueError, 3: ValueError, 4: ValueError, 5: RuntimeError,
-               6: RuntimeError}
+               6: RuntimeError, 7: ValueError}
 GATE_PER_DIM = 0
 GATE_PER_HEAD = 1
 
 EXPORTED = ("cdr_check", "cdr_workspace_bytes", "chunk_dr_fwd", "chunk_dr_fwd_stages",
+            "chunk_dr_fwd_noalloc",
             "cdr_bwd_workspace_bytes", "chunk_dr_bwd", "chunk_dr_bwd_stages",
             "chunk_dr_segment_map", "chunk_dr_merge_states",
             "cdr_recurrent_check", "chunk_dr_recurrent_fwd", "cdr_status_str", "cdr_version")
 STATE_SEPARATE, STATE_POOL, STATE_POOL_SPEC = 0, 1, 2
 STAGE_INTRA, STAGE_CHAIN, STAGE_OUTPUT, STAGE_ALL = 1, 2, 4, 7
+NOALLOC_SCRATCH_BYTES = 256 * 1024 * 1024   # CDR_NOALLOC_SCRATCH_BYTES of chunk_dr.h
 BWD_PREP, BWD_CHAINS, BWD_LOCAL, BWD_ALL = 1, 2, 4, 7
 
 
@@ -71,6 +73,8 @@ def load_library(path: str = LIB_PATH):
     lib.chunk_dr_fwd_stages.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t,
                                         ctypes.c_int32, vp]
     lib.chunk_dr_fwd_stages.restype = ctypes.c_int
+    lib.chunk_dr_fwd_noalloc.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.chunk_dr_fwd_noalloc.restype = ctypes.c_int
     lib.cdr_bwd_workspace_bytes.argtypes = [P]
     lib.cdr_bwd_workspace_bytes.restype = ctypes.c_size_t
     lib.chunk_dr_bwd.argtypes = [P] + [vp] * 16 + [ctypes.c_size_t, vp]
@@ -153,7 +157,7 @@ class PreparedForward:
 
     def __init__(self, q, k, v, g, beta, scale=None, initial_state=None, cu_seqlens=None,
                  chunk_size=64, output_final_state=False, workspace=None, out=None,
-                 final_state_out=None, use_qk_l2norm_in_kernel=False):
+                 final_state_out=None, use_qk_l2norm_in_kernel=False, noalloc=False):
         lib = load_library()
         _need(q, "q", torch.bfloat16)
         if q.dim() != 4:
@@ -209,21 +213,35 @@ class PreparedForward:
             else:
                 _need(final_state_out, "final_state_out", torch.float32, (N, HV, V, K))
             self.S = final_state_out
-        nbytes = lib.cdr_workspace_bytes(ctypes.byref(self.problem))
-        if workspace is None:
-            workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
-        elif workspace.numel() * workspace.element_size() < nbytes:
-            raise ValueError("workspace too small")
-        self.workspace = workspace
         ptr = lambda t: None if t is None else _dev_ptr(t, device)  # noqa: E731
         qq, kk, vv, gg, bb = self.inputs
-        self._args = (ctypes.byref(self.problem), ptr(qq), ptr(kk), ptr(vv), ptr(gg), ptr(bb),
-                      ptr(self.s0), ptr(self.cu), ptr(self.o), ptr(self.S), ptr(workspace),
-                      workspace.numel() * workspace.element_size())
+        self.noalloc = bool(noalloc)
+        if self.noalloc:
+            # the library's static workspace (chunk_dr_fwd_noalloc): none is allocated here
+            self.workspace = None
+            self._args = (ctypes.byref(self.problem), ptr(qq), ptr(kk), ptr(vv), ptr(gg), ptr(bb),
+                          ptr(self.s0), ptr(self.cu), ptr(self.o), ptr(self.S))
+        else:
+            nbytes = lib.cdr_workspace_bytes(ctypes.byref(self.problem))
+            if workspace is None:
+                workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+            elif workspace.numel() * workspace.element_size() < nbytes:
+                raise ValueError("workspace too small")
+            self.workspace = workspace
+            self._args = (ctypes.byref(self.problem), ptr(qq), ptr(kk), ptr(vv), ptr(gg), ptr(bb),
+                          ptr(self.s0), ptr(self.cu), ptr(self.o), ptr(self.S), ptr(workspace),
+                          workspace.numel() * workspace.element_size())
         self._lib = lib
 
     def __call__(self, stages: int = STAGE_ALL):
         stream = torch.cuda.current_stream(self.device).cuda_stream
+        if self.noalloc:
+            if stages != STAGE_ALL:
+                raise ValueError("the no-allocation entry point runs all stages")
+            st = self._lib.chunk_dr_fwd_noalloc(*self._args, stream)
+            if st != CDR_OK:
+                _raise(st, "chunk_dr_fwd_noalloc")
+            return self.o, self.S
         if stages == STAGE_ALL:
             st = self._lib.chunk_dr_fwd(*self._args, stream)
         else:
@@ -265,6 +283,21 @@ def chunk_dr_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Ten
                            final_state_out=final_state_out,
                            use_qk_l2norm_in_kernel=use_qk_l2norm_in_kernel)
     return call(stages)
+
+
+def chunk_dr_fwd_noalloc(q, k, v, g, beta, scale=None, initial_state=None, cu_seqlens=None,
+                         chunk_size=64, output_final_state=False, out=None, final_state_out=None,
+                         use_qk_l2norm_in_kernel=False):
+    """:func:`chunk_dr_fwd` through the library's no-allocation entry point: the workspace is the
+    library's static device array (at most ``NOALLOC_SCRATCH_BYTES``; larger problems raise
+    ValueError).  Pass ``out`` (and ``final_state_out``) to allocate nothing in this call either.
+    Calls whose kernels overlap in time on one device share that array and race."""
+    call = PreparedForward(q, k, v, g, beta, scale=scale, initial_state=initial_state,
+                           cu_seqlens=cu_seqlens, chunk_size=chunk_size,
+                           output_final_state=output_final_state, out=out,
+                           final_state_out=final_state_out,
+                           use_qk_l2norm_in_kernel=use_qk_l2norm_in_kernel, noalloc=True)
+    return call()
 
 
 def segment_map(q, k, v, g, beta, cu_seqlens=None, chunk_size=64, scale=None,

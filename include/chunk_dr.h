@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define CDR_VERSION 6
+#define CDR_VERSION 7
 
 typedef enum {
     CDR_OK = 0,
@@ -53,7 +53,9 @@ typedef enum {
     CDR_ERR_UNSUPPORTED = 3,   /* K or V != 128, chunk_size not 64 or 128, unknown gate */
     CDR_ERR_VARLEN_BATCH = 4,  /* cu_seqlens given with B != 1 */
     CDR_ERR_WORKSPACE = 5,     /* workspace NULL or smaller than cdr_workspace_bytes() */
-    CDR_ERR_HIP = 6            /* a kernel launch failed (hipGetLastError) */
+    CDR_ERR_HIP = 6,           /* a kernel launch failed (hipGetLastError) */
+    CDR_ERR_SCRATCH_LIMIT = 7  /* chunk_dr_fwd_noalloc: the problem needs more workspace than its
+                                  static array holds (CDR_NOALLOC_SCRATCH_BYTES) */
 } cdr_status;
 
 typedef enum {
@@ -169,6 +171,31 @@ cdr_status chunk_dr_fwd_stages(const cdr_problem* p,
                                void* o, float* final_state,
                                void* workspace, size_t workspace_bytes,
                                int32_t stages, void* stream);
+
+/* ------------------------------------------------------------------------------------------
+ * The forward for callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation.
+ *
+ * chunk_dr_fwd_noalloc is chunk_dr_fwd (same arguments, same kernels, same bits) with its
+ * workspace in a static device array of CDR_NOALLOC_SCRATCH_BYTES owned by the library: one such
+ * array per device the entry point runs on, taken when the library's code for it is first used
+ * on that device and held until the process ends.  It allocates and frees nothing.  Problems
+ * whose cdr_workspace_bytes() exceeds CDR_NOALLOC_SCRATCH_BYTES are rejected with
+ * CDR_ERR_SCRATCH_LIMIT before anything is launched; the limit holds the workspace of 8192
+ * tokens x 16 heads at chunk_size 128.  The caller still passes (and owns) inputs and outputs.
+ *
+ * Every call on one device uses that device's one array: two calls whose kernels overlap in time
+ * on the same device (different streams, or different threads without ordering) race on it and
+ * give undefined results.  Calls ordered on one stream are safe.  The forward reads nothing of
+ * the workspace that the same call has not written, so what a previous call left there does not
+ * matter and nothing is cleared.
+ * ------------------------------------------------------------------------------------------ */
+#define CDR_NOALLOC_SCRATCH_BYTES (256u * 1024u * 1024u)
+cdr_status chunk_dr_fwd_noalloc(const cdr_problem* p,
+                                const void* q, const void* k, const void* v,
+                                const float* g, const float* beta,
+                                const float* initial_state, const int32_t* cu_seqlens,
+                                void* o, float* final_state, void* stream);
 
 /* ------------------------------------------------------------------------------------------
  * Context parallelism, the part one device computes (page "flash-linear-attention KCP 精度失效

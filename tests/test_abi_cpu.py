@@ -203,3 +203,17 @@ def test_recurrent_binding_errors():
                                 output_final_state=True)
     with pytest.raises(ValueError):  # host tensors: no CPU path exists
         cdr.fused_recurrent_fwd(q, q, v, g, beta, state_pool=pool, ssm_state_indices=idx)
+
+
+def test_noalloc_rejects_a_problem_beyond_its_array_without_touching_device():
+    """chunk_dr_fwd_noalloc checks the workspace the problem needs against its static array before
+    any device call: kda_t65536 (16384 chunks x heads) does not fit."""
+    import chunked_gated_delta_chunk_amd as cdr
+    p = cdr.make_problem(1, 65536, 32, 128, 128, 1, True, 128, 128 ** -0.5, False, True, False)
+    assert cdr.workspace_bytes(p) > cdr.NOALLOC_SCRATCH_BYTES
+    lib = cdr.load_library()
+    st = lib.chunk_dr_fwd_noalloc(ctypes.byref(p), *([None] * 9), None)
+    assert st == 7 and "static array" in lib.cdr_status_str(st).decode()
+    # the workload the limit is stated for fits
+    q = cdr.make_problem(1, 8192, 16, 128, 128, 1, True, 128, 128 ** -0.5, True, True, False)
+    assert cdr.workspace_bytes(q) <= cdr.NOALLOC_SCRATCH_BYTES
