@@ -43,6 +43,28 @@ def nominal_flops(w, lengths):
     return f
 
 
+def min_flops(w, lengths):
+    """F_min: F_nom with the triangular products counted once per pair (A, A2, w, u and A2 v_new
+    are lower-triangular n x n products, so their n^2 terms halve)."""
+    K, V, C, H = w.K, w.V, w.chunk_size, w.H
+    f = 0.0
+    for L in lengths:
+        for c0 in range(0, L, C):
+            n = min(C, L - c0)
+            f += H * (2.0 * (1.5 * n * n * K + n * n * V + 3 * n * K * V) + n ** 3 / 3.0)
+    return f
+
+
+def compulsory_bytes(w, lengths):
+    """The forward's compulsory HBM bytes: q, k, v and o in bf16, g in fp32 (per dimension or one
+    per token and head), beta in fp32, the initial state when given and the final state, fp32."""
+    tokens = sum(lengths)
+    gate_bytes = 4 * w.K if w.per_dim_gate else 4
+    state = w.K * w.V * 4
+    return (tokens * w.H * (2 * 2 * w.K + 2 * 2 * w.V + gate_bytes + 4)
+            + len(lengths) * w.H * state * (2 if w.initial_state else 1))
+
+
 def kernel_work(w, lengths):
     """Algorithmic flops and compulsory bytes per kernel of this implementation, in which the
     chunk step is re-associated (S' = exp(gamma_C) S - P S + B, o = Q S + U).  Per chunk of n
@@ -90,9 +112,10 @@ def source_hash(kernel):
     return h.hexdigest()[:16]
 
 
-def load_traffic(kernel, workload):
-    """HBM bytes per launch from the committed counter summary, if it matches the sources."""
-    path = os.path.join(ROOT, "profiles", f"{workload}_hbm_traffic.json")
+def load_counters(kernel, workload, what="hbm_traffic", field="hbm_bytes"):
+    """A per-launch figure from a committed counter summary (profiles/<workload>_<what>.json),
+    if the summary was taken on the current sources of the kernel."""
+    path = os.path.join(ROOT, "profiles", f"{workload}_{what}.json")
     try:
         with open(path) as fh:
             data = json.load(fh)
@@ -101,7 +124,23 @@ def load_traffic(kernel, workload):
     rec = data.get(workload, {}).get(kernel)
     if not rec or rec.get("source_sha") != source_hash(kernel):
         return None
-    return rec.get("hbm_bytes")
+    return rec.get(field)
+
+
+def load_traffic(kernel, workload):
+    """HBM bytes per launch from the committed counter summary, if it matches the sources."""
+    return load_counters(kernel, workload)
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def decode_bytes(w):
@@ -285,13 +324,20 @@ def cpu_baseline(inp, w, budget_s):
     tsub = T if dt * T / probe <= budget_s else max(probe, int(budget_s / dt * probe) // 64 * 64)
     if tsub != probe:
         dt = run(tsub)
+    # repeat a short sample until about a second of wall time has been measured
+    reps = max(1, min(20, int(1.0 / max(dt, 1e-3))))
+    if reps > 1:
+        dt = min(dt, min(run(tsub) for _ in range(reps - 1)))
     return {"value": tsub * w.B / dt if w.lengths is None else tsub / dt, "unit": "tokens/s",
-            "cores": min(threads, chains), "kind": "oracle",
+            "cores": min(threads, chains), "cpu_model": cpu_model(), "kind": "oracle",
             "sample": (f"fp64 per-token recurrence (C, OpenMP over {chains} (sequence, head) chains) "
-                       f"on the first {tsub} of {T} tokens of every head, {dt:.2f} s wall")}
+                       f"on the first {tsub} of {T} tokens of every head, best of {reps} runs, "
+                       f"{dt:.3f} s wall each")}
 
 
-EV_STRIDE = 10  # timed steps per step with per-kernel events
+EV_STRIDE = 10        # timed steps per step with per-kernel events
+CLOCK_WARMUP_S = 0.3  # untimed forward calls before the warmup steps (clock ramp)
+COLD_STEPS = 20       # event-timed single forwards, flushed and warm
 
 
 def main():
@@ -367,6 +413,13 @@ def main():
 
     stages = (cdr.STAGE_INTRA, cdr.STAGE_CHAIN, cdr.STAGE_OUTPUT)
     names = ("intra", "chain", "output")
+    # clocks: the first tens of milliseconds of GPU work run below the sustained clock, so the
+    # forward runs untimed for CLOCK_WARMUP_S before the warmup steps
+    tw = time.perf_counter()
+    while time.perf_counter() - tw < CLOCK_WARMUP_S:
+        for i in range(20):
+            calls[i % nsets]()
+        torch.cuda.synchronize()
     for i in range(args.warmup):
         for s in stages:
             calls[i % nsets](s)
@@ -374,8 +427,7 @@ def main():
 
     K = args.steps
     # HIP events between the kernels on every EV_STRIDE-th timed step only: an event between
-    # every pair of kernels costs about 13 us of GPU time per step (6 %), which the wall-clock
-    # throughput would otherwise include
+    # every pair of kernels costs GPU time, which the wall-clock throughput would otherwise include
     ev = {i: [torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)]
           for i in range(0, K, EV_STRIDE)}
     torch.cuda.synchronize()
@@ -398,9 +450,34 @@ def main():
                for j, n in enumerate(names)}
     gpu_ms = sum(kern_ms.values())
 
+    # one forward per measurement with events around it: after a 1 GiB write that pushes the
+    # inputs out of the L2s and the memory-side cache (cold), and the same input set repeated
+    # (warm)
+    flush = torch.empty(2 ** 30 // 4, dtype=torch.float32, device=dev)
+
+    def event_steps(n, cold):
+        ts = []
+        for i in range(n):
+            if cold:
+                flush.fill_(float(i))
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            calls[0]()
+            b.record()
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b))
+        ts.sort()
+        return {"median_ms": round(ts[len(ts) // 2], 5), "min_ms": round(ts[0], 5), "steps": n}
+
+    cold = event_steps(COLD_STEPS, True)
+    warm = event_steps(COLD_STEPS, False)
+    del flush
+
     lengths = list(w.lengths) if w.lengths is not None else [w.T] * w.B
     flops, bytes_ = kernel_work(w, lengths)
     f_nom = nominal_flops(w, lengths)
+    f_min = min_flops(w, lengths)
+    comp = compulsory_bytes(w, lengths)
     tokens = w.tokens
     value = tokens / (ms_step * 1e-3)
     step_tflops = f_nom / (ms_step * 1e-3) / 1e12
@@ -412,17 +489,27 @@ def main():
         gbs = bytes_[n] / sec / 1e9
         per_kernel[n] = {"us": round(kern_ms[n] * 1e3, 2), "tflops": round(tf, 2),
                          "mfma_frac": round(tf / PEAK_BF16_TFLOPS, 4),
-                         "hbm_gbs": round(gbs, 1), "hbm_frac": round(gbs / PEAK_HBM_GBS, 4)}
+                         "hbm_gbs": round(gbs, 1), "hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
+                         "mfma_busy": load_counters(n, args.workload, "sq_counters", "mfma_busy_frac")}
+    # Roofline of the dominant kernel: the path is HBM-bound (its arithmetic intensity is below the
+    # ridge), so the achieved figure is the forward's compulsory bytes (1540 B per token and head
+    # for per-dimension gates, plus the states) over that kernel's average launch time.
     dom = max(names, key=lambda n: kern_ms[n])
-    pk = per_kernel[dom]
-    if pk["mfma_frac"] >= pk["hbm_frac"]:
-        roof = {"bound": "mfma", "achieved": pk["tflops"], "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s"}
-    else:
-        roof = {"bound": "hbm", "achieved": pk["hbm_gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s"}
+    dom_s = kern_ms[dom] * 1e-3
+    roof = {"bound": "hbm", "achieved": round(comp / dom_s / 1e9, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
     roof["traffic"] = load_traffic(dom, args.workload)
     roof["kernel"] = dom
-    roof["duration_us"] = pk["us"]
+    roof["duration_us"] = round(kern_ms[dom] * 1e3, 2)
+    roof["algorithmic_bytes"] = comp
+    whole_step = {"hbm_gbs": round(comp / (ms_step * 1e-3) / 1e9, 1),
+                  "hbm_frac": round(comp / (ms_step * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                  "mfma_frac_f_nom": round(step_tflops / PEAK_BF16_TFLOPS, 4),
+                  "mfma_frac_f_min": round(f_min / (ms_step * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                  "f_nom_gflop": round(f_nom / 1e9, 3), "f_min_gflop": round(f_min / 1e9, 3),
+                  "compulsory_mb": round(comp / 1e6, 2),
+                  "cold_flushed": cold, "warm_same_inputs": warm,
+                  "clock_warmup_s": CLOCK_WARMUP_S}
 
     # parity spot check of the timed buffers against the oracle on one head, so the
     # reported number is for a forward that is correct
@@ -472,6 +559,7 @@ def main():
         "tflops_nominal": round(step_tflops, 2),
         "mfma_frac_bf16_peak": round(step_tflops / PEAK_BF16_TFLOPS, 4),
         "gpu_ms_per_step_events": round(gpu_ms, 5),
+        "whole_step": whole_step,
         "per_kernel": per_kernel,
         "roofline": roof,
         "cpu_baseline": cpu,

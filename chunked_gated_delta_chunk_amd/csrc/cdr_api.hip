@@ -171,10 +171,9 @@ cdr_status chunk_dr_fwd_stages(const cdr_problem* p, const void* q, const void* 
                               (int)scratch_slots(p), s) != hipSuccess)
             return CDR_ERR_HIP;
     }
+    int32_t* order_ws = p->varlen ? reinterpret_cast<int32_t*>(wb + L.off[7]) : nullptr;
     if (stages & CDR_STAGE_CHAIN) {
-        int32_t* order_ws = reinterpret_cast<int32_t*>(wb + L.off[7]);
-        if (cdr::launch_chain(map, p->N, (int)value_heads(p), s0, s_out, ws, p->varlen ? order_ws : nullptr, s) !=
-            hipSuccess)
+        if (cdr::launch_chain(map, p->N, (int)value_heads(p), s0, s_out, ws, order_ws, s) != hipSuccess)
             return CDR_ERR_HIP;
     }
     if ((stages & CDR_STAGE_OUTPUT) && nslots > 0) {

@@ -37,17 +37,25 @@ struct ChainOps {
     float4 gc;      // exp(gamma_C) of the wave's state rows
 };
 
+// per-lane byte offsets of a wave's operands inside one chunk's arrays, the same for every chunk;
+// the per-chunk bases go into buffer descriptors (scalar registers), so no 64-bit address is kept
+// per lane and buffer
+struct ChainOffsets {
+    uint32_t p, b, g;
+};
+
 template <bool MAP>
-__device__ __forceinline__ void chain_load(ChainOps& op, const Work& ws, size_t ch, int x, int lane, int q4, int vb) {
+__device__ __forceinline__ void chain_load(ChainOps& op, const Work& ws, size_t ch, const ChainOffsets& of) {
+    // one descriptor per part, so that every -P load is the lane offset plus an immediate
+    const rsrc_t prh = make_rsrc(ws.Pn + ch * 2 * KD * KD, KD * KD * 2);
+    const rsrc_t prl = make_rsrc(ws.Pn + ch * 2 * KD * KD + KD * KD, KD * KD * 2);
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
-        const size_t off = ch * 2 * KD * KD + frag(x, s, KS) + lane * 8;
-        op.ph[s] = *reinterpret_cast<const uint4*>(ws.Pn + off);
-        op.pl[s] = *reinterpret_cast<const uint4*>(ws.Pn + off + KD * KD);
+        op.ph[s] = bload16(prh, of.p + 1024u * s);
+        op.pl[s] = bload16(prl, of.p + 1024u * s);
     }
-    op.b = MAP ? make_float4(0.f, 0.f, 0.f, 0.f)
-               : *reinterpret_cast<const float4*>(ws.Bm + ch * KD * VD + ((size_t)(x * (VD / 16) + vb) * 64 + lane) * 4);
-    op.gc = *reinterpret_cast<const float4*>(ws.gC + ch * KD + 16 * x + 4 * q4);
+    op.b = MAP ? make_float4(0.f, 0.f, 0.f, 0.f) : bload16f(make_rsrc(ws.Bm + ch * KD * VD, KD * VD * 4), of.b);
+    op.gc = bload16f(make_rsrc(ws.gC + ch * KD, KD * 4), of.g);
 }
 
 // sbuf: one published state, [2 (high, low)][KS fragments][512] bf16
@@ -112,20 +120,26 @@ __global__ __launch_bounds__(CTHREADS) void chain_kernel(ChunkMap map, int H, co
         S = f32x4{v.x, v.y, v.z, v.w};
     }
 
+    ChainOffsets of;
+    of.p = (uint32_t)(frag(x, 0, KS) + lane * 8) * 2u;
+    of.b = (uint32_t)((x * (VD / 16) + vb) * 64 + lane) * 16u;
+    of.g = (uint32_t)(16 * x + 4 * q4) * 4u;
     // Chunk c is computed from ring buffer c % 3 and publishes into LDS buffer c % 2; before
     // it, chunk c + 2 is loaded into the buffer chunk c - 1 used.  Loads are issued
     // unconditionally (the index is clamped to the last chunk) so that the compiler keeps
     // them ahead of the previous chunks' work instead of sinking them next to their use.
+    // (Three chunks ahead measured the same: a step's time grows with the bytes it brings into
+    // the CU, not with how early they are requested.)
     ChainOps op0, op1, op2;
     const int last = nchunks - 1;
     auto chunk_of = [&](int c) { return (size_t)(slot0 + max(min(c, last), 0)) * H + h; };
     auto step = [&](ChainOps& next, int cload, const ChainOps& cur, int c, int buf) {
-        chain_load<MAP>(next, ws, chunk_of(cload), x, lane, q4, vb);
+        chain_load<MAP>(next, ws, chunk_of(cload), of);
         chain_step<MAP>(cur, S, ws, chunk_of(c), x, lane, r16, q4, vb, sbuf[buf]);
     };
     if (nchunks > 0) {
-        chain_load<MAP>(op0, ws, chunk_of(0), x, lane, q4, vb);
-        chain_load<MAP>(op1, ws, chunk_of(1), x, lane, q4, vb);
+        chain_load<MAP>(op0, ws, chunk_of(0), of);
+        chain_load<MAP>(op1, ws, chunk_of(1), of);
     }
     for (int c = 0; c < nchunks; c += 6) {
         step(op2, c + 2, op0, c, 0);

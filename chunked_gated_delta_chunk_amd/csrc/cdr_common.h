@@ -110,6 +110,28 @@ __device__ __forceinline__ void st_nt(float4* p, const float4& v) {
                                 reinterpret_cast<u32x4v*>(p));
 }
 
+// Buffer loads: the base address and size sit in a resource descriptor in scalar registers and
+// each lane gives a 32-bit byte offset, so a per-lane address never takes two vector registers
+// (the compiler folds a uniform base plus a lane offset of a plain global load into a 64-bit
+// per-lane address, kept live per load).  A lane whose offset + access size exceeds `bytes` reads
+// zero.  The third descriptor word is the raw 32-bit data format of the gfx9 family.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ uint4 bload16(rsrc_t r, uint32_t off) {
+    const u32x4v v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ float4 bload16f(rsrc_t r, uint32_t off) {
+    const u32x4v v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+    return make_float4(__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z), __uint_as_float(v.w));
+}
+__device__ __forceinline__ uint2 bload8(rsrc_t r, uint32_t off) {
+    const u32x2v v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+    return make_uint2(v.x, v.y);
+}
+
 // wait for this wave's own LDS traffic; keeps the compiler from reordering across it
 __device__ __forceinline__ void wave_lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
