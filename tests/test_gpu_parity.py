@@ -353,7 +353,7 @@ def test_workload_parity_t65536_all_heads():
     check(inp, heads=[0, 9, 17, 31], label="kda_t65536 heads 0 9 17 31", o_gpu=o, S_gpu=S)
 
 
-@pytest.mark.parametrize("name", ["kda_t8192", "kda_t65536"])
+@pytest.mark.parametrize("name", ["kda_small", "gdn_b2_t2048", "kda_t8192", "kda_varlen", "kda_t65536"])
 def test_workload_repeats_are_bit_identical(name):
     """[chunk_kda] §test_chunk_kda.py E2E: the same input run twice gives the same bits."""
     inp = workload(name)

@@ -360,3 +360,31 @@ def test_teacher_inputs_are_predicted_by_the_initial_state():
     norms = t.k.float().norm(dim=-1)[0, :, 0].view(4, 64)
     assert ((norms - norms[:, :1]).abs() < 0.02).all()        # one scale per chunk
     assert norms.min().item() >= 0.29 and norms.max().item() <= 1.21
+
+
+def test_cancellation_measure_closed_forms():
+    """oracle.chunked.cancellation (|v_new| / |u| per chunk, section M4's v_new = u - w S):
+    from a zero state the first chunk's v_new is u itself (ratio 1); with one-hot keys, g = 0
+    and values that are exactly the state's prediction W k, every v_new is 0 (ratio 0)."""
+    from oracle.chunked import cancellation
+    gen = torch.Generator().manual_seed(11)
+    T, H, K, V = 96, 2, 8, 4
+    q = torch.randn(1, T, H, K, generator=gen, dtype=torch.float64)
+    k = torch.randn(1, T, H, K, generator=gen, dtype=torch.float64)
+    v = torch.randn(1, T, H, V, generator=gen, dtype=torch.float64)
+    g = -torch.rand(1, T, H, K, generator=gen, dtype=torch.float64)
+    beta = torch.rand(1, T, H, generator=gen, dtype=torch.float64)
+    zero = torch.zeros(1, H, V, K, dtype=torch.float64)
+    c = cancellation(q, k, v, g, beta, zero, chunk_size=32)
+    assert c.shape == (H, 3)
+    assert np.allclose(c[:, 0], 1.0, rtol=0, atol=1e-12)
+    # linear teacher that the initial state already holds exactly: v_t = W k_t
+    W = torch.randint(-8, 9, (H, V, K), generator=gen).double() / 4
+    idx = torch.randint(0, K, (T, H), generator=gen)
+    k1 = torch.nn.functional.one_hot(idx, K).double().unsqueeze(0)
+    v1 = torch.einsum("hvk,bthk->bthv", W, k1)
+    c0 = cancellation(q, k1, v1, torch.zeros_like(g), beta, W.unsqueeze(0), chunk_size=32)
+    assert np.all(c0 <= 1e-12)
+    # a state that does not hold the teacher leaves a visible correction
+    c1 = cancellation(q, k1, v1, torch.zeros_like(g), beta, zero, chunk_size=32)
+    assert c1[:, 0].min() > 0.5
