@@ -48,22 +48,28 @@
 
 namespace cdr {
 
-constexpr int IWAVES = 8;
 constexpr float L2N_EPS = 1e-6f;  // in-kernel q/k normalisation: x / sqrt(|x|^2 + eps)
 // Largest gate span (|gamma_i - gamma_m| over a 16-row tile and its middle row m) for which the
 // tile-middle pivot factors exp(+-(gamma_i - gamma_m)) are used: they stay below e^64, so the
 // decayed operands, even times a large key, and their products stay finite in fp32.  A chunk
 // with a wider tile takes pivots that make every factor <= 1 and exact diagonal tiles.
 constexpr float SAFE_SPAN = 64.f;
-constexpr int ITHREADS = 64 * IWAVES;
+constexpr int IMAXTHREADS = 512;  // the largest workgroup (C = 128)
 
 template <int C>
 struct IntraShape {
     static constexpr int NT = C / 16;                  // 16-row tiles per chunk
+    // one wave per row tile: 8 waves at C = 128; at C = 64 four, and two workgroups share a CU
+    // (phases E, AA2 and INV have one row tile's work per wave either way)
+    static constexpr int IW = NT;
+    static constexpr int THREADS = 64 * IW;
+    static constexpr int DTW = (KD / 16) / IW;          // 16-column blocks of w and u per wave
     static constexpr int NPAIR = NT * (NT + 1) / 2;    // lower tiles incl. diagonal
     static constexpr int NOFF = NT * (NT - 1) / 2;     // strictly lower tiles
     static constexpr int HF = (NT + 1) / 2;            // tiles of a row pair done by the first wave
     static constexpr int SMAX = NT + 1 - HF;           // tiles per wave in phase AA2
+    // dummy stores on the item loop's entry paths (see vm_pad)
+    static constexpr int NPAD = DTW * (2 * (KD / 16) + 2 * NT);
     static constexpr int EP_LD = KD + 4;               // padded row stride (floats)
     static constexpr int COL_LD = KD + 8;              // padded row stride (bf16)
     static constexpr int TILE_LD = 20;                 // padded 16x16 tile row stride
@@ -200,10 +206,10 @@ __device__ __forceinline__ void e_load_kv(EIn& in, const uint16_t* k, const uint
 // A lane stores at distinct addresses 16 words apart (no store is merged or dropped, and all
 // offsets fit the instruction's immediate field); lanes of the workgroup overlap, all storing
 // zero; nothing reads the pad.
-constexpr int PAD_WORDS = 1024;  // per workgroup: ITHREADS + 16 * (N - 1) words for N <= 32
-template <int N>
+constexpr int PAD_WORDS = 1024;  // per workgroup: threads + 16 * (N - 1) words for N <= 32
+template <int N, int THREADS>
 __device__ __forceinline__ void vm_pad(uint32_t* p) {
-    static_assert(ITHREADS + 16 * (N - 1) <= PAD_WORDS, "pad area");
+    static_assert(THREADS + 16 * (N - 1) <= PAD_WORDS, "pad area");
     // the stores must follow the loads issued before: without this the compiler is free to
     // move them ahead (they touch no input), and then they pad nothing
     asm volatile("" ::: "memory");
@@ -303,7 +309,7 @@ __device__ __forceinline__ void intra_item(
         const ELoc nl = e_locate(map, H, next_item);
         e_load_g<C, PER_DIM>(ein, g, beta, nl, H, tid);
         e_load_kv<C>(ein, k, v, nl, H, Hk, tid);
-        vm_pad<2 * (KD / 16) + 2 * NT>(pad);
+        vm_pad<S::NPAD, S::THREADS>(pad);
         return;
     }
     const size_t ch = (size_t)slot * H + h;
@@ -520,7 +526,7 @@ __device__ __forceinline__ void intra_item(
             // strictly lower pairs p = R(R-1)/2 + J: F = exp(row pivot of R - column pivot of J) <= 1.
             // The column pivot of J is its row pivot, or with wide gates gamma at its last row, which
             // is the row pivot of J + 1 <= R
-            for (int e = 4 * tid; e < S::NOFF * KD; e += 4 * ITHREADS) {
+            for (int e = 4 * tid; e < S::NOFF * KD; e += 4 * S::THREADS) {
                 const int p = e / KD, d = e % KD;
                 const int R = (int)((1.f + __builtin_sqrtf(8.f * p + 1.f)) * 0.5f);  // R(R-1)/2 <= p < R(R+1)/2
                 const int J = p - R * (R - 1) / 2;
@@ -753,17 +759,17 @@ __device__ __forceinline__ void intra_item(
     lds_barrier();
 
     // ------------------------------------------------------------------ phase INV
-    const int dt = wave;  // 16-block of K (for w) and of V (for u) this wave produces in WU
+    // 16-blocks of K (for w) and of V (for u) this wave produces in WU: wave + IW di
     // high part of kg^T for phase PQ from scratch, the same number of fragments per wave; it
     // goes to LDS (R1) after the solve
     constexpr int NKG = 2 * (KD / 16) * NS;  // kg^T fragments in LDS (high, then low)
-    constexpr int KPW = NKG / 2 / IWAVES;    // high fragments per wave
-    static_assert(NKG % (2 * IWAVES) == 0, "kg^T fragments per wave");
+    constexpr int KPW = NKG / 2 / S::IW;     // high fragments per wave
+    static_assert(NKG % (2 * S::IW) == 0, "kg^T fragments per wave");
     static_assert(NKG * 1024 <= S::R1, "kg^T staging");
     u32x4v kgr[KPW];  // a vector type: a struct copy would go through private memory
 #pragma unroll
     for (int i = 0; i < KPW; ++i) {
-        const int f = wave + IWAVES * i;  // fragment (f / NS, f % NS)
+        const int f = wave + S::IW * i;  // fragment (f / NS, f % NS)
         kgr[i] = *cptr<u32x4v>(kgS, (frag32(f / NS, f % NS, C / 32) + lane * 8) * 2u);
     }
     // the gates and beta of the next item (phase E inputs), in flight from here on
@@ -866,13 +872,17 @@ __device__ __forceinline__ void intra_item(
     // the gates and beta of the next item (phase E inputs), in flight from here on
     e_load_g<C, PER_DIM>(ein, g, beta, nl, H, tid);
     // Blocked forward substitution for [w | u] = (I + A)^-1 diag(beta) [exp(gamma) k | v], wave
-    // dt producing columns 16 dt .. + 15 of each:  Z_R = T'_RR Y_R - sum_{J<R} M_RJ Z_J.  The Z
-    // tiles stay in registers, split, in the D layout (lane (r16, q4), element e: row
+    // producing columns 16 dt .. + 15 of each (dt = wave + IW di):
+    //     Z_R = T'_RR Y_R - sum_{J<R} M_RJ Z_J.
+    // The Z tiles stay in registers, split, in the D layout (lane (r16, q4), element e: row
     // 16 R + 4 q4 + e, column 16 dt + r16), which two at a time are the pi-order B operand of
     // the 16x16x32 instruction.
-    uint2 wzh[NT], wzl[NT], uzh[NT], uzl[NT];
+    uint2 wzh[S::DTW][NT], wzl[S::DTW][NT], uzh[S::DTW][NT], uzl[S::DTW][NT];
 #pragma unroll
-    for (int R = 0; R < NT; ++R) {
+    for (int R = 0; R < NT; ++R)
+#pragma unroll
+    for (int di = 0; di < S::DTW; ++di) {
+        const int dt = wave + S::IW * di;
         f32x4 aw = {0.f, 0.f, 0.f, 0.f}, au = aw;
         {   // T'_RR Y_R (Y = exp(gamma) k split, v exact in bf16): Y rows 32 (R / 2) + 8 q4 + i in
             // the normal-order fragment R / 2
@@ -906,12 +916,12 @@ __device__ __forceinline__ void intra_item(
             const uint2 ml1 = two ? *reinterpret_cast<const uint2*>(m0 + 768) : z2;
             const bf16x8 Mh = as_bf16x8(make_uint4(mh0.x, mh0.y, mh1.x, mh1.y));
             const bf16x8 Ml = as_bf16x8(make_uint4(ml0.x, ml0.y, ml1.x, ml1.y));
-            const uint2 wh1 = two ? wzh[2 * s + 1] : z2, wl1 = two ? wzl[2 * s + 1] : z2;
-            const uint2 uh1 = two ? uzh[2 * s + 1] : z2, ul1 = two ? uzl[2 * s + 1] : z2;
-            const bf16x8 Zwh = as_bf16x8(make_uint4(wzh[2 * s].x, wzh[2 * s].y, wh1.x, wh1.y));
-            const bf16x8 Zwl = as_bf16x8(make_uint4(wzl[2 * s].x, wzl[2 * s].y, wl1.x, wl1.y));
-            const bf16x8 Zuh = as_bf16x8(make_uint4(uzh[2 * s].x, uzh[2 * s].y, uh1.x, uh1.y));
-            const bf16x8 Zul = as_bf16x8(make_uint4(uzl[2 * s].x, uzl[2 * s].y, ul1.x, ul1.y));
+            const uint2 wh1 = two ? wzh[di][2 * s + 1] : z2, wl1 = two ? wzl[di][2 * s + 1] : z2;
+            const uint2 uh1 = two ? uzh[di][2 * s + 1] : z2, ul1 = two ? uzl[di][2 * s + 1] : z2;
+            const bf16x8 Zwh = as_bf16x8(make_uint4(wzh[di][2 * s].x, wzh[di][2 * s].y, wh1.x, wh1.y));
+            const bf16x8 Zwl = as_bf16x8(make_uint4(wzl[di][2 * s].x, wzl[di][2 * s].y, wl1.x, wl1.y));
+            const bf16x8 Zuh = as_bf16x8(make_uint4(uzh[di][2 * s].x, uzh[di][2 * s].y, uh1.x, uh1.y));
+            const bf16x8 Zul = as_bf16x8(make_uint4(uzl[di][2 * s].x, uzl[di][2 * s].y, ul1.x, ul1.y));
             aw = mfma32(Mh, Zwh, aw);
             aw = mfma32(Ml, Zwh, aw);
             aw = mfma32(Mh, Zwl, aw);
@@ -919,10 +929,10 @@ __device__ __forceinline__ void intra_item(
             au = mfma32(Ml, Zuh, au);
             au = mfma32(Mh, Zul, au);
         }
-        split2(aw[0], aw[1], wzh[R].x, wzl[R].x);
-        split2(aw[2], aw[3], wzh[R].y, wzl[R].y);
-        split2(au[0], au[1], uzh[R].x, uzl[R].x);
-        split2(au[2], au[3], uzh[R].y, uzl[R].y);
+        split2(aw[0], aw[1], wzh[di][R].x, wzl[di][R].x);
+        split2(aw[2], aw[3], wzh[di][R].y, wzl[di][R].y);
+        split2(au[0], au[1], uzh[di][R].x, uzl[di][R].x);
+        split2(au[2], au[3], uzh[di][R].y, uzl[di][R].y);
     }
 
     // ------------------------------------------------------------------ phase PQ
@@ -935,7 +945,7 @@ __device__ __forceinline__ void intra_item(
     uint16_t* kgL = reinterpret_cast<uint16_t*>(smem);
 #pragma unroll
     for (int i = 0; i < KPW; ++i)
-        *reinterpret_cast<u32x4v*>(kgL + (wave + IWAVES * i) * 512 + lane * 8) = kgr[i];
+        *reinterpret_cast<u32x4v*>(kgL + (wave + S::IW * i) * 512 + lane * 8) = kgr[i];
     if ((tid >> 6) < NT) {
         const int R = tid >> 6, d0 = 2 * (tid & 63);
 #pragma unroll
@@ -970,18 +980,23 @@ __device__ __forceinline__ void intra_item(
     }
     // w and u as pi-order operands: tiles 2s and 2s+1 give the 32 contracted rows of step s.
     // Both keep their split for P and B; Q and U take the high parts.
-    uint4 wh[NS], wl[NS], uh[NS], ul[NS];
+    uint4 wh[S::DTW][NS], wl[S::DTW][NS], uh[S::DTW][NS], ul[S::DTW][NS];
+#pragma unroll
+    for (int di = 0; di < S::DTW; ++di)
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
-        wh[s] = make_uint4(wzh[2 * s].x, wzh[2 * s].y, wzh[2 * s + 1].x, wzh[2 * s + 1].y);
-        wl[s] = make_uint4(wzl[2 * s].x, wzl[2 * s].y, wzl[2 * s + 1].x, wzl[2 * s + 1].y);
-        uh[s] = make_uint4(uzh[2 * s].x, uzh[2 * s].y, uzh[2 * s + 1].x, uzh[2 * s + 1].y);
-        ul[s] = make_uint4(uzl[2 * s].x, uzl[2 * s].y, uzl[2 * s + 1].x, uzl[2 * s + 1].y);
+        wh[di][s] = make_uint4(wzh[di][2 * s].x, wzh[di][2 * s].y, wzh[di][2 * s + 1].x, wzh[di][2 * s + 1].y);
+        wl[di][s] = make_uint4(wzl[di][2 * s].x, wzl[di][2 * s].y, wzl[di][2 * s + 1].x, wzl[di][2 * s + 1].y);
+        uh[di][s] = make_uint4(uzh[di][2 * s].x, uzh[di][2 * s].y, uzh[di][2 * s + 1].x, uzh[di][2 * s + 1].y);
+        ul[di][s] = make_uint4(uzl[di][2 * s].x, uzl[di][2 * s].y, uzl[di][2 * s + 1].x, uzl[di][2 * s + 1].y);
     }
     lds_barrier();  // staged kg^T, A2 and qg are in LDS
-    uint2 qgv[NT];    // (qg)^T tiles (I, dt)
+    uint2 qgv[S::DTW][NT];    // (qg)^T tiles (I, dt)
 #pragma unroll
-    for (int I = 0; I < NT; ++I) qgv[I] = *reinterpret_cast<const uint2*>(qgL + ((I * (KD / 16) + dt) * 64 + lane) * 4);
+    for (int di = 0; di < S::DTW; ++di)
+#pragma unroll
+    for (int I = 0; I < NT; ++I)
+        qgv[di][I] = *reinterpret_cast<const uint2*>(qgL + ((I * (KD / 16) + wave + S::IW * di) * 64 + lane) * 4);
     // P^T tile (rows d in block dt, columns k in block x) = w^T kg; B tile (rows k in x,
     // columns v in dt) = kg^T u.  -P goes out in pi order as the A operand of -P S.
     // Outputs of the item through uniform bases and 32-bit byte offsets.
@@ -990,7 +1005,10 @@ __device__ __forceinline__ void intra_item(
     uint16_t* QpI = ws.Qp + ch * C * KD;
     uint16_t* UpI = ws.Up + ch * C * VD;
 #pragma unroll
-    for (int x = 0; x < KD / 16; ++x) {
+    for (int x = 0; x < KD / 16; ++x)
+#pragma unroll
+    for (int di = 0; di < S::DTW; ++di) {
+        const int dt = wave + S::IW * di;
         // P and B from split operands (three MFMAs each): the state goes through P in every
         // chunk, so a single bf16 rounding of w or kg grows into its error where it persists
         f32x4 pt = {0.f, 0.f, 0.f, 0.f}, p1 = pt, b0 = pt, b1 = pt;
@@ -998,12 +1016,12 @@ __device__ __forceinline__ void intra_item(
         for (int s = 0; s < NS; ++s) {
             const bf16x8 kh = as_bf16x8(*reinterpret_cast<const uint4*>(kgL + (x * NS + s) * 512 + lane * 8));
             const bf16x8 kl = as_bf16x8(*reinterpret_cast<const uint4*>(kgL + (NKG / 2 + x * NS + s) * 512 + lane * 8));
-            pt = mfma32(as_bf16x8(wh[s]), kh, pt);
-            p1 = mfma32(as_bf16x8(wl[s]), kh, p1);
-            p1 = mfma32(as_bf16x8(wh[s]), kl, p1);
-            b0 = mfma32(kh, as_bf16x8(uh[s]), b0);
-            b1 = mfma32(kl, as_bf16x8(uh[s]), b1);
-            b1 = mfma32(kh, as_bf16x8(ul[s]), b1);
+            pt = mfma32(as_bf16x8(wh[di][s]), kh, pt);
+            p1 = mfma32(as_bf16x8(wl[di][s]), kh, p1);
+            p1 = mfma32(as_bf16x8(wh[di][s]), kl, p1);
+            b0 = mfma32(kh, as_bf16x8(uh[di][s]), b0);
+            b1 = mfma32(kl, as_bf16x8(uh[di][s]), b1);
+            b1 = mfma32(kh, as_bf16x8(ul[di][s]), b1);
         }
         f32x4 bt;
 #pragma unroll
@@ -1023,8 +1041,11 @@ __device__ __forceinline__ void intra_item(
     // Q^T tile (rows d in dt, columns i in I) = (qg)^T - w^T A2^T; U^T tile (rows v in dt,
     // columns i in I) = u^T A2^T.  A2 fragment (I, s) is the B operand of both.
 #pragma unroll
-    for (int I = 0; I < NT; ++I) {
-        const uint2 qv = qgv[I];
+    for (int I = 0; I < NT; ++I)
+#pragma unroll
+    for (int di = 0; di < S::DTW; ++di) {
+        const int dt = wave + S::IW * di;
+        const uint2 qv = qgv[di][I];
         f32x4 qt = {__uint_as_float(qv.x << 16), __uint_as_float(qv.x & 0xffff0000u), __uint_as_float(qv.y << 16),
                     __uint_as_float(qv.y & 0xffff0000u)};
         f32x4 ut = {0.f, 0.f, 0.f, 0.f};
@@ -1032,8 +1053,8 @@ __device__ __forceinline__ void intra_item(
         for (int s = 0; s < NS; ++s) {
             if (2 * s > I) break;
             const bf16x8 a2 = as_bf16x8(*reinterpret_cast<const uint4*>(a2L + a2_slot(I, s) * 512 + lane * 8));
-            qt = mfma32(as_bf16x8(neg_bf16x8(wh[s])), a2, qt);
-            ut = mfma32(as_bf16x8(uh[s]), a2, ut);
+            qt = mfma32(as_bf16x8(neg_bf16x8(wh[di][s])), a2, qt);
+            ut = mfma32(as_bf16x8(uh[di][s]), a2, ut);
         }
         // Q and U are read only by the output kernel, after the chain: streamed past the caches,
         // so that they do not displace -P and B, which the chain reads next
@@ -1046,7 +1067,7 @@ __device__ __forceinline__ void intra_item(
 // Persistent: workgroup b takes items b, b + gridDim.x, ... (item = slot * H + head) and
 // keeps its scratch in slot b, so the scratch of all workgroups stays cache-resident.
 template <int C, bool PER_DIM, bool L2N>
-__global__ __launch_bounds__(ITHREADS) void intra_kernel(
+__global__ __launch_bounds__(IntraShape<C>::THREADS) __attribute__((amdgpu_waves_per_eu(2, 2))) void intra_kernel(
     const uint16_t* q, const uint16_t* k, const uint16_t* v,
     const float* g, const float* beta, ChunkMap map, int H, int Hk,
     float scale, Work ws, int nitems, uint32_t* pad_all) {
@@ -1058,7 +1079,7 @@ __global__ __launch_bounds__(ITHREADS) void intra_kernel(
         e_load_g<C, PER_DIM>(ein, g, beta, l0, H, threadIdx.x);
         e_load_kv<C>(ein, k, v, l0, H, Hk, threadIdx.x);
     }
-    vm_pad<2 * (KD / 16) + 2 * (C / 16)>(pad);
+    vm_pad<IntraShape<C>::NPAD, IntraShape<C>::THREADS>(pad);
     for (int item = blockIdx.x; item < nitems; item += gridDim.x) {
         // the previous item is done with LDS.  An LDS-only barrier: __syncthreads() would also
         // wait for every load and store in flight (this item's inputs, prefetched during the
@@ -1083,7 +1104,8 @@ static int resident_groups() {
     }
     int ncu = 0, per_cu = 0;
     if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, intra_kernel<C, PER_DIM, L2N>, ITHREADS, 0) != hipSuccess)
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, intra_kernel<C, PER_DIM, L2N>, IntraShape<C>::THREADS, 0) !=
+            hipSuccess)
         return 1;
     const int r = max(1, ncu * per_cu);
     if (dev >= 0 && dev < 64) cache[dev].store(r, std::memory_order_relaxed);
@@ -1098,7 +1120,8 @@ static hipError_t launch_intra_t(const uint16_t* q, const uint16_t* k, const uin
     const int grid = min(min(nitems, nscratch), resident_groups<C, PER_DIM, L2N>());
     // the pad areas of the scratch slots, after the kg^T planes
     uint32_t* pad = reinterpret_cast<uint32_t*>(ws.kgT + (size_t)nscratch * KD * C);
-    hipLaunchKernelGGL((intra_kernel<C, PER_DIM, L2N>), dim3(grid), dim3(ITHREADS), 0, stream, q, k, v, g, beta, map,
+    hipLaunchKernelGGL((intra_kernel<C, PER_DIM, L2N>), dim3(grid), dim3(IntraShape<C>::THREADS), 0, stream, q, k, v, g,
+                       beta, map,
                        H, Hk, scale, ws, nitems, pad);
     return hipGetLastError();
 }
