@@ -628,6 +628,8 @@ __device__ __forceinline__ void intra_item(
                     if (p >= phi || (p <= cp) != (o == 0)) continue;
                     const int J = (o == 0) ? p : p - cp - 1;
                     const int j = 16 * J + r16;
+                    const bf16x8 bhi = as_bf16x8(*reinterpret_cast<const uint4*>(colh + j * S::COL_LD + dd));
+                    const bf16x8 blo = as_bf16x8(*reinterpret_cast<const uint4*>(coll + j * S::COL_LD + dd));
                     uint4 ah, al, aq;
                     if (J < R) {
                         const float4* fp = reinterpret_cast<const float4*>(F + (R * (R - 1) / 2 + J) * KD + dd);
@@ -668,8 +670,6 @@ __device__ __forceinline__ void intra_item(
                         aq.w = pack_bf2(qE[6], qE[7]);
                     }
                     const bf16x8 ahi = as_bf16x8(ah), alo = as_bf16x8(al), aqv = as_bf16x8(aq);
-                    const bf16x8 bhi = as_bf16x8(*reinterpret_cast<const uint4*>(colh + j * S::COL_LD + dd));
-                    const bf16x8 blo = as_bf16x8(*reinterpret_cast<const uint4*>(coll + j * S::COL_LD + dd));
                     acc1[s] = mfma32(ahi, bhi, acc1[s]);
                     acc1[s] = mfma32(alo, bhi, acc1[s]);
                     acc1[s] = mfma32(ahi, blo, acc1[s]);
