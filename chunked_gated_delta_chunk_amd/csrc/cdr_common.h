@@ -132,6 +132,12 @@ __device__ __forceinline__ uint2 bload8(rsrc_t r, uint32_t off) {
     return make_uint2(v.x, v.y);
 }
 
+// c + a.lo * b.lo + a.hi * b.hi for two packed bf16 pairs, accumulated in fp32
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+    typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
 // wait for this wave's own LDS traffic; keeps the compiler from reordering across it
 __device__ __forceinline__ void wave_lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 

@@ -553,17 +553,21 @@ __device__ __forceinline__ void intra_item(
     if constexpr (L2N) {
 #pragma unroll
         for (int o = 0; o < 2; ++o) {
+            // sums of squares straight from the packed bf16 pairs (two products per
+            // instruction): unpacking them here would let the compiler keep the unpacked
+            // values alive into the tile loop below, which needs them only scaled
             float sk = 0.f, sq = 0.f;
 #pragma unroll
             for (int ks = 0; ks < KD / 32; ++ks) {
-                float kf[8], qf[8];
-                unpack8(kfr[o][ks], kf);
-                unpack8(qfr[o][ks], qf);
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    sk += kf[e] * kf[e];
-                    sq += qf[e] * qf[e];
-                }
+                const uint4 kv = kfr[o][ks], qv = qfr[o][ks];
+                sk = dot2_bf16(kv.x, kv.x, sk);
+                sk = dot2_bf16(kv.y, kv.y, sk);
+                sk = dot2_bf16(kv.z, kv.z, sk);
+                sk = dot2_bf16(kv.w, kv.w, sk);
+                sq = dot2_bf16(qv.x, qv.x, sq);
+                sq = dot2_bf16(qv.y, qv.y, sq);
+                sq = dot2_bf16(qv.z, qv.z, sq);
+                sq = dot2_bf16(qv.w, qv.w, sq);
             }
             sk += __shfl_xor(sk, 16, 64);
             sk += __shfl_xor(sk, 32, 64);
