@@ -192,7 +192,13 @@ __global__ __launch_bounds__(OTHREADS) void output_kernel(ChunkMap map, int nslo
     for (int f = wave; f < NSF; f += OWAVES) frag_to_lds(ws.Sc + ch * VD * KD + f * 512, sS + f * 512, lane);
     uint4 qf[KS];
 #pragma unroll
-    for (int s = 0; s < KS; ++s) qf[s] = *reinterpret_cast<const uint4*>(ws.Qp + ch * C * KD + frag(it, s, KS) + lane * 8);
+    for (int s = 0; s < KS; ++s) {
+        // a Q fragment is stored half-major: the pi-order operand's two 8-byte halves of a lane
+        // are 512 bytes apart
+        const uint16_t* fq = ws.Qp + ch * C * KD + frag(it, s, KS);
+        const uint2 a = *reinterpret_cast<const uint2*>(fq + lane * 4), b = *reinterpret_cast<const uint2*>(fq + 256 + lane * 4);
+        qf[s] = make_uint4(a.x, a.y, b.x, b.y);
+    }
     f32x4 acc[VTW];
 #pragma unroll
     for (int t = 0; t < VTW; ++t) {

@@ -1061,8 +1061,11 @@ __device__ __forceinline__ void intra_item(
             ut = mfma32(as_bf16x8(uh[di][s]), a2, ut);
         }
         // Q and U are read only by the output kernel, after the chain: streamed past the caches,
-        // so that they do not displace -P and B, which the chain reads next
-        st_nt(mptr<uint2>(QpI, (frag32(I, dt >> 1, KD / 32) + fragP(dt & 1, r16, q4)) * 2u),
+        // so that they do not displace -P and B, which the chain reads next.  A Q^T fragment is
+        // stored half-major (the 16-row half of tile dt is one contiguous 512-byte block), so each
+        // of these stores writes whole cache lines; in pi order two waves would each write half
+        // of every line, and lines that bypass the caches are not merged
+        st_nt(mptr<uint2>(QpI, (frag32(I, dt >> 1, KD / 32) + (dt & 1) * 256u + lane * 4u) * 2u),
               make_uint2(pack_bf2(qt[0], qt[1]), pack_bf2(qt[2], qt[3])));
         st_nt(mptr<uint2>(UpI, ((I * (VD / 16) + dt) * 64 + lane) * 8u), make_uint2(pack_bf2(ut[0], ut[1]), pack_bf2(ut[2], ut[3])));
     }
