@@ -164,12 +164,14 @@ __global__ __launch_bounds__(CTHREADS) void chain_kernel(ChunkMap map, int H, co
 // straight from memory and U^T initialises the accumulators.  The parts of one (chunk, head)
 // are 8 workgroups apart in launch order, so they run on the same XCD and the second finds
 // the staged state in that XCD's L2.  More, smaller workgroups than the CUs hold at once, so
-// that some load while others store.
+// that some load while others store; built for five waves per SIMD (96 VGPRs, no spills:
+// five workgroups per CU, the most their 32 KiB of LDS allows), one more than the
+// compiler picks by itself.
 constexpr int OWAVES = 4;
 constexpr int OTHREADS = 64 * OWAVES;
 
 template <int C>
-__global__ __launch_bounds__(OTHREADS) void output_kernel(ChunkMap map, int nslots, int H, uint16_t* __restrict__ o,
+__global__ __launch_bounds__(OTHREADS) __attribute__((amdgpu_waves_per_eu(5, 5))) void output_kernel(ChunkMap map, int nslots, int H, uint16_t* __restrict__ o,
                                                            Work ws) {
     constexpr int NT = C / 16;                     // row tiles of the chunk
     constexpr int NPART = NT / OWAVES;             // workgroups per (chunk, head)
