@@ -7,4 +7,4 @@ from .ops import (chunk_dr_fwd, PreparedForward, load_library, workspace_bytes, 
                   STAGE_INTRA, STAGE_CHAIN, STAGE_OUTPUT, STAGE_ALL, fused_recurrent_fwd, PreparedRecurrent,
                   chunk_dr_bwd, PreparedBackward, bwd_workspace_bytes,
                   BWD_PREP, BWD_CHAINS, BWD_LOCAL, BWD_ALL, segment_map, merge_states,
-                  chunk_dr_fwd_noalloc, NOALLOC_SCRATCH_BYTES)
+                  chunk_dr_fwd_noalloc, NOALLOC_SCRATCH_BYTES, check_cu_seqlens)

@@ -190,6 +190,42 @@ cdr_status chunk_dr_fwd(const cdr_problem* p, const void* q, const void* k, cons
                                workspace_bytes, CDR_STAGE_ALL, stream);
 }
 
+namespace {
+
+constexpr int kCuCheckThreads = 256;
+
+// One workgroup: every offset is checked against its rules, the smallest failing index + 1 is
+// reduced in LDS, and thread 0 writes it (0 when none fails).  The result is written on every
+// call, so nothing needs clearing beforehand.
+__global__ __launch_bounds__(kCuCheckThreads) void cu_check_kernel(const int32_t* __restrict__ cu, int32_t N, int32_t T,
+                                                                   int32_t* __restrict__ result) {
+    __shared__ int32_t first;
+    if (threadIdx.x == 0) first = N + 2;
+    __syncthreads();
+    int32_t mine = N + 2;
+    for (int32_t i = (int32_t)threadIdx.x; i <= N; i += kCuCheckThreads) {
+        const int32_t c = cu[i];
+        const bool bad = (c < 0) || (c > T) || (i == 0 && c != 0) || (i > 0 && c < cu[i - 1]) || (i == N && c != T);
+        if (bad) {
+            mine = i + 1;
+            break;  // i grows, so this is the thread's first failure
+        }
+    }
+    if (mine <= N + 1) atomicMin(&first, mine);
+    __syncthreads();
+    if (threadIdx.x == 0) *result = first <= N + 1 ? first : 0;
+}
+
+}  // namespace
+
+cdr_status cdr_check_cu_seqlens(const int32_t* cu_seqlens, int32_t N, int32_t T, int32_t* result, void* stream) {
+    if (!cu_seqlens || !result) return CDR_ERR_NULL_ARG;
+    if (N < 1 || T < 0) return CDR_ERR_BAD_SHAPE;
+    hipLaunchKernelGGL(cu_check_kernel, dim3(1), dim3(kCuCheckThreads), 0, static_cast<hipStream_t>(stream),
+                       cu_seqlens, N, T, result);
+    return hipGetLastError() == hipSuccess ? CDR_OK : CDR_ERR_HIP;
+}
+
 cdr_status chunk_dr_segment_map(const cdr_problem* p, const void* q, const void* k, const void* v, const float* g,
                                 const float* beta, const int32_t* cu_seqlens, float* M, float* X, void* workspace,
                                 size_t workspace_bytes, void* stream) {

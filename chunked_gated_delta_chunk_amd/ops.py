@@ -24,7 +24,8 @@ EXPORTED = ("cdr_check", "cdr_workspace_bytes", "chunk_dr_fwd", "chunk_dr_fwd_st
             "chunk_dr_fwd_noalloc",
             "cdr_bwd_workspace_bytes", "chunk_dr_bwd", "chunk_dr_bwd_stages",
             "chunk_dr_segment_map", "chunk_dr_merge_states",
-            "cdr_recurrent_check", "chunk_dr_recurrent_fwd", "cdr_status_str", "cdr_version")
+            "cdr_recurrent_check", "chunk_dr_recurrent_fwd", "cdr_check_cu_seqlens", "cdr_status_str",
+            "cdr_version")
 STATE_SEPARATE, STATE_POOL, STATE_POOL_SPEC = 0, 1, 2
 STAGE_INTRA, STAGE_CHAIN, STAGE_OUTPUT, STAGE_ALL = 1, 2, 4, 7
 NOALLOC_SCRATCH_BYTES = 256 * 1024 * 1024   # CDR_NOALLOC_SCRATCH_BYTES of chunk_dr.h
@@ -90,6 +91,8 @@ def load_library(path: str = LIB_PATH):
     lib.cdr_recurrent_check.restype = ctypes.c_int
     lib.chunk_dr_recurrent_fwd.argtypes = [R] + [vp] * 13
     lib.chunk_dr_recurrent_fwd.restype = ctypes.c_int
+    lib.cdr_check_cu_seqlens.argtypes = [vp, ctypes.c_int32, ctypes.c_int32, vp, vp]
+    lib.cdr_check_cu_seqlens.restype = ctypes.c_int
     lib.cdr_status_str.argtypes = [ctypes.c_int]
     lib.cdr_status_str.restype = ctypes.c_char_p
     lib.cdr_version.argtypes = []
@@ -363,6 +366,27 @@ def merge_states(M, X, initial_state=None):
     if st != CDR_OK:
         _raise(st, "chunk_dr_merge_states")
     return s_in
+
+
+def check_cu_seqlens(cu_seqlens, T) -> int:
+    """Checks the contents of ``cu_seqlens`` (int32 ``[N+1]`` on a GPU) on the device, which the
+    forward does not: 0 when the offsets start at 0, never decrease and end at ``T``, else
+    ``i + 1`` for the first offending index ``i``.  Waits for the current stream (a debugging
+    aid, not for the hot path)."""
+    lib = load_library()
+    _need(cu_seqlens, "cu_seqlens", torch.int32)
+    if cu_seqlens.dim() != 1 or cu_seqlens.numel() < 2:
+        raise ValueError("cu_seqlens must be a 1-D tensor of N + 1 >= 2 offsets")
+    device = cu_seqlens.device
+    cu = _aligned(cu_seqlens)
+    result = torch.empty(4, dtype=torch.int32, device=device)   # 16 bytes: the first is the result
+    stream = torch.cuda.current_stream(device)
+    st = lib.cdr_check_cu_seqlens(_dev_ptr(cu, device), cu.numel() - 1, int(T), _dev_ptr(result, device),
+                                  stream.cuda_stream)
+    if st != CDR_OK:
+        _raise(st, "cdr_check_cu_seqlens")
+    stream.synchronize()
+    return int(result[0].item())
 
 
 def bwd_workspace_bytes(p: cdr_problem) -> int:

@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define CDR_VERSION 7
+#define CDR_VERSION 8
 
 typedef enum {
     CDR_OK = 0,
@@ -142,6 +142,27 @@ cdr_status chunk_dr_fwd(const cdr_problem* p,
                         const float* initial_state, const int32_t* cu_seqlens,
                         void* o, float* final_state,
                         void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Device-side check of the contents of cu_seqlens, which chunk_dr_fwd does not read on the
+ * host and does not validate.  The rules are the varlen input checks of the chunk_kda page's
+ * host wrapper (section 主机侧 wrapper 与输入校验) and of the G_T_CONTIG page's varlen checklist
+ * (section 3): the offsets start at 0, never decrease, and end at the total token count.
+ *
+ *   cu_seqlens  int32 [N + 1] device array
+ *   N           sequences, >= 1
+ *   T           total packed tokens, >= 0 (the problem's T)
+ *   result      device int32, written by the check: 0 when every rule holds, else i + 1 for
+ *               the first index i in 0..N where one fails (cu[0] != 0; cu[i] < cu[i - 1];
+ *               cu[i] outside 0..T; cu[N] != T)
+ *   stream      hipStream_t to launch on (NULL = the default stream)
+ *
+ * Queues one small kernel and returns without waiting; read *result after the stream has
+ * finished it.  The kernel writes *result on every call, so no clearing is needed and the call
+ * can be captured in a graph.  Returns CDR_ERR_NULL_ARG for a NULL array or result,
+ * CDR_ERR_BAD_SHAPE for N < 1 or T < 0, CDR_ERR_HIP if the launch failed, else CDR_OK.
+ */
+cdr_status cdr_check_cu_seqlens(const int32_t* cu_seqlens, int32_t N, int32_t T, int32_t* result, void* stream);
 
 /*
  * The same forward, split into its three kernel stages so that each can be timed or

@@ -217,3 +217,18 @@ def test_noalloc_rejects_a_problem_beyond_its_array_without_touching_device():
     # the workload the limit is stated for fits
     q = cdr.make_problem(1, 8192, 16, 128, 128, 1, True, 128, 128 ** -0.5, True, True, False)
     assert cdr.workspace_bytes(q) <= cdr.NOALLOC_SCRATCH_BYTES
+
+
+def test_cu_seqlens_check_rejects_bad_arguments_without_touching_device():
+    """cdr_check_cu_seqlens validates its arguments on the host before launching anything."""
+    lib = cdr.load_library()
+    buf = (ctypes.c_int32 * 4)()   # host memory: never handed to a kernel by these calls
+    res = (ctypes.c_int32 * 1)()
+    assert lib.cdr_check_cu_seqlens(None, 1, 10, ctypes.addressof(res), None) == 1    # NULL array
+    assert lib.cdr_check_cu_seqlens(ctypes.addressof(buf), 1, 10, None, None) == 1    # NULL result
+    assert lib.cdr_check_cu_seqlens(ctypes.addressof(buf), 0, 10, ctypes.addressof(res), None) == 2
+    assert lib.cdr_check_cu_seqlens(ctypes.addressof(buf), 2, -1, ctypes.addressof(res), None) == 2
+    with pytest.raises(TypeError):
+        cdr.check_cu_seqlens(torch.tensor([0, 4], dtype=torch.int64), 4)
+    with pytest.raises(ValueError):
+        cdr.check_cu_seqlens(torch.tensor([0], dtype=torch.int32), 0)
