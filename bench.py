@@ -338,6 +338,7 @@ def cpu_baseline(inp, w, budget_s):
 EV_STRIDE = 10        # timed steps per step with per-kernel events
 CLOCK_WARMUP_S = 0.3  # untimed forward calls before the warmup steps (clock ramp)
 COLD_STEPS = 20       # event-timed single forwards, flushed and warm
+GRAPH_REPLAYS = 200   # replays of one captured forward (same input set)
 
 
 def main():
@@ -473,6 +474,29 @@ def main():
     warm = event_steps(COLD_STEPS, False)
     del flush
 
+    # the same forward replayed from a captured graph (one launch per replay instead of three or
+    # four): what launch overhead costs the small configurations; `value` stays the plain call
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        calls[0]()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph):
+        calls[0]()
+    for _ in range(COLD_STEPS):
+        graph.replay()
+    torch.cuda.synchronize()
+    ga, gb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ga.record()
+    for _ in range(GRAPH_REPLAYS):
+        graph.replay()
+    gb.record()
+    torch.cuda.synchronize()
+    graph_ms = ga.elapsed_time(gb) / GRAPH_REPLAYS
+    del graph
+
     lengths = list(w.lengths) if w.lengths is not None else [w.T] * w.B
     flops, bytes_ = kernel_work(w, lengths)
     f_nom = nominal_flops(w, lengths)
@@ -509,6 +533,8 @@ def main():
                   "f_nom_gflop": round(f_nom / 1e9, 3), "f_min_gflop": round(f_min / 1e9, 3),
                   "compulsory_mb": round(comp / 1e6, 2),
                   "cold_flushed": cold, "warm_same_inputs": warm,
+                  "graph_replay": {"ms_per_forward": round(graph_ms, 5), "replays": GRAPH_REPLAYS,
+                                   "input_sets": 1},
                   "clock_warmup_s": CLOCK_WARMUP_S}
 
     # parity spot check of the timed buffers against the oracle on one head, so the

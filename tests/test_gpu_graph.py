@@ -1,0 +1,62 @@
+"""The forward captured in a HIP graph (torch.cuda.CUDAGraph) and replayed: every replay, with
+new input contents copied into the captured buffers and eager GPU work in between, must give
+the bits of an eager call on the same inputs.  Covers both the workspace entry point and the
+no-allocation one (whose static workspace is what a capturing caller uses)."""
+import pytest
+import torch
+
+import chunked_gated_delta_chunk_amd as cdr
+from chunked_gated_delta_chunk_amd.synth import make_inputs
+
+pytestmark = pytest.mark.gpu
+
+# label, make_inputs keywords (shapes fixed across replays)
+CASES = [
+    ("kda_C128_tail", dict(B=1, T=600, H=2, chunk_size=128, initial_state=True)),
+    ("kda_C64_varlen", dict(B=1, T=483, H=2, chunk_size=64, lengths=(150, 0, 333), initial_state=True)),
+    ("gdn_C64_grouped", dict(B=2, T=200, H=1, HV=2, chunk_size=64, per_dim_gate=False)),
+]
+
+
+def _draw(kw, seed):
+    return make_inputs(seed=seed, **kw).to("cuda:0")
+
+
+def _eager(inp):
+    call = cdr.PreparedForward(inp.q, inp.k, inp.v, inp.g, inp.beta, initial_state=inp.initial_state,
+                               cu_seqlens=inp.cu_seqlens, chunk_size=inp.chunk_size, output_final_state=True)
+    o, S = call()
+    torch.cuda.synchronize()
+    return o.clone(), S.clone()
+
+
+@pytest.mark.parametrize("noalloc", [False, True], ids=["workspace", "noalloc"])
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_graph_replays_match_eager_calls(case, noalloc):
+    label, kw = case
+    print(f"[graph] {label} noalloc={noalloc}", flush=True)
+    st = _draw(kw, seed=700)   # the captured buffers
+    call = cdr.PreparedForward(st.q, st.k, st.v, st.g, st.beta, initial_state=st.initial_state,
+                               cu_seqlens=st.cu_seqlens, chunk_size=st.chunk_size, output_final_state=True,
+                               noalloc=noalloc)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):   # warm-up off the capture, as torch recommends
+        call()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call()
+    for r in range(3):
+        new = _draw(kw, seed=701 + r)
+        for dst, src in ((st.q, new.q), (st.k, new.k), (st.v, new.v), (st.g, new.g), (st.beta, new.beta),
+                         (st.initial_state, new.initial_state)):
+            if dst is not None:
+                dst.copy_(src)
+        graph.replay()
+        torch.cuda.synchronize()
+        o_ref, S_ref = _eager(new)
+        assert torch.equal(call.o, o_ref), f"replay {r}: o differs"
+        assert torch.equal(call.S, S_ref), f"replay {r}: final state differs"
+        torch.randn(4096, device="cuda:0").abs().sum().item()   # eager work between replays
