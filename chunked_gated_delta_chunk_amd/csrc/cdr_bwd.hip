@@ -223,9 +223,12 @@ __device__ __forceinline__ void split8(const float* x, bf16x8& h, bf16x8& l) {
 
 // ------------------------------------------------------------------------------------
 // Pivoted pair products.  e^(gamma_i - gamma_j) (j <= i, per key dimension) is written as
-// e^(gamma_i - p) e^(p - gamma_j) with p the gamma of the middle row of one 16-row tile, so
-// that both factors stay finite for gates within the forward's range (no more than 88 of
-// log decay inside a tile; gates <= 0 across tiles).  Staged operands are hi/lo bf16 in LDS.
+// e^(gamma_i - p) e^(p - gamma_j).  For g <= 0, gamma never increases along the chunk, so with
+// i in row tile I, j in an earlier tile J < I and p the gamma of the first row of tile I (or
+// of the last row of tile J), both factors are <= 1 for every gate: nothing overflows, and a
+// factor that underflows belongs to a pair whose decay underflows too.  Pairs inside one
+// 16-row tile have no such pivot; they are summed exactly, one exponential per pair and key
+// dimension.  Staged operands are hi/lo bf16 in LDS.
 
 // B panel [rows][d] (d contiguous) of X[j][d] * e^(sgn (p[d] - gamma[j][d])) for j < jhi
 // and j >= jlo (zero elsewhere), rows 0..nrows-1
@@ -394,9 +397,42 @@ __global__ __launch_bounds__(BTHREADS) __attribute__((amdgpu_waves_per_eu(4))) v
         const float* QFp = mat(w, ch, QF);
         float* AHp = mat(w, ch, AH);
         float* A2p = mat(w, ch, A2M);
-        for (int I = 0; I < NT; ++I) {
+        // the diagonal tiles exactly, one per wave, all at once: lane (r, q) of wave I sums rows
+        // i = 16 I + 4 q + e against row j = 16 I + r; exp(-|gamma_i - gamma_j|) is the decay of the
+        // later row over the earlier one (pairs with j > i are masked when stored)
+        if (wave < NT) {
+            const int I = wave, j = 16 * I + (lane & 15);
+            f32x4 ak = {0.f, 0.f, 0.f, 0.f}, aq = {0.f, 0.f, 0.f, 0.f};
+            for (int d = 0; d < KD; d += 4) {
+                const float4 kj = *reinterpret_cast<const float4*>(KFp + j * 128 + d);
+                const float4 gj = *reinterpret_cast<const float4*>(gam + j * 128 + d);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int i = 16 * I + 4 * (lane >> 4) + e;
+                    const float4 ki = *reinterpret_cast<const float4*>(KFp + i * 128 + d);
+                    const float4 qi = *reinterpret_cast<const float4*>(QFp + i * 128 + d);
+                    const float4 gi = *reinterpret_cast<const float4*>(gam + i * 128 + d);
+                    const float f0 = kj.x * ex(-fabsf(gi.x - gj.x)), f1 = kj.y * ex(-fabsf(gi.y - gj.y));
+                    const float f2 = kj.z * ex(-fabsf(gi.z - gj.z)), f3 = kj.w * ex(-fabsf(gi.w - gj.w));
+                    ak[e] += ki.x * f0 + ki.y * f1 + ki.z * f2 + ki.w * f3;
+                    aq[e] += qi.x * f0 + qi.y * f1 + qi.z * f2 + qi.w * f3;
+                }
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int i = 16 * I + 4 * (lane >> 4) + e;
+                AHp[i * 128 + j] = (j < i) ? ak[e] : 0.f;
+                A2p[i * 128 + j] = (j <= i) ? scale * aq[e] : 0.f;
+                // the tiles right of the diagonal are zero (both matrices are read whole)
+                for (int J2 = I + 1; J2 < NT; ++J2) {
+                    AHp[i * 128 + 16 * J2 + (lane & 15)] = 0.f;
+                    A2p[i * 128 + 16 * J2 + (lane & 15)] = 0.f;
+                }
+            }
+        }
+        for (int I = 1; I < NT; ++I) {
             __syncthreads();
-            if (tid < 128) piv[tid] = gam[(16 * I + 8) * 128 + tid];
+            if (tid < 128) piv[tid] = gam[(16 * I) * 128 + tid];   // the tile's first row
             __syncthreads();
 #pragma unroll 4
             for (int e = tid; e < 16 * 128; e += BTHREADS) {
@@ -414,7 +450,7 @@ __global__ __launch_bounds__(BTHREADS) __attribute__((amdgpu_waves_per_eu(4))) v
             const int J = wave;
             if (J < NT) {
                 f32x4 ak = {0.f, 0.f, 0.f, 0.f}, aq = {0.f, 0.f, 0.f, 0.f};
-                if (J <= I) {
+                if (J < I) {
                     const int j = 16 * J + (lane & 15);
                     for (int s2 = 0; s2 < KD / 32; s2 += 2) {
                         float4 kx[2][2], gx[2][2];
@@ -446,11 +482,13 @@ __global__ __launch_bounds__(BTHREADS) __attribute__((amdgpu_waves_per_eu(4))) v
                         }
                     }
                 }
+                if (J < I) {
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int i = 16 * I + 4 * (lane >> 4) + e, j = 16 * J + (lane & 15);
-                    AHp[i * 128 + j] = (j < i) ? ak[e] : 0.f;
-                    A2p[i * 128 + j] = (j <= i) ? scale * aq[e] : 0.f;
+                    for (int e = 0; e < 4; ++e) {
+                        const int i = 16 * I + 4 * (lane >> 4) + e, j = 16 * J + (lane & 15);
+                        AHp[i * 128 + j] = ak[e];
+                        A2p[i * 128 + j] = scale * aq[e];
+                    }
                 }
             }
         }
@@ -788,16 +826,19 @@ __global__ __launch_bounds__(BTHREADS) __attribute__((amdgpu_waves_per_eu(4))) v
             *reinterpret_cast<uint2*>(lo + r * PC + c4) = make_uint2(l0, l1);
         }
     };
-    // R_i = sum_j G_ij k_j e^(gamma_i - gamma_j), R2_i = sum_j dA2_ij k_j e^(...), j <= i
+    // R_i = sum_j G_ij k_j e^(gamma_i - gamma_j), R2_i = sum_j dA2_ij k_j e^(...), j < i.  The j = i
+    // term of R2 (dA2_ii k_i, no decay) is added to dq in the assembly; left out of R2 it cannot
+    // cancel against C2's in dgamma, where it has no part (e^0 does not depend on gamma).
     for (int which = 0; which < 2; ++which) {
         const float* Mx = mat(w, ch, which ? DA2 : GG);
         float* Out = mat(w, ch, which ? R2 : RR);
         for (int I = 0; I < NT; ++I) {
             __syncthreads();
-            if (tid < 128) piv[tid] = gam[(16 * I + 8) * 128 + tid];
+            if (tid < 128) piv[tid] = gam[(16 * I) * 128 + tid];   // the tile's first row
             __syncthreads();
-            const int nr = 16 * (I + 1), nrp = (nr + 31) & ~31;
-            stage_piv_colmajor<PC>(KFp, gam, piv, 1, 0, nr, nrp, bh, bl, tid);
+            // rows j of earlier tiles (j < 16 I) through the pivot; the tile's own rows below
+            const int nrp = (16 * I + 31) & ~31;
+            stage_piv_colmajor<PC>(KFp, gam, piv, 1, 0, 16 * I, nrp, bh, bl, tid);
             stage_rows(Mx, 16 * I, nrp, m1h, m1l);
             __syncthreads();
             const int Dt = wave;
@@ -809,24 +850,49 @@ __global__ __launch_bounds__(BTHREADS) __attribute__((amdgpu_waves_per_eu(4))) v
                 acc = mfma3(*reinterpret_cast<const bf16x8*>(m1h + ao), *reinterpret_cast<const bf16x8*>(m1l + ao),
                             *reinterpret_cast<const bf16x8*>(bh + bo), *reinterpret_cast<const bf16x8*>(bl + bo), acc);
             }
+            {   // plus the tile's own rows j < ii, exactly (exp(-|.|) keeps masked pairs finite)
+                const int d = 16 * Dt + (lane & 15);
+                float xj[16], gj[16];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int ii = 16 * I + 4 * (lane >> 4) + e, d = 16 * Dt + (lane & 15);
-                Out[ii * 128 + d] = ex(gam[ii * 128 + d] - piv[d]) * acc[e];
+                for (int jr = 0; jr < 16; ++jr) {
+                    xj[jr] = KFp[(16 * I + jr) * 128 + d];
+                    gj[jr] = gam[(16 * I + jr) * 128 + d];
+                }
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int r = 4 * (lane >> 4) + e, ii = 16 * I + r;
+                    const float gi = gam[ii * 128 + d];
+                    float m[16];
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) {
+                        const float4 t = *reinterpret_cast<const float4*>(Mx + ii * 128 + 16 * I + 4 * c);
+                        m[4 * c] = t.x;
+                        m[4 * c + 1] = t.y;
+                        m[4 * c + 2] = t.z;
+                        m[4 * c + 3] = t.w;
+                    }
+                    float v = ex(gi - piv[d]) * acc[e];
+#pragma unroll
+                    for (int jr = 0; jr < 16; ++jr)
+                        v += (jr < r ? m[jr] : 0.f) * xj[jr] * ex(-fabsf(gi - gj[jr]));
+                    Out[ii * 128 + d] = v;
+                }
             }
         }
     }
-    // Cc_j = sum_i G_ij k_i e^(gamma_i - gamma_j), C2_j = sum_i dA2_ij q_i e^(...), i >= j
+    // Cc_j = sum_i G_ij k_i e^(gamma_i - gamma_j), C2_j = sum_i dA2_ij q_i e^(...), i > j (the i = j
+    // term of C2 goes to dk in the assembly, as R2's to dq)
     for (int which = 0; which < 2; ++which) {
         const float* Mt = mat(w, ch, which ? DA2T : GT);
         const float* X = which ? QFp : KFp;
         float* Out = mat(w, ch, which ? C2 : CC);
         for (int J = 0; J < NT; ++J) {
             __syncthreads();
-            if (tid < 128) piv[tid] = gam[(16 * J + 8) * 128 + tid];
+            if (tid < 128) piv[tid] = gam[(16 * J + 15) * 128 + tid];   // the tile's last row
             __syncthreads();
-            const int i0 = (16 * J) & ~31;          // first contraction block
-            stage_piv_colmajor<PC>(X, gam, piv, -1, 16 * J, C, C, bh, bl, tid);
+            // rows i of later tiles (i >= 16 (J + 1)) through the pivot; the tile's own rows below
+            const int i0 = (16 * (J + 1)) & ~31;    // first contraction block
+            stage_piv_colmajor<PC>(X, gam, piv, -1, 16 * (J + 1), C, C, bh, bl, tid);
             stage_rows(Mt, 16 * J, C, m1h, m1l);
             __syncthreads();
             const int Dt = wave;
@@ -838,10 +904,33 @@ __global__ __launch_bounds__(BTHREADS) __attribute__((amdgpu_waves_per_eu(4))) v
                 acc = mfma3(*reinterpret_cast<const bf16x8*>(m1h + ao), *reinterpret_cast<const bf16x8*>(m1l + ao),
                             *reinterpret_cast<const bf16x8*>(bh + bo), *reinterpret_cast<const bf16x8*>(bl + bo), acc);
             }
+            {   // plus the tile's own rows i > jj, exactly (exp(-|.|) keeps masked pairs finite)
+                const int d = 16 * Dt + (lane & 15);
+                float xi[16], gi[16];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int jj = 16 * J + 4 * (lane >> 4) + e, d = 16 * Dt + (lane & 15);
-                Out[jj * 128 + d] = ex(piv[d] - gam[jj * 128 + d]) * acc[e];
+                for (int ir = 0; ir < 16; ++ir) {
+                    xi[ir] = X[(16 * J + ir) * 128 + d];
+                    gi[ir] = gam[(16 * J + ir) * 128 + d];
+                }
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int r = 4 * (lane >> 4) + e, jj = 16 * J + r;
+                    const float gj = gam[jj * 128 + d];
+                    float m[16];
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) {
+                        const float4 t = *reinterpret_cast<const float4*>(Mt + jj * 128 + 16 * J + 4 * c);
+                        m[4 * c] = t.x;
+                        m[4 * c + 1] = t.y;
+                        m[4 * c + 2] = t.z;
+                        m[4 * c + 3] = t.w;
+                    }
+                    float v = ex(piv[d] - gj) * acc[e];
+#pragma unroll
+                    for (int ir = 0; ir < 16; ++ir)
+                        v += (ir > r ? m[ir] : 0.f) * xi[ir] * ex(-fabsf(gi[ir] - gj));
+                    Out[jj * 128 + d] = v;
+                }
             }
         }
     }
@@ -851,6 +940,7 @@ __global__ __launch_bounds__(BTHREADS) __attribute__((amdgpu_waves_per_eu(4))) v
     // thread per round, loads first)
     {
         const float *Rp = mat(w, ch, RR), *Cp = mat(w, ch, CC), *R2p = mat(w, ch, R2), *C2p = mat(w, ch, C2);
+        const float* DA2d = mat(w, ch, DA2);
         const float *DQDp = mat(w, ch, DQD), *DKGp = mat(w, ch, DKG), *DKTp = mat(w, ch, DKT), *DBTp = mat(w, ch, DBT);
         const float *QDp = mat(w, ch, QD), *KDp = mat(w, ch, KDM), *KGp = mat(w, ch, KG);
         float *DQHp = mat(w, ch, DQH), *DKHp = mat(w, ch, DKH), *DGMp = mat(w, ch, DGM);
@@ -879,10 +969,13 @@ __global__ __launch_bounds__(BTHREADS) __attribute__((amdgpu_waves_per_eu(4))) v
                 const int e = e0 + u * BTHREADS, i = e >> 7, d = e & 127;
                 const float eg = ex(gm[u]), egc = ex(sGC[d] - gm[u]), b = sBeta[i];
                 const float dkd = b * dkt[u];
-                DQHp[e] = scale * r2[u] + scale * eg * dqd[u];
-                DKHp[e] = rr[u] + cc[u] + scale * c2[u] + eg * dkd + egc * dkg[u];
+                const float a2d = DA2d[i * 129];   // dA2_ii
+                DQHp[e] = scale * (r2[u] + a2d * kf[u]) + scale * eg * dqd[u];
+                DKHp[e] = rr[u] + cc[u] + scale * (c2[u] + a2d * qf[u]) + eg * dkd + egc * dkg[u];
+                // dgamma_i without the kg_i dkg_i term: in dg that term and its part of dgamma_C
+                // sum to the prefix over earlier rows (taken in the scan below)
                 DGMp[e] = kf[u] * rr[u] - kf[u] * cc[u] + scale * (qf[u] * r2[u] - kf[u] * c2[u]) + qd[u] * dqd[u] +
-                          kd[u] * dkd - kg[u] * dkg[u];
+                          kd[u] * dkd;
                 if (i < rows) in.dv[((tok0 + i) * H + hv) * VD + d] = b * dbt[u];
             }
         }
@@ -935,11 +1028,18 @@ __global__ __launch_bounds__(BTHREADS) __attribute__((amdgpu_waves_per_eu(4))) v
             }
         }
     }
-    // ---- per key dimension: dgamma_C and the reverse prefix sum of dgamma over the chunk rows
+    // ---- per key dimension: dg.  With dgamma_i' = dgamma_i + kg_i dkg_i (what the assembly left
+    // in DGM) and dgamma_C = sum_i kg_i dkg_i + e^gamma_C (S_in . dS_out), the reverse prefix sum
+    //     dg_t = dgamma_C + sum_{i >= t} dgamma_i
+    //          = e^gamma_C (S_in . dS_out) + sum_{i < t} kg_i dkg_i + sum_{i >= t} dgamma_i'
+    // has no term that cancels: for strong gates every term is small where dg is, instead of the
+    // difference of O(1) sums.
     {
-        float (*sPart)[128] = reinterpret_cast<float (*)[128]>(smem);   // [4][128], pivot panels are done
-        float* sSd = reinterpret_cast<float*>(smem) + 4 * 128;
+        float (*sKg)[128] = reinterpret_cast<float (*)[128]>(smem);           // [4][128], pivot panels are done
+        float (*sSeg)[128] = reinterpret_cast<float (*)[128]>(smem) + 4;      // [4][128]
+        float* sSd = reinterpret_cast<float*>(smem) + 8 * 128;
         const float *KGp = mat(w, ch, KG), *DKGp = mat(w, ch, DKG), *DGMp = mat(w, ch, DGM);
+        float* DGSp = mat(w, ch, DGS);   // per row: the prefix over earlier rows, then dg itself
         // S_in . dS_out along the value columns of row d of both (a wave per row)
         for (int d = wave; d < 128; d += BWAVES) {
             float x = SINp[d * 128 + lane] * DSp[d * 128 + lane] + SINp[d * 128 + lane + 64] * DSp[d * 128 + lane + 64];
@@ -957,23 +1057,27 @@ __global__ __launch_bounds__(BTHREADS) __attribute__((amdgpu_waves_per_eu(4))) v
             kgsum += KGp[i * 128 + d] * DKGp[i * 128 + d];
             seg += (i < rows) ? DGMp[i * 128 + d] : 0.f;
         }
-        sPart[part][d] = kgsum;
+        sKg[part][d] = kgsum;
+        sSeg[part][d] = seg;
         __syncthreads();
-        const float dgc = sPart[0][d] + sPart[1][d] + sPart[2][d] + sPart[3][d] + ex(sGC[d]) * sSd[d];
-        __syncthreads();
-        sPart[part][d] = seg;
-        __syncthreads();
-        // suffix offset: later segments, plus dgamma_C (it enters at the last row, i.e. every row's sum)
-        float acc = dgc;
-        for (int p2 = part + 1; p2 < 4; ++p2) acc += sPart[p2][d];
-        float* DGSp = mat(w, ch, DGS);
+        float pre = 0.f;                                   // kg dkg over the rows before this part
+        for (int p2 = 0; p2 < part; ++p2) pre += sKg[p2][d];
+        float acc = ex(sGC[d]) * sSd[d];                   // dgamma_i' over the rows after it, and
+        for (int p2 = part + 1; p2 < 4; ++p2) acc += sSeg[p2][d];   // the state-decay term
 #pragma unroll 8
-        for (int u = SEG - 1; u >= 0; --u) {
+        for (int u = 0; u < SEG; ++u) {                    // exclusive prefix, rows ascending
+            const int i = i0 + u;
+            DGSp[i * 128 + d] = pre;
+            pre += KGp[i * 128 + d] * DKGp[i * 128 + d];
+        }
+#pragma unroll 8
+        for (int u = SEG - 1; u >= 0; --u) {               // suffix, rows descending
             const int i = i0 + u;
             acc += (i < rows) ? DGMp[i * 128 + d] : 0.f;
+            const float dgv = acc + DGSp[i * 128 + d];
             if (i < rows) {
-                if (PER_DIM) in.dg[((tok0 + i) * H + hv) * KD + d] = acc;
-                else DGSp[i * 128 + d] = acc;
+                if (PER_DIM) in.dg[((tok0 + i) * H + hv) * KD + d] = dgv;
+                else DGSp[i * 128 + d] = dgv;
             }
         }
     }

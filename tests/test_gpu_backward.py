@@ -96,6 +96,28 @@ SMALL = [
 ]
 
 
+# Gates far stronger than the workloads' (as in the forward's strong-gate cases): every
+# per-token gate near -12, so a 16-token tile spans about 190 in gamma, and isolated tokens
+# that forget everything (g = -40 with probability 1/8).  Pair decays inside a tile are then
+# far beyond any fp32 pivot factor, and dg is small where the other gradients are not.
+STRONG = [
+    # label, B, T, H, HV, C, per_dim, lengths, initial, gate_mean, spike_prob
+    ("kda_ls_m12_C128", 1, 300, 2, None, 128, True, None, True, -12.0, 0.0),
+    ("kda_ls_m12_C64_varlen", 1, 333, 2, None, 64, True, (100, 0, 233), True, -12.0, 0.0),
+    ("gdn_ls_m12_C128", 1, 260, 2, None, 128, False, None, True, -12.0, 0.0),
+    ("kda_spikes40_C128", 1, 384, 2, None, 128, True, None, True, 0.0, 0.125),
+    ("gdn_spikes40_grouped_C64", 1, 200, 1, 2, 64, False, None, True, 0.0, 0.125),
+]
+
+
+@pytest.mark.parametrize("case", STRONG, ids=[c[0] for c in STRONG])
+def test_backward_strong_gates(case):
+    label, B, T, H, HV, C, per_dim, lengths, init, gm, sp = case
+    inp = make_inputs(B, T, H, seed=900 + T, per_dim_gate=per_dim, lengths=lengths, initial_state=init,
+                      chunk_size=C, gate_mean=gm, HV=HV, spike_prob=sp)
+    check(inp, label)
+
+
 @pytest.mark.parametrize("case", SMALL, ids=[c[0] for c in SMALL])
 def test_backward_parity(case):
     label, B, T, H, HV, C, per_dim, lengths, init, gm, l2n = case
