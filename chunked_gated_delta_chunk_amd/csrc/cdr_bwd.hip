@@ -228,47 +228,7 @@ __device__ __forceinline__ void split8(const float* x, bf16x8& h, bf16x8& l) {
 // of the last row of tile J), both factors are <= 1 for every gate: nothing overflows, and a
 // factor that underflows belongs to a pair whose decay underflows too.  Pairs inside one
 // 16-row tile have no such pivot; they are summed exactly, one exponential per pair and key
-// dimension.  Staged operands are hi/lo bf16 in LDS.
-
-// B panel [rows][d] (d contiguous) of X[j][d] * e^(sgn (p[d] - gamma[j][d])) for j < jhi
-// and j >= jlo (zero elsewhere), rows 0..nrows-1
-template <int PITCH>
-__device__ __forceinline__ void stage_piv_rowmajor(const float* X, const float* gam, const float* piv, int sgn,
-                                                   int jlo, int jhi, int nrows, uint16_t* hi, uint16_t* lo, int tid) {
-    for (int e = tid; e < nrows * 32; e += BTHREADS) {
-        const int j = e >> 5, d = (e & 31) * 4;
-        float xs[4] = {0.f, 0.f, 0.f, 0.f};
-        if (j >= jlo && j < jhi) {
-            const float4 x = *reinterpret_cast<const float4*>(X + j * 128 + d);
-            const float4 gm = *reinterpret_cast<const float4*>(gam + j * 128 + d);
-            xs[0] = x.x * ex(sgn * (piv[d] - gm.x));
-            xs[1] = x.y * ex(sgn * (piv[d + 1] - gm.y));
-            xs[2] = x.z * ex(sgn * (piv[d + 2] - gm.z));
-            xs[3] = x.w * ex(sgn * (piv[d + 3] - gm.w));
-        }
-        uint32_t h0, l0, h1, l1;
-        split_pk(xs[0], xs[1], h0, l0);
-        split_pk(xs[2], xs[3], h1, l1);
-        *reinterpret_cast<uint2*>(hi + j * PITCH + d) = make_uint2(h0, h1);
-        *reinterpret_cast<uint2*>(lo + j * PITCH + d) = make_uint2(l0, l1);
-    }
-}
-
-// the same values stored transposed, [d][j] (j contiguous), rows j = 0..nrows-1
-template <int PITCH>
-__device__ __forceinline__ void stage_piv_colmajor(const float* X, const float* gam, const float* piv, int sgn,
-                                                   int jlo, int jhi, int nrows, uint16_t* hi, uint16_t* lo, int tid) {
-#pragma unroll 4
-    for (int e = tid; e < nrows * 128; e += BTHREADS) {
-        const int j = e >> 7, d = e & 127;
-        float x = 0.f;
-        if (j >= jlo && j < jhi) x = X[j * 128 + d] * ex(sgn * (piv[d] - gam[j * 128 + d]));
-        short h, l;
-        split_bf(x, h, l);
-        hi[d * PITCH + j] = (uint16_t)h;
-        lo[d * PITCH + j] = (uint16_t)l;
-    }
-}
+// dimension.
 
 // ------------------------------------------------------------------------------------
 template <int C, bool PER_DIM, bool L2N>
@@ -709,10 +669,11 @@ __global__ __launch_bounds__(BTHREADS) void bwd_chain_kernel(ChunkMap map, int H
 template <int C, bool PER_DIM, bool L2N>
 __global__ __launch_bounds__(BTHREADS) __attribute__((amdgpu_waves_per_eu(4))) void bwd_local_kernel(In in, ChunkMap map, int H, int Hk, float scale, Work w) {
     constexpr int NT = C / 16;
-    constexpr int PC = C + 8;                          // pitch of [d][j] pivot panels
-    constexpr int PIV_BYTES = (128 * PC * 2 + 2 * 16 * PC) * 2 + 128 * 4;
+    constexpr int DIAG_BYTES = NT * 256 * 2 * 4;      // diagonal blocks of G and dA2
+    constexpr int SCAN_BYTES = 9 * 128 * 4;           // the dg scan's panels
     constexpr int GEMM_BYTES = 256 * LDP * 2 * 2;
-    constexpr int SMEM = PIV_BYTES > GEMM_BYTES ? PIV_BYTES : GEMM_BYTES;
+    constexpr int SMEM0 = DIAG_BYTES > SCAN_BYTES ? DIAG_BYTES : SCAN_BYTES;
+    constexpr int SMEM = SMEM0 > GEMM_BYTES ? SMEM0 : GEMM_BYTES;
     __shared__ __attribute__((aligned(16))) unsigned char smem[SMEM];
     __shared__ float sBeta[128], sGC[128];
 
@@ -804,133 +765,137 @@ __global__ __launch_bounds__(BTHREADS) __attribute__((amdgpu_waves_per_eu(4))) v
     }
     __syncthreads();
 
-    // ---- pair products with per-dimension decay.  Per row tile: the decayed right factor
-    // (all rows, [d][j] so that the contraction index is contiguous) and the tile's rows of the
-    // coefficient matrices are staged as hi/lo bf16 in LDS; wave w computes key dimensions
-    // 16 w .. 16 w + 15.
-    uint16_t* bh = reinterpret_cast<uint16_t*>(smem);
-    uint16_t* bl = bh + 128 * PC;
-    uint16_t* m1h = bl + 128 * PC;          // [16][PC] the tile's rows of the coefficient matrix
-    uint16_t* m1l = m1h + 16 * PC;
-    float* piv = reinterpret_cast<float*>(m1l + 16 * PC);
+    // ---- pair products with per-dimension decay
     const float* KFp = mat(w, ch, KF);
     const float* QFp = mat(w, ch, QF);
-    auto stage_rows = [&](const float* Mx, int r0, int ncol, uint16_t* hi, uint16_t* lo) {
-        for (int e = tid; e < 16 * (ncol / 4); e += BTHREADS) {
-            const int r = e / (ncol / 4), c4 = (e % (ncol / 4)) * 4;
-            const float4 x = *reinterpret_cast<const float4*>(Mx + (r0 + r) * 128 + c4);
-            uint32_t h0, l0, h1, l1;
-            split_pk(x.x, x.y, h0, l0);
-            split_pk(x.z, x.w, h1, l1);
-            *reinterpret_cast<uint2*>(hi + r * PC + c4) = make_uint2(h0, h1);
-            *reinterpret_cast<uint2*>(lo + r * PC + c4) = make_uint2(l0, l1);
+    // R_i = sum_j G_ij k_j e^(gamma_i - gamma_j), R2_i = sum_j dA2_ij k_j e^(...)   (j < i)
+    // Cc_j = sum_i G_ij k_i e^(gamma_i - gamma_j), C2_j = sum_i dA2_ij q_i e^(...)  (i > j)
+    // The i = j terms of R2 and C2 (no decay) are added to dq and dk in the assembly; left out
+    // here they cannot cancel in dgamma, where they have no part (e^0 does not depend on gamma).
+    //
+    // Pairs inside one 16-row tile first, exactly: a thread per (tile, key dimension) walks the
+    // tile's 120 pairs, and each factor e^(gamma_i - gamma_j) is computed once for all four sums.
+    {
+        float* sGd = reinterpret_cast<float*>(smem);   // [NT][16][16] diagonal blocks of G
+        float* sDd = sGd + NT * 256;                    // and of dA2
+        const float* Gp = mat(w, ch, GG);
+        const float* DA2p = mat(w, ch, DA2);
+        for (int e = tid; e < NT * 256; e += BTHREADS) {
+            const int t = e >> 8, o = (16 * t + ((e >> 4) & 15)) * 128 + 16 * t + (e & 15);
+            sGd[e] = Gp[o];
+            sDd[e] = DA2p[o];
         }
-    };
-    // R_i = sum_j G_ij k_j e^(gamma_i - gamma_j), R2_i = sum_j dA2_ij k_j e^(...), j < i.  The j = i
-    // term of R2 (dA2_ii k_i, no decay) is added to dq in the assembly; left out of R2 it cannot
-    // cancel against C2's in dgamma, where it has no part (e^0 does not depend on gamma).
-    for (int which = 0; which < 2; ++which) {
-        const float* Mx = mat(w, ch, which ? DA2 : GG);
-        float* Out = mat(w, ch, which ? R2 : RR);
-        for (int I = 0; I < NT; ++I) {
-            __syncthreads();
-            if (tid < 128) piv[tid] = gam[(16 * I) * 128 + tid];   // the tile's first row
-            __syncthreads();
-            // rows j of earlier tiles (j < 16 I) through the pivot; the tile's own rows below
-            const int nrp = (16 * I + 31) & ~31;
-            stage_piv_colmajor<PC>(KFp, gam, piv, 1, 0, 16 * I, nrp, bh, bl, tid);
-            stage_rows(Mx, 16 * I, nrp, m1h, m1l);
-            __syncthreads();
-            const int Dt = wave;
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            for (int s = 0; s < nrp / 32; ++s) {
-                const int jo = 32 * s + 8 * (lane >> 4);
-                const int ao = (lane & 15) * PC + jo;
-                const int bo = (16 * Dt + (lane & 15)) * PC + jo;
-                acc = mfma3(*reinterpret_cast<const bf16x8*>(m1h + ao), *reinterpret_cast<const bf16x8*>(m1l + ao),
-                            *reinterpret_cast<const bf16x8*>(bh + bo), *reinterpret_cast<const bf16x8*>(bl + bo), acc);
+        __syncthreads();
+        float *Rp = mat(w, ch, RR), *R2p = mat(w, ch, R2), *Cp = mat(w, ch, CC), *C2p = mat(w, ch, C2);
+        for (int it = tid; it < NT * 128; it += BTHREADS) {
+            const int t = it >> 7, d = it & 127, base = 16 * t * 128 + d;
+            const float* gb = sGd + t * 256;
+            const float* db = sDd + t * 256;
+            float kx[16], gx[16], cc[16], c2[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                kx[r] = KFp[base + r * 128];
+                gx[r] = gam[base + r * 128];
+                cc[r] = 0.f;
+                c2[r] = 0.f;
             }
-            {   // plus the tile's own rows j < ii, exactly (exp(-|.|) keeps masked pairs finite)
-                const int d = 16 * Dt + (lane & 15);
-                float xj[16], gj[16];
 #pragma unroll
-                for (int jr = 0; jr < 16; ++jr) {
-                    xj[jr] = KFp[(16 * I + jr) * 128 + d];
-                    gj[jr] = gam[(16 * I + jr) * 128 + d];
+            for (int i = 0; i < 16; ++i) {
+                const float qi = QFp[base + i * 128];
+                float r1 = 0.f, r2 = 0.f;
+#pragma unroll
+                for (int j = 0; j < i; ++j) {
+                    const float e = ex(gx[i] - gx[j]);
+                    const float gij = gb[16 * i + j], dij = db[16 * i + j];
+                    const float ke = kx[j] * e;
+                    r1 = fmaf(gij, ke, r1);
+                    r2 = fmaf(dij, ke, r2);
+                    cc[j] = fmaf(gij, kx[i] * e, cc[j]);
+                    c2[j] = fmaf(dij, qi * e, c2[j]);
                 }
+                Rp[base + i * 128] = r1;
+                R2p[base + i * 128] = r2;
+            }
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int r = 4 * (lane >> 4) + e, ii = 16 * I + r;
-                    const float gi = gam[ii * 128 + d];
-                    float m[16];
-#pragma unroll
-                    for (int c = 0; c < 4; ++c) {
-                        const float4 t = *reinterpret_cast<const float4*>(Mx + ii * 128 + 16 * I + 4 * c);
-                        m[4 * c] = t.x;
-                        m[4 * c + 1] = t.y;
-                        m[4 * c + 2] = t.z;
-                        m[4 * c + 3] = t.w;
-                    }
-                    float v = ex(gi - piv[d]) * acc[e];
-#pragma unroll
-                    for (int jr = 0; jr < 16; ++jr)
-                        v += (jr < r ? m[jr] : 0.f) * xj[jr] * ex(-fabsf(gi - gj[jr]));
-                    Out[ii * 128 + d] = v;
-                }
+            for (int r = 0; r < 16; ++r) {
+                Cp[base + r * 128] = cc[r];
+                C2p[base + r * 128] = c2[r];
             }
         }
     }
-    // Cc_j = sum_i G_ij k_i e^(gamma_i - gamma_j), C2_j = sum_i dA2_ij q_i e^(...), i > j (the i = j
-    // term of C2 goes to dk in the assembly, as R2's to dq)
-    for (int which = 0; which < 2; ++which) {
-        const float* Mt = mat(w, ch, which ? DA2T : GT);
-        const float* X = which ? QFp : KFp;
-        float* Out = mat(w, ch, which ? C2 : CC);
-        for (int J = 0; J < NT; ++J) {
-            __syncthreads();
-            if (tid < 128) piv[tid] = gam[(16 * J + 15) * 128 + tid];   // the tile's last row
-            __syncthreads();
-            // rows i of later tiles (i >= 16 (J + 1)) through the pivot; the tile's own rows below
-            const int i0 = (16 * (J + 1)) & ~31;    // first contraction block
-            stage_piv_colmajor<PC>(X, gam, piv, -1, 16 * (J + 1), C, C, bh, bl, tid);
-            stage_rows(Mt, 16 * J, C, m1h, m1l);
-            __syncthreads();
-            const int Dt = wave;
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            for (int io = i0; io < C; io += 32) {
-                const int ii = io + 8 * (lane >> 4);
-                const int ao = (lane & 15) * PC + ii;
-                const int bo = (16 * Dt + (lane & 15)) * PC + ii;
-                acc = mfma3(*reinterpret_cast<const bf16x8*>(m1h + ao), *reinterpret_cast<const bf16x8*>(m1l + ao),
-                            *reinterpret_cast<const bf16x8*>(bh + bo), *reinterpret_cast<const bf16x8*>(bl + bo), acc);
+    // Then the pairs across tiles, through one pivot per tile, added on top.  Wave w owns key
+    // dimensions 16 w .. 16 w + 15 in every tile and forms its own decayed operands in registers
+    // (the B fragment of a 16x16x32 MFMA: rows 8 (lane / 16) .. + 7 of a 32-row block, column
+    // lane % 16); the coefficient rows (A fragments) are read straight from memory.  No LDS, no
+    // barrier.
+    __syncthreads();
+    {
+        const int n = lane & 15, kq = lane >> 4, d = 16 * wave + n;
+        const float *Gp = mat(w, ch, GG), *DA2p = mat(w, ch, DA2), *GTp = mat(w, ch, GT), *DA2Tp = mat(w, ch, DA2T);
+        float *Rp = mat(w, ch, RR), *R2p = mat(w, ch, R2), *Cp = mat(w, ch, CC), *C2p = mat(w, ch, C2);
+        auto afrag = [&](const float* M, int row, int col, bf16x8& h, bf16x8& l) {
+            const float4 x0 = *reinterpret_cast<const float4*>(M + row * 128 + col);
+            const float4 x1 = *reinterpret_cast<const float4*>(M + row * 128 + col + 4);
+            const float x[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+            split8(x, h, l);
+        };
+        // rows of tile I against the rows j < 16 I of the earlier tiles; pivot: gamma of the
+        // tile's first row
+        for (int I = 1; I < NT; ++I) {
+            const float p = gam[(16 * I) * 128 + d];
+            f32x4 ar = {0.f, 0.f, 0.f, 0.f}, ar2 = {0.f, 0.f, 0.f, 0.f};
+            // the trip count is the same in every lane (the MFMA reads all 64)
+            for (int j0 = 8 * kq; j0 < ((16 * I + 31) & ~31); j0 += 32) {
+                float b[8];
+#pragma unroll
+                for (int t = 0; t < 8; ++t) {
+                    const int j = j0 + t;
+                    const float x = KFp[j * 128 + d] * ex(p - gam[j * 128 + d]);
+                    b[t] = j < 16 * I ? x : 0.f;
+                }
+                bf16x8 bh, bl, ah, al;
+                split8(b, bh, bl);
+                afrag(Gp, 16 * I + n, j0, ah, al);
+                ar = mfma3(ah, al, bh, bl, ar);
+                afrag(DA2p, 16 * I + n, j0, ah, al);
+                ar2 = mfma3(ah, al, bh, bl, ar2);
             }
-            {   // plus the tile's own rows i > jj, exactly (exp(-|.|) keeps masked pairs finite)
-                const int d = 16 * Dt + (lane & 15);
-                float xi[16], gi[16];
 #pragma unroll
-                for (int ir = 0; ir < 16; ++ir) {
-                    xi[ir] = X[(16 * J + ir) * 128 + d];
-                    gi[ir] = gam[(16 * J + ir) * 128 + d];
+            for (int e = 0; e < 4; ++e) {
+                const int o = (16 * I + 4 * kq + e) * 128 + d;
+                const float f = ex(gam[o] - p);
+                Rp[o] += f * ar[e];
+                R2p[o] += f * ar2[e];
+            }
+        }
+        // columns of tile J against the rows i >= 16 (J + 1) of the later tiles; pivot: gamma of
+        // the tile's last row
+        for (int J = 0; J + 1 < NT; ++J) {
+            const float p = gam[(16 * J + 15) * 128 + d];
+            f32x4 ac = {0.f, 0.f, 0.f, 0.f}, ac2 = {0.f, 0.f, 0.f, 0.f};
+            for (int i0 = ((16 * (J + 1)) & ~31) + 8 * kq; i0 < C; i0 += 32) {   // as many trips in every lane
+                float bk[8], bq[8];
+#pragma unroll
+                for (int t = 0; t < 8; ++t) {
+                    const int i = i0 + t;
+                    const float e = i >= 16 * (J + 1) ? ex(gam[i * 128 + d] - p) : 0.f;
+                    bk[t] = KFp[i * 128 + d] * e;
+                    bq[t] = QFp[i * 128 + d] * e;
                 }
+                bf16x8 bh, bl, ah, al;
+                split8(bk, bh, bl);
+                afrag(GTp, 16 * J + n, i0, ah, al);
+                ac = mfma3(ah, al, bh, bl, ac);
+                split8(bq, bh, bl);
+                afrag(DA2Tp, 16 * J + n, i0, ah, al);
+                ac2 = mfma3(ah, al, bh, bl, ac2);
+            }
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int r = 4 * (lane >> 4) + e, jj = 16 * J + r;
-                    const float gj = gam[jj * 128 + d];
-                    float m[16];
-#pragma unroll
-                    for (int c = 0; c < 4; ++c) {
-                        const float4 t = *reinterpret_cast<const float4*>(Mt + jj * 128 + 16 * J + 4 * c);
-                        m[4 * c] = t.x;
-                        m[4 * c + 1] = t.y;
-                        m[4 * c + 2] = t.z;
-                        m[4 * c + 3] = t.w;
-                    }
-                    float v = ex(piv[d] - gj) * acc[e];
-#pragma unroll
-                    for (int ir = 0; ir < 16; ++ir)
-                        v += (ir > r ? m[ir] : 0.f) * xi[ir] * ex(-fabsf(gi[ir] - gj));
-                    Out[jj * 128 + d] = v;
-                }
+            for (int e = 0; e < 4; ++e) {
+                const int o = (16 * J + 4 * kq + e) * 128 + d;
+                const float f = ex(p - gam[o]);
+                Cp[o] += f * ac[e];
+                C2p[o] += f * ac2[e];
             }
         }
     }
