@@ -70,11 +70,11 @@ Layout layout(const cdr_problem* p) {
 }
 
 struct BwdLayout {
-    size_t m, gcr, rq, rk, bet, dqp, dkp, total;
+    size_t m, gcr, rq, rk, bet, wide, dqp, dkp, total;
 };
 
-// backward workspace: NMAT fp32 128 x 128 matrices and four 128-vectors per (chunk slot, value
-// head), and per-value-head dq, dk partials when value heads are grouped
+// backward workspace: NMAT fp32 128 x 128 matrices, four 128-vectors and a word of tile flags per
+// (chunk slot, value head), and per-value-head dq, dk partials when value heads are grouped
 BwdLayout bwd_layout(const cdr_problem* p) {
     const size_t nch = (size_t)num_slots(p) * (size_t)value_heads(p);
     const size_t tokens = (size_t)p->B * p->T;
@@ -90,6 +90,7 @@ BwdLayout bwd_layout(const cdr_problem* p) {
     L.rq = take(nch * 128 * sizeof(float));
     L.rk = take(nch * 128 * sizeof(float));
     L.bet = take(nch * 128 * sizeof(float));
+    L.wide = take(nch * sizeof(uint32_t));
     const bool grouped = value_heads(p) != p->H;
     L.dqp = take(grouped ? tokens * value_heads(p) * p->K * sizeof(float) : 0);
     L.dkp = take(grouped ? tokens * value_heads(p) * p->K * sizeof(float) : 0);
@@ -299,6 +300,7 @@ cdr_status chunk_dr_bwd_stages(const cdr_problem* p, const void* q, const void* 
     w.rq = reinterpret_cast<float*>(wb + L.rq);
     w.rk = reinterpret_cast<float*>(wb + L.rk);
     w.bet = reinterpret_cast<float*>(wb + L.bet);
+    w.wide = reinterpret_cast<uint32_t*>(wb + L.wide);
     const bool grouped = value_heads(p) != p->H;
     w.dqp = grouped ? reinterpret_cast<float*>(wb + L.dqp) : nullptr;
     w.dkp = grouped ? reinterpret_cast<float*>(wb + L.dkp) : nullptr;

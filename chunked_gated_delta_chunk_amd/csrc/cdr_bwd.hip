@@ -38,6 +38,10 @@ constexpr int KB = 32;        // contraction block of a staged GEMM panel
 constexpr int LDP = KB + 8;   // LDS pitch (bf16) of a staged panel row
 constexpr int MSZ = 128 * 128;
 constexpr float EPS = 1e-6f;  // in-kernel normalisation: x / sqrt(|x|^2 + eps)
+// Largest gate span |gamma_i - gamma_m| over a 16-row tile and its middle row m for which the
+// tile's own pairs go through the middle-row pivot: every factor is then <= e^32, so the
+// decayed operands stay finite in fp32, and so do their products for the pairs that are masked.
+constexpr float SAFE_SPAN = 32.f;
 
 // per (chunk, value head) matrices, each 128 x 128 fp32 with row pitch 128
 enum Mat {
@@ -92,7 +96,7 @@ __device__ __forceinline__ void panel_load(Panel<M>& r, const View& v, int k0, i
         const int e = tid + u * BTHREADS;
         if (e < Panel<M>::NF4) {
             if (v.ks == 1) {
-                const int m = e >> 3, kk = (e & 7) * 4;
+                const int m = e / (KB / 4), kk = (e % (KB / 4)) * 4;
                 r.x[u] = *reinterpret_cast<const float4*>(v.p + (size_t)m * v.ms + k0 + kk);
             } else {
                 const int kk = e / (M / 4), m = (e % (M / 4)) * 4;
@@ -110,7 +114,7 @@ __device__ __forceinline__ void panel_store(const Panel<M>& r, const View& v, ui
         if (e < Panel<M>::NF4) {
             const float4 x = r.x[u];
             if (v.ks == 1) {
-                const int m = e >> 3, kk = (e & 7) * 4;
+                const int m = e / (KB / 4), kk = (e % (KB / 4)) * 4;
                 uint32_t h0, l0, h1, l1;
                 split_pk(x.x, x.y, h0, l0);
                 split_pk(x.z, x.w, h1, l1);
@@ -180,11 +184,14 @@ __device__ void gemm(const View a1, const View b1, int k1, const View a2, const 
             const int tile = wave + BWAVES * t;
             if (tile < NTL) {
                 const int I = tile / NTN, J = tile % NTN;
-                const int ro = (16 * I + (lane & 15)) * LDP + 8 * (lane >> 4);
-                const int co = (16 * J + (lane & 15)) * LDP + 8 * (lane >> 4);
-                acc[t] = mfma3(*reinterpret_cast<const bf16x8*>(ahi + ro), *reinterpret_cast<const bf16x8*>(alo + ro),
-                               *reinterpret_cast<const bf16x8*>(bhi + co), *reinterpret_cast<const bf16x8*>(blo + co),
-                               acc[t]);
+#pragma unroll
+                for (int kk = 0; kk < KB; kk += 32) {
+                    const int ro = (16 * I + (lane & 15)) * LDP + kk + 8 * (lane >> 4);
+                    const int co = (16 * J + (lane & 15)) * LDP + kk + 8 * (lane >> 4);
+                    acc[t] = mfma3(*reinterpret_cast<const bf16x8*>(ahi + ro), *reinterpret_cast<const bf16x8*>(alo + ro),
+                                   *reinterpret_cast<const bf16x8*>(bhi + co), *reinterpret_cast<const bf16x8*>(blo + co),
+                                   acc[t]);
+                }
             }
         }
     }
@@ -242,6 +249,7 @@ __global__ __launch_bounds__(BTHREADS) __attribute__((amdgpu_waves_per_eu(4))) v
                                                 : (PIV_BYTES > GEMM_BYTES ? PIV_BYTES : GEMM_BYTES));
     __shared__ __attribute__((aligned(16))) unsigned char smem[SMEM];
     __shared__ float sRq[128], sRk[128], sBeta[128], sGC[128];
+    __shared__ uint32_t sWide[2];
 
     const int slot = blockIdx.x, hv = blockIdx.y;
     int64_t tok0;
@@ -286,7 +294,8 @@ __global__ __launch_bounds__(BTHREADS) __attribute__((amdgpu_waves_per_eu(4))) v
     if (tid < 128) {
         const int d = tid;
         float acc = 0.f;
-        for (int i0 = 0; i0 < C; i0 += 16) {  // 16 independent loads in flight per block
+        uint32_t wide = 0;   // tiles whose span around the middle row exceeds SAFE_SPAN
+        for (int i0 = 0; i0 < C; i0 += 16) {  // one row tile: 16 independent loads in flight
             float gv[16];
 #pragma unroll
             for (int u = 0; u < 16; ++u) {
@@ -298,13 +307,24 @@ __global__ __launch_bounds__(BTHREADS) __attribute__((amdgpu_waves_per_eu(4))) v
 #pragma unroll
             for (int u = 0; u < 16; ++u) {
                 acc += gv[u];
+                gv[u] = acc;
                 gam[(i0 + u) * 128 + d] = acc;
             }
+            float span = 0.f;
+#pragma unroll
+            for (int u = 0; u < 16; ++u) span = fmaxf(span, fabsf(gv[u] - gv[8]));
+            if (!(span <= SAFE_SPAN)) wide |= 1u << (i0 >> 4);
         }
         sGC[d] = acc;
         w.gcr[ch * 128 + d] = acc;
+        uint32_t wm = 0;   // the same in every lane of the wave
+        for (int t = 0; t < NT; ++t)
+            if (__ballot((wide >> t) & 1u) != 0) wm |= 1u << t;
+        if (lane == 0) sWide[wave] = wm;
     }
     __syncthreads();
+    const uint32_t wide = sWide[0] | sWide[1];
+    if (tid == 0) w.wide[ch] = wide;
 
     // ---- inputs and their decayed forms (four elements per thread per round, loads first)
     {
@@ -344,9 +364,11 @@ __global__ __launch_bounds__(BTHREADS) __attribute__((amdgpu_waves_per_eu(4))) v
     }
     __syncthreads();
 
-    // ---- A-hat (strict) and A2 (inclusive) by row tiles: pivot p = gamma of row 16 I + 8.
-    // The tile rows' left factors (shared by the waves) are staged in LDS; wave J forms its
-    // right factor k_j e^(p - gamma_j) for its 16 rows in registers.
+    // ---- A-hat (strict) and A2 (inclusive) by row tiles.  The tile rows' left factors
+    // x_i e^(gamma_i - p) (shared by the waves) are staged in LDS; wave J forms its right factor
+    // k_j e^(p - gamma_j) for its 16 rows in registers.  Pivot p: gamma of the tile's middle row,
+    // and the diagonal tile goes through it too, unless the tile's gates are too wide (span above
+    // SAFE_SPAN); then the first row (every factor <= 1) and the diagonal tile exactly.
     {
         uint16_t* kh = reinterpret_cast<uint16_t*>(smem);
         uint16_t* kl = kh + 16 * P2;
@@ -357,10 +379,18 @@ __global__ __launch_bounds__(BTHREADS) __attribute__((amdgpu_waves_per_eu(4))) v
         const float* QFp = mat(w, ch, QF);
         float* AHp = mat(w, ch, AH);
         float* A2p = mat(w, ch, A2M);
-        // the diagonal tiles exactly, one per wave, all at once: lane (r, q) of wave I sums rows
-        // i = 16 I + 4 q + e against row j = 16 I + r; exp(-|gamma_i - gamma_j|) is the decay of the
-        // later row over the earlier one (pairs with j > i are masked when stored)
-        if (wave < NT) {
+        // the tiles right of the diagonal are zero (both matrices are read whole)
+        for (int e = tid; e < C * C; e += BTHREADS) {
+            const int i = e / C, j = e % C;
+            if (j >= 16 * (i / 16 + 1)) {
+                AHp[i * 128 + j] = 0.f;
+                A2p[i * 128 + j] = 0.f;
+            }
+        }
+        // the wide diagonal tiles exactly, one per wave, all at once: lane (r, q) of wave I sums
+        // rows i = 16 I + 4 q + e against row j = 16 I + r; exp(-|gamma_i - gamma_j|) is the decay
+        // of the later row over the earlier one (pairs with j > i are masked when stored)
+        if (wave < NT && ((wide >> wave) & 1u)) {
             const int I = wave, j = 16 * I + (lane & 15);
             f32x4 ak = {0.f, 0.f, 0.f, 0.f}, aq = {0.f, 0.f, 0.f, 0.f};
             for (int d = 0; d < KD; d += 4) {
@@ -383,16 +413,13 @@ __global__ __launch_bounds__(BTHREADS) __attribute__((amdgpu_waves_per_eu(4))) v
                 const int i = 16 * I + 4 * (lane >> 4) + e;
                 AHp[i * 128 + j] = (j < i) ? ak[e] : 0.f;
                 A2p[i * 128 + j] = (j <= i) ? scale * aq[e] : 0.f;
-                // the tiles right of the diagonal are zero (both matrices are read whole)
-                for (int J2 = I + 1; J2 < NT; ++J2) {
-                    AHp[i * 128 + 16 * J2 + (lane & 15)] = 0.f;
-                    A2p[i * 128 + 16 * J2 + (lane & 15)] = 0.f;
-                }
             }
         }
-        for (int I = 1; I < NT; ++I) {
+        for (int I = 0; I < NT; ++I) {
+            const bool mid = !((wide >> I) & 1u);    // the same in every thread
+            if (!mid && I == 0) continue;            // the first tile has no earlier one
             __syncthreads();
-            if (tid < 128) piv[tid] = gam[(16 * I) * 128 + tid];   // the tile's first row
+            if (tid < 128) piv[tid] = gam[(16 * I + (mid ? 8 : 0)) * 128 + tid];
             __syncthreads();
 #pragma unroll 4
             for (int e = tid; e < 16 * 128; e += BTHREADS) {
@@ -408,9 +435,10 @@ __global__ __launch_bounds__(BTHREADS) __attribute__((amdgpu_waves_per_eu(4))) v
             }
             __syncthreads();
             const int J = wave;
+            const bool run = J < I || (J == I && mid);
             if (J < NT) {
                 f32x4 ak = {0.f, 0.f, 0.f, 0.f}, aq = {0.f, 0.f, 0.f, 0.f};
-                if (J < I) {
+                if (run) {
                     const int j = 16 * J + (lane & 15);
                     for (int s2 = 0; s2 < KD / 32; s2 += 2) {
                         float4 kx[2][2], gx[2][2];
@@ -442,12 +470,12 @@ __global__ __launch_bounds__(BTHREADS) __attribute__((amdgpu_waves_per_eu(4))) v
                         }
                     }
                 }
-                if (J < I) {
+                if (run) {   // the diagonal tile masked: A-hat strict, A2 inclusive
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const int i = 16 * I + 4 * (lane >> 4) + e, j = 16 * J + (lane & 15);
-                        AHp[i * 128 + j] = ak[e];
-                        A2p[i * 128 + j] = scale * aq[e];
+                        AHp[i * 128 + j] = (J < I || j < i) ? ak[e] : 0.f;
+                        A2p[i * 128 + j] = (J < I || j <= i) ? scale * aq[e] : 0.f;
                     }
                 }
             }
@@ -773,9 +801,12 @@ __global__ __launch_bounds__(BTHREADS) __attribute__((amdgpu_waves_per_eu(4))) v
     // The i = j terms of R2 and C2 (no decay) are added to dq and dk in the assembly; left out
     // here they cannot cancel in dgamma, where they have no part (e^0 does not depend on gamma).
     //
-    // Pairs inside one 16-row tile first, exactly: a thread per (tile, key dimension) walks the
-    // tile's 120 pairs, and each factor e^(gamma_i - gamma_j) is computed once for all four sums.
-    {
+    // A tile whose gates are narrow (the bit of `wide` clear, set by bwd_prep) has its own pairs
+    // summed with the others below, through a pivot at its middle row.  The pairs inside a wide
+    // tile are summed first, exactly: a thread per (tile, key dimension) walks the tile's 120
+    // pairs, and each factor e^(gamma_i - gamma_j) is computed once for all four sums.
+    const uint32_t wide = w.wide[ch];
+    if (wide != 0) {
         float* sGd = reinterpret_cast<float*>(smem);   // [NT][16][16] diagonal blocks of G
         float* sDd = sGd + NT * 256;                    // and of dA2
         const float* Gp = mat(w, ch, GG);
@@ -789,6 +820,7 @@ __global__ __launch_bounds__(BTHREADS) __attribute__((amdgpu_waves_per_eu(4))) v
         float *Rp = mat(w, ch, RR), *R2p = mat(w, ch, R2), *Cp = mat(w, ch, CC), *C2p = mat(w, ch, C2);
         for (int it = tid; it < NT * 128; it += BTHREADS) {
             const int t = it >> 7, d = it & 127, base = 16 * t * 128 + d;
+            if (!((wide >> t) & 1u)) continue;   // the same in every lane of the wave
             const float* gb = sGd + t * 256;
             const float* db = sDd + t * 256;
             float kx[16], gx[16], cc[16], c2[16];
@@ -823,79 +855,89 @@ __global__ __launch_bounds__(BTHREADS) __attribute__((amdgpu_waves_per_eu(4))) v
             }
         }
     }
-    // Then the pairs across tiles, through one pivot per tile, added on top.  Wave w owns key
-    // dimensions 16 w .. 16 w + 15 in every tile and forms its own decayed operands in registers
-    // (the B fragment of a 16x16x32 MFMA: rows 8 (lane / 16) .. + 7 of a 32-row block, column
-    // lane % 16); the coefficient rows (A fragments) are read straight from memory.  No LDS, no
-    // barrier.
+    // Then the pairs through one pivot per tile (added to the exact part of a wide tile).  Wave w
+    // owns key dimensions 16 w .. 16 w + 15 in every tile and forms its own decayed operands in
+    // registers (the B fragment of a 16x16x32 MFMA: rows 8 (lane / 16) .. + 7 of a 32-row block,
+    // column lane % 16); the coefficient rows (A fragments) are read straight from memory.  No
+    // LDS, no barrier.  The pairs of a narrow tile with itself need no mask beyond the triangle
+    // of the coefficients (G is strictly lower), except the diagonal of dA2, which is zeroed.
     __syncthreads();
     {
         const int n = lane & 15, kq = lane >> 4, d = 16 * wave + n;
         const float *Gp = mat(w, ch, GG), *DA2p = mat(w, ch, DA2), *GTp = mat(w, ch, GT), *DA2Tp = mat(w, ch, DA2T);
         float *Rp = mat(w, ch, RR), *R2p = mat(w, ch, R2), *Cp = mat(w, ch, CC), *C2p = mat(w, ch, C2);
-        auto afrag = [&](const float* M, int row, int col, bf16x8& h, bf16x8& l) {
+        // A fragment: row `row` of M, columns col .. col + 7, the diagonal element zeroed if asked
+        auto afrag = [&](const float* M, int row, int col, bool nodiag, bf16x8& h, bf16x8& l) {
             const float4 x0 = *reinterpret_cast<const float4*>(M + row * 128 + col);
             const float4 x1 = *reinterpret_cast<const float4*>(M + row * 128 + col + 4);
-            const float x[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+            float x[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+#pragma unroll
+            for (int t = 0; t < 8; ++t) x[t] = (nodiag && col + t == row) ? 0.f : x[t];
             split8(x, h, l);
         };
-        // rows of tile I against the rows j < 16 I of the earlier tiles; pivot: gamma of the
-        // tile's first row
-        for (int I = 1; I < NT; ++I) {
-            const float p = gam[(16 * I) * 128 + d];
+        // rows of tile I against the rows j < lim: the earlier tiles, and the tile itself when
+        // narrow; pivot: gamma of the tile's middle row when narrow, else of its first row
+        for (int I = 0; I < NT; ++I) {
+            const bool mid = !((wide >> I) & 1u);
+            if (!mid && I == 0) continue;
+            const int lim = 16 * I + (mid ? 16 : 0);
+            const float p = gam[(16 * I + (mid ? 8 : 0)) * 128 + d];
             f32x4 ar = {0.f, 0.f, 0.f, 0.f}, ar2 = {0.f, 0.f, 0.f, 0.f};
             // the trip count is the same in every lane (the MFMA reads all 64)
-            for (int j0 = 8 * kq; j0 < ((16 * I + 31) & ~31); j0 += 32) {
+            for (int j0 = 8 * kq; j0 < ((lim + 31) & ~31); j0 += 32) {
                 float b[8];
 #pragma unroll
                 for (int t = 0; t < 8; ++t) {
                     const int j = j0 + t;
                     const float x = KFp[j * 128 + d] * ex(p - gam[j * 128 + d]);
-                    b[t] = j < 16 * I ? x : 0.f;
+                    b[t] = j < lim ? x : 0.f;
                 }
                 bf16x8 bh, bl, ah, al;
                 split8(b, bh, bl);
-                afrag(Gp, 16 * I + n, j0, ah, al);
+                afrag(Gp, 16 * I + n, j0, false, ah, al);
                 ar = mfma3(ah, al, bh, bl, ar);
-                afrag(DA2p, 16 * I + n, j0, ah, al);
+                afrag(DA2p, 16 * I + n, j0, true, ah, al);
                 ar2 = mfma3(ah, al, bh, bl, ar2);
             }
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int o = (16 * I + 4 * kq + e) * 128 + d;
                 const float f = ex(gam[o] - p);
-                Rp[o] += f * ar[e];
-                R2p[o] += f * ar2[e];
+                Rp[o] = (mid ? 0.f : Rp[o]) + f * ar[e];
+                R2p[o] = (mid ? 0.f : R2p[o]) + f * ar2[e];
             }
         }
-        // columns of tile J against the rows i >= 16 (J + 1) of the later tiles; pivot: gamma of
-        // the tile's last row
-        for (int J = 0; J + 1 < NT; ++J) {
-            const float p = gam[(16 * J + 15) * 128 + d];
+        // columns of tile J against the rows i >= lo: the later tiles, and the tile itself when
+        // narrow; pivot: gamma of the tile's middle row when narrow, else of its last row
+        for (int J = 0; J < NT; ++J) {
+            const bool mid = !((wide >> J) & 1u);
+            if (!mid && J == NT - 1) continue;
+            const int lo = 16 * J + (mid ? 0 : 16);
+            const float p = gam[(16 * J + (mid ? 8 : 15)) * 128 + d];
             f32x4 ac = {0.f, 0.f, 0.f, 0.f}, ac2 = {0.f, 0.f, 0.f, 0.f};
-            for (int i0 = ((16 * (J + 1)) & ~31) + 8 * kq; i0 < C; i0 += 32) {   // as many trips in every lane
+            for (int i0 = (lo & ~31) + 8 * kq; i0 < C; i0 += 32) {   // as many trips in every lane
                 float bk[8], bq[8];
 #pragma unroll
                 for (int t = 0; t < 8; ++t) {
                     const int i = i0 + t;
-                    const float e = i >= 16 * (J + 1) ? ex(gam[i * 128 + d] - p) : 0.f;
+                    const float e = i >= lo ? ex(gam[i * 128 + d] - p) : 0.f;
                     bk[t] = KFp[i * 128 + d] * e;
                     bq[t] = QFp[i * 128 + d] * e;
                 }
                 bf16x8 bh, bl, ah, al;
                 split8(bk, bh, bl);
-                afrag(GTp, 16 * J + n, i0, ah, al);
+                afrag(GTp, 16 * J + n, i0, false, ah, al);
                 ac = mfma3(ah, al, bh, bl, ac);
                 split8(bq, bh, bl);
-                afrag(DA2Tp, 16 * J + n, i0, ah, al);
+                afrag(DA2Tp, 16 * J + n, i0, true, ah, al);
                 ac2 = mfma3(ah, al, bh, bl, ac2);
             }
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int o = (16 * J + 4 * kq + e) * 128 + d;
                 const float f = ex(p - gam[o]);
-                Cp[o] += f * ac[e];
-                C2p[o] += f * ac2[e];
+                Cp[o] = (mid ? 0.f : Cp[o]) + f * ac[e];
+                C2p[o] = (mid ? 0.f : C2p[o]) + f * ac2[e];
             }
         }
     }

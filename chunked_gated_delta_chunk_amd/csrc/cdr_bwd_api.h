@@ -13,6 +13,7 @@ struct Work {
     float* rq;     // [nch][128] L2 scales of q rows (1 when off)
     float* rk;     // [nch][128] L2 scales of k rows
     float* bet;    // [nch][128] beta of the chunk rows (0 on rows past the end)
+    uint32_t* wide;  // [nch] bit t set: the gates of row tile t are too wide for a middle-row pivot
     float* dqp;    // [B*T][HV][K] per-value-head dq (grouped heads), or null
     float* dkp;
 };

@@ -98,8 +98,9 @@ SMALL = [
 
 # Gates far stronger than the workloads' (as in the forward's strong-gate cases): every
 # per-token gate near -12, so a 16-token tile spans about 190 in gamma, and isolated tokens
-# that forget everything (g = -40 with probability 1/8).  Pair decays inside a tile are then
-# far beyond any fp32 pivot factor, and dg is small where the other gradients are not.
+# that forget everything (g = -40 with probability 1/8, or 1/50 so that most tiles stay narrow
+# and the two kinds of tile meet in one chunk).  Pair decays inside a tile are then far beyond
+# any fp32 pivot factor, and dg is small where the other gradients are not.
 STRONG = [
     # label, B, T, H, HV, C, per_dim, lengths, initial, gate_mean, spike_prob
     ("kda_ls_m12_C128", 1, 300, 2, None, 128, True, None, True, -12.0, 0.0),
@@ -107,6 +108,8 @@ STRONG = [
     ("gdn_ls_m12_C128", 1, 260, 2, None, 128, False, None, True, -12.0, 0.0),
     ("kda_spikes40_C128", 1, 384, 2, None, 128, True, None, True, 0.0, 0.125),
     ("gdn_spikes40_grouped_C64", 1, 200, 1, 2, 64, False, None, True, 0.0, 0.125),
+    ("kda_sparse_spikes40_C128", 1, 512, 2, None, 128, True, None, True, 0.0, 0.02),
+    ("kda_sparse_spikes40_C64_varlen", 1, 390, 2, None, 64, True, (70, 320), True, 1.0, 0.02),
 ]
 
 
