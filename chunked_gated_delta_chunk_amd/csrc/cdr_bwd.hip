@@ -49,7 +49,7 @@ enum Mat {
     AH, A2M, TT, WW, UU, PP, PT, BB, BD, YY,                // prep
     SIN, DS,                                                // chains
     DL, DDL, DA2, DA2T, DQD, DKG, DWM, DTM, DBT, DKT, XX,   // local
-    DAM, GG, GT, RR, CC, R2, C2, DGM, DQH, DKH, DGS,
+    DAM, GG, GT, RR, CC, R2, C2, DGM, DGS,
     NMAT
 };
 
@@ -943,74 +943,44 @@ __global__ __launch_bounds__(BTHREADS) __attribute__((amdgpu_waves_per_eu(4))) v
     }
     __syncthreads();
 
-    // ---- assembly: gradients of the normalised q, k and of gamma; dv (two elements per
-    // thread per round, loads first)
+    // ---- per row (a wave per row, two key dimensions per lane): the gradients of the
+    // normalised q and k, the part of dgamma the scan below needs, dv, dbeta, and dq, dk (raw,
+    // through the normalisation)
     {
         const float *Rp = mat(w, ch, RR), *Cp = mat(w, ch, CC), *R2p = mat(w, ch, R2), *C2p = mat(w, ch, C2);
         const float* DA2d = mat(w, ch, DA2);
         const float *DQDp = mat(w, ch, DQD), *DKGp = mat(w, ch, DKG), *DKTp = mat(w, ch, DKT), *DBTp = mat(w, ch, DBT);
-        const float *QDp = mat(w, ch, QD), *KDp = mat(w, ch, KDM), *KGp = mat(w, ch, KG);
-        float *DQHp = mat(w, ch, DQH), *DKHp = mat(w, ch, DKH), *DGMp = mat(w, ch, DGM);
-        for (int e0 = tid; e0 < C * 128; e0 += 2 * BTHREADS) {
-            float gm[2], kf[2], qf[2], dkt[2], dqd[2], dkg[2], rr[2], cc[2], r2[2], c2[2], qd[2], kd[2], kg[2], dbt[2];
-#pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                const int e = e0 + u * BTHREADS;
-                gm[u] = gam[e];
-                kf[u] = KFp[e];
-                qf[u] = QFp[e];
-                dkt[u] = DKTp[e];
-                dqd[u] = DQDp[e];
-                dkg[u] = DKGp[e];
-                rr[u] = Rp[e];
-                cc[u] = Cp[e];
-                r2[u] = R2p[e];
-                c2[u] = C2p[e];
-                qd[u] = QDp[e];
-                kd[u] = KDp[e];
-                kg[u] = KGp[e];
-                dbt[u] = DBTp[e];
-            }
-#pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                const int e = e0 + u * BTHREADS, i = e >> 7, d = e & 127;
-                const float eg = ex(gm[u]), egc = ex(sGC[d] - gm[u]), b = sBeta[i];
-                const float dkd = b * dkt[u];
-                const float a2d = DA2d[i * 129];   // dA2_ii
-                DQHp[e] = scale * (r2[u] + a2d * kf[u]) + scale * eg * dqd[u];
-                DKHp[e] = rr[u] + cc[u] + scale * (c2[u] + a2d * qf[u]) + eg * dkd + egc * dkg[u];
-                // dgamma_i without the kg_i dkg_i term: in dg that term and its part of dgamma_C
-                // sum to the prefix over earlier rows (taken in the scan below)
-                DGMp[e] = kf[u] * rr[u] - kf[u] * cc[u] + scale * (qf[u] * r2[u] - kf[u] * c2[u]) + qd[u] * dqd[u] +
-                          kd[u] * dkd;
-                if (i < rows) in.dv[((tok0 + i) * H + hv) * VD + d] = b * dbt[u];
-            }
-        }
-    }
-    __syncthreads();
-    // ---- per row (a wave per row, two key dimensions per lane): dbeta, dq, dk (raw, through
-    // the normalisation)
-    {
-        const float *DBTp = mat(w, ch, DBT), *VFp = mat(w, ch, VF), *DKTp = mat(w, ch, DKT), *KDp = mat(w, ch, KDM);
+        const float *QDp = mat(w, ch, QD), *KDp = mat(w, ch, KDM), *VFp = mat(w, ch, VF);
         const float *DAp = mat(w, ch, DAM), *AHp = mat(w, ch, AH);
-        const float *DQHp = mat(w, ch, DQH), *DKHp = mat(w, ch, DKH);
-        for (int i = wave; i < rows; i += BWAVES) {
-            const size_t tok = tok0 + i;
+        float* DGMp = mat(w, ch, DGM);
+        for (int i = wave; i < C; i += BWAVES) {
             const int r = i * 128;
+            const float b = sBeta[i];
+            const float a2d = DA2d[i * 129];   // dA2_ii
             float db = 0.f, dotq = 0.f, dotk = 0.f;
             float gq[2], gk[2], qv[2], kv[2];
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
-                const int d = lane + 64 * h;
-                db += DBTp[r + d] * VFp[r + d] + DKTp[r + d] * KDp[r + d];
-                if (d < i) db += DAp[r + d] * AHp[r + d];
-                gq[h] = DQHp[r + d];
-                gk[h] = DKHp[r + d];
-                qv[h] = QFp[r + d];
-                kv[h] = KFp[r + d];
-                dotq += qv[h] * gq[h];
-                dotk += kv[h] * gk[h];
+                const int d = lane + 64 * h, e = r + d;
+                const float gm = gam[e], kf = KFp[e], qf = QFp[e], dkt = DKTp[e], dqd = DQDp[e], dkg = DKGp[e];
+                const float rr = Rp[e], cc = Cp[e], r2 = R2p[e], c2 = C2p[e], qd = QDp[e], kd = KDp[e];
+                const float dbt = DBTp[e], vf = VFp[e];
+                const float dah = d < i ? DAp[e] * AHp[e] : 0.f;
+                const float eg = ex(gm), egc = ex(sGC[d] - gm);
+                const float dkd = b * dkt;
+                gq[h] = scale * (r2 + a2d * kf) + scale * eg * dqd;
+                gk[h] = rr + cc + scale * (c2 + a2d * qf) + eg * dkd + egc * dkg;
+                // dgamma_i without the kg_i dkg_i term: in dg that term and its part of dgamma_C
+                // sum to the prefix over earlier rows (taken in the scan below)
+                DGMp[e] = kf * rr - kf * cc + scale * (qf * r2 - kf * c2) + qd * dqd + kd * dkd;
+                if (i < rows) in.dv[((tok0 + i) * H + hv) * VD + d] = b * dbt;
+                db += dbt * vf + dkt * kd + dah;
+                qv[h] = qf;
+                kv[h] = kf;
+                dotq += qf * gq[h];
+                dotk += kf * gk[h];
             }
+            if (i >= rows) continue;   // the same in every lane of the wave
 #pragma unroll
             for (int m = 1; m < 64; m <<= 1) {
                 db += __shfl_xor(db, m, 64);
@@ -1019,6 +989,7 @@ __global__ __launch_bounds__(BTHREADS) __attribute__((amdgpu_waves_per_eu(4))) v
                     dotk += __shfl_xor(dotk, m, 64);
                 }
             }
+            const size_t tok = tok0 + i;
             if (lane == 0) in.dbeta[tok * H + hv] = db;
             float* dqo = w.dqp ? w.dqp + (tok * H + hv) * KD : in.dq + (tok * Hk + hk) * KD;
             float* dko = w.dkp ? w.dkp + (tok * H + hv) * KD : in.dk + (tok * Hk + hk) * KD;
@@ -1035,18 +1006,20 @@ __global__ __launch_bounds__(BTHREADS) __attribute__((amdgpu_waves_per_eu(4))) v
             }
         }
     }
-    // ---- per key dimension: dg.  With dgamma_i' = dgamma_i + kg_i dkg_i (what the assembly left
-    // in DGM) and dgamma_C = sum_i kg_i dkg_i + e^gamma_C (S_in . dS_out), the reverse prefix sum
+    __syncthreads();
+    // ---- per key dimension: dg.  With dgamma_i' = dgamma_i + kg_i dkg_i (what the rows above
+    // left in DGM) and dgamma_C = sum_i kg_i dkg_i + e^gamma_C (S_in . dS_out), the reverse prefix
+    // sum
     //     dg_t = dgamma_C + sum_{i >= t} dgamma_i
     //          = e^gamma_C (S_in . dS_out) + sum_{i < t} kg_i dkg_i + sum_{i >= t} dgamma_i'
     // has no term that cancels: for strong gates every term is small where dg is, instead of the
     // difference of O(1) sums.
     {
-        float (*sKg)[128] = reinterpret_cast<float (*)[128]>(smem);           // [4][128], pivot panels are done
+        float (*sKg)[128] = reinterpret_cast<float (*)[128]>(smem);           // [4][128]
         float (*sSeg)[128] = reinterpret_cast<float (*)[128]>(smem) + 4;      // [4][128]
         float* sSd = reinterpret_cast<float*>(smem) + 8 * 128;
         const float *KGp = mat(w, ch, KG), *DKGp = mat(w, ch, DKG), *DGMp = mat(w, ch, DGM);
-        float* DGSp = mat(w, ch, DGS);   // per row: the prefix over earlier rows, then dg itself
+        float* DGSp = mat(w, ch, DGS);   // per-head gates: dg per row and key dimension
         // S_in . dS_out along the value columns of row d of both (a wave per row)
         for (int d = wave; d < 128; d += BWAVES) {
             float x = SINp[d * 128 + lane] * DSp[d * 128 + lane] + SINp[d * 128 + lane + 64] * DSp[d * 128 + lane + 64];
@@ -1054,15 +1027,18 @@ __global__ __launch_bounds__(BTHREADS) __attribute__((amdgpu_waves_per_eu(4))) v
             for (int m = 1; m < 64; m <<= 1) x += __shfl_xor(x, m, 64);
             if (lane == 0) sSd[d] = x;
         }
-        // thread (d, part): rows part * C/4 .. + C/4 - 1
+        // thread (d, part): rows part * C/4 .. + C/4 - 1, their terms held in registers
         constexpr int SEG = C / 4;
         const int d = tid & 127, part = tid >> 7, i0 = part * SEG;
+        float kgd[SEG], dgm[SEG];
         float kgsum = 0.f, seg = 0.f;
-#pragma unroll 8
+#pragma unroll
         for (int u = 0; u < SEG; ++u) {
             const int i = i0 + u;
-            kgsum += KGp[i * 128 + d] * DKGp[i * 128 + d];
-            seg += (i < rows) ? DGMp[i * 128 + d] : 0.f;
+            kgd[u] = KGp[i * 128 + d] * DKGp[i * 128 + d];
+            dgm[u] = (i < rows) ? DGMp[i * 128 + d] : 0.f;
+            kgsum += kgd[u];
+            seg += dgm[u];
         }
         sKg[part][d] = kgsum;
         sSeg[part][d] = seg;
@@ -1071,17 +1047,17 @@ __global__ __launch_bounds__(BTHREADS) __attribute__((amdgpu_waves_per_eu(4))) v
         for (int p2 = 0; p2 < part; ++p2) pre += sKg[p2][d];
         float acc = ex(sGC[d]) * sSd[d];                   // dgamma_i' over the rows after it, and
         for (int p2 = part + 1; p2 < 4; ++p2) acc += sSeg[p2][d];   // the state-decay term
-#pragma unroll 8
+#pragma unroll
         for (int u = 0; u < SEG; ++u) {                    // exclusive prefix, rows ascending
-            const int i = i0 + u;
-            DGSp[i * 128 + d] = pre;
-            pre += KGp[i * 128 + d] * DKGp[i * 128 + d];
+            const float t = kgd[u];
+            kgd[u] = pre;
+            pre += t;
         }
-#pragma unroll 8
+#pragma unroll
         for (int u = SEG - 1; u >= 0; --u) {               // suffix, rows descending
             const int i = i0 + u;
-            acc += (i < rows) ? DGMp[i * 128 + d] : 0.f;
-            const float dgv = acc + DGSp[i * 128 + d];
+            acc += dgm[u];
+            const float dgv = acc + kgd[u];
             if (i < rows) {
                 if (PER_DIM) in.dg[((tok0 + i) * H + hv) * KD + d] = dgv;
                 else DGSp[i * 128 + d] = dgv;
