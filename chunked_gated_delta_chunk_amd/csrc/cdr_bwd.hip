@@ -48,8 +48,8 @@ enum Mat {
     KF, QF, VF, DOF, GAM, QD, KDM, KG, BKD, BV,             // inputs and decayed inputs
     AH, A2M, TT, WW, UU, PP, PT, BB, BD, YY,                // prep
     SIN, DS,                                                // chains
-    DL, DDL, DA2, DA2T, DQD, DKG, DWM, DTM, DBT, DKT, XX,   // local
-    DAM, GG, GT, RR, CC, R2, C2, DGM, DGS,
+    DL, DDL, DA2, DQD, DKG, DWM, DTM, DBT, DKT, XX,         // local
+    GG, RR, CC, R2, C2, DGM, DGS,
     NMAT
 };
 
@@ -704,6 +704,7 @@ __global__ __launch_bounds__(BTHREADS) __attribute__((amdgpu_waves_per_eu(4))) v
     constexpr int SMEM = SMEM0 > GEMM_BYTES ? SMEM0 : GEMM_BYTES;
     __shared__ __attribute__((aligned(16))) unsigned char smem[SMEM];
     __shared__ float sBeta[128], sGC[128];
+    __shared__ float sDbA[(C / 16) * 128];   // dbeta's dA . A-hat term, [column block][row]
 
     const int slot = blockIdx.x, hv = blockIdx.y;
     int64_t tok0;
@@ -733,7 +734,6 @@ __global__ __launch_bounds__(BTHREADS) __attribute__((amdgpu_waves_per_eu(4))) v
     {
         float* DDLp = mat(w, ch, DDL);
         float* DA2p = mat(w, ch, DA2);
-        float* DA2Tp = mat(w, ch, DA2T);
         float* DQDp = mat(w, ch, DQD);
         float* DKGp = mat(w, ch, DKG);
         const float* DOp = mat(w, ch, DOF);
@@ -743,7 +743,6 @@ __global__ __launch_bounds__(BTHREADS) __attribute__((amdgpu_waves_per_eu(4))) v
         gemm1<C, C>(vw(DOp, 128, 1), vw(DLp, 128, 1), VD, smem, [&](int m, int n, float x) {
             const float y = (n <= m) ? x : 0.f;
             DA2p[m * 128 + n] = y;
-            DA2Tp[n * 128 + m] = y;
         });
         gemm1<C, 128>(vw(DOp, 128, 1), vw(SINp, 128, 1), VD, smem,
                       [&](int m, int n, float x) { DQDp[m * 128 + n] = x; });
@@ -779,16 +778,18 @@ __global__ __launch_bounds__(BTHREADS) __attribute__((amdgpu_waves_per_eu(4))) v
                     [&](int m, int n, float x) { Xp[m * 128 + n] = x; });
     }
     __syncthreads();
-    // dA = -(X T^T) (j < i);  G = beta_i dA (and its transpose)
+    // dA = -(X T^T) (j < i);  G = beta_i dA;  and dbeta's term sum_j dA_ij A-hat_ij, per row and
+    // 16-column block (the block's 16 lanes reduced; every lane of the wave takes part)
     {
-        float* DAp = mat(w, ch, DAM);
         float* Gp = mat(w, ch, GG);
-        float* GTp = mat(w, ch, GT);
+        const float* AHp = mat(w, ch, AH);
         gemm1<C, C>(vw(mat(w, ch, XX), 128, 1), vw(mat(w, ch, TT), 128, 1), C, smem, [&](int m, int n, float x) {
             const float da = (n < m) ? -x : 0.f;
-            DAp[m * 128 + n] = da;
             Gp[m * 128 + n] = sBeta[m] * da;
-            GTp[n * 128 + m] = sBeta[m] * da;
+            float t = da * AHp[m * 128 + n];
+#pragma unroll
+            for (int o = 1; o < 16; o <<= 1) t += __shfl_xor(t, o, 64);
+            if ((n & 15) == 0) sDbA[(n >> 4) * 128 + m] = t;
         });
     }
     __syncthreads();
@@ -864,7 +865,7 @@ __global__ __launch_bounds__(BTHREADS) __attribute__((amdgpu_waves_per_eu(4))) v
     __syncthreads();
     {
         const int n = lane & 15, kq = lane >> 4, d = 16 * wave + n;
-        const float *Gp = mat(w, ch, GG), *DA2p = mat(w, ch, DA2), *GTp = mat(w, ch, GT), *DA2Tp = mat(w, ch, DA2T);
+        const float *Gp = mat(w, ch, GG), *DA2p = mat(w, ch, DA2);
         float *Rp = mat(w, ch, RR), *R2p = mat(w, ch, R2), *Cp = mat(w, ch, CC), *C2p = mat(w, ch, C2);
         // A fragment: row `row` of M, columns col .. col + 7, the diagonal element zeroed if asked
         auto afrag = [&](const float* M, int row, int col, bool nodiag, bf16x8& h, bf16x8& l) {
@@ -873,6 +874,14 @@ __global__ __launch_bounds__(BTHREADS) __attribute__((amdgpu_waves_per_eu(4))) v
             float x[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
 #pragma unroll
             for (int t = 0; t < 8; ++t) x[t] = (nodiag && col + t == row) ? 0.f : x[t];
+            split8(x, h, l);
+        };
+        // the same from the transposed matrix: column `row` of M, rows col .. col + 7 (16 lanes
+        // read 16 consecutive columns of a row)
+        auto afragT = [&](const float* M, int row, int col, bool nodiag, bf16x8& h, bf16x8& l) {
+            float x[8];
+#pragma unroll
+            for (int t = 0; t < 8; ++t) x[t] = (nodiag && col + t == row) ? 0.f : M[(col + t) * 128 + row];
             split8(x, h, l);
         };
         // rows of tile I against the rows j < lim: the earlier tiles, and the tile itself when
@@ -926,10 +935,10 @@ __global__ __launch_bounds__(BTHREADS) __attribute__((amdgpu_waves_per_eu(4))) v
                 }
                 bf16x8 bh, bl, ah, al;
                 split8(bk, bh, bl);
-                afrag(GTp, 16 * J + n, i0, false, ah, al);
+                afragT(Gp, 16 * J + n, i0, false, ah, al);
                 ac = mfma3(ah, al, bh, bl, ac);
                 split8(bq, bh, bl);
-                afrag(DA2Tp, 16 * J + n, i0, true, ah, al);
+                afragT(DA2p, 16 * J + n, i0, true, ah, al);
                 ac2 = mfma3(ah, al, bh, bl, ac2);
             }
 #pragma unroll
@@ -951,7 +960,6 @@ __global__ __launch_bounds__(BTHREADS) __attribute__((amdgpu_waves_per_eu(4))) v
         const float* DA2d = mat(w, ch, DA2);
         const float *DQDp = mat(w, ch, DQD), *DKGp = mat(w, ch, DKG), *DKTp = mat(w, ch, DKT), *DBTp = mat(w, ch, DBT);
         const float *QDp = mat(w, ch, QD), *KDp = mat(w, ch, KDM), *VFp = mat(w, ch, VF);
-        const float *DAp = mat(w, ch, DAM), *AHp = mat(w, ch, AH);
         float* DGMp = mat(w, ch, DGM);
         for (int i = wave; i < C; i += BWAVES) {
             const int r = i * 128;
@@ -965,7 +973,6 @@ __global__ __launch_bounds__(BTHREADS) __attribute__((amdgpu_waves_per_eu(4))) v
                 const float gm = gam[e], kf = KFp[e], qf = QFp[e], dkt = DKTp[e], dqd = DQDp[e], dkg = DKGp[e];
                 const float rr = Rp[e], cc = Cp[e], r2 = R2p[e], c2 = C2p[e], qd = QDp[e], kd = KDp[e];
                 const float dbt = DBTp[e], vf = VFp[e];
-                const float dah = d < i ? DAp[e] * AHp[e] : 0.f;
                 const float eg = ex(gm), egc = ex(sGC[d] - gm);
                 const float dkd = b * dkt;
                 gq[h] = scale * (r2 + a2d * kf) + scale * eg * dqd;
@@ -974,7 +981,7 @@ __global__ __launch_bounds__(BTHREADS) __attribute__((amdgpu_waves_per_eu(4))) v
                 // sum to the prefix over earlier rows (taken in the scan below)
                 DGMp[e] = kf * rr - kf * cc + scale * (qf * r2 - kf * c2) + qd * dqd + kd * dkd;
                 if (i < rows) in.dv[((tok0 + i) * H + hv) * VD + d] = b * dbt;
-                db += dbt * vf + dkt * kd + dah;
+                db += dbt * vf + dkt * kd;
                 qv[h] = qf;
                 kv[h] = kf;
                 dotq += qf * gq[h];
@@ -989,6 +996,8 @@ __global__ __launch_bounds__(BTHREADS) __attribute__((amdgpu_waves_per_eu(4))) v
                     dotk += __shfl_xor(dotk, m, 64);
                 }
             }
+#pragma unroll
+            for (int J = 0; J < C / 16; ++J) db += sDbA[J * 128 + i];
             const size_t tok = tok0 + i;
             if (lane == 0) in.dbeta[tok * H + hv] = db;
             float* dqo = w.dqp ? w.dqp + (tok * H + hv) * KD : in.dq + (tok * Hk + hk) * KD;
