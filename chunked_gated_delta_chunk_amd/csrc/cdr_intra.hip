@@ -50,10 +50,14 @@ namespace cdr {
 
 constexpr float L2N_EPS = 1e-6f;  // in-kernel q/k normalisation: x / sqrt(|x|^2 + eps)
 // Largest gate span (|gamma_i - gamma_m| over a 16-row tile and its middle row m) for which the
-// tile-middle pivot factors exp(+-(gamma_i - gamma_m)) are used: they stay below e^64, so the
-// decayed operands, even times a large key, and their products stay finite in fp32.  A chunk
-// with a wider tile takes pivots that make every factor <= 1 and exact diagonal tiles.
-constexpr float SAFE_SPAN = 64.f;
+// tile-middle pivot factors exp(+-(gamma_i - gamma_m)) are used.  A row factor and a column factor
+// are then at most e^32 each, so nothing overflows, and when the pivot ratio F between two tile
+// middles underflows fp32 (below e^-87), the pair it belongs to has a true decay below
+// e^(2 * 32 - 87) = e^-23, small enough to drop.  With a larger limit two moderate tiles could
+// compensate a flushed F: g = -40 at rows 30 and 33 of a chunk puts 93 between the middles of
+// tiles 1 and 2 while rows 30..32 stay close.  A chunk with a wider tile takes pivots that make
+// every factor <= 1 and exact diagonal tiles.
+constexpr float SAFE_SPAN = 32.f;
 constexpr int IMAXTHREADS = 512;  // the largest workgroup (C = 128)
 
 template <int C>

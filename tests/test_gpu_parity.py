@@ -220,6 +220,41 @@ def test_strong_gates_with_l2norm_and_grouped_heads():
     check(inp, label="kda_ls_m12_l2n_gva", l2n=True)
 
 
+# Two g = -40 tokens on either side of a tile boundary (rows 30 and 33 of a chunk): each tile is
+# narrow on its own (a half-tile span near 46), but 93 in gamma separates the two tile middles
+# while rows 30..32 stay close.  A pivot ratio between the middles underflows there, and the
+# pairs it carries must not be lost: with a half-tile limit of 64 row 32's o was 25-80 % off
+# (relative to the row's largest element), still inside the 1e-2 absolute floor.  Checked also
+# against the row's own scale.
+STRADDLE = [
+    # label, T, C, per_dim, spike rows (chunk-relative, every chunk), initial state
+    ("kda_C64_rows30_33", 64, 64, True, (30, 33), False),
+    ("kda_C128_rows30_33", 128, 128, True, (30, 33), False),
+    ("kda_C128_rows62_65_94_97", 384, 128, True, (62, 65, 94, 97), True),
+    ("kda_C64_rows14_17_46_49", 320, 64, True, (14, 17, 46, 49), True),
+    ("gdn_C64_rows30_33", 192, 64, False, (30, 33), True),
+]
+
+
+@pytest.mark.parametrize("case", STRADDLE, ids=[c[0] for c in STRADDLE])
+def test_spikes_straddling_a_tile_boundary(case):
+    label, T, C, per_dim, rows, init = case
+    inp = make_inputs(1, T, 2, seed=470 + T, per_dim_gate=per_dim, initial_state=init, chunk_size=C)
+    g = inp.g.clone()
+    for c0 in range(0, T, C):
+        for r in rows:
+            if c0 + r < T:
+                g[0, c0 + r] = -40.0
+    inp.g = g
+    o, S = check(inp, label=label)
+    o_ref, _ = oracle_ref(inp)
+    err = np.abs(o.float().cpu().numpy().astype(np.float64) - o_ref).max(axis=-1)
+    row_scale = np.abs(o_ref).max(axis=-1) + 1e-30
+    worst = float((err / row_scale).max())
+    note(f"[parity] {label}: worst o error relative to its row's scale {worst:.3f}")
+    assert worst <= 0.1
+
+
 # ---------------------------------------------------------------- invariants of the GPU path
 def test_repeat_runs_are_bit_identical_and_workspace_independent():
     inp = make_inputs(1, 1000, 4, seed=9, initial_state=True, chunk_size=128, gate_mean=2.0)

@@ -1,0 +1,107 @@
+"""Seeded sweep over mixed configurations, forward and backward, through the C interface.
+
+Each case draws its shape and options from a fixed seed: chunk size, gate kind, head count and
+grouping, fixed-length batches or packed sequences (empty ones included), initial state, gate
+strength (weak gates that carry the state, ordinary ones, and isolated g = -40 tokens), and
+in-kernel q/k normalisation.  The bars are those of the other parity tests: the forward against
+the fp64 per-token recurrence element by element (o 1e-2, S 1e-3, page "PyPTO-Gym 的 chunk_kda
+算子实战", section 支持的 dtype 与形状约束), the backward by norm ratio against the fp64 gradient
+of the same rule (5e-3, page "flash-linear-attention KCP 精度失效根因排查手册", section 验收标准).
+"""
+import random
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle.backward import recurrent_bwd, norm_ratio
+import chunked_gated_delta_chunk_amd as cdr
+from chunked_gated_delta_chunk_amd.synth import make_inputs
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+O_TOL, S_TOL, G_TOL = 1e-2, 1e-3, 5e-3
+
+
+def draw(seed, max_T, max_heads):
+    rng = random.Random(seed)
+    c = dict(C=rng.choice([64, 128]), per_dim=rng.random() < 0.7, H=rng.choice([1, 2, 3]))
+    c["HV"] = c["H"] * rng.choice([1, 1, 2])
+    if c["HV"] > max_heads:
+        c["HV"] = c["H"]
+    if rng.random() < 0.4:
+        n = rng.randint(1, 6)
+        lengths = [rng.choice([0, rng.randint(1, 40), rng.randint(1, max_T // 2)]) for _ in range(n)]
+        if sum(lengths) == 0:
+            lengths[-1] = 1
+        c.update(B=1, lengths=tuple(lengths), T=sum(lengths))
+    else:
+        c.update(B=rng.choice([1, 2]), lengths=None, T=rng.randint(1, max_T))
+    c.update(init=rng.random() < 0.7, gate_mean=rng.choice([-2.0, 0.0, 2.0, 4.0]), l2n=rng.random() < 0.3,
+             spikes=rng.choice([0.0, 0.0, 0.05]))
+    return c
+
+
+def inputs(c, seed):
+    return make_inputs(c["B"], c["T"], c["H"], seed=seed, per_dim_gate=c["per_dim"], lengths=c["lengths"],
+                       initial_state=c["init"], chunk_size=c["C"], gate_mean=c["gate_mean"], HV=c["HV"],
+                       normalise=not c["l2n"], spike_prob=c["spikes"])
+
+
+def ratio(x, ref, tol):
+    x = np.asarray(x, dtype=np.float64)
+    return float(np.max(np.abs(x - ref) / (tol + tol * np.abs(ref)))) if ref.size else 0.0
+
+
+@pytest.mark.parametrize("case", range(24))
+def test_forward_sweep(case):
+    c = draw(7000 + case, max_T=700, max_heads=6)
+    print(f"[sweep fwd {case}] {c}", file=sys.stderr, flush=True)
+    inp = inputs(c, 7100 + case)
+    d = inp.to(DEV)
+    N = d.q.shape[0] if d.cu_seqlens is None else d.cu_seqlens.numel() - 1
+    out = torch.full(tuple(d.v.shape), float("nan"), dtype=torch.bfloat16, device=DEV)
+    fs = torch.full((N, c["HV"], 128, 128), float("nan"), dtype=torch.float32, device=DEV)
+    o, S = cdr.chunk_dr_fwd(d.q, d.k, d.v, d.g, d.beta, initial_state=d.initial_state, cu_seqlens=d.cu_seqlens,
+                            chunk_size=c["C"], output_final_state=True, out=out, final_state_out=fs,
+                            use_qk_l2norm_in_kernel=c["l2n"])
+    torch.cuda.synchronize()
+    assert torch.isfinite(o.float()).all() and torch.isfinite(S).all()
+    o_ref, S_ref = oracle.recurrent_fwd(inp.q, inp.k, inp.v, inp.g, inp.beta, initial_state=inp.initial_state,
+                                        cu_seqlens=inp.cu_seqlens, use_qk_l2norm=c["l2n"])
+    ro = ratio(o.float().cpu().numpy(), o_ref, O_TOL)
+    rs = ratio(S.cpu().numpy(), S_ref, S_TOL)
+    print(f"[sweep fwd {case}] o err/tol {ro:.3f}  S err/tol {rs:.3f}", file=sys.stderr, flush=True)
+    assert ro <= 1.0 and rs <= 1.0
+
+
+@pytest.mark.parametrize("case", range(10))
+def test_backward_sweep(case):
+    c = draw(8000 + case, max_T=300, max_heads=4)
+    print(f"[sweep bwd {case}] {c}", file=sys.stderr, flush=True)
+    inp = inputs(c, 8100 + case)
+    gen = torch.Generator("cpu").manual_seed(8200 + case)
+    N = inp.q.shape[0] if inp.cu_seqlens is None else inp.cu_seqlens.numel() - 1
+    do = torch.randn(tuple(inp.v.shape), generator=gen).to(torch.bfloat16)
+    dht = 0.1 * torch.randn(N, c["HV"], 128, 128, generator=gen)
+    d = inp.to(DEV)
+    got = cdr.chunk_dr_bwd(d.q, d.k, d.v, d.g, d.beta, do.to(DEV), dht=dht.to(DEV), initial_state=d.initial_state,
+                           cu_seqlens=d.cu_seqlens, chunk_size=c["C"], use_qk_l2norm_in_kernel=c["l2n"])
+    torch.cuda.synchronize()
+    names = ("dq", "dk", "dv", "dg", "dbeta", "dh0")
+    got = dict(zip(names, (None if t is None else t.cpu().numpy() for t in got)))
+    ref = recurrent_bwd(inp.q, inp.k, inp.v, inp.g, inp.beta, do, dht=dht, initial_state=inp.initial_state,
+                        cu_seqlens=inp.cu_seqlens, use_qk_l2norm=c["l2n"])
+    worst = {}
+    for name in names:
+        if got[name] is None:
+            assert inp.initial_state is None and name == "dh0"
+            continue
+        assert np.isfinite(got[name]).all(), name
+        worst[name] = norm_ratio(got[name], ref[name])
+    print(f"[sweep bwd {case}] " + "  ".join(f"{k} {v:.2e}" for k, v in worst.items()), file=sys.stderr, flush=True)
+    for k, v in worst.items():
+        assert v <= G_TOL, f"{k} norm ratio {v:.3e}"
