@@ -224,8 +224,8 @@ def test_strong_gates_with_l2norm_and_grouped_heads():
 # narrow on its own (a half-tile span near 46), but 93 in gamma separates the two tile middles
 # while rows 30..32 stay close.  A pivot ratio between the middles underflows there, and the
 # pairs it carries must not be lost: with a half-tile limit of 64 row 32's o was 25-80 % off
-# (relative to the row's largest element), still inside the 1e-2 absolute floor.  Checked also
-# against the row's own scale.
+# (relative to the largest |o| of the rows around it), still inside the 1e-2 absolute floor.
+# Checked also against that local scale.
 STRADDLE = [
     # label, T, C, per_dim, spike rows (chunk-relative, every chunk), initial state
     ("kda_C64_rows30_33", 64, 64, True, (30, 33), False),
@@ -249,10 +249,11 @@ def test_spikes_straddling_a_tile_boundary(case):
     o, S = check(inp, label=label)
     o_ref, _ = oracle_ref(inp)
     err = np.abs(o.float().cpu().numpy().astype(np.float64) - o_ref).max(axis=-1)
-    row_scale = np.abs(o_ref).max(axis=-1) + 1e-30
-    worst = float((err / row_scale).max())
-    note(f"[parity] {label}: worst o error relative to its row's scale {worst:.3f}")
-    assert worst <= 0.1
+    m = np.abs(o_ref).max(axis=-1)   # [B, T, H]: largest |o| of each row, then over rows t +- 8
+    scale = np.stack([m[:, max(0, t - 8):t + 9].max(axis=1) for t in range(m.shape[1])], axis=1) + 1e-30
+    worst = float((err / scale).max())
+    note(f"[parity] {label}: worst o error relative to the local scale of o {worst:.4f}")
+    assert worst <= 0.05
 
 
 # ---------------------------------------------------------------- invariants of the GPU path
