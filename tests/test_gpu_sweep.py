@@ -124,11 +124,21 @@ def test_forward_sweep_harsh_gates(case):
     assert row <= 0.05
 
 
-@pytest.mark.parametrize("case", range(10))
+@pytest.mark.parametrize("case", range(20))
 def test_backward_sweep(case):
-    c = draw(8000 + case, max_T=300, max_heads=4)
+    """Cases 0-9 draw like the forward sweep, 10-19 with the harsh gates."""
+    c = draw(8000 + case, max_T=300, max_heads=4) if case < 10 else draw_harsh(8000 + case)
+    if case >= 10:
+        c["T"] = min(c["T"], 300)
+        if c["lengths"] is not None:
+            c["lengths"] = tuple(min(x, 100) for x in c["lengths"])
+            c["T"] = max(sum(c["lengths"]), 1)
+            if sum(c["lengths"]) == 0:
+                c["lengths"] = c["lengths"][:-1] + (1,)
     print(f"[sweep bwd {case}] {c}", file=sys.stderr, flush=True)
-    inp = inputs(c, 8100 + case)
+    inp = make_inputs(c["B"], c["T"], c["H"], seed=8100 + case, per_dim_gate=c["per_dim"], lengths=c["lengths"],
+                      initial_state=c["init"], chunk_size=c["C"], gate_mean=c["gate_mean"], HV=c["HV"],
+                      normalise=not c["l2n"], spike_prob=c["spikes"], spike_value=c.get("spike_value", -40.0))
     gen = torch.Generator("cpu").manual_seed(8200 + case)
     N = inp.q.shape[0] if inp.cu_seqlens is None else inp.cu_seqlens.numel() - 1
     do = torch.randn(tuple(inp.v.shape), generator=gen).to(torch.bfloat16)
