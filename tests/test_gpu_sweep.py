@@ -161,3 +161,36 @@ def test_backward_sweep(case):
     print(f"[sweep bwd {case}] " + "  ".join(f"{k} {v:.2e}" for k, v in worst.items()), file=sys.stderr, flush=True)
     for k, v in worst.items():
         assert v <= G_TOL, f"{k} norm ratio {v:.3e}"
+
+
+@pytest.mark.parametrize("case", range(16))
+def test_decode_sweep(case):
+    """The per-token kernel on a state pool: sequences, tokens per sequence (packed or not),
+    heads and grouping, speculative columns, padding entries, gate kind and strength, in-kernel
+    normalisation; checked as the decode tests check a pool call (untouched slots bit for bit)."""
+    from test_gpu_decode import check_pool
+    from chunked_gated_delta_chunk_amd.synth import make_decode_inputs
+    rng = random.Random(9500 + case)
+    N = rng.randint(1, 12)
+    H = rng.choice([1, 2])
+    HV = H * rng.choice([1, 2])
+    spec = rng.random() < 0.5
+    if rng.random() < 0.3:
+        lengths = tuple(rng.randint(0, 4 if spec else 6) for _ in range(N))
+        if sum(lengths) == 0:
+            lengths = lengths[:-1] + (1,)
+        T, cols = 0, (max(lengths) if spec else 0)
+    else:
+        lengths = None
+        T = rng.randint(1, 4 if spec else 6)
+        cols = rng.randint(T, 4) if spec else 0
+    padded = tuple(i for i in range(N) if rng.random() < 0.15)
+    per_dim, l2n = rng.random() < 0.7, rng.random() < 0.5
+    gm = rng.choice([-4.0, 0.0, 4.0])
+    slots = N * max(cols, 1) + rng.randint(0, 8)
+    label = (f"N{N} T{T} lengths{lengths} H{H} HV{HV} cols{cols} padded{padded} per_dim{per_dim} "
+             f"l2n{l2n} gm{gm} slots{slots}")
+    print(f"[sweep decode {case}] {label}", file=sys.stderr, flush=True)
+    d = make_decode_inputs(N, T, H, HV, slots, seed=9600 + case, index_cols=cols, per_dim_gate=per_dim,
+                           normalise=not l2n, lengths=lengths, padded=padded, gate_mean=gm)
+    check_pool(d, l2n, f"sweep {case}")
