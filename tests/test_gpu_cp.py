@@ -35,23 +35,27 @@ def ratio(x, ref, tol):
 
 
 CASES = [
-    # label, cuts, H, HV, C, per_dim, gate_mean, l2n
+    # label, cuts, H, HV, C, per_dim, gate_mean, l2n[, spike probability]
     ("kda_4_segments_C64", [0, 300, 301, 700, 1000], 2, 2, 64, True, 0.0, False),
     ("kda_weak_C128", [0, 256, 640, 900], 1, 2, 128, True, 3.0, True),
     ("gdn_grouped_C64", [0, 128, 500, 512], 1, 2, 64, False, 1.0, False),
     # no forgetting (g = 0, gate_mean None): the segment maps carry everything across segments
     ("kda_g0_C128", [0, 384, 700, 1024], 2, 2, 128, True, None, False),
     ("kda_g0_C64", [0, 130, 600, 1000], 1, 1, 64, True, None, False),
+    # isolated g = -40 tokens (1 in 20), with ordinary and with weak gates: wide and narrow tiles
+    ("kda_spikes_C64", [0, 200, 450, 700], 2, 2, 64, True, 0.0, False, 0.05),
+    ("kda_spikes_weak_C128", [0, 300, 301, 800], 1, 1, 128, True, 3.0, True, 0.02),
 ]
 
 
 @pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
 def test_segments_merge_to_the_unsplit_sequence(case):
-    label, cuts, H, HV, C, per_dim, gm, l2n = case
+    label, cuts, H, HV, C, per_dim, gm, l2n = case[:8]
+    spikes = case[8] if len(case) > 8 else 0.0
     T = cuts[-1]
     inp = make_inputs(1, T, H, seed=600 + T, per_dim_gate=per_dim, initial_state=True, chunk_size=C,
                       gate="zero" if gm is None else "logsigmoid", gate_mean=gm or 0.0, HV=HV,
-                      normalise=not l2n)
+                      normalise=not l2n, spike_prob=spikes)
     note(f"[cp] {label} T={T} segments {np.diff(cuts).tolist()} C={C}")
     d = inp.to(DEV)
     cu = torch.tensor(cuts, dtype=torch.int32)
