@@ -124,13 +124,17 @@ def workspace_bytes(p: cdr_problem) -> int:
     return load_library().cdr_workspace_bytes(ctypes.byref(p))
 
 
-def _need(t, name, dtype, shape=None):
+def _need(t, name, dtype, shape=None, dense=False):
+    """Type and shape of an argument; `dense` for a buffer the kernels write (an output or the
+    workspace), which must be contiguous since the library addresses it row-major."""
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
     if t.dtype != dtype:
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
     if shape is not None and tuple(t.shape) != tuple(shape):
         raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if dense and not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous (the kernels write it row-major)")
 
 
 def _aligned(t: Optional[torch.Tensor]) -> Optional[torch.Tensor]:
@@ -196,6 +200,10 @@ class PreparedForward:
         st = lib.cdr_check(ctypes.byref(self.problem))
         if st != CDR_OK:
             _raise(st, "chunk_dr_fwd")
+        if out is not None:
+            _need(out, "out", torch.bfloat16, (B, T, HV, V), dense=True)
+        if output_final_state and final_state_out is not None:
+            _need(final_state_out, "final_state_out", torch.float32, (N, HV, V, K), dense=True)
         device = q.device
         if device.type != "cuda":
             raise ValueError("inputs must be on a GPU device")
@@ -206,15 +214,11 @@ class PreparedForward:
         self.cu = _aligned(cu_seqlens)
         if out is None:
             out = torch.empty((B, T, HV, V), dtype=torch.bfloat16, device=device)
-        else:
-            _need(out, "out", torch.bfloat16, (B, T, HV, V))
         self.o = out
         self.S = None
         if output_final_state:
             if final_state_out is None:
                 final_state_out = torch.empty((N, HV, V, K), dtype=torch.float32, device=device)
-            else:
-                _need(final_state_out, "final_state_out", torch.float32, (N, HV, V, K))
             self.S = final_state_out
         ptr = lambda t: None if t is None else _dev_ptr(t, device)  # noqa: E731
         qq, kk, vv, gg, bb = self.inputs
@@ -230,6 +234,8 @@ class PreparedForward:
                 workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
             elif workspace.numel() * workspace.element_size() < nbytes:
                 raise ValueError("workspace too small")
+            elif not workspace.is_contiguous():
+                raise ValueError("workspace must be contiguous")
             self.workspace = workspace
             self._args = (ctypes.byref(self.problem), ptr(qq), ptr(kk), ptr(vv), ptr(gg), ptr(bb),
                           ptr(self.s0), ptr(self.cu), ptr(self.o), ptr(self.S), ptr(workspace),
@@ -569,6 +575,10 @@ class PreparedRecurrent:
         st = lib.cdr_recurrent_check(ctypes.byref(self.problem))
         if st != CDR_OK:
             _raise(st, "fused_recurrent_fwd")
+        if out is not None:
+            _need(out, "out", torch.bfloat16, (B, T, HV, V), dense=True)
+        if mode == STATE_SEPARATE and output_final_state and final_state_out is not None:
+            _need(final_state_out, "final_state_out", torch.float32, (N, HV, V, K), dense=True)
         device = q.device
         if device.type != "cuda":
             raise ValueError("inputs must be on a GPU device")
@@ -582,15 +592,11 @@ class PreparedRecurrent:
         self.pool = state_pool
         if out is None:
             out = torch.empty((B, T, HV, V), dtype=torch.bfloat16, device=device)
-        else:
-            _need(out, "out", torch.bfloat16, (B, T, HV, V))
         self.o = out
         self.S = None
         if mode == STATE_SEPARATE and output_final_state:
             if final_state_out is None:
                 final_state_out = torch.empty((N, HV, V, K), dtype=torch.float32, device=device)
-            else:
-                _need(final_state_out, "final_state_out", torch.float32, (N, HV, V, K))
             self.S = final_state_out
         ptr = lambda t: None if t is None else _dev_ptr(t, device)  # noqa: E731
         qq, kk, vv, gg, bb = self.inputs

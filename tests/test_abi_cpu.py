@@ -120,6 +120,16 @@ def test_binding_type_and_shape_errors():
                          cu_seqlens=torch.tensor([0, 8], dtype=torch.int32))
     with pytest.raises(ValueError):  # host tensors are not accepted: no CPU path exists
         cdr.chunk_dr_fwd(q, q, q, g, beta)
+    # caller-supplied outputs are written row-major: a strided view is refused before anything
+    # else happens
+    o_view = torch.zeros(B, T, K, H, dtype=torch.bfloat16).transpose(2, 3)
+    with pytest.raises(ValueError, match="contiguous"):
+        cdr.chunk_dr_fwd(q, q, q, g, beta, out=o_view)
+    s_view = torch.zeros(B, H, K, K).transpose(2, 3)
+    with pytest.raises(ValueError, match="contiguous"):
+        cdr.chunk_dr_fwd(q, q, q, g, beta, output_final_state=True, final_state_out=s_view)
+    with pytest.raises(ValueError, match="contiguous"):
+        cdr.fused_recurrent_fwd(q, q, q, g, beta, out=o_view)
 
 
 def test_no_cpu_fallback_when_library_missing(monkeypatch, tmp_path):
