@@ -242,7 +242,7 @@ template <int C, bool PER_DIM, bool L2N>
 __global__ __launch_bounds__(BTHREADS) __attribute__((amdgpu_waves_per_eu(4))) void bwd_prep_kernel(In in, ChunkMap map, int H, int Hk, float scale, Work w) {
     constexpr int NT = C / 16;
     constexpr int P2 = 128 + 8;                     // pitch of pivot panels
-    constexpr int INV_BYTES = (C * (C + 1) + 16 * C) * 4;   // A then T in place (pitch C + 1), X (16 x C)
+    constexpr int INV_BYTES = C * (C + 1) * 4;   // A then T in place (pitch C + 1)
     constexpr int PIV_BYTES = 4 * 16 * P2 * 2 + 128 * 4;
     constexpr int GEMM_BYTES = 256 * LDP * 2 * 2;
     constexpr int SMEM = (INV_BYTES > PIV_BYTES ? (INV_BYTES > GEMM_BYTES ? INV_BYTES : GEMM_BYTES)
@@ -483,14 +483,15 @@ __global__ __launch_bounds__(BTHREADS) __attribute__((amdgpu_waves_per_eu(4))) v
     }
     __syncthreads();
 
-    // ---- T = (I + A)^-1, A = beta_i A-hat (strictly lower), blocked by 16-row tiles in fp32,
-    // in place: each block of T replaces the block of A it is computed from (A_{I, <I} is last
-    // read to form X = A_{I, <I} T_{<I, <I}, and the diagonal block's column substitution
-    // only reads rows above the one it writes)
+    // ---- T = (I + A)^-1, A = beta_i A-hat (strictly lower), blocked by 16-row tiles, in place:
+    // each block of T replaces the block of A it is computed from.  The diagonal blocks by
+    // forward substitution in fp32 (a block's column substitution only reads rows above the one
+    // it writes); then row block by row block, X_IJ = sum_{J <= K < I} A_IK T_KJ (T's unit
+    // diagonal inserted) and T_IJ = -T_II X_IJ on split-bf16 16x16x16 MFMAs, wave J taking
+    // tile (I, J), all X of a row block formed before any of its A blocks is overwritten.
     {
         constexpr int LP = C + 1;
         float* sT = reinterpret_cast<float*>(smem);
-        float* sX = sT + C * LP;
         const float* AHp = mat(w, ch, AH);
         for (int e = tid; e < C * C; e += BTHREADS) {
             const int i = e / C, j = e % C;
@@ -517,20 +518,55 @@ __global__ __launch_bounds__(BTHREADS) __attribute__((amdgpu_waves_per_eu(4))) v
             }
         }
         __syncthreads();
+        // lane (r16, q4): A operand row r16, columns 4 q4 .. + 3; B operand rows 4 q4 .. + 3,
+        // column r16; accumulator rows 4 q4 + e, column r16
+        const int r16 = lane & 15, q4 = lane >> 4;
+        auto split4 = [](float a, float b, float c, float d, bf16x4& h, bf16x4& l) {
+            uint2 hh, ll;
+            split_pk(a, b, hh.x, ll.x);
+            split_pk(c, d, hh.y, ll.y);
+            h = __builtin_bit_cast(bf16x4, hh);
+            l = __builtin_bit_cast(bf16x4, ll);
+        };
         for (int I = 1; I < NT; ++I) {
-            const int o = 16 * I;
-            for (int e = tid; e < 16 * o; e += BTHREADS) {
-                const int r = e / o, col = e % o;
-                float s = sT[(o + r) * LP + col];             // A[o+r][col] * T[col][col] (= 1)
-                for (int j = col + 1; j < o; ++j) s += sT[(o + r) * LP + j] * sT[j * LP + col];
-                sX[r * C + col] = s;
+            const int o = 16 * I, J = wave;
+            f32x4 x = {0.f, 0.f, 0.f, 0.f};
+            if (J < I) {
+                for (int K = J; K < I; ++K) {
+                    const float* ar = sT + (o + r16) * LP + 16 * K + 4 * q4;
+                    float t[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int kr = 4 * q4 + e;   // row of block T_KJ; T_JJ holds 0 on its diagonal
+                        const float v = sT[(16 * K + kr) * LP + 16 * J + r16];
+                        t[e] = (K == J && kr == r16) ? 1.f : v;
+                    }
+                    bf16x4 ah, al, bh, bl;
+                    split4(ar[0], ar[1], ar[2], ar[3], ah, al);
+                    split4(t[0], t[1], t[2], t[3], bh, bl);
+                    x = mfma16(ah, bh, x);
+                    x = mfma16(al, bh, x);
+                    x = mfma16(ah, bl, x);
+                }
             }
             __syncthreads();
-            for (int e = tid; e < 16 * o; e += BTHREADS) {
-                const int r = e / o, col = e % o;
-                float s = sX[r * C + col];                    // T[r][r] = 1
-                for (int j = 0; j < r; ++j) s += sT[(o + r) * LP + o + j] * sX[j * C + col];
-                sT[(o + r) * LP + col] = -s;
+            if (J < I) {
+                float d[4];   // T_II, row r16, columns 4 q4 .. + 3 (unit lower)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int c = 4 * q4 + e;
+                    const float v = sT[(o + r16) * LP + o + c];
+                    d[e] = c < r16 ? v : (c == r16 ? 1.f : 0.f);
+                }
+                bf16x4 ah, al, bh, bl;
+                split4(d[0], d[1], d[2], d[3], ah, al);
+                split4(x[0], x[1], x[2], x[3], bh, bl);   // X_IJ: its accumulator layout is the B operand's
+                f32x4 t = {0.f, 0.f, 0.f, 0.f};
+                t = mfma16(ah, bh, t);
+                t = mfma16(al, bh, t);
+                t = mfma16(ah, bl, t);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) sT[(o + 4 * q4 + e) * LP + 16 * J + r16] = -t[e];
             }
             __syncthreads();
         }
