@@ -45,7 +45,7 @@ constexpr float SAFE_SPAN = 32.f;
 
 // per (chunk, value head) matrices, each 128 x 128 fp32 with row pitch 128
 enum Mat {
-    KF, QF, VF, DOF, GAM, QD, KDM, KG, BKD, BV,             // inputs and decayed inputs
+    KF, QF, VF, DOF, GAM, QD, KDM, KG,                      // inputs and decayed inputs
     AH, A2M, TT, WW, UU, PP, PT, BB, BD, YY,                // prep
     SIN, DS,                                                // chains
     DL, DDL, DA2, DQD, DKG, DWM, DTM, DBT, DKT, XX,         // local
@@ -75,10 +75,12 @@ __device__ __forceinline__ int dtile_elem(int m, int n) {
 // Split-bf16 GEMM of a workgroup: D[m][n] = sum_k A(m, k) B(n, k) (+ s2 * second pair),
 // A and B read from fp32 views, staged through LDS 32 contraction indices at a time as
 // hi/lo bf16, 16x16 output tiles dealt to the 8 waves.  epi(m, n, value) consumes D.
-// A view must have either ks == 1 (and ms % 4 == 0) or ms == 1 (and ks % 4 == 0).
+// A view must have either ks == 1 (and ms % 4 == 0) or ms == 1 (and ks % 4 == 0).  With rs set,
+// row r of the matrix in memory (r = m for ks == 1, r = k for ms == 1) is read times rs[r].
 struct View {
     const float* p;
     int ms, ks;
+    const float* rs;
 };
 
 // A panel of M x 32 fp32 values moves global -> registers (issued early) -> LDS (split).
@@ -98,9 +100,17 @@ __device__ __forceinline__ void panel_load(Panel<M>& r, const View& v, int k0, i
             if (v.ks == 1) {
                 const int m = e / (KB / 4), kk = (e % (KB / 4)) * 4;
                 r.x[u] = *reinterpret_cast<const float4*>(v.p + (size_t)m * v.ms + k0 + kk);
+                if (v.rs != nullptr) {
+                    const float f = v.rs[m];
+                    r.x[u] = make_float4(r.x[u].x * f, r.x[u].y * f, r.x[u].z * f, r.x[u].w * f);
+                }
             } else {
                 const int kk = e / (M / 4), m = (e % (M / 4)) * 4;
                 r.x[u] = *reinterpret_cast<const float4*>(v.p + (size_t)(k0 + kk) * v.ks + m);
+                if (v.rs != nullptr) {
+                    const float f = v.rs[k0 + kk];
+                    r.x[u] = make_float4(r.x[u].x * f, r.x[u].y * f, r.x[u].z * f, r.x[u].w * f);
+                }
             }
         }
     }
@@ -215,7 +225,9 @@ __device__ __forceinline__ void gemm1(const View a, const View b, int kd, unsign
     gemm<M, N>(a, b, kd, a, b, 0, 1.f, lds, epi);
 }
 
-__device__ __forceinline__ View vw(const float* p, int ms, int ks) { return View{p, ms, ks}; }
+__device__ __forceinline__ View vw(const float* p, int ms, int ks, const float* rs = nullptr) {
+    return View{p, ms, ks, rs};
+}
 
 // fp32 -> (hi, lo) bf16x8 of 8 values
 __device__ __forceinline__ void split8(const float* x, bf16x8& h, bf16x8& l) {
@@ -329,8 +341,7 @@ __global__ __launch_bounds__(BTHREADS) __attribute__((amdgpu_waves_per_eu(4))) v
     // ---- inputs and their decayed forms (four elements per thread per round, loads first)
     {
         float *KFp = mat(w, ch, KF), *QFp = mat(w, ch, QF), *VFp = mat(w, ch, VF), *DOp = mat(w, ch, DOF);
-        float *QDp = mat(w, ch, QD), *KDp = mat(w, ch, KDM), *KGp = mat(w, ch, KG), *BKp = mat(w, ch, BKD);
-        float* BVp = mat(w, ch, BV);
+        float *QDp = mat(w, ch, QD), *KDp = mat(w, ch, KDM), *KGp = mat(w, ch, KG);
         for (int e0 = tid; e0 < C * 128; e0 += 4 * BTHREADS) {
             float kf[4], qf[4], vf[4], df[4], gm[4];
 #pragma unroll
@@ -349,7 +360,7 @@ __global__ __launch_bounds__(BTHREADS) __attribute__((amdgpu_waves_per_eu(4))) v
                 const bool ok = i < rows;   // rows past the end are zero
                 const float k_ = ok ? kf[u] * sRk[i] : 0.f, q_ = ok ? qf[u] * sRq[i] : 0.f;
                 const float v_ = ok ? vf[u] : 0.f, d_ = ok ? df[u] : 0.f;
-                const float eg = ex(gm[u]), egc = ex(sGC[d] - gm[u]), b = sBeta[i];
+                const float eg = ex(gm[u]), egc = ex(sGC[d] - gm[u]);
                 KFp[e] = k_;
                 QFp[e] = q_;
                 VFp[e] = v_;
@@ -357,8 +368,6 @@ __global__ __launch_bounds__(BTHREADS) __attribute__((amdgpu_waves_per_eu(4))) v
                 QDp[e] = scale * q_ * eg;
                 KDp[e] = k_ * eg;
                 KGp[e] = k_ * egc;
-                BKp[e] = b * k_ * eg;
-                BVp[e] = b * v_;
             }
         }
     }
@@ -583,9 +592,10 @@ __global__ __launch_bounds__(BTHREADS) __attribute__((amdgpu_waves_per_eu(4))) v
         float* Wp = mat(w, ch, WW);
         float* Up = mat(w, ch, UU);
         const float* TTp = mat(w, ch, TT);
-        gemm1<C, 128>(vw(TTp, 128, 1), vw(mat(w, ch, BKD), 1, 128), C, smem,
+        const float* bet = w.bet + ch * 128;   // beta of the chunk rows: the rows of kd and v
+        gemm1<C, 128>(vw(TTp, 128, 1), vw(mat(w, ch, KDM), 1, 128, bet), C, smem,
                       [&](int m, int n, float x) { Wp[m * 128 + n] = x; });
-        gemm1<C, 128>(vw(TTp, 128, 1), vw(mat(w, ch, BV), 1, 128), C, smem,
+        gemm1<C, 128>(vw(TTp, 128, 1), vw(mat(w, ch, VF), 1, 128, bet), C, smem,
                       [&](int m, int n, float x) { Up[m * 128 + n] = x; });
     }
     __syncthreads();
@@ -799,8 +809,10 @@ __global__ __launch_bounds__(BTHREADS) __attribute__((amdgpu_waves_per_eu(4))) v
         float* DBTp = mat(w, ch, DBT);
         float* DKTp = mat(w, ch, DKT);
         const float* TTp = mat(w, ch, TT);
-        gemm<C, C>(vw(mat(w, ch, DDL), 128, 1), vw(mat(w, ch, BV), 128, 1), VD, vw(mat(w, ch, DWM), 128, 1),
-                   vw(mat(w, ch, BKD), 128, 1), KD, 1.f, smem, [&](int m, int n, float x) { DTp[m * 128 + n] = x; });
+        // beta_j multiplies column j of both products: applied once, to the sum
+        gemm<C, C>(vw(mat(w, ch, DDL), 128, 1), vw(mat(w, ch, VF), 128, 1), VD, vw(mat(w, ch, DWM), 128, 1),
+                   vw(mat(w, ch, KDM), 128, 1), KD, 1.f, smem,
+                   [&](int m, int n, float x) { DTp[m * 128 + n] = sBeta[n] * x; });
         gemm1<C, 128>(vw(TTp, 1, 128), vw(mat(w, ch, DDL), 1, 128), C, smem,
                       [&](int m, int n, float x) { DBTp[m * 128 + n] = x; });
         gemm1<C, 128>(vw(TTp, 1, 128), vw(mat(w, ch, DWM), 1, 128), C, smem,
