@@ -424,65 +424,76 @@ __global__ __launch_bounds__(BTHREADS) __attribute__((amdgpu_waves_per_eu(4))) v
                 A2p[i * 128 + j] = (j <= i) ? scale * aq[e] : 0.f;
             }
         }
-        for (int I = 0; I < NT; ++I) {
+        // Wave J's right factors come from the same 16 rows for every row tile: their k and
+        // gamma stay in registers.  The next row tile's staging inputs are loaded while the
+        // current one's products run.
+        constexpr int NSG = (16 * 128) / BTHREADS;   // staged elements per thread
+        const int J = wave, j = 16 * J + (lane & 15);
+        float kreg[KD / 32][8], greg[KD / 32][8];
+        if (J < NT) {
+#pragma unroll
+            for (int s = 0; s < KD / 32; ++s) {
+                const int d0 = 32 * s + 8 * (lane >> 4);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    kreg[s][e] = KFp[j * 128 + d0 + e];
+                    greg[s][e] = gam[j * 128 + d0 + e];
+                }
+            }
+        }
+        auto pivot_row = [&](int I) { return 16 * I + (((wide >> I) & 1u) ? 0 : 8); };
+        float stk[NSG], stq[NSG], stg[NSG], stp[NSG];
+        auto load_stage = [&](int I) {
+#pragma unroll
+            for (int u = 0; u < NSG; ++u) {
+                const int e = tid + u * BTHREADS, r = e >> 7, d = e & 127, i = 16 * I + r;
+                stk[u] = KFp[i * 128 + d];
+                stq[u] = QFp[i * 128 + d];
+                stg[u] = gam[i * 128 + d];
+                stp[u] = gam[pivot_row(I) * 128 + d];
+            }
+        };
+        const int I0 = (wide & 1u) ? 1 : 0;   // a wide first tile has no earlier one to pair with
+        if (I0 < NT) load_stage(I0);
+        for (int I = I0; I < NT; ++I) {
             const bool mid = !((wide >> I) & 1u);    // the same in every thread
-            if (!mid && I == 0) continue;            // the first tile has no earlier one
-            __syncthreads();
-            if (tid < 128) piv[tid] = gam[(16 * I + (mid ? 8 : 0)) * 128 + tid];
-            __syncthreads();
-#pragma unroll 4
-            for (int e = tid; e < 16 * 128; e += BTHREADS) {
-                const int r = e >> 7, d = e & 127, i = 16 * I + r;
-                const float sc = ex(gam[i * 128 + d] - piv[d]);
+            __syncthreads();                         // the previous tile's operands are consumed
+            if (tid < 128) piv[tid] = gam[pivot_row(I) * 128 + tid];
+#pragma unroll
+            for (int u = 0; u < NSG; ++u) {
+                const int e = tid + u * BTHREADS, r = e >> 7, d = e & 127;
+                const float sc = ex(stg[u] - stp[u]);
                 short h, l;
-                split_bf(KFp[i * 128 + d] * sc, h, l);
+                split_bf(stk[u] * sc, h, l);
                 kh[r * P2 + d] = (uint16_t)h;
                 kl[r * P2 + d] = (uint16_t)l;
-                split_bf(QFp[i * 128 + d] * sc, h, l);
+                split_bf(stq[u] * sc, h, l);
                 qh[r * P2 + d] = (uint16_t)h;
                 ql[r * P2 + d] = (uint16_t)l;
             }
+            if (I + 1 < NT) load_stage(I + 1);
             __syncthreads();
-            const int J = wave;
             const bool run = J < I || (J == I && mid);
             if (J < NT) {
                 f32x4 ak = {0.f, 0.f, 0.f, 0.f}, aq = {0.f, 0.f, 0.f, 0.f};
                 if (run) {
-                    const int j = 16 * J + (lane & 15);
-                    for (int s2 = 0; s2 < KD / 32; s2 += 2) {
-                        float4 kx[2][2], gx[2][2];
 #pragma unroll
-                        for (int t = 0; t < 2; ++t) {
-                            const int d0 = 32 * (s2 + t) + 8 * (lane >> 4);
-                            kx[t][0] = *reinterpret_cast<const float4*>(KFp + j * 128 + d0);
-                            kx[t][1] = *reinterpret_cast<const float4*>(KFp + j * 128 + d0 + 4);
-                            gx[t][0] = *reinterpret_cast<const float4*>(gam + j * 128 + d0);
-                            gx[t][1] = *reinterpret_cast<const float4*>(gam + j * 128 + d0 + 4);
-                        }
+                    for (int s = 0; s < KD / 32; ++s) {
+                        const int d0 = 32 * s + 8 * (lane >> 4);
+                        float bv[8];
 #pragma unroll
-                        for (int t = 0; t < 2; ++t) {
-                            const int s = s2 + t, d0 = 32 * s + 8 * (lane >> 4);
-                            const float kk[8] = {kx[t][0].x, kx[t][0].y, kx[t][0].z, kx[t][0].w,
-                                                 kx[t][1].x, kx[t][1].y, kx[t][1].z, kx[t][1].w};
-                            const float gg[8] = {gx[t][0].x, gx[t][0].y, gx[t][0].z, gx[t][0].w,
-                                                 gx[t][1].x, gx[t][1].y, gx[t][1].z, gx[t][1].w};
-                            float bv[8];
-#pragma unroll
-                            for (int e = 0; e < 8; ++e) bv[e] = kk[e] * ex(piv[d0 + e] - gg[e]);
-                            bf16x8 b_h, b_l;
-                            split8(bv, b_h, b_l);
-                            const int ao = (lane & 15) * P2 + d0;
-                            ak = mfma3(*reinterpret_cast<const bf16x8*>(kh + ao), *reinterpret_cast<const bf16x8*>(kl + ao),
-                                       b_h, b_l, ak);
-                            aq = mfma3(*reinterpret_cast<const bf16x8*>(qh + ao), *reinterpret_cast<const bf16x8*>(ql + ao),
-                                       b_h, b_l, aq);
-                        }
+                        for (int e = 0; e < 8; ++e) bv[e] = kreg[s][e] * ex(piv[d0 + e] - greg[s][e]);
+                        bf16x8 b_h, b_l;
+                        split8(bv, b_h, b_l);
+                        const int ao = (lane & 15) * P2 + d0;
+                        ak = mfma3(*reinterpret_cast<const bf16x8*>(kh + ao), *reinterpret_cast<const bf16x8*>(kl + ao),
+                                   b_h, b_l, ak);
+                        aq = mfma3(*reinterpret_cast<const bf16x8*>(qh + ao), *reinterpret_cast<const bf16x8*>(ql + ao),
+                                   b_h, b_l, aq);
                     }
-                }
-                if (run) {   // the diagonal tile masked: A-hat strict, A2 inclusive
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int i = 16 * I + 4 * (lane >> 4) + e, j = 16 * J + (lane & 15);
+                    for (int e = 0; e < 4; ++e) {   // the diagonal tile masked: A-hat strict, A2 inclusive
+                        const int i = 16 * I + 4 * (lane >> 4) + e;
                         AHp[i * 128 + j] = (J < I || j < i) ? ak[e] : 0.f;
                         A2p[i * 128 + j] = (J < I || j <= i) ? scale * aq[e] : 0.f;
                     }
