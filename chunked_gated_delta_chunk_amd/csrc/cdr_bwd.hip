@@ -17,8 +17,9 @@
 //
 // Kernels (fp32 storage, products on split-bf16 MFMA: every operand is hi + lo bf16 and
 // three 16x16x32 instructions give a 16-bit-mantissa product with fp32 accumulation):
-//   bwd_prep   per (chunk, value head): gamma, A, A2 (pivoted pair products), T (blocked
-//              forward substitution in fp32), W, U, P, B and Q^T dO.
+//   bwd_prep   per (chunk, value head): gamma, A, A2 (pivoted pair products), T (fp32
+//              diagonal blocks, the others on split-bf16 16x16x16 MFMAs), W, U, P, B and
+//              Q^T dO.
 //   bwd_chain  per (sequence, value head, 16 value columns): the chunk entry states S_in
 //              (forward direction) and the chunk exit gradients dS_out (reverse direction),
 //              fp32 states and records, -P (-P^T) with one bf16 rounding on MFMA as in the
