@@ -1,7 +1,8 @@
-"""The forward captured in a HIP graph (torch.cuda.CUDAGraph) and replayed: every replay, with
-new input contents copied into the captured buffers and eager GPU work in between, must give
-the bits of an eager call on the same inputs.  Covers both the workspace entry point and the
-no-allocation one (whose static workspace is what a capturing caller uses)."""
+"""The forward and the backward captured in a HIP graph (torch.cuda.CUDAGraph) and replayed:
+every replay, with new input contents copied into the captured buffers and eager GPU work in
+between, must give the bits of an eager call on the same inputs.  The forward is covered through
+both the workspace entry point and the no-allocation one (whose static workspace is what a
+capturing caller uses)."""
 import pytest
 import torch
 
@@ -59,4 +60,55 @@ def test_graph_replays_match_eager_calls(case, noalloc):
         o_ref, S_ref = _eager(new)
         assert torch.equal(call.o, o_ref), f"replay {r}: o differs"
         assert torch.equal(call.S, S_ref), f"replay {r}: final state differs"
+        torch.randn(4096, device="cuda:0").abs().sum().item()   # eager work between replays
+
+
+# ---------------------------------------------------------------- backward
+BWD_CASES = [
+    ("kda_C128_tail", dict(B=1, T=300, H=2, chunk_size=128, initial_state=True)),
+    ("kda_C64_varlen_grouped", dict(B=1, T=260, H=1, HV=2, chunk_size=64, lengths=(100, 0, 160),
+                                    initial_state=True)),
+]
+
+
+def _bwd_draw(kw, seed):
+    inp = make_inputs(seed=seed, **kw)
+    gen = torch.Generator("cpu").manual_seed(seed + 50)
+    N = inp.q.shape[0] if inp.cu_seqlens is None else inp.cu_seqlens.numel() - 1
+    do = torch.randn(tuple(inp.v.shape), generator=gen).to(torch.bfloat16)
+    dht = 0.1 * torch.randn(N, inp.v.shape[2], 128, 128, generator=gen)
+    return inp.to("cuda:0"), do.to("cuda:0"), dht.to("cuda:0")
+
+
+@pytest.mark.parametrize("case", BWD_CASES, ids=[c[0] for c in BWD_CASES])
+def test_backward_graph_replays_match_eager_calls(case):
+    """The backward has no allocation or memset inside its calls: captured once, each replay on
+    new input contents gives the bits of an eager call."""
+    label, kw = case
+    print(f"[graph bwd] {label}", flush=True)
+    st, do, dht = _bwd_draw(kw, seed=800)
+    call = cdr.PreparedBackward(st.q, st.k, st.v, st.g, st.beta, do, dht=dht, initial_state=st.initial_state,
+                                cu_seqlens=st.cu_seqlens, chunk_size=st.chunk_size)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call()
+    for r in range(3):
+        new, do_n, dht_n = _bwd_draw(kw, seed=801 + r)
+        for dst, src in ((st.q, new.q), (st.k, new.k), (st.v, new.v), (st.g, new.g), (st.beta, new.beta),
+                         (st.initial_state, new.initial_state), (do, do_n), (dht, dht_n)):
+            dst.copy_(src)
+        graph.replay()
+        torch.cuda.synchronize()
+        ref = cdr.PreparedBackward(new.q, new.k, new.v, new.g, new.beta, do_n, dht=dht_n,
+                                   initial_state=new.initial_state, cu_seqlens=new.cu_seqlens,
+                                   chunk_size=new.chunk_size)()
+        torch.cuda.synchronize()
+        for name, a, b in zip(("dq", "dk", "dv", "dg", "dbeta", "dh0"), call.grads, ref):
+            assert torch.equal(a, b), f"replay {r}: {name} differs"
         torch.randn(4096, device="cuda:0").abs().sum().item()   # eager work between replays
