@@ -1,4 +1,4 @@
-"""The forward and the backward captured in a HIP graph (torch.cuda.CUDAGraph) and replayed:
+"""The forward, the backward and a decode step captured in a HIP graph (torch.cuda.CUDAGraph) and replayed:
 every replay, with new input contents copied into the captured buffers and eager GPU work in
 between, must give the bits of an eager call on the same inputs.  The forward is covered through
 both the workspace entry point and the no-allocation one (whose static workspace is what a
@@ -111,4 +111,53 @@ def test_backward_graph_replays_match_eager_calls(case):
         torch.cuda.synchronize()
         for name, a, b in zip(("dq", "dk", "dv", "dg", "dbeta", "dh0"), call.grads, ref):
             assert torch.equal(a, b), f"replay {r}: {name} differs"
+        torch.randn(4096, device="cuda:0").abs().sum().item()   # eager work between replays
+
+
+# ---------------------------------------------------------------- decode on a state pool
+DEC_CASES = [
+    # label, N, T, H, HV, slots, speculative columns
+    ("decode_T1", 16, 1, 2, 2, 48, 0),
+    ("spec_L3_grouped", 8, 3, 1, 2, 40, 3),
+]
+
+
+@pytest.mark.parametrize("case", DEC_CASES, ids=[c[0] for c in DEC_CASES])
+def test_decode_graph_replays_match_eager_calls(case):
+    """A serving loop captures the decode step once and replays it: new tokens, slot indices,
+    accepted counts and pool contents go into the captured buffers before each replay."""
+    from chunked_gated_delta_chunk_amd.synth import make_decode_inputs
+    label, N, T, H, HV, slots, cols = case
+    print(f"[graph decode] {label}", flush=True)
+    draw = lambda seed: make_decode_inputs(N, T, H, HV, slots, seed=seed, index_cols=cols,  # noqa: E731
+                                           normalise=False).to("cuda:0")
+    st = draw(900)
+    call = cdr.PreparedRecurrent(st.q, st.k, st.v, st.g, st.beta, use_qk_l2norm_in_kernel=True,
+                                 state_pool=st.state_pool, ssm_state_indices=st.ssm_state_indices,
+                                 num_accepted_tokens=st.num_accepted_tokens)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call()
+    for r in range(3):
+        new = draw(901 + r)
+        for dst, src in ((st.q, new.q), (st.k, new.k), (st.v, new.v), (st.g, new.g), (st.beta, new.beta),
+                         (st.state_pool, new.state_pool), (st.ssm_state_indices, new.ssm_state_indices),
+                         (st.num_accepted_tokens, new.num_accepted_tokens)):
+            if dst is not None:
+                dst.copy_(src)
+        graph.replay()
+        torch.cuda.synchronize()
+        pool_ref = new.state_pool.clone()
+        o_ref, _ = cdr.PreparedRecurrent(new.q, new.k, new.v, new.g, new.beta, use_qk_l2norm_in_kernel=True,
+                                         state_pool=pool_ref, ssm_state_indices=new.ssm_state_indices,
+                                         num_accepted_tokens=new.num_accepted_tokens)()
+        torch.cuda.synchronize()
+        assert torch.equal(call.o, o_ref), f"replay {r}: o differs"
+        assert torch.equal(st.state_pool, pool_ref), f"replay {r}: pool differs"
         torch.randn(4096, device="cuda:0").abs().sum().item()   # eager work between replays
