@@ -1,8 +1,8 @@
-"""The forward, the backward and a decode step captured in a HIP graph (torch.cuda.CUDAGraph) and replayed:
-every replay, with new input contents copied into the captured buffers and eager GPU work in
-between, must give the bits of an eager call on the same inputs.  The forward is covered through
-both the workspace entry point and the no-allocation one (whose static workspace is what a
-capturing caller uses)."""
+"""The forward, the backward and a decode step captured in a HIP graph (torch.cuda.CUDAGraph)
+and replayed: every replay, with new input contents copied into the captured buffers and eager
+GPU work in between, must give the bits of an eager call on the same inputs.  The forward is
+covered through both the workspace entry point and the no-allocation one (whose static workspace
+is what a capturing caller uses)."""
 import pytest
 import torch
 
