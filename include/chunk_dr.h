@@ -112,7 +112,7 @@ size_t cdr_workspace_bytes(const cdr_problem* p);
  *   g             fp32 [B*T, HV, K] (CDR_GATE_PER_DIM) or [B*T, HV] (CDR_GATE_PER_HEAD);
  *                 log-domain forget gate.  Supported: every finite g <= 0 (the page's gates
  *                 are logsigmoid values); the in-chunk sums of g must be finite in fp32.
- *                 A chunk in which a per-dimension gate sums to more than 64 in magnitude
+ *                 A chunk in which a per-dimension gate sums to more than 32 in magnitude
  *                 over half a 16-token tile takes an exact path for its diagonal 16 x 16
  *                 blocks (one exponential per pair and dimension), about as slow again as
  *                 the rest of the chunk's work; other chunks are unaffected.  g > 0 is
