@@ -58,8 +58,8 @@ __device__ __forceinline__ float* mat(const Work& w, size_t ch, int id) {
     return w.M + (ch * NMAT + id) * (size_t)MSZ;
 }
 
-// Operand layouts of the state chains, kept in the first half of a matrix slot (PP, PT) or in
-// all of it (BB, BD):
+// Operand layouts of the state chains: -P and -P^T as high bf16 parts in the first half of a
+// matrix slot and low parts in the second (PP, PT), B and Q^T dO in all of it (BB, BD):
 // element (m, k) of a 128 x 128 MFMA A operand stored as bf16 pi-order fragments (rows m,
 // contracted index k), the layout of the forward chain's -P
 __device__ __forceinline__ int pi_elem(int m, int k) {
@@ -620,9 +620,12 @@ __global__ __launch_bounds__(BTHREADS) __attribute__((amdgpu_waves_per_eu(4))) v
         float* Yp = mat(w, ch, YY);
         const float* KGp = mat(w, ch, KG);
         gemm1<128, 128>(vw(KGp, 1, 128), vw(mat(w, ch, WW), 1, 128), C, smem, [&](int m, int n, float x) {
-            const uint16_t nb = f2bf(-x);
-            Pp[pi_elem(m, n)] = nb;
-            PTp[pi_elem(n, m)] = nb;
+            short h, l;   // high parts in the slot's first half, low parts in its second
+            split_bf(-x, h, l);
+            Pp[pi_elem(m, n)] = (uint16_t)h;
+            Pp[MSZ + pi_elem(m, n)] = (uint16_t)l;
+            PTp[pi_elem(n, m)] = (uint16_t)h;
+            PTp[MSZ + pi_elem(n, m)] = (uint16_t)l;
         });
         gemm1<128, 128>(vw(KGp, 1, 128), vw(mat(w, ch, UU), 1, 128), C, smem,
                         [&](int m, int n, float x) { Bp[dtile_elem(m, n)] = x; });
@@ -646,15 +649,16 @@ __global__ __launch_bounds__(BTHREADS) __attribute__((amdgpu_waves_per_eu(4))) v
 // workgroup of 8 waves per (sequence, value head, 16 value columns); wave x keeps rows
 // 16 x .. 16 x + 15 of the fp32 slice in registers (accumulator layout).  Per chunk the slice
 // is recorded (fp32), published in LDS as hi + lo bf16 (the B operand of the product), and
-// -P (or -P^T), stored by bwd_prep with one bf16 rounding, multiplies both halves: two MFMAs
-// per 32-step.  The operands of the next two chunks are in flight in a ring of three
+// -P (or -P^T), stored by bwd_prep as hi + lo bf16 too, multiplies it in three MFMA chains
+// (P_hi S_hi, P_lo S_hi, P_hi S_lo), as in the forward chain.  The operands of the next two chunks are in flight in a ring of three
 // register buffers; the value blocks of one (sequence, head) are numbered onto one XCD.
 constexpr int CH_NXCD = 8;          // workgroups are dealt to the 8 XCDs round-robin
 constexpr int CH_NVB = VD / 16;     // value blocks per (sequence, head)
 constexpr int CH_KS = KD / 32;      // 32-wide contraction steps over the state rows
 
 struct ChainOps {
-    uint4 ph[CH_KS];  // -P (or -P^T) fragments (x, s)
+    uint4 ph[CH_KS];  // -P (or -P^T) fragments (x, s), high bf16 parts
+    uint4 pl[CH_KS];  // and low parts
     float4 b;         // B (or Q^T dO) tile (x, value block)
     float4 gl;        // gamma_C of the wave's rows (log domain)
 };
@@ -663,7 +667,10 @@ template <bool REV>
 __device__ __forceinline__ void chain_load(ChainOps& op, const Work& w, size_t ch, int x, int lane, int q4, int vb) {
     const uint16_t* Pm = reinterpret_cast<const uint16_t*>(mat(w, ch, REV ? PT : PP));
 #pragma unroll
-    for (int s = 0; s < CH_KS; ++s) op.ph[s] = *reinterpret_cast<const uint4*>(Pm + frag(x, s, CH_KS) + lane * 8);
+    for (int s = 0; s < CH_KS; ++s) {
+        op.ph[s] = *reinterpret_cast<const uint4*>(Pm + frag(x, s, CH_KS) + lane * 8);
+        op.pl[s] = *reinterpret_cast<const uint4*>(Pm + MSZ + frag(x, s, CH_KS) + lane * 8);
+    }
     op.b = *reinterpret_cast<const float4*>(mat(w, ch, REV ? BD : BB) + ((x * 8 + vb) * 64 + lane) * 4);
     op.gl = *reinterpret_cast<const float4*>(w.gcr + ch * 128 + 16 * x + 4 * q4);
 }
@@ -685,16 +692,17 @@ __device__ __forceinline__ void chain_step(const ChainOps& op, f32x4& S, const W
     lds_barrier();
     f32x4 a0 = {ex(op.gl.x) * S[0] + op.b.x, ex(op.gl.y) * S[1] + op.b.y, ex(op.gl.z) * S[2] + op.b.z,
                 ex(op.gl.w) * S[3] + op.b.w};
-    f32x4 a2 = {0.f, 0.f, 0.f, 0.f};
+    f32x4 a1 = {0.f, 0.f, 0.f, 0.f}, a2 = a1;
 #pragma unroll
     for (int s = 0; s < CH_KS; ++s) {
         const bf16x8 bh = as_bf16x8(*reinterpret_cast<const uint4*>(sb + s * 512 + lane * 8));
         const bf16x8 bl = as_bf16x8(*reinterpret_cast<const uint4*>(sb + (CH_KS + s) * 512 + lane * 8));
         a0 = mfma32(as_bf16x8(op.ph[s]), bh, a0);
+        a1 = mfma32(as_bf16x8(op.pl[s]), bh, a1);
         a2 = mfma32(as_bf16x8(op.ph[s]), bl, a2);
     }
 #pragma unroll
-    for (int e = 0; e < 4; ++e) S[e] = a0[e] + a2[e];
+    for (int e = 0; e < 4; ++e) S[e] = a0[e] + (a1[e] + a2[e]);
 }
 
 template <bool REV>

@@ -52,7 +52,7 @@ def seq_slices(inp):
     return [(0, slice(cu[n], cu[n + 1])) for n in range(len(cu) - 1)]
 
 
-def check(inp, label, l2n=False, dht=True, seed=1):
+def check(inp, label, l2n=False, dht=True, seed=1, tol=TOL):
     note(f"[bwd] {label} q{tuple(inp.q.shape)} v{tuple(inp.v.shape)} C={inp.chunk_size} l2n={l2n}")
     do, ht = upstream(inp, seed, dht)
     got = run_gpu(inp, do, ht, l2n)
@@ -77,7 +77,7 @@ def check(inp, label, l2n=False, dht=True, seed=1):
             worst[name] = max(worst.get(name, 0.0), norm_ratio(x, y))
     note(f"[bwd] {label}: " + "  ".join(f"{k} {v:.2e}" for k, v in worst.items()))
     for k, v in worst.items():
-        assert v <= TOL, f"{k} norm ratio {v:.3e} > {TOL}"
+        assert v <= tol, f"{k} norm ratio {v:.3e} > {tol}"
 
 
 SMALL = [
@@ -111,6 +111,24 @@ STRONG = [
     ("kda_sparse_spikes40_C128", 1, 512, 2, None, 128, True, None, True, 0.0, 0.02),
     ("kda_sparse_spikes40_C64_varlen", 1, 390, 2, None, 64, True, (70, 320), True, 1.0, 0.02),
 ]
+
+
+# The state carries over every chunk (g = 0) or nearly (logsigmoid(N(6,1))): the two chains
+# multiply -P into their state 32 to 64 times, so its rounding compounds.  With -P kept as hi + lo
+# bf16 the norm ratios stay near 1e-5; with one bf16 rounding they were about 1.3e-3, under the
+# page's bar but far above the rest.  Checked against 2e-4.
+CARRY = [
+    ("g0_T2048_C64", 2048, 64, dict(gate="zero")),
+    ("g0_T4096_C128", 4096, 128, dict(gate="zero")),
+    ("weak6_T2048_C128", 2048, 128, dict(gate_mean=6.0)),
+]
+
+
+@pytest.mark.parametrize("case", CARRY, ids=[c[0] for c in CARRY])
+def test_backward_where_the_state_carries(case):
+    label, T, C, kw = case
+    inp = make_inputs(1, T, 1, seed=77, initial_state=True, chunk_size=C, **kw)
+    check(inp, label, tol=2e-4)
 
 
 @pytest.mark.parametrize("case", STRONG, ids=[c[0] for c in STRONG])
