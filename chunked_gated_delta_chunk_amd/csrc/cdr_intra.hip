@@ -19,7 +19,10 @@
 //        pivots: for rows i in tile R and columns j in tile J <= R,
 //          exp(g_i - g_j) = [exp(g_i - g_m(R)) exp(g_m(R) - g_m(J))] * exp(g_m(J) - g_j)
 //        so no factor exceeds exp(half a tile's gate span) and the product never
-//        overflows.  The row operands times exp(g_i - g_m(R)) are formed once per row and
+//        overflows.  A (tile, key dimension) column whose gates span more than SAFE_SPAN
+//        on a side of the middle row takes other pivots in that dimension: the gamma before
+//        the tile's first row for its rows, at its last row for its columns, and its pairs
+//        inside the diagonal tile are summed exactly (diag_exact).  The row operands times exp(g_i - g_m(R)) are formed once per row and
 //        32-column step; a tile below the diagonal multiplies them by the pivot ratio
 //        only.  A uses hi/lo split operands (three MFMAs); A2 feeds only the output
 //        and uses single bf16 operands (stored transposed, scratch).  Per-head gates use
@@ -55,8 +58,8 @@ constexpr float L2N_EPS = 1e-6f;  // in-kernel q/k normalisation: x / sqrt(|x|^2
 // middles underflows fp32 (below e^-87), the pair it belongs to has a true decay below
 // e^(2 * 32 - 87) = e^-23, small enough to drop.  With a larger limit two moderate tiles could
 // compensate a flushed F: g = -40 at rows 30 and 33 of a chunk puts 93 between the middles of
-// tiles 1 and 2 while rows 30..32 stay close.  A chunk with a wider tile takes pivots that make
-// every factor <= 1 and exact diagonal tiles.
+// tiles 1 and 2 while rows 30..32 stay close.  A wider (tile, key dimension) column takes pivots
+// that make every factor <= 1 in that dimension, and exact sums in its diagonal tile.
 constexpr float SAFE_SPAN = 32.f;
 constexpr int IMAXTHREADS = 512;  // the largest workgroup (C = 128)
 
@@ -221,16 +224,19 @@ __device__ __forceinline__ void vm_pad(uint32_t* p) {
     for (int i = 0; i < N; ++i) p[16 * i] = 0u;
 }
 
-// Exact decayed products of the diagonal tile (R, R), for chunks whose gates are too wide for
-// pivot factors: one exponential per pair and dimension, exp(-|gamma_a - gamma_b|), which for
-// g <= 0 is the decay exp(gamma_i - gamma_j) of the pair's later row i over its earlier row j.
+// Exact decayed products of the diagonal tile (R, R) in its wide key dimensions, those whose
+// gates are too wide for pivot factors: one exponential per pair and dimension,
+// exp(-|gamma_a - gamma_b|), which for g <= 0 is the decay exp(gamma_i - gamma_j) of the pair's
+// later row i over its earlier row j.  The other dimensions are left to the pivot products.
 // Lane (r16, q4) returns, in the accumulator layouts of phase AA2 (a = 16 R + r16,
 // b = 16 R + 4 q4 + e),
 //     dA[e] = sum_d k_b k_a decay      (A tile: row b, column a)
 //     dQ[e] = sum_d q_a k_b decay      (A2^T tile: row b, column a)
 // with the L2 scales of the rows applied (knr for keys, rq for the lane's query row) and rows at
 // or past `rows` taken as zero; the caller applies the triangle masks, beta and scale.  gam holds
-// gamma by row, row stride ld floats.
+// phase E's row factors, row stride ld floats: in a wide dimension the log factor against the
+// tile's row pivot minus one (<= -1; gamma up to a constant of the tile), in the others the
+// factor itself (> 0), which marks them.
 template <bool L2N>
 __device__ __forceinline__ void diag_exact(const float* gam, int ld, const uint16_t* kbase, const uint16_t* qbase,
                                            uint32_t rsk, int rows, int R, int r16, int q4, const float* knr,
@@ -249,12 +255,23 @@ __device__ __forceinline__ void diag_exact(const float* gam, int ld, const uint1
         dQ[e] = 0.f;
     }
     for (int dc = 0; dc < KD / 8; ++dc) {
-        float ka[8], qa[8];
-        unpack8(*cptr<uint4>(kbase, oa + 16u * dc), ka);
-        unpack8(*cptr<uint4>(qbase, oa + 16u * dc), qa);
+        // dimensions 8 dc .. 8 dc + 7: only the wide ones (ga < 0, which holds for every row of
+        // the tile alike) are summed, the others' operands of row a are zeroed
         const float4* gpa = reinterpret_cast<const float4*>(gam + a * ld + 8 * dc);
         const float4 a0 = gpa[0], a1 = gpa[1];
         const float ga[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+        bool any = false;
+#pragma unroll
+        for (int t = 0; t < 8; ++t) any |= ga[t] < 0.f;
+        if (__ballot(any) == 0) continue;
+        float ka[8], qa[8];
+        unpack8(*cptr<uint4>(kbase, oa + 16u * dc), ka);
+        unpack8(*cptr<uint4>(qbase, oa + 16u * dc), qa);
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            ka[t] = ga[t] < 0.f ? ka[t] : 0.f;
+            qa[t] = ga[t] < 0.f ? qa[t] : 0.f;
+        }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             float kb[8];
@@ -265,7 +282,7 @@ __device__ __forceinline__ void diag_exact(const float* gam, int ld, const uint1
             float sA = 0.f, sQ = 0.f;
 #pragma unroll
             for (int t = 0; t < 8; ++t) {
-                const float kd = kb[t] * ex(-fabsf(ga[t] - gb[t]));
+                const float kd = kb[t] * ex(-fabsf(ga[t] - gb[t]));   // finite in every column
                 sA += kd * ka[t];
                 sQ += kd * qa[t];
             }
@@ -358,8 +375,10 @@ __device__ __forceinline__ void intra_item(
     uint4 xs[2][2], xls[2][2], vs[2][2];  // exp(gamma) k split into high (xs) and low parts
     uint4 kls[2][2];  // low part of kg^T, the two pi-order halves of each slot, to LDS after the solve
     // per-dimension gates too wide for the tile-middle pivots somewhere in the chunk (same value in
-    // every thread of the workgroup after phase E's first barrier)
+    // every thread of the workgroup after phase E's first barrier).  Which (tile, key dimension)
+    // columns are wide is kept in LDS as two 64-bit masks per tile, even and odd dimensions.
     bool wide = false;
+    uint64_t* wmask = reinterpret_cast<uint64_t*>(grow);   // [NT][2]
     // ------------------------------------------------------------------ phase E
     {
         const int R = tid >> 6, d0 = 2 * (tid & 63);  // tile row R, columns d0, d0 + 1
@@ -383,15 +402,21 @@ __device__ __forceinline__ void intra_item(
             }
             *reinterpret_cast<float2*>(ttot + R * KD + d0) = make_float2(gm2[15][0], gm2[15][1]);
             if constexpr (PER_DIM) {
-                // gate span of the tile on either side of its middle row, the exponent of the
-                // largest pivot factor; a wave flags its tile when it exceeds SAFE_SPAN
-                float span = 0.f;
+                // per column, the gate span of the tile on either side of its middle row (the
+                // exponent of the largest pivot factor); the column is wide above SAFE_SPAN
+                bool wc[2];
 #pragma unroll
-                for (int ii = 0; ii < 16; ++ii)
+                for (int c = 0; c < 2; ++c) {
+                    float span = 0.f;
 #pragma unroll
-                    for (int c = 0; c < 2; ++c) span = fmaxf(span, fabsf(gm2[ii][c] - gm2[8][c]));
-                const bool wflag = __ballot(!(span <= SAFE_SPAN)) != 0;
-                if ((tid & 63) == 0) reinterpret_cast<int*>(grow)[R] = wflag ? 1 : 0;
+                    for (int ii = 0; ii < 16; ++ii) span = fmaxf(span, fabsf(gm2[ii][c] - gm2[8][c]));
+                    wc[c] = !(span <= SAFE_SPAN);
+                }
+                const uint64_t m0 = __ballot(wc[0]), m1 = __ballot(wc[1]);
+                if ((tid & 63) == 0) {
+                    wmask[2 * R] = m0;
+                    wmask[2 * R + 1] = m1;
+                }
             }
         }
         // in-kernel L2 normalisation of keys: k / sqrt(|k|^2 + eps) per token, the row sum of
@@ -416,7 +441,7 @@ __device__ __forceinline__ void intra_item(
         lds_barrier();
         if constexpr (PER_DIM) {
 #pragma unroll
-            for (int Rp = 0; Rp < NT; ++Rp) wide |= reinterpret_cast<const int*>(grow)[Rp] != 0;
+            for (int Rp = 0; Rp < NT; ++Rp) wide |= (wmask[2 * Rp] | wmask[2 * Rp + 1]) != 0;
         }
         if (act) {
             float off[2] = {0.f, 0.f}, gcl[2] = {0.f, 0.f};
@@ -434,16 +459,20 @@ __device__ __forceinline__ void intra_item(
                 gm2[ii][0] += off[0];
                 gm2[ii][1] += off[1];
             }
-            // pivots of the tile: gpr for its rows, gpc for its columns.  Narrow gates: both the
-            // middle row's gamma.  Wide gates: gamma before the tile's first row (off) for the rows
-            // and at its last row for the columns, so that every factor is <= 1 for g <= 0
-            float gpr[2], gpc[2], e_gm[2], e_cm[2];
+            // pivots of the tile, per column: gpr for its rows, gpc for its columns.  Narrow:
+            // both the middle row's gamma.  Wide: gamma before the tile's first row (off) for the
+            // rows and at its last row for the columns, so that every factor is <= 1 for g <= 0
+            // dgc = gpc - gpr: 0 in a narrow column, the tile's total log decay (< -SAFE_SPAN) in a
+            // wide one
+            float gpr[2], dgc[2], e_gm[2], e_cm[2];
 #pragma unroll
             for (int c = 0; c < 2; ++c) {
-                gpr[c] = wide ? off[c] : gm2[8][c];
-                gpc[c] = wide ? gm2[15][c] : gm2[8][c];
-                e_gm[c] = ex(gpr[c]);            // exp(gamma at the row pivot) <= 1
-                e_cm[c] = ex(gcl[c] - gpc[c]);   // exp(gamma_C - gamma at the column pivot) <= 1
+                const bool wcol = PER_DIM && ((wmask[2 * R + c] >> (tid & 63)) & 1u) != 0u;
+                const float gpc = wcol ? gm2[15][c] : gm2[8][c];
+                gpr[c] = wcol ? off[c] : gm2[8][c];
+                dgc[c] = gpc - gpr[c];
+                e_gm[c] = ex(gpr[c]);         // exp(gamma at the row pivot) <= 1
+                e_cm[c] = ex(gcl[c] - gpc);   // exp(gamma_C - gamma at the column pivot) <= 1
             }
             *reinterpret_cast<float2*>(gmid + R * KD + d0) = make_float2(gpr[0], gpr[1]);
             *reinterpret_cast<float2*>(egm + R * KD + d0) = make_float2(e_gm[0], e_gm[1]);
@@ -469,20 +498,21 @@ __device__ __forceinline__ void intra_item(
                         kf[rr][0] = __uint_as_float(kr[ii] << 16) * rnk[ii];
                         kf[rr][1] = __uint_as_float(kr[ii] & 0xffff0000u) * rnk[ii];
                         if constexpr (PER_DIM) {
-                            float ep[2], em[2];
+                            float ep[2], em[2], lg[2];
 #pragma unroll
                             for (int c = 0; c < 2; ++c) {
-                                ep[c] = ex(gm2[ii][c] - gpr[c]);   // exp(gamma_i - row pivot)
-                                // exp(column pivot - gamma_i): the reciprocal when the pivots agree
-                                em[c] = wide ? ex(gpc[c] - gm2[ii][c]) : __builtin_amdgcn_rcpf(ep[c]);
+                                lg[c] = gm2[ii][c] - gpr[c];
+                                ep[c] = ex(lg[c]);   // exp(gamma_i - row pivot)
+                                em[c] = ex(dgc[c] - lg[c]);   // exp(column pivot - gamma_i)
                                 fx[rr][c] = e_gm[c] * ep[c];
                                 fk[rr][c] = em[c] * e_cm[c];
                             }
                             const int i = 16 * R + ii;
-                            // row factors of phase AA2; with wide gates gamma itself, from which AA2
-                            // forms them and the diagonal tiles their exact pair decays
+                            // row factors of phase AA2 (> 0); for a wide column instead the log
+                            // factor minus one (<= -1), from which AA2 forms the factor and the
+                            // diagonal tile the exact pair decays
                             *reinterpret_cast<float2*>(Ep + i * S::EP_LD + d0) =
-                                wide ? make_float2(gm2[ii][0], gm2[ii][1]) : make_float2(ep[0], ep[1]);
+                                make_float2(dgc[0] < 0.f ? lg[0] - 1.f : ep[0], dgc[1] < 0.f ? lg[1] - 1.f : ep[1]);
                             uint32_t chv, clv;
                             split2(kf[rr][0] * em[0], kf[rr][1] * em[1], chv, clv);
                             *reinterpret_cast<uint32_t*>(colh + i * S::COL_LD + d0) = chv;
@@ -528,14 +558,19 @@ __device__ __forceinline__ void intra_item(
         lds_barrier();
         if constexpr (PER_DIM) {
             // strictly lower pairs p = R(R-1)/2 + J: F = exp(row pivot of R - column pivot of J) <= 1.
-            // The column pivot of J is its row pivot, or with wide gates gamma at its last row, which
-            // is the row pivot of J + 1 <= R
+            // The column pivot of J is its row pivot (the middle row's gamma), or in a wide column
+            // gamma at its last row: the row pivot plus the log factor that Ep holds there
             for (int e = 4 * tid; e < S::NOFF * KD; e += 4 * S::THREADS) {
                 const int p = e / KD, d = e % KD;
                 const int R = (int)((1.f + __builtin_sqrtf(8.f * p + 1.f)) * 0.5f);  // R(R-1)/2 <= p < R(R+1)/2
                 const int J = p - R * (R - 1) / 2;
                 const float4 a = *reinterpret_cast<const float4*>(gmid + R * KD + d);
-                const float4 b = *reinterpret_cast<const float4*>(gmid + (J + (wide ? 1 : 0)) * KD + d);
+                float4 b = *reinterpret_cast<const float4*>(gmid + J * KD + d);
+                if (wide) {
+                    const float4 gl = *reinterpret_cast<const float4*>(Ep + (16 * J + 15) * S::EP_LD + d);
+                    b = make_float4(gl.x < 0.f ? b.x + (gl.x + 1.f) : b.x, gl.y < 0.f ? b.y + (gl.y + 1.f) : b.y,
+                                    gl.z < 0.f ? b.z + (gl.z + 1.f) : b.z, gl.w < 0.f ? b.w + (gl.w + 1.f) : b.w);
+                }
                 *reinterpret_cast<float4*>(F + e) = make_float4(ex(a.x - b.x), ex(a.y - b.y), ex(a.z - b.z), ex(a.w - b.w));
             }
         }
@@ -617,12 +652,9 @@ __device__ __forceinline__ void intra_item(
                     const float4* epp = reinterpret_cast<const float4*>(Ep + i * S::EP_LD + dd);
                     const float4 e0 = epp[0], e1 = epp[1];
                     float ep[8] = {e0.x, e0.y, e0.z, e0.w, e1.x, e1.y, e1.z, e1.w};
-                    if (wide) {  // Ep holds gamma: the factor against the row pivot, <= 1
-                        const float4* gp = reinterpret_cast<const float4*>(gmid + R * KD + dd);
-                        const float4 p0 = gp[0], p1 = gp[1];
-                        const float pv[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
+                    if (wide) {  // a wide column holds the log factor minus one: the factor, <= 1
 #pragma unroll
-                        for (int e = 0; e < 8; ++e) ep[e] = ex(ep[e] - pv[e]);
+                        for (int e = 0; e < 8; ++e) ep[e] = ep[e] < 0.f ? ex(ep[e] + 1.f) : ep[e];
                     }
 #pragma unroll
                     for (int e = 0; e < 8; ++e) {
@@ -668,6 +700,9 @@ __device__ __forceinline__ void intra_item(
                         pq.z = pack_bf2(scale * qE[4] * eg[4], scale * qE[5] * eg[5]);
                         pq.w = pack_bf2(scale * qE[6] * eg[6], scale * qE[7] * eg[7]);
                         qgkeep[ks] = pq;
+                        // in a wide column the pivot product of a pair (i, j) in this tile is its
+                        // decay times the tile's total decay, below exp(-SAFE_SPAN): left in, next
+                        // to the exact sum of those columns (diag_exact)
                         split2(kE[0], kE[1], ah.x, al.x);
                         split2(kE[2], kE[3], ah.y, al.y);
                         split2(kE[4], kE[5], ah.z, al.z);
@@ -686,12 +721,15 @@ __device__ __forceinline__ void intra_item(
             }
         }
     }
-    // wide gates: the wave's diagonal tile exactly (its pivot products above are finite but not the
-    // pair decays); tile row cp for the first wave of a pair, NT-1-cp for the second
+    // wide columns: the wave's diagonal tile exactly in those columns (their pivot products above
+    // are finite but not the pair decays), added to the pivot products of the other columns; tile
+    // row cp for the first wave of a pair, NT-1-cp for the second
     f32x4 dA = {0.f, 0.f, 0.f, 0.f}, dQ = dA;
-    if (PER_DIM && wide && aa_active)
-        diag_exact<L2N>(Ep, S::EP_LD, kbase, qbase, rsk, rows, part ? NT - 1 - cp : cp, r16, q4, knr,
+    if (PER_DIM && wide && aa_active) {
+        const int Rd = part ? NT - 1 - cp : cp;
+        diag_exact<L2N>(Ep, S::EP_LD, kbase, qbase, rsk, rows, Rd, r16, q4, knr,
                         L2N ? (part ? rq2[1] : rq2[0]) : 1.f, dA, dQ);
+    }
     if constexpr (!PER_DIM) {
 #pragma unroll
         for (int s = 0; s < S::SMAX; ++s) {
@@ -745,8 +783,8 @@ __device__ __forceinline__ void intra_item(
             float a = acc1[s][rr], a2 = acc2[s][rr];
             if constexpr (PER_DIM) {
                 if (wide && J == R) {
-                    a = dA[rr];
-                    a2 = dQ[rr];
+                    a += dA[rr];
+                    a2 += dQ[rr];
                 }
             } else {
                 a *= (jj <= ii) ? ex(grow[ii] - grow[jj]) : 0.f;

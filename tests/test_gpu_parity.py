@@ -247,13 +247,58 @@ def test_spikes_straddling_a_tile_boundary(case):
                 g[0, c0 + r] = -40.0
     inp.g = g
     o, S = check(inp, label=label)
-    o_ref, _ = oracle_ref(inp)
+    check_local_scale(inp, o, label)
+
+
+def check_local_scale(inp, o, label, l2n=False, bound=0.05):
+    """Worst o error relative to the largest |o| over the rows t - 8 .. t + 8 of the same head."""
+    o_ref, _ = oracle_ref(inp, l2n=l2n)
     err = np.abs(o.float().cpu().numpy().astype(np.float64) - o_ref).max(axis=-1)
     m = np.abs(o_ref).max(axis=-1)   # [B, T, H]: largest |o| of each row, then over rows t +- 8
     scale = np.stack([m[:, max(0, t - 8):t + 9].max(axis=1) for t in range(m.shape[1])], axis=1) + 1e-30
     worst = float((err / scale).max())
     note(f"[parity] {label}: worst o error relative to the local scale of o {worst:.4f}")
-    assert worst <= 0.05
+    assert worst <= bound
+
+
+# Strong gates in a few key dimensions only: those (tile, dimension) columns take the wide
+# pivots and exact diagonal sums while the rest of the chunk keeps the tile-middle pivots.
+# Strong dimensions draw g = logsigmoid(N(-6, 1)) (about -6 per token, a 16-row tile then
+# spans ~100); "some tiles" makes them strong only in rows 16..47 of each chunk, so a dimension
+# is wide in some row tiles and narrow in others; "spikes" sets single elements to -40 with
+# probability 1/64, which makes a scatter of (tile, dimension) columns wide.
+MIXED = [
+    # label, T, C, l2n, strong dimensions, rows (None: all), spike probability
+    ("kda_C128_one_strong_dim", 512, 128, False, (0,), None, 0.0),
+    ("kda_C128_last_dim_strong", 300, 128, False, (127,), None, 0.0),
+    ("kda_C64_eight_strong_dims_l2n", 448, 64, True, (3, 17, 40, 63, 64, 90, 111, 126), None, 0.0),
+    ("kda_C128_strong_dims_in_some_tiles", 384, 128, False, tuple(range(5, 13)), (16, 48), 0.0),
+    ("kda_C64_strong_dims_in_some_tiles", 320, 64, False, (1, 2, 99), (16, 48), 0.0),
+    ("kda_C128_element_spikes", 512, 128, False, (), None, 1.0 / 64),
+    ("kda_C64_element_spikes_l2n", 400, 64, True, (), None, 1.0 / 64),
+]
+
+
+@pytest.mark.parametrize("case", MIXED, ids=[c[0] for c in MIXED])
+def test_strong_gates_in_some_dimensions(case):
+    label, T, C, l2n, dims, rows, sp = case
+    inp = make_inputs(1, T, 2, seed=480 + T, initial_state=True, chunk_size=C, normalise=not l2n)
+    g = inp.g.clone()
+    gen = torch.Generator().manual_seed(490 + T)
+    if dims:
+        strong = torch.nn.functional.logsigmoid(torch.randn(g.shape[:3] + (len(dims),), generator=gen) - 6.0)
+        for n, d in enumerate(dims):
+            if rows is None:
+                g[..., d] = strong[..., n]
+            else:
+                for c0 in range(0, T, C):
+                    g[:, c0 + rows[0]:min(T, c0 + rows[1]), :, d] = strong[:, c0 + rows[0]:min(T, c0 + rows[1]), :, n]
+    if sp > 0:
+        hit = torch.rand(g.shape, generator=gen) < sp
+        g = torch.where(hit, torch.full_like(g, -40.0), g)
+    inp.g = g
+    o, S = check(inp, label=label, l2n=l2n)
+    check_local_scale(inp, o, label, l2n=l2n)
 
 
 # ---------------------------------------------------------------- invariants of the GPU path
