@@ -1027,7 +1027,7 @@ __global__ __launch_bounds__(BTHREADS) __attribute__((amdgpu_waves_per_eu(4))) v
         const float *Rp = mat(w, ch, RR), *Cp = mat(w, ch, CC), *R2p = mat(w, ch, R2), *C2p = mat(w, ch, C2);
         const float* DA2d = mat(w, ch, DA2);
         const float *DQDp = mat(w, ch, DQD), *DKGp = mat(w, ch, DKG), *DKTp = mat(w, ch, DKT), *DBTp = mat(w, ch, DBT);
-        const float *QDp = mat(w, ch, QD), *KDp = mat(w, ch, KDM), *VFp = mat(w, ch, VF);
+        const float* VFp = mat(w, ch, VF);
         float* DGMp = mat(w, ch, DGM);
         for (int i = wave; i < C; i += BWAVES) {
             const int r = i * 128;
@@ -1039,9 +1039,12 @@ __global__ __launch_bounds__(BTHREADS) __attribute__((amdgpu_waves_per_eu(4))) v
             for (int h = 0; h < 2; ++h) {
                 const int d = lane + 64 * h, e = r + d;
                 const float gm = gam[e], kf = KFp[e], qf = QFp[e], dkt = DKTp[e], dqd = DQDp[e], dkg = DKGp[e];
-                const float rr = Rp[e], cc = Cp[e], r2 = R2p[e], c2 = C2p[e], qd = QDp[e], kd = KDp[e];
+                const float rr = Rp[e], cc = Cp[e], r2 = R2p[e], c2 = C2p[e];
                 const float dbt = DBTp[e], vf = VFp[e];
                 const float eg = ex(gm), egc = ex(sGC[d] - gm);
+                // qd and kd as bwd_prep formed them (the same operations, so the same values),
+                // rather than two more matrices read
+                const float qd = scale * qf * eg, kd = kf * eg;
                 const float dkd = b * dkt;
                 gq[h] = scale * (r2 + a2d * kf) + scale * eg * dqd;
                 gk[h] = rr + cc + scale * (c2 + a2d * qf) + eg * dkd + egc * dkg;
