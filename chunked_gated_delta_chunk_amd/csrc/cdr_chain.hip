@@ -18,7 +18,10 @@
 // so that all value blocks of one (sequence, head) land on the same XCD and share its L2.
 //
 // output_kernel: independent per (chunk, head): o^T = S_entry^T Q^T + U^T on bf16 MFMA, so
-// each lane ends with four consecutive value columns of one token (8-byte stores).
+// each lane ends with four consecutive value columns of one token per value tile; pairs of
+// lanes trade halves of two tiles and store 8 columns (16 bytes) each.  Q and U are read once,
+// with non-temporal loads, so that they do not displace the staged state that the other
+// workgroup of the same (chunk, head) finds in L2.
 #include "cdr_common.h"
 
 namespace cdr {
@@ -198,13 +201,15 @@ __global__ __launch_bounds__(OTHREADS) __attribute__((amdgpu_waves_per_eu(5, 5))
         // a Q fragment is stored half-major: the pi-order operand's two 8-byte halves of a lane
         // are 512 bytes apart
         const uint16_t* fq = ws.Qp + ch * C * KD + frag(it, s, KS);
-        const uint2 a = *reinterpret_cast<const uint2*>(fq + lane * 4), b = *reinterpret_cast<const uint2*>(fq + 256 + lane * 4);
+        const u32x2v a = __builtin_nontemporal_load(reinterpret_cast<const u32x2v*>(fq + lane * 4));
+        const u32x2v b = __builtin_nontemporal_load(reinterpret_cast<const u32x2v*>(fq + 256 + lane * 4));
         qf[s] = make_uint4(a.x, a.y, b.x, b.y);
     }
     f32x4 acc[VTW];
 #pragma unroll
     for (int t = 0; t < VTW; ++t) {
-        const uint2 u = *reinterpret_cast<const uint2*>(ws.Up + ch * C * VD + ((size_t)(it * (VD / 16) + t) * 64 + lane) * 4);
+        const u32x2v u = __builtin_nontemporal_load(
+            reinterpret_cast<const u32x2v*>(ws.Up + ch * C * VD + ((size_t)(it * (VD / 16) + t) * 64 + lane) * 4));
         acc[t] = f32x4{__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u), __uint_as_float(u.y << 16),
                        __uint_as_float(u.y & 0xffff0000u)};
     }
@@ -218,13 +223,21 @@ __global__ __launch_bounds__(OTHREADS) __attribute__((amdgpu_waves_per_eu(5, 5))
             acc[t] = mfma32(a, as_bf16x8(qf[s]), acc[t]);
         }
     // acc[t]: rows v = 16 t + 4 q4 + e, column i = 16 it + r16
+    // lanes q4 and q4 ^ 1 trade halves of value tiles 2p and 2p + 1, so that each lane stores 8
+    // consecutive values (16 bytes): tile 2p's for even q4, tile 2p + 1's for odd q4
     const int i = 16 * it + r16;
-    if (i < rows) {
-        uint16_t* orow = o + ((size_t)(tok0 + i) * H + h) * VD;
+    const bool ev = (q4 & 1) == 0;
+    uint16_t* orow = o + ((size_t)(tok0 + min(i, rows - 1)) * H + h) * VD;
 #pragma unroll
-        for (int t = 0; t < VTW; ++t)
-            *reinterpret_cast<uint2*>(orow + 16 * t + 4 * q4) =
-                make_uint2(pack_bf2(acc[t][0], acc[t][1]), pack_bf2(acc[t][2], acc[t][3]));
+    for (int p = 0; p < VTW / 2; ++p) {
+        const uint2 x0 = make_uint2(pack_bf2(acc[2 * p][0], acc[2 * p][1]), pack_bf2(acc[2 * p][2], acc[2 * p][3]));
+        const uint2 x1 = make_uint2(pack_bf2(acc[2 * p + 1][0], acc[2 * p + 1][1]),
+                                    pack_bf2(acc[2 * p + 1][2], acc[2 * p + 1][3]));
+        const uint2 snd = ev ? x1 : x0;
+        const uint2 rcv = make_uint2((uint32_t)__shfl_xor((int)snd.x, 16, 64), (uint32_t)__shfl_xor((int)snd.y, 16, 64));
+        const uint4 val = ev ? make_uint4(x0.x, x0.y, rcv.x, rcv.y) : make_uint4(rcv.x, rcv.y, x1.x, x1.y);
+        const int col = 32 * p + (ev ? 4 * q4 : 16 + 4 * (q4 - 1));
+        if (i < rows) *reinterpret_cast<uint4*>(orow + col) = val;
     }
 }
 
