@@ -678,10 +678,11 @@ __device__ __forceinline__ void chain_load(ChainOps& op, const Work& w, size_t c
 template <bool REV>
 __device__ __forceinline__ void chain_step(const ChainOps& op, f32x4& S, const Work& w, size_t ch, int x, int lane,
                                            int r16, int q4, int vb, uint16_t* sb) {
-    // record: rows 16 x + 4 q4 + e, column 16 vb + r16 of the [k][v] matrix
+    // record: rows 16 x + 4 q4 + e, column 16 vb + r16 of the [k][v] matrix, past the caches
+    // (bwd_local reads it after both chains; here it would only displace -P and B)
     float* rec = mat(w, ch, REV ? DS : SIN) + (16 * x + 4 * q4) * 128 + 16 * vb + r16;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) rec[e * 128] = S[e];
+    for (int e = 0; e < 4; ++e) __builtin_nontemporal_store(S[e], rec + e * 128);
     // publish: pi-order fragment x / 2 of the B operand, half x % 2
     uint2 sh, sl;
     split_pk(S[0], S[1], sh.x, sl.x);
