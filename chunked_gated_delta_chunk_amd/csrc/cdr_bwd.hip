@@ -1023,7 +1023,8 @@ __global__ __launch_bounds__(BTHREADS) __attribute__((amdgpu_waves_per_eu(4))) v
 
     // ---- per row (a wave per row, two key dimensions per lane): the gradients of the
     // normalised q and k, the part of dgamma the scan below needs, dv, dbeta, and dq, dk (raw,
-    // through the normalisation)
+    // through the normalisation).  The gradients leave with non-temporal stores: nothing here
+    // reads them again, and the matrices this kernel re-reads keep the caches.
     {
         const float *Rp = mat(w, ch, RR), *Cp = mat(w, ch, CC), *R2p = mat(w, ch, R2), *C2p = mat(w, ch, C2);
         const float* DA2d = mat(w, ch, DA2);
@@ -1052,7 +1053,7 @@ __global__ __launch_bounds__(BTHREADS) __attribute__((amdgpu_waves_per_eu(4))) v
                 // dgamma_i without the kg_i dkg_i term: in dg that term and its part of dgamma_C
                 // sum to the prefix over earlier rows (taken in the scan below)
                 DGMp[e] = kf * rr - kf * cc + scale * (qf * r2 - kf * c2) + qd * dqd + kd * dkd;
-                if (i < rows) in.dv[((tok0 + i) * H + hv) * VD + d] = b * dbt;
+                if (i < rows) __builtin_nontemporal_store(b * dbt, in.dv + ((tok0 + i) * H + hv) * VD + d);
                 db += dbt * vf + dkt * kd;
                 qv[h] = qf;
                 kv[h] = kf;
@@ -1082,8 +1083,8 @@ __global__ __launch_bounds__(BTHREADS) __attribute__((amdgpu_waves_per_eu(4))) v
                     xq = rq * (xq - qv[h] * dotq);
                     xk = rk * (xk - kv[h] * dotk);
                 }
-                dqo[lane + 64 * h] = xq;
-                dko[lane + 64 * h] = xk;
+                __builtin_nontemporal_store(xq, dqo + lane + 64 * h);
+                __builtin_nontemporal_store(xk, dko + lane + 64 * h);
             }
         }
     }
@@ -1140,7 +1141,7 @@ __global__ __launch_bounds__(BTHREADS) __attribute__((amdgpu_waves_per_eu(4))) v
             acc += dgm[u];
             const float dgv = acc + kgd[u];
             if (i < rows) {
-                if (PER_DIM) in.dg[((tok0 + i) * H + hv) * KD + d] = dgv;
+                if (PER_DIM) __builtin_nontemporal_store(dgv, in.dg + ((tok0 + i) * H + hv) * KD + d);
                 else DGSp[i * 128 + d] = dgv;
             }
         }
