@@ -1023,8 +1023,9 @@ __global__ __launch_bounds__(BTHREADS) __attribute__((amdgpu_waves_per_eu(4))) v
 
     // ---- per row (a wave per row, two key dimensions per lane): the gradients of the
     // normalised q and k, the part of dgamma the scan below needs, dv, dbeta, and dq, dk (raw,
-    // through the normalisation).  The gradients leave with non-temporal stores: nothing here
-    // reads them again, and the matrices this kernel re-reads keep the caches.
+    // through the normalisation).  The gradients leave with non-temporal stores, and the matrices
+    // read here for the last time come in with non-temporal loads: neither takes cache space
+    // from what the kernel reads again (dkg, the scan's inputs).
     {
         const float *Rp = mat(w, ch, RR), *Cp = mat(w, ch, CC), *R2p = mat(w, ch, R2), *C2p = mat(w, ch, C2);
         const float* DA2d = mat(w, ch, DA2);
@@ -1040,9 +1041,12 @@ __global__ __launch_bounds__(BTHREADS) __attribute__((amdgpu_waves_per_eu(4))) v
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
                 const int d = lane + 64 * h, e = r + d;
-                const float gm = gam[e], kf = KFp[e], qf = QFp[e], dkt = DKTp[e], dqd = DQDp[e], dkg = DKGp[e];
-                const float rr = Rp[e], cc = Cp[e], r2 = R2p[e], c2 = C2p[e];
-                const float dbt = DBTp[e], vf = VFp[e];
+                const float gm = gam[e], kf = __builtin_nontemporal_load(KFp + e), qf = __builtin_nontemporal_load(QFp + e);
+                const float dkt = __builtin_nontemporal_load(DKTp + e), dqd = __builtin_nontemporal_load(DQDp + e);
+                const float dkg = DKGp[e];
+                const float rr = __builtin_nontemporal_load(Rp + e), cc = __builtin_nontemporal_load(Cp + e);
+                const float r2 = __builtin_nontemporal_load(R2p + e), c2 = __builtin_nontemporal_load(C2p + e);
+                const float dbt = __builtin_nontemporal_load(DBTp + e), vf = __builtin_nontemporal_load(VFp + e);
                 const float eg = ex(gm), egc = ex(sGC[d] - gm);
                 // qd and kd as bwd_prep formed them (the same operations, so the same values),
                 // rather than two more matrices read
