@@ -139,6 +139,39 @@ def test_backward_strong_gates(case):
     check(inp, label)
 
 
+# Strong gates in a few key dimensions only (logsigmoid(N(-6,1)) there, about -6 per token), in
+# every row or in rows 16..47 of each chunk, or as scattered single elements set to -40: a tile
+# is then wide through one or a few of its dimensions while the others are narrow, and the
+# gradients of the narrow dimensions must not lose precision to the wide ones.
+MIXED = [
+    # label, T, C, l2n, strong dimensions, rows (None: all), element spike probability
+    ("kda_C128_one_strong_dim", 300, 128, False, (0,), None, 0.0),
+    ("kda_C64_strong_dims_l2n", 260, 64, True, (5, 64, 127), None, 0.0),
+    ("kda_C128_strong_dims_in_some_tiles", 384, 128, False, (3, 70), (16, 48), 0.0),
+    ("kda_C128_element_spikes", 256, 128, False, (), None, 1.0 / 64),
+]
+
+
+@pytest.mark.parametrize("case", MIXED, ids=[c[0] for c in MIXED])
+def test_backward_strong_gates_in_some_dimensions(case):
+    label, T, C, l2n, dims, rows, sp = case
+    inp = make_inputs(1, T, 2, seed=960 + T, initial_state=True, chunk_size=C, normalise=not l2n)
+    g = inp.g.clone()
+    gen = torch.Generator().manual_seed(970 + T)
+    if dims:
+        strong = torch.nn.functional.logsigmoid(torch.randn(g.shape[:3] + (len(dims),), generator=gen) - 6.0)
+        for n, d in enumerate(dims):
+            if rows is None:
+                g[..., d] = strong[..., n]
+            else:
+                for c0 in range(0, T, C):
+                    g[:, c0 + rows[0]:min(T, c0 + rows[1]), :, d] = strong[:, c0 + rows[0]:min(T, c0 + rows[1]), :, n]
+    if sp > 0:
+        g = torch.where(torch.rand(g.shape, generator=gen) < sp, torch.full_like(g, -40.0), g)
+    inp.g = g
+    check(inp, label, l2n=l2n)
+
+
 @pytest.mark.parametrize("case", SMALL, ids=[c[0] for c in SMALL])
 def test_backward_parity(case):
     label, B, T, H, HV, C, per_dim, lengths, init, gm, l2n = case
