@@ -35,7 +35,7 @@ def ratio(x, ref, tol):
 
 
 CASES = [
-    # label, cuts, H, HV, C, per_dim, gate_mean, l2n[, spike probability]
+    # label, cuts, H, HV, C, per_dim, gate_mean, l2n[, spike probability[, strong key dimensions]]
     ("kda_4_segments_C64", [0, 300, 301, 700, 1000], 2, 2, 64, True, 0.0, False),
     ("kda_weak_C128", [0, 256, 640, 900], 1, 2, 128, True, 3.0, True),
     ("gdn_grouped_C64", [0, 128, 500, 512], 1, 2, 64, False, 1.0, False),
@@ -45,6 +45,9 @@ CASES = [
     # isolated g = -40 tokens (1 in 20), with ordinary and with weak gates: wide and narrow tiles
     ("kda_spikes_C64", [0, 200, 450, 700], 2, 2, 64, True, 0.0, False, 0.05),
     ("kda_spikes_weak_C128", [0, 300, 301, 800], 1, 1, 128, True, 3.0, True, 0.02),
+    # weak gates (the maps carry) except in a few key dimensions, which forget fast
+    # (logsigmoid(N(-6,1))): tiles wide in those dimensions only
+    ("kda_weak_strong_dims_C128", [0, 256, 500, 900], 1, 1, 128, True, 3.0, False, 0.0, (0, 77)),
 ]
 
 
@@ -52,10 +55,17 @@ CASES = [
 def test_segments_merge_to_the_unsplit_sequence(case):
     label, cuts, H, HV, C, per_dim, gm, l2n = case[:8]
     spikes = case[8] if len(case) > 8 else 0.0
+    dims = case[9] if len(case) > 9 else ()
     T = cuts[-1]
     inp = make_inputs(1, T, H, seed=600 + T, per_dim_gate=per_dim, initial_state=True, chunk_size=C,
                       gate="zero" if gm is None else "logsigmoid", gate_mean=gm or 0.0, HV=HV,
                       normalise=not l2n, spike_prob=spikes)
+    if dims:
+        g = inp.g.clone()
+        gen = torch.Generator().manual_seed(610 + T)
+        for d in dims:
+            g[..., d] = torch.nn.functional.logsigmoid(torch.randn(g.shape[:3], generator=gen) - 6.0)
+        inp.g = g
     note(f"[cp] {label} T={T} segments {np.diff(cuts).tolist()} C={C}")
     d = inp.to(DEV)
     cu = torch.tensor(cuts, dtype=torch.int32)
