@@ -24,6 +24,8 @@
 // workgroup of the same (chunk, head) finds in L2.
 #include "cdr_common.h"
 
+#include <atomic>
+
 namespace cdr {
 
 constexpr int NXCD = 8;     // MI355X: workgroups are dealt to the 8 XCDs round-robin
@@ -47,7 +49,10 @@ struct ChainOffsets {
     uint32_t p, b, g;
 };
 
-template <bool MAP>
+// BNT: the workgroup's slice of B, read once, comes in with a non-temporal load.  Measured: with
+// more chain workgroups than the device holds at once (packed sequences), 5 % off the forward;
+// with all of them resident, slower (the plain load finds B where the intra kernel left it).
+template <bool MAP, bool BNT>
 __device__ __forceinline__ void chain_load(ChainOps& op, const Work& ws, size_t ch, const ChainOffsets& of) {
     // one descriptor per part, so that every -P load is the lane offset plus an immediate
     const rsrc_t prh = make_rsrc(ws.Pn + ch * 2 * KD * KD, KD * KD * 2);
@@ -57,7 +62,13 @@ __device__ __forceinline__ void chain_load(ChainOps& op, const Work& ws, size_t 
         op.ph[s] = bload16(prh, of.p + 1024u * s);
         op.pl[s] = bload16(prl, of.p + 1024u * s);
     }
-    op.b = MAP ? make_float4(0.f, 0.f, 0.f, 0.f) : bload16f(make_rsrc(ws.Bm + ch * KD * VD, KD * VD * 4), of.b);
+    if (MAP) {
+        op.b = make_float4(0.f, 0.f, 0.f, 0.f);
+    } else {
+        const u32x4v v = __builtin_amdgcn_raw_buffer_load_b128(make_rsrc(ws.Bm + ch * KD * VD, KD * VD * 4), of.b, 0,
+                                                                BNT ? 2 : 0);   // cache policy bit 1: non-temporal
+        op.b = make_float4(__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z), __uint_as_float(v.w));
+    }
     op.gc = bload16f(make_rsrc(ws.gC + ch * KD, KD * 4), of.g);
 }
 
@@ -92,7 +103,7 @@ __device__ __forceinline__ void chain_step(const ChainOps& op, f32x4& S, const W
 // MAP: the chunk maps without their offsets, S <- (exp(gamma_C) - P) S from S = I, which
 // leaves the sequence's linear map (the final state is S_in M + X, X being the final state
 // from a zero start); no chunk-entry states are written.
-template <bool MAP>
+template <bool MAP, bool BNT>
 __global__ __launch_bounds__(CTHREADS) void chain_kernel(ChunkMap map, int H, const float* __restrict__ s0,
                                                           float* __restrict__ s_out, Work ws,
                                                           const int32_t* __restrict__ order) {
@@ -137,12 +148,12 @@ __global__ __launch_bounds__(CTHREADS) void chain_kernel(ChunkMap map, int H, co
     const int last = nchunks - 1;
     auto chunk_of = [&](int c) { return (size_t)(slot0 + max(min(c, last), 0)) * H + h; };
     auto step = [&](ChainOps& next, int cload, const ChainOps& cur, int c, int buf) {
-        chain_load<MAP>(next, ws, chunk_of(cload), of);
+        chain_load<MAP, BNT>(next, ws, chunk_of(cload), of);
         chain_step<MAP>(cur, S, ws, chunk_of(c), x, lane, r16, q4, vb, sbuf[buf]);
     };
     if (nchunks > 0) {
-        chain_load<MAP>(op0, ws, chunk_of(0), of);
-        chain_load<MAP>(op1, ws, chunk_of(1), of);
+        chain_load<MAP, BNT>(op0, ws, chunk_of(0), of);
+        chain_load<MAP, BNT>(op1, ws, chunk_of(1), of);
     }
     for (int c = 0; c < nchunks; c += 6) {
         step(op2, c + 2, op0, c, 0);
@@ -266,12 +277,33 @@ static const int32_t* chain_order(const ChunkMap& map, int N, int32_t* order_ws,
     return order_ws;
 }
 
+// Chain workgroups the current device holds at once (cached per device).
+static int chain_resident() {
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 1 << 30;
+    if (dev >= 0 && dev < 64) {
+        const int c = cache[dev].load(std::memory_order_relaxed);
+        if (c > 0) return c;
+    }
+    int ncu = 0, per_cu = 0;
+    if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, chain_kernel<false, false>, CTHREADS, 0) != hipSuccess)
+        return 1 << 30;
+    const int r = max(1, ncu * per_cu);
+    if (dev >= 0 && dev < 64) cache[dev].store(r, std::memory_order_relaxed);
+    return r;
+}
+
 hipError_t launch_chain(const ChunkMap& map, int N, int H, const float* s0, float* s_out, const Work& ws,
                         int32_t* order_ws, hipStream_t stream) {
     const int groups = (N * H + NXCD - 1) / NXCD;
     const int32_t* order = chain_order(map, N, order_ws, stream);
-    hipLaunchKernelGGL(chain_kernel<false>, dim3(groups * NXCD * NVB), dim3(CTHREADS), 0, stream, map, H,
-                       s0, s_out, ws, order);
+    const int nwg = groups * NXCD * NVB;
+    if (nwg > chain_resident())
+        hipLaunchKernelGGL((chain_kernel<false, true>), dim3(nwg), dim3(CTHREADS), 0, stream, map, H, s0, s_out, ws, order);
+    else
+        hipLaunchKernelGGL((chain_kernel<false, false>), dim3(nwg), dim3(CTHREADS), 0, stream, map, H, s0, s_out, ws, order);
     return hipGetLastError();
 }
 
@@ -279,7 +311,7 @@ hipError_t launch_chain_map(const ChunkMap& map, int N, int H, float* m_out, con
                             hipStream_t stream) {
     const int groups = (N * H + NXCD - 1) / NXCD;
     const int32_t* order = chain_order(map, N, order_ws, stream);
-    hipLaunchKernelGGL(chain_kernel<true>, dim3(groups * NXCD * NVB), dim3(CTHREADS), 0, stream, map, H,
+    hipLaunchKernelGGL((chain_kernel<true, false>), dim3(groups * NXCD * NVB), dim3(CTHREADS), 0, stream, map, H,
                        (const float*)nullptr, m_out, ws, order);
     return hipGetLastError();
 }
