@@ -124,6 +124,53 @@ def test_forward_sweep_harsh_gates(case):
     assert row <= 0.05
 
 
+def dimension_gates(g, seed):
+    """Per-dimension gate patterns on a per-dimension gate tensor [B, T, H, K]: a random set of 1 to 16
+    key dimensions made strong (logsigmoid(N(m, 1)), m from -4 to -10), in all rows or in one
+    random row range, and optionally scattered single elements set to -40."""
+    rng = random.Random(seed)
+    gen = torch.Generator().manual_seed(seed)
+    g = g.clone()
+    B, T, H, K = g.shape
+    dims = rng.sample(range(K), rng.choice([1, 2, 4, 16]))
+    m = rng.choice([-4.0, -6.0, -10.0])
+    r0, r1 = (0, T) if rng.random() < 0.5 else sorted(rng.sample(range(T + 1), 2))
+    strong = torch.nn.functional.logsigmoid(torch.randn(B, T, H, len(dims), generator=gen) + m)
+    for n, d in enumerate(dims):
+        g[:, r0:r1, :, d] = strong[:, r0:r1, :, n]
+    sp = rng.choice([0.0, 1.0 / 256, 1.0 / 32])
+    if sp > 0:
+        g = torch.where(torch.rand(g.shape, generator=gen) < sp, torch.full_like(g, -40.0), g)
+    return g, dict(dims=len(dims), mean=m, rows=(r0, r1), spikes=sp)
+
+
+@pytest.mark.parametrize("case", range(16))
+def test_forward_sweep_dimension_gates(case):
+    """Strong gates in some key dimensions only: (tile, dimension) columns take the wide pivots
+    and exact diagonal sums beside narrow ones in the same tiles."""
+    c = draw(9500 + case, max_T=600, max_heads=4)
+    inp = make_inputs(c["B"], c["T"], c["H"], seed=9600 + case, per_dim_gate=True, lengths=c["lengths"],
+                      initial_state=c["init"], chunk_size=c["C"], gate_mean=c["gate_mean"], HV=c["HV"],
+                      normalise=not c["l2n"])
+    inp.g, pat = dimension_gates(inp.g, 9700 + case)
+    print(f"[sweep dims {case}] {c} {pat}", file=sys.stderr, flush=True)
+    d = inp.to(DEV)
+    o, S = cdr.chunk_dr_fwd(d.q, d.k, d.v, d.g, d.beta, initial_state=d.initial_state, cu_seqlens=d.cu_seqlens,
+                            chunk_size=c["C"], output_final_state=True, use_qk_l2norm_in_kernel=c["l2n"])
+    torch.cuda.synchronize()
+    assert torch.isfinite(o.float()).all() and torch.isfinite(S).all()
+    o_ref, S_ref = oracle.recurrent_fwd(inp.q, inp.k, inp.v, inp.g, inp.beta, initial_state=inp.initial_state,
+                                        cu_seqlens=inp.cu_seqlens, use_qk_l2norm=c["l2n"])
+    og = o.float().cpu().numpy().astype(np.float64)
+    ro = ratio(og, o_ref, O_TOL)
+    rs = ratio(S.cpu().numpy(), S_ref, S_TOL)
+    row = (np.abs(og - o_ref).max(axis=-1) / local_scale(o_ref)).max()
+    print(f"[sweep dims {case}] o err/tol {ro:.3f}  S err/tol {rs:.3f}  o row error / local scale {row:.4f}",
+          file=sys.stderr, flush=True)
+    assert ro <= 1.0 and rs <= 1.0
+    assert row <= 0.05
+
+
 @pytest.mark.parametrize("case", range(20))
 def test_backward_sweep(case):
     """Cases 0-9 draw like the forward sweep, 10-19 with the harsh gates."""
